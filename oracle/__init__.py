@@ -1,0 +1,231 @@
+"""CPU oracle of the DSpark sequential Markov draft-sampling step.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the library under
+``markov_draft_sampling_step_amd`` never does. It wraps ``markov_oracle.c``
+(plain C, built with contraction and fast-math off) through ctypes; arrays
+are numpy, bf16 travels as ``uint16`` bit patterns.
+
+``brute`` holds a second, independent statement of the same definition in
+pure Python (exact rationals, mpmath logs) for tiny vocabularies.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "markov_oracle.c")
+LIBRARY = os.path.join(HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``liboracle.so`` next to its source with gcc (no fast-math,
+    no contraction, OpenMP for row-parallel runs)."""
+    cmd = [
+        "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+        "-shared", "-o", LIBRARY + ".tmp", SOURCE, "-lm",
+    ]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    os.replace(LIBRARY + ".tmp", LIBRARY)
+    return LIBRARY
+
+
+_P = ctypes.c_void_p
+_I32, _I64, _U32, _F32, _F64 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                                ctypes.c_float, ctypes.c_double)
+_SIGS = {
+    "oracle_bf16_to_f32": (_F32, [ctypes.c_uint16]),
+    "oracle_bf16_round": (ctypes.c_uint16, [_F32]),
+    "oracle_ulp32": (_F64, [_F32]),
+    "oracle_ulp_bf16": (_F64, [_F32]),
+    "oracle_logf_cr": (_F32, [_F32]),
+    "oracle_tanhf_cr": (_F32, [_F32]),
+    "oracle_murmur3_x86_32": (_U32, [_P, ctypes.c_uint64, _U32]),
+    "oracle_noise_hash": (_U32, [_I64, _I32, _I64, _U32]),
+    "oracle_uniform": (_F32, [_U32]),
+    "oracle_log1m": (_F32, [_F32]),
+    "oracle_noisy": (ctypes.c_int, [_F32]),
+    "oracle_gumbel_key": (_F32, [_F32, _F32, _U32, _P, _P]),
+    "oracle_bias": (ctypes.c_uint16, [_P, _P, _I32, _P, _P]),
+    "oracle_cache_value": (ctypes.c_uint16, [ctypes.c_uint16, ctypes.c_uint16, _F32, _F32]),
+    "oracle_before": (ctypes.c_int, [_F32, _I64, _F32, _I64]),
+    "oracle_argmax": (_I64, [_P, _I64]),
+    "oracle_w1_row": (_I64, [_I64, _I32]),
+    "oracle_step": (None, [_I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _I64, _I32, _P,
+                           _F32, _F32, _P, _I64, _P, _I64, _P, _I64, _P, _I32]),
+    "oracle_sample_sequential": (None, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                        _F32, _F32, _P, _P, _I32]),
+    "oracle_decided": (ctypes.c_int, [_I32, _P, _P, _F32, _I64, _I32, _I64, _I32, _P]),
+    "oracle_log_hard_cases": (_I64, [_F32, _F32, _F64, _P, _I64]),
+}
+
+
+def lib():
+    """The loaded oracle library (built on first use if absent)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        handle = ctypes.CDLL(LIBRARY)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# -- scalar pieces -----------------------------------------------------------
+
+def bf16_to_f32(b: int) -> float:
+    return lib().oracle_bf16_to_f32(int(b))
+
+
+def bf16_round(x: float) -> int:
+    return int(lib().oracle_bf16_round(float(x)))
+
+
+def murmur3_x86_32(data: bytes, seed: int = 0) -> int:
+    buf = np.frombuffer(bytes(data) + b"\0", dtype=np.uint8)
+    return int(lib().oracle_murmur3_x86_32(_ptr(buf), len(data), seed & 0xFFFFFFFF))
+
+
+def noise_hash(seed: int, step: int, position: int, token: int) -> int:
+    return int(lib().oracle_noise_hash(int(seed), int(step), int(position), int(token)))
+
+
+def uniform(h: int) -> float:
+    return lib().oracle_uniform(int(h) & 0xFFFFFFFF)
+
+
+def log1m(u: float) -> float:
+    return lib().oracle_log1m(float(u))
+
+
+def logf_cr(x: float) -> float:
+    return lib().oracle_logf_cr(float(x))
+
+
+def tanhf_cr(x: float) -> float:
+    return lib().oracle_tanhf_cr(float(x))
+
+
+def gumbel_key(l: float, T: float, h: int) -> float:
+    return lib().oracle_gumbel_key(float(l), float(T), int(h) & 0xFFFFFFFF, None, None)
+
+
+def bias(e: np.ndarray, w: np.ndarray) -> tuple[int, float, float]:
+    """(bf16 bias, binary64 sum, sum of |products|) of two bf16 rows."""
+    e = np.ascontiguousarray(e, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    s64, sabs = ctypes.c_double(), ctypes.c_double()
+    b = lib().oracle_bias(_ptr(e), _ptr(w), len(e), ctypes.byref(s64), ctypes.byref(sabs))
+    return int(b), s64.value, sabs.value
+
+
+def cache_value(base: int, bias_bits: int, mult: float, softcap: float) -> int:
+    return int(lib().oracle_cache_value(int(base), int(bias_bits), float(mult), float(softcap)))
+
+
+def before(v1: float, i1: int, v2: float, i2: int) -> bool:
+    return bool(lib().oracle_before(float(v1), int(i1), float(v2), int(i2)))
+
+
+def argmax(keys: np.ndarray) -> int:
+    keys = np.ascontiguousarray(keys, dtype=np.float32)
+    return int(lib().oracle_argmax(_ptr(keys), len(keys)))
+
+
+def w1_row(token: int, V: int) -> int:
+    return int(lib().oracle_w1_row(int(token), int(V)))
+
+
+# -- whole steps -----------------------------------------------------------
+
+def step(base_step: np.ndarray, w1: np.ndarray, w2: np.ndarray, prev: np.ndarray,
+         seeds: np.ndarray, positions_step: np.ndarray, step_index: int,
+         temperature: np.ndarray, mult: float = 1.0, softcap: float = 0.0,
+         want_keys: bool = False, want_bias: bool = False, threads: int = 1):
+    """One teacher-forced draft step for every row.
+
+    base_step: bf16 bits [rows, V] of this step; positions_step: [rows].
+    Returns dict(cache [rows,V] u16, tokens [rows] i64, keys?, bias?).
+    """
+    rows, V = base_step.shape
+    R = w1.shape[1]
+    base_step = np.ascontiguousarray(base_step, dtype=np.uint16)
+    w1 = np.ascontiguousarray(w1, dtype=np.uint16)
+    w2 = np.ascontiguousarray(w2, dtype=np.uint16)
+    prev = np.ascontiguousarray(prev, dtype=np.int64)
+    seeds = np.ascontiguousarray(seeds, dtype=np.int64)
+    pos = np.ascontiguousarray(positions_step, dtype=np.int64)
+    temp = np.ascontiguousarray(temperature, dtype=np.float32)
+    cache = np.empty((rows, V), dtype=np.uint16)
+    tokens = np.empty(rows, dtype=np.int64)
+    keys = np.empty((rows, V), dtype=np.float32) if want_keys else None
+    bias_out = np.empty((rows, V), dtype=np.uint16) if want_bias else None
+    lib().oracle_step(rows, V, R, _ptr(base_step), V, _ptr(w1), _ptr(w2), _ptr(prev),
+                      _ptr(seeds), _ptr(pos), 1, int(step_index), _ptr(temp), float(mult),
+                      float(softcap), _ptr(cache), V, _ptr(keys), V, _ptr(bias_out), V,
+                      _ptr(tokens), int(threads))
+    out = {"cache": cache, "tokens": tokens}
+    if want_keys:
+        out["keys"] = keys
+    if want_bias:
+        out["bias"] = bias_out
+    return out
+
+
+def sample_sequential(base: np.ndarray, w1: np.ndarray, w2: np.ndarray, prev: np.ndarray,
+                      seeds: np.ndarray, positions: np.ndarray, temperature: np.ndarray,
+                      mult: float = 1.0, softcap: float = 0.0, threads: int = 1):
+    """The k-step loop. base: bf16 bits [rows, k, V]; positions [rows, k].
+    Returns (cache [rows,k,V] u16, tokens [rows,k] i64)."""
+    rows, k, V = base.shape
+    R = w1.shape[1]
+    base = np.ascontiguousarray(base, dtype=np.uint16)
+    w1 = np.ascontiguousarray(w1, dtype=np.uint16)
+    w2 = np.ascontiguousarray(w2, dtype=np.uint16)
+    prev = np.ascontiguousarray(prev, dtype=np.int64)
+    seeds = np.ascontiguousarray(seeds, dtype=np.int64)
+    positions = np.ascontiguousarray(positions, dtype=np.int64)
+    temp = np.ascontiguousarray(temperature, dtype=np.float32)
+    cache = np.empty((rows, k, V), dtype=np.uint16)
+    tokens = np.empty((rows, k), dtype=np.int64)
+    lib().oracle_sample_sequential(rows, V, R, k, _ptr(base), _ptr(w1), _ptr(w2), _ptr(prev),
+                                   _ptr(seeds), _ptr(positions), _ptr(temp), float(mult),
+                                   float(softcap), _ptr(cache), _ptr(tokens), int(threads))
+    return cache, tokens
+
+
+def decided(cache_o_row: np.ndarray, cache_g_row: np.ndarray, T: float, seed: int,
+            step_index: int, position: int, literal: bool = False) -> tuple[bool, int]:
+    """(decided?, oracle winner) of one row-step; see ``oracle_decided``."""
+    co = np.ascontiguousarray(cache_o_row, dtype=np.uint16)
+    cg = np.ascontiguousarray(cache_g_row, dtype=np.uint16)
+    w = ctypes.c_int64()
+    ok = lib().oracle_decided(len(co), _ptr(co), _ptr(cg), float(T), int(seed), int(step_index),
+                              int(position), 1 if literal else 0, ctypes.byref(w))
+    return bool(ok), int(w.value)
+
+
+def log_hard_cases(lo: float, hi: float, ulps: float = 1.0, cap: int = 4096):
+    out = np.zeros(cap, dtype=np.float32)
+    n = int(lib().oracle_log_hard_cases(float(lo), float(hi), float(ulps), _ptr(out), cap))
+    return n, out[: min(n, cap)].copy()

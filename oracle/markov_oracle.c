@@ -1,0 +1,529 @@
+/*
+ * Oracle for the DSpark sequential Markov draft-sampling step.
+ *
+ * TEST INFRASTRUCTURE ONLY. This is a plain, slow, obviously-correct CPU
+ * statement of what one draft step computes. Only the tests, the smoke check
+ * and the CPU-baseline leg of the benchmark may load it. It shares no code,
+ * header, table or helper with the HIP library; the two meet only through
+ * the seeded inputs the tests hand to both.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
+ * Contraction is off so every float expression below rounds exactly where it
+ * is written; x86-64 evaluates float in SSE (no excess precision).
+ *
+ * Sources (the pages this follows; sections named, not line-numbered):
+ *   [KIMI]  vLLM API page "vllm.models.kimi_k3.nvidia.specialized_decode.
+ *           drafter.markov": module docstring (exactness paragraph),
+ *           `_gumbel_key`, `_gumbel_log_arg32`, `_loop_rest`.
+ *   [MUSE]  vLLM API page "vllm.models.muse_spark.nvidia.specialized_decode.
+ *           cutedsl.draft.markov": module docstring, `_StepKernel.kernel`,
+ *           `_logit`, `_gumbel`, `_murmur_prefix`, `_nonzero_f32`,
+ *           `_combine`, `_w1_row`.
+ *   [DSV41] vLLM API page "vllm.models.deepseek_v41.amd.ops.fused_markov":
+ *           module docstring, `_loop_rest`.
+ *
+ * Readings taken where the pages leave a step open (each repeated at its
+ * function):
+ *   - the block step of MurmurHash3_x86_32 is not printed; the public
+ *     MurmurHash3_x86_32 definition is used (its finaliser constants are the
+ *     ones [MUSE] `_gumbel` prints);
+ *   - logs and tanh are the correctly rounded binary32 values (the pages'
+ *     own libdevice routines are NVIDIA code and are not reproduced);
+ *   - the division logit / temperature is IEEE round-to-nearest;
+ *   - the bias sum is taken in index order j = 0..R-1 in binary32 (the pages
+ *     leave the order free);
+ *   - parity with vLLM's own draws is unpinned: no page prints a value.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define EXPORT __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+static float bits_to_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f32_to_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* bf16 -> binary32 is exact: the bf16 pattern is the high half of the float. */
+EXPORT float oracle_bf16_to_f32(uint16_t b) { return bits_to_f32((uint32_t)b << 16); }
+
+/*
+ * binary32 -> bf16, round to nearest, ties to even, as the pages' conversions
+ * do ([MUSE] `_logit`: the cache value is a round-to-nearest bf16 of the
+ * transformed logit). Written from the definition: take the two bf16 values
+ * that bracket x (truncation toward zero, and one bf16 ulp further from
+ * zero), and keep the nearer one; on an exact tie keep the one with an even
+ * last bit. Distances are computed in binary64, where they are exact (both
+ * operands carry at most 24 significant bits within a factor of 2).
+ * Overflow follows IEEE: the value one ulp past the largest finite bf16 is
+ * 2^128, and it rounds to infinity. NaN stays NaN (quiet, same sign).
+ */
+EXPORT uint16_t oracle_bf16_round(float x) {
+  uint32_t u = f32_to_bits(x);
+  if (isnan(x)) return (uint16_t)((u >> 16) | 0x0040u);
+  if (isinf(x)) return (uint16_t)(u >> 16);
+  uint16_t lo = (uint16_t)(u >> 16);            /* toward zero */
+  uint16_t hi = (uint16_t)(lo + 1u);            /* away from zero */
+  double dx = fabs((double)x);
+  double dlo = fabs((double)oracle_bf16_to_f32(lo));
+  double dhi;
+  if ((hi & 0x7fffu) == 0x7f80u)
+    dhi = ldexp(1.0, 128);                      /* one ulp past the top */
+  else
+    dhi = fabs((double)oracle_bf16_to_f32(hi));
+  double below = dx - dlo, above = dhi - dx;
+  if (below < above) return lo;
+  if (above < below) return hi;
+  return (lo & 1u) ? hi : lo;
+}
+
+/* Unit in the last place of a binary32 magnitude (the gap above |x|). */
+EXPORT double oracle_ulp32(float x) {
+  float a = fabsf(x);
+  if (isnan(a) || isinf(a)) return INFINITY;
+  return (double)nextafterf(a, INFINITY) - (double)a;
+}
+
+/* Unit in the last place of a bf16 magnitude. */
+EXPORT double oracle_ulp_bf16(float x) {
+  float a = fabsf(x);
+  if (isnan(a) || isinf(a)) return INFINITY;
+  uint16_t b = oracle_bf16_round(a);
+  float v = oracle_bf16_to_f32(b);
+  if (v > a) { b = (uint16_t)(b - 1u); v = oracle_bf16_to_f32(b); }
+  uint16_t n = (uint16_t)(b + 1u);
+  double vn = ((n & 0x7fffu) == 0x7f80u) ? ldexp(1.0, 128) : (double)oracle_bf16_to_f32(n);
+  return vn - (double)v;
+}
+
+/*
+ * Correctly rounded binary32 log and tanh (see the readings above). The
+ * binary64 library value, good to under one binary64 ulp, rounds to the
+ * right binary32 unless it lies within a few binary64 ulps of a binary32
+ * rounding midpoint; there (two inputs on the step's whole log domain) the
+ * 64-bit-significand long double routine decides the rounding.
+ */
+static int near_midpoint(double y) {
+  float f = (float)y;
+  if (isnan(f) || isinf(f)) return 0;
+  double fd = (double)f;
+  double up = (double)nextafterf(f, INFINITY), dn = (double)nextafterf(f, -INFINITY);
+  double tol = 8.0 * (nextafter(fabs(y), INFINITY) - fabs(y));
+  return fabs(y - 0.5 * (fd + up)) <= tol || fabs(y - 0.5 * (fd + dn)) <= tol;
+}
+EXPORT float oracle_logf_cr(float x) {
+  double y = log((double)x);
+  if (near_midpoint(y)) return (float)logl((long double)x);
+  return (float)y;
+}
+EXPORT float oracle_tanhf_cr(float x) {
+  double y = tanh((double)x);
+  if (near_midpoint(y)) return (float)tanhl((long double)x);
+  return (float)y;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Noise: MurmurHash3 of (seed, step, position, token id)                    */
+/* ------------------------------------------------------------------------ */
+
+static uint32_t rotl32(uint32_t x, int r) { return (x << r) | (x >> (32 - r)); }
+
+/*
+ * MurmurHash3_x86_32 of `len` bytes, written from its public definition:
+ * 4-byte little-endian blocks, each scrambled (x c1, rotl 15, x c2), xored
+ * into the state, which is rotated left 13 and advanced as h*5 + 0xe6546b64;
+ * then the 1-3 tail bytes; then h ^= len and the fmix32 finaliser (the two
+ * finaliser multipliers 0x85ebca6b and 0xc2b2ae35 are the ones [MUSE]
+ * `_gumbel` prints as signed decimals).
+ */
+EXPORT uint32_t oracle_murmur3_x86_32(const uint8_t* data, uint64_t len, uint32_t seed) {
+  const uint32_t c1 = 0xcc9e2d51u, c2 = 0x1b873593u;
+  uint32_t h = seed;
+  uint64_t nblocks = len / 4;
+  for (uint64_t i = 0; i < nblocks; ++i) {
+    const uint8_t* p = data + 4 * i;
+    uint32_t k = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) |
+                 ((uint32_t)p[3] << 24);
+    k *= c1;
+    k = rotl32(k, 15);
+    k *= c2;
+    h ^= k;
+    h = rotl32(h, 13);
+    h = h * 5u + 0xe6546b64u;
+  }
+  const uint8_t* tail = data + 4 * nblocks;
+  uint32_t k = 0;
+  switch (len & 3u) {
+    case 3: k ^= (uint32_t)tail[2] << 16; /* fall through */
+    case 2: k ^= (uint32_t)tail[1] << 8;  /* fall through */
+    case 1:
+      k ^= (uint32_t)tail[0];
+      k *= c1;
+      k = rotl32(k, 15);
+      k *= c2;
+      h ^= k;
+  }
+  h ^= (uint32_t)len;
+  h ^= h >> 16;
+  h *= 0x85ebca6bu;
+  h ^= h >> 13;
+  h *= 0xc2b2ae35u;
+  h ^= h >> 16;
+  return h;
+}
+
+/*
+ * The hash behind one token's noise ([MUSE] `_StepKernel.kernel` and
+ * `_murmur_prefix`; [KIMI] exactness paragraph): four little-endian words,
+ *   lo32(S), hi32(S), lo32(P), token id,   hashed with seed 0, where
+ *   S = seed XOR (step << 32)        (the step seed, step = 0-based draft step)
+ *   P = (position - 1) + 2^30        (the position before the sampled token
+ *                                     plus the draft salt)
+ * `position` is the sample position of this row at this step.
+ */
+EXPORT uint32_t oracle_noise_hash(int64_t seed, int32_t step, int64_t position, uint32_t token) {
+  uint64_t S = (uint64_t)seed ^ ((uint64_t)(uint32_t)step << 32);
+  int64_t P = (position - 1) + ((int64_t)1 << 30);
+  uint32_t words[4] = {(uint32_t)(S & 0xffffffffu), (uint32_t)(S >> 32),
+                       (uint32_t)((uint64_t)P & 0xffffffffu), token};
+  uint8_t bytes[16];
+  for (int w = 0; w < 4; ++w)
+    for (int b = 0; b < 4; ++b) bytes[4 * w + b] = (uint8_t)(words[w] >> (8 * b));
+  return oracle_murmur3_x86_32(bytes, 16, 0u);
+}
+
+/*
+ * The hash's uniform ([MUSE] `_gumbel`): u = RN32((h + 1/2) * 2^-32), one
+ * rounding. (h + 1/2) * 2^-32 is exact in binary64, so the only rounding is
+ * the conversion to binary32. h = 0 gives 2^-33; the top 128 hash values give
+ * exactly 1.0.
+ */
+EXPORT float oracle_uniform(uint32_t h) { return (float)(((double)h + 0.5) * 0x1p-32); }
+
+/*
+ * L = log(1 - u), the stable form the pages use ([MUSE] `_gumbel`; [KIMI]
+ * `_gumbel_key` calls it `_log1p_neg_stable`). For u < 1/4 (strict): the
+ * Taylor series -(u + u^2/2 + ... + u^8/8), evaluated in binary32 as a Horner
+ * chain of fused multiply-adds over the coefficients RN32(1/k), k = 8..1,
+ * then one multiply by -u. Otherwise log(max(RN32(1 - u), 2^-24)).
+ */
+EXPORT float oracle_log1m(float u) {
+  if (u < 0.25f) {
+    const float coef[7] = {(float)(1.0 / 7.0), (float)(1.0 / 6.0), (float)(1.0 / 5.0), 0.25f,
+                           (float)(1.0 / 3.0), 0.5f, 1.0f};
+    float p = 0.125f;
+    for (int i = 0; i < 7; ++i) p = fmaf(u, p, coef[i]);
+    return p * (-u);
+  }
+  float om = 1.0f - u;
+  float x = om > 0x1p-24f ? om : 0x1p-24f;
+  return oracle_logf_cr(x);
+}
+
+/*
+ * Whether a row's temperature makes it noisy: T != 0 by an ordered compare
+ * ([MUSE] `_nonzero_f32`). NaN is noisy; -0.0 is not.
+ */
+EXPORT int oracle_noisy(float T) { return !(T == 0.0f); }
+
+/*
+ * The sampling key of a cached logit l ([KIMI] `_gumbel_key`, [MUSE]
+ * `_gumbel`): at a noisy temperature, RN32(RN32(l / T) - log(-L)) where
+ * L = log1m(u(h)); at T = 0 the plain logit. The noise -log(-L) is never
+ * rounded separately: the subtraction of the rounded log is the one step
+ * ([KIMI] `_gumbel_log_arg32` explains why a stored noise would differ).
+ * `lb_out` / `L_out` (optional) receive the two log values.
+ */
+EXPORT float oracle_gumbel_key(float l, float T, uint32_t h, float* lb_out, float* L_out) {
+  if (!oracle_noisy(T)) {
+    if (lb_out) *lb_out = 0.0f;
+    if (L_out) *L_out = 0.0f;
+    return l;
+  }
+  float u = oracle_uniform(h);
+  float L = oracle_log1m(u);
+  float lb = oracle_logf_cr(-L);
+  float q = l / T;
+  if (lb_out) *lb_out = lb;
+  if (L_out) *L_out = L;
+  return q - lb;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Logits                                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The Markov bias of one (row, token): the binary32 dot product of the
+ * row's embedding and the token's w2 row, rounded once to bf16 ([KIMI]
+ * exactness paragraph; [DSV41] module docstring). Products of two bf16 are
+ * exact in binary32; the sum runs j = 0..R-1. `s64` (optional) gets the sum
+ * in binary64 and `sabs` the sum of |products|, for the order-free bound.
+ */
+EXPORT uint16_t oracle_bias(const uint16_t* e, const uint16_t* w, int32_t R, double* s64,
+                            double* sabs) {
+  float acc = 0.0f;
+  double d = 0.0, a = 0.0;
+  for (int32_t j = 0; j < R; ++j) {
+    float p = oracle_bf16_to_f32(e[j]) * oracle_bf16_to_f32(w[j]);
+    acc = acc + p;
+    d += (double)p;
+    a += fabs((double)p);
+  }
+  if (s64) *s64 = d;
+  if (sabs) *sabs = a;
+  return oracle_bf16_round(acc);
+}
+
+/*
+ * The cached logit ([MUSE] `_logit`, module docstring): the bf16 add of base
+ * and bias (one binary32 add rounded to bf16, [KIMI] exactness paragraph),
+ * times the multiplier, then with a soft cap cap * tanh(y * RN32(1/cap)),
+ * rounded to bf16. softcap <= 0 means no cap.
+ */
+EXPORT uint16_t oracle_cache_value(uint16_t base, uint16_t bias, float mult, float softcap) {
+  float x = oracle_bf16_to_f32(oracle_bf16_round(oracle_bf16_to_f32(base) + oracle_bf16_to_f32(bias)));
+  float y = mult * x;
+  float w = y;
+  if (softcap > 0.0f) {
+    float inv_cap = 1.0f / softcap;
+    float z = y * inv_cap;
+    w = softcap * oracle_tanhf_cr(z);
+  }
+  return oracle_bf16_round(w);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Argmax under the total order                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Whether (v1, i1) comes before (v2, i2) in the order every argmax of the
+ * method uses ([MUSE] module docstring and `_combine`): a NaN value beats
+ * every non-NaN value; among NaNs the lower id wins; otherwise the larger
+ * value wins, and equal values (IEEE ==, so -0 == +0) go to the lower id.
+ */
+EXPORT int oracle_before(float v1, int64_t i1, float v2, int64_t i2) {
+  int n1 = isnan(v1), n2 = isnan(v2);
+  if (n1 || n2) {
+    if (n1 && n2) return i1 < i2;
+    return n1;
+  }
+  if (v1 > v2) return 1;
+  if (v1 < v2) return 0;
+  return i1 < i2;
+}
+
+/* Argmax of keys[0..n) under that order, scanning ids upward. */
+EXPORT int64_t oracle_argmax(const float* keys, int64_t n) {
+  int64_t best = 0;
+  for (int64_t v = 1; v < n; ++v)
+    if (oracle_before(keys[v], v, keys[best], best)) best = v;
+  return best;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One draft step and the k-step loop                                        */
+/* ------------------------------------------------------------------------ */
+
+/* The w1 row of a token: clamped to V-1 as an unsigned value ([MUSE] `_w1_row`). */
+EXPORT int64_t oracle_w1_row(int64_t token, int32_t V) {
+  uint64_t t = (uint64_t)token, last = (uint64_t)(V - 1);
+  return (int64_t)(t < last ? t : last);
+}
+
+/*
+ * One draft step for every row, teacher-forced from `prev` (the token that
+ * feeds this step). Follows one iteration of the eager loop ([KIMI] and
+ * [DSV41] `_loop_rest`): embed the previous token, form the bias over the
+ * whole vocabulary, add the base logits, transform and cache, then sample.
+ *   base       bf16, row r of this step at base + r*base_rs, V entries
+ *   w1, w2     bf16 [V, R] row-major
+ *   prev       [rows] token feeding this step
+ *   seeds      [rows]; positions: row r's sample position at positions[r*pos_rs]
+ *   temperature[rows] binary32
+ *   cache      out, bf16, row r at cache + r*cache_rs
+ *   keys       out (may be NULL), binary32 [rows, V] at keys + r*keys_rs
+ *   bias       out (may be NULL), bf16 [rows, V] at bias + r*bias_rs
+ *   tokens     out [rows]
+ * threads > 1 runs rows in parallel (rows are independent).
+ */
+EXPORT void oracle_step(int32_t rows, int32_t V, int32_t R, const uint16_t* base, int64_t base_rs,
+                        const uint16_t* w1, const uint16_t* w2, const int64_t* prev,
+                        const int64_t* seeds, const int64_t* positions, int64_t pos_rs,
+                        int32_t step, const float* temperature, float mult, float softcap,
+                        uint16_t* cache, int64_t cache_rs, float* keys, int64_t keys_rs,
+                        uint16_t* bias, int64_t bias_rs, int64_t* tokens, int32_t threads) {
+#ifdef _OPENMP
+  int nt = threads > 0 ? threads : 1;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+#endif
+  for (int32_t r = 0; r < rows; ++r) {
+    const uint16_t* e = w1 + (size_t)oracle_w1_row(prev[r], V) * (size_t)R;
+    float T = temperature[r];
+    int64_t position = positions[(int64_t)r * pos_rs];
+    int64_t best = -1;
+    float best_key = 0.0f;
+    for (int32_t v = 0; v < V; ++v) {
+      uint16_t b = oracle_bias(e, w2 + (size_t)v * (size_t)R, R, NULL, NULL);
+      uint16_t c = oracle_cache_value(base[(int64_t)r * base_rs + v], b, mult, softcap);
+      cache[(int64_t)r * cache_rs + v] = c;
+      if (bias) bias[(int64_t)r * bias_rs + v] = b;
+      float l = oracle_bf16_to_f32(c);
+      uint32_t h = oracle_noisy(T) ? oracle_noise_hash(seeds[r], step, position, (uint32_t)v) : 0u;
+      float key = oracle_gumbel_key(l, T, h, NULL, NULL);
+      if (keys) keys[(int64_t)r * keys_rs + v] = key;
+      if (best < 0 || oracle_before(key, v, best_key, best)) {
+        best = v;
+        best_key = key;
+      }
+    }
+    tokens[r] = best;
+  }
+}
+
+/*
+ * The k-step loop ([KIMI] `_loop_rest`): step s feeds on prev (s = 0) or on
+ * the token step s-1 sampled. Layouts as the library's entry point:
+ *   base, cache  bf16 [rows, k, V] contiguous
+ *   positions    [rows, k];  tokens out [rows, k]
+ */
+EXPORT void oracle_sample_sequential(int32_t rows, int32_t V, int32_t R, int32_t k,
+                                     const uint16_t* base, const uint16_t* w1,
+                                     const uint16_t* w2, const int64_t* prev,
+                                     const int64_t* seeds, const int64_t* positions,
+                                     const float* temperature, float mult, float softcap,
+                                     uint16_t* cache, int64_t* tokens, int32_t threads) {
+  int64_t* feed = (int64_t*)malloc(sizeof(int64_t) * (size_t)(rows > 0 ? rows : 1));
+  int64_t* out = (int64_t*)malloc(sizeof(int64_t) * (size_t)(rows > 0 ? rows : 1));
+  for (int32_t r = 0; r < rows; ++r) feed[r] = prev[r];
+  int64_t row_stride = (int64_t)k * V;
+  for (int32_t s = 0; s < k; ++s) {
+    oracle_step(rows, V, R, base + (int64_t)s * V, row_stride, w1, w2, feed, seeds, positions + s,
+                k, s, temperature, mult, softcap, cache + (int64_t)s * V, row_stride, NULL, 0,
+                NULL, 0, out, threads);
+    for (int32_t r = 0; r < rows; ++r) {
+      tokens[(int64_t)r * k + s] = out[r];
+      feed[r] = out[r];
+    }
+  }
+  free(feed);
+  free(out);
+}
+
+/* ------------------------------------------------------------------------ */
+/* The tolerance: which row-steps the definition decides                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Whether one row-step's token is decided despite the differences the
+ * definition admits, and its winner. The only freedoms are the bias
+ * summation order ([KIMI] and [DSV41]: the last bf16 bit of a bias may
+ * differ) and the last ulp of the two logs. A token v competes with the
+ * winner w through its key K(v); its key may move by
+ *   d(v) = dc(v) / |T| + eps(v)    (T noisy),   d(v) = dc(v)   (T = 0)
+ * where dc(v) is the cache difference allowed at v, and
+ *   eps(v) = 2 ulp32(K(v)) + 2 ulp32(lb(v)) + 2 |ulp32(L(v)) / L(v)|
+ * bounds a one-ulp change of either log and of the rounded quotient.
+ * `literal` != 0 takes dc(v) = one bf16 ulp of the oracle's cache value at
+ * every v; otherwise dc(v) = |cache_g(v) - cache_o(v)| (the realized
+ * difference; 0 where the two agree).
+ * Decided: for every v != w, K(w) - K(v) > d(w) + d(v), or K(w) == K(v) with
+ * d(w) = d(v) = 0 and w < v. A NaN winner is decided when its NaN comes from
+ * the cache on both sides and no lower id has a NaN cache value on either
+ * side, or when T itself is NaN (then every key is NaN).
+ * Any v where exactly one of the two caches is NaN makes the step undecided.
+ * Returns 1 (decided) or 0; *winner gets the oracle's token.
+ */
+EXPORT int oracle_decided(int32_t V, const uint16_t* cache_o, const uint16_t* cache_g, float T,
+                          int64_t seed, int32_t step, int64_t position, int32_t literal,
+                          int64_t* winner) {
+  float* K = (float*)malloc(sizeof(float) * (size_t)V);
+  double* d = (double*)malloc(sizeof(double) * (size_t)V);
+  int ok = 1;
+  int noisy = oracle_noisy(T);
+  for (int32_t v = 0; v < V; ++v) {
+    float lo = oracle_bf16_to_f32(cache_o[v]);
+    float lg = oracle_bf16_to_f32(cache_g[v]);
+    if (isnan(lo) != isnan(lg)) ok = 0;
+    double dc;
+    if (literal)
+      dc = oracle_ulp_bf16(lo);
+    else
+      dc = (isnan(lo) && isnan(lg)) ? 0.0 : fabs((double)lg - (double)lo);
+    float lb = 0.0f, L = 0.0f;
+    uint32_t h = noisy ? oracle_noise_hash(seed, step, position, (uint32_t)v) : 0u;
+    K[v] = oracle_gumbel_key(lo, T, h, &lb, &L);
+    if (noisy) {
+      double eps = 2.0 * oracle_ulp32(K[v]) + 2.0 * oracle_ulp32(lb) +
+                   2.0 * fabs(oracle_ulp32(L) / (double)L);
+      d[v] = dc / fabs((double)T) + eps;
+    } else {
+      d[v] = dc;
+    }
+  }
+  int64_t w = oracle_argmax(K, V);
+  *winner = w;
+  if (ok && isnan(K[w])) {
+    if (isnan(T)) {
+      ok = 1;
+    } else {
+      int structural = isnan(oracle_bf16_to_f32(cache_o[w])) && isnan(oracle_bf16_to_f32(cache_g[w]));
+      for (int64_t v = 0; v < w && structural; ++v)
+        if (isnan(oracle_bf16_to_f32(cache_o[v])) || isnan(oracle_bf16_to_f32(cache_g[v])))
+          structural = 0;
+      ok = structural;
+    }
+  } else if (ok) {
+    for (int32_t v = 0; v < V && ok; ++v) {
+      if (v == w) continue;
+      if (isnan(K[v])) { ok = 0; break; }
+      double gap = (double)K[w] - (double)K[v];
+      if (gap > d[w] + d[v]) continue;
+      if (K[w] == K[v] && d[w] == 0.0 && d[v] == 0.0 && w < v) continue;
+      ok = 0;
+    }
+  }
+  free(K);
+  free(d);
+  return ok;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Self-check support                                                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Scan every binary32 x in [lo, hi] and list those where the binary64 log
+ * lies within `ulps` binary64 ulps of a binary32 rounding midpoint: only
+ * there can RN32(log64(x)) differ from the correctly rounded log, given a
+ * binary64 log accurate to under one ulp. Returns the count (the first
+ * `cap` are written to out).
+ */
+EXPORT int64_t oracle_log_hard_cases(float lo, float hi, double ulps, float* out, int64_t cap) {
+  /* the raw binary64 log, before the long double fallback */
+  int64_t n = 0;
+  for (uint32_t b = f32_to_bits(lo); b <= f32_to_bits(hi); ++b) {
+    float x = bits_to_f32(b);
+    double y = log((double)x);
+    float f = (float)y;
+    /* the two binary32 midpoints around f */
+    double fd = (double)f;
+    double up = (double)nextafterf(f, INFINITY), dn = (double)nextafterf(f, -INFINITY);
+    double m1 = 0.5 * (fd + up), m2 = 0.5 * (fd + dn);
+    double tol = ulps * (nextafter(fabs(y), INFINITY) - fabs(y));
+    if (fabs(y - m1) <= tol || fabs(y - m2) <= tol) {
+      if (n < cap) out[n] = x;
+      ++n;
+    }
+    if (b == 0xffffffffu) break;
+  }
+  return n;
+}

@@ -1,0 +1,521 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each test checks the oracle against something it cannot agree with by
+construction: values the pages print, published known answers, exact
+rational arithmetic, high-precision mpmath, numpy's argmax, the Gumbel-max
+law, or the independent brute force in ``oracle/brute.py``.
+"""
+
+import json
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32_from_hex(s):
+    return struct.unpack("<f", struct.pack("<I", int(s, 16)))[0]
+
+
+def f32_bits(x):
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def same_bf16(a, b):
+    """bf16 bit patterns equal, or both NaN (any payload)."""
+    a, b = int(a), int(b)
+    na = (a & 0x7F80) == 0x7F80 and (a & 0x7F) != 0
+    nb = (b & 0x7F80) == 0x7F80 and (b & 0x7F) != 0
+    return (na and nb) or a == b
+
+
+# -- MurmurHash3 -----------------------------------------------------------------
+
+def test_murmur3_known_answers(oracle_lib):
+    from oracle import brute
+
+    g = json.load(open(os.path.join(GOLDEN, "murmur3_x86_32.json")))
+    for v in g["vectors"]:
+        data = bytes.fromhex(v["data_hex"]) if "data_hex" in v else v["data_ascii"].encode()
+        want = int(v["hash"], 16)
+        assert oracle_lib.murmur3_x86_32(data, v["seed"]) == want, v
+        assert brute.murmur3(data, v["seed"]) == want, v
+
+
+def test_murmur3_finaliser_constants_match_page():
+    g = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    m1, m2 = (x & 0xFFFFFFFF for x in g["fmix32_multipliers_signed"])
+    assert (m1, m2) == (0x85EBCA6B, 0xC2B2AE35)
+    assert g["fmix32_after_len_xor"] == 16  # 4 words = 16 bytes
+
+
+def test_noise_hash_two_implementations_agree(oracle_lib):
+    from oracle import brute
+
+    rng = np.random.default_rng(123)
+    for _ in range(4000):
+        seed = int(rng.integers(-(2 ** 63), 2 ** 63 - 1))
+        step = int(rng.integers(0, 16))
+        pos = int(rng.integers(-5, 2 ** 40))
+        tok = int(rng.integers(0, 2 ** 32))
+        assert oracle_lib.noise_hash(seed, step, pos, tok) == brute.noise_hash(seed, step, pos, tok)
+
+
+def test_noise_hash_word_layout(oracle_lib):
+    # seed, step and position enter as the words lo(S), hi(S), lo(P): check
+    # against the general byte-wise hash of the message built by hand.
+    seed, step, pos, tok = 0x0123456789ABCDEF, 3, 4096, 77
+    S = seed ^ (step << 32)
+    P = (pos - 1 + (1 << 30)) & 0xFFFFFFFF
+    msg = struct.pack("<IIII", S & 0xFFFFFFFF, S >> 32, P, tok)
+    assert oracle_lib.noise_hash(seed, step, pos, tok) == oracle_lib.murmur3_x86_32(msg, 0)
+
+
+# -- uniform -----------------------------------------------------------------------
+
+def _rn32_exact(q: Fraction) -> float:
+    from oracle.brute import rn32
+
+    return rn32(q)
+
+
+def test_uniform_exact_rounding(oracle_lib):
+    rng = np.random.default_rng(7)
+    hs = [0, 1, 2, 3, 255, 256, 2 ** 23 - 1, 2 ** 23, 2 ** 24 - 1, 2 ** 24, 2 ** 24 + 1,
+          2 ** 31 - 1, 2 ** 31, 2 ** 32 - 129, 2 ** 32 - 128, 2 ** 32 - 1]
+    hs += [int(x) for x in rng.integers(0, 2 ** 32, size=20000)]
+    for e in range(24, 32):  # values near rounding boundaries in each binade
+        for d in (-3, -1, 0, 1, 2):
+            hs.append((1 << e) + d)
+            hs.append((1 << e) + (1 << (e - 24)) + d)
+    for h in hs:
+        h &= 0xFFFFFFFF
+        assert oracle_lib.uniform(h) == _rn32_exact(Fraction(2 * h + 1, 2 ** 33)), h
+
+
+def test_uniform_extremes(oracle_lib):
+    assert oracle_lib.uniform(0) == 2.0 ** -33
+    for h in range(2 ** 32 - 128, 2 ** 32):
+        assert oracle_lib.uniform(h) == 1.0
+    assert oracle_lib.uniform(2 ** 32 - 129) < 1.0
+
+
+def test_uniform_matches_page_recipe(oracle_lib):
+    # The page forms u as fma(hi16, 2^-16, (lo16 + 0.5) * 2^-32) with its
+    # printed constants; that is one rounding of the exact value.
+    g = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    s_hi = f32_from_hex(g["uniform"]["hi16_scale_2^-16"])
+    s_lo = f32_from_hex(g["uniform"]["lo16_scale_2^-32"])
+    half = f32_from_hex(g["uniform"]["half"])
+    assert (s_hi, s_lo, half) == (2.0 ** -16, 2.0 ** -32, 0.5)
+    rng = np.random.default_rng(8)
+    for h in [int(x) for x in rng.integers(0, 2 ** 32, size=3000)]:
+        hi, lo = h >> 16, h & 0xFFFF
+        fl = _rn32_exact(Fraction(lo) + Fraction(half))
+        fl = _rn32_exact(Fraction(fl) * Fraction(s_lo))
+        u = _rn32_exact(Fraction(hi) * Fraction(s_hi) + Fraction(fl))
+        assert oracle_lib.uniform(h) == u
+
+
+# -- log(1 - u) ------------------------------------------------------------------------
+
+def test_series_constants_match_page():
+    from oracle.brute import rn32
+
+    g = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    assert f32_from_hex(g["log1m_series_horner_start_1/8"]) == rn32(Fraction(1, 8))
+    for k, hx in zip((7, 6, 5, 4, 3, 2, 1), g["log1m_series_coefficients_k7_to_k1"]):
+        assert f32_from_hex(hx) == rn32(Fraction(1, k)), k
+    assert f32_from_hex(g["log1m_series_branch_below"]) == 0.25
+    assert f32_from_hex(g["log1m_clamp_min_2^-24"]) == 2.0 ** -24
+
+
+def test_log1m_series_branch_bit_exact_and_accurate(oracle_lib):
+    import mpmath
+
+    from oracle import brute
+
+    rng = np.random.default_rng(9)
+    us = [2.0 ** -33, 2.0 ** -20, 1e-4, 0.1, np.nextafter(np.float32(0.25), np.float32(0))]
+    us += [float(np.float32(x)) for x in rng.uniform(0, 0.25, size=400)]
+    for u in us:
+        u = float(np.float32(u))
+        L = oracle_lib.log1m(u)
+        assert L == brute.log1m(u), u           # the fma chain, exactly
+        exact = float(mpmath.log1p(-mpmath.mpf(u)))
+        trunc = u ** 9 / (9 * (1 - u))          # the series' tail after u^8/8
+        ulp = float(np.spacing(np.float32(abs(L))))
+        assert abs(L - exact) <= trunc + 4 * ulp, u
+
+
+def test_log1m_log_branch_and_clamp(oracle_lib):
+    from oracle import brute
+
+    for u in (0.25, 0.5, 0.75, 0.999, float(np.float32(1 - 2 ** -24)), 1.0):
+        u = float(np.float32(u))
+        assert oracle_lib.log1m(u) == brute.log1m(u), u
+    # u = 1.0 takes the clamp: log(2^-24)
+    assert oracle_lib.log1m(1.0) == brute.log_cr(2.0 ** -24)
+
+
+@pytest.mark.slow
+def test_logf_cr_correctly_rounded_on_reachable_domains(oracle_lib):
+    """RN32(log64(x)) is the correctly rounded log on every binary32 the step
+    can feed it: the inner log's [2^-24, 0.75] and the outer log's
+    [u_min, 16.64]. Outside the listed hard cases a binary64 log good to
+    under an ulp cannot round differently; the hard cases are settled by
+    mpmath at 200 bits."""
+    from oracle import brute
+
+    for lo, hi in ((2.0 ** -24, 0.75), (1.1e-10, 16.7)):
+        n, xs = oracle_lib.log_hard_cases(lo, hi, 16.0, 4096)
+        assert n < 4096
+        for x in xs:
+            assert oracle_lib.logf_cr(float(x)) == brute.log_cr(float(x)), x
+
+
+def test_tanhf_cr_on_every_softcap_input(oracle_lib):
+    """Every bf16 logit x reaches tanh as z = RN32(x * RN32(1/30)) under the
+    Large workload's soft cap; the oracle's tanh must be correctly rounded
+    there (mpmath at 200 bits)."""
+    from oracle import brute
+
+    inv = float(np.float32(1.0) / np.float32(30.0))
+    zs = set()
+    for b in range(0, 0x7F80):                    # every positive finite bf16
+        x = brute.bf_value(b)
+        zs.add(float(np.float32(np.float32(x) * np.float32(inv))))
+    for z in sorted(zs):
+        assert oracle_lib.tanhf_cr(z) == brute.tanh_cr(z), z
+        assert oracle_lib.tanhf_cr(-z) == -oracle_lib.tanhf_cr(z)
+
+
+# -- keys and noise ------------------------------------------------------------------
+
+def test_gumbel_extremes(oracle_lib):
+    gmax = oracle_lib.gumbel_key(0.0, 1.0, 0)           # key = 0/1 - lb = g
+    gmin = oracle_lib.gumbel_key(0.0, 1.0, 2 ** 32 - 1)
+    assert abs(gmax - 22.874) < 1e-3, gmax
+    assert abs(gmin - (-2.8115)) < 1e-3, gmin
+    assert abs(gmin - (-math.log(24 * math.log(2)))) < 1e-5
+
+
+def test_gumbel_noise_monotone_in_hash(oracle_lib):
+    # g = -log(-log(1-u)) falls as u rises; the rounded keys may wiggle by an
+    # ulp but never rise by more.
+    rng = np.random.default_rng(11)
+    hs = np.sort(rng.integers(0, 2 ** 32, size=5000))
+    g = [oracle_lib.gumbel_key(0.0, 1.0, int(h)) for h in hs]
+    for a, b in zip(g, g[1:]):
+        assert b <= a + 2 * float(np.spacing(np.float32(abs(a)))) + 1e-12
+
+
+def test_temperature_zero_is_plain_logit(oracle_lib):
+    for l in (-3.5, 0.0, 7.25):
+        assert oracle_lib.gumbel_key(l, 0.0, 12345) == l
+        assert oracle_lib.gumbel_key(l, -0.0, 12345) == l     # -0 is not noisy
+    assert math.isnan(oracle_lib.gumbel_key(1.0, float("nan"), 1))  # NaN T is noisy
+
+
+def test_key_matches_brute(oracle_lib):
+    from oracle import brute
+
+    rng = np.random.default_rng(12)
+    for _ in range(300):
+        l = brute.bf_value(int(rng.integers(0, 0x5F00)) | (int(rng.integers(0, 2)) << 15))
+        T = float(np.float32(rng.choice([1.0, 0.7, 0.8, 2.0, 1e-3, 5.5])))
+        h = int(rng.integers(0, 2 ** 32))
+        assert oracle_lib.gumbel_key(l, T, h) == brute.key(l, T, h), (l, T, h)
+
+
+# -- bf16, bias, transform -------------------------------------------------------------
+
+def test_bf16_round_exact(oracle_lib):
+    from oracle.brute import rnbf
+
+    rng = np.random.default_rng(13)
+    xs = [0.0, -0.0, 1.0, 1.00390625, 1.005859375, 1.0078125, 3.3895313892515355e38,
+          3.3961775292304e38, 3.4028234663852886e38, 1e-40, -1e-40, 2.0 ** -133, 2.0 ** -134,
+          2.0 ** -126]
+    # exact ties at several exponents: odd and even last bf16 bits
+    for e in (-130, -10, 0, 5, 100):
+        for m in (0x80, 0x81, 0xFE, 0xFF):
+            xs.append(float(np.float32((m + 0.5) * 2.0 ** (e - 7))))
+    xs += [float(x) for x in rng.standard_normal(3000).astype(np.float32) * 100]
+    xs += [float(x) for x in (rng.standard_normal(1000) * 1e-38).astype(np.float32)]
+    for x in xs:
+        x = float(np.float32(x))
+        got = oracle_lib.bf16_to_f32(oracle_lib.bf16_round(x))
+        want = rnbf(Fraction(x))
+        assert got == want or (math.isinf(got) and math.isinf(want) and got == want), x
+    assert oracle_lib.bf16_round(float("nan")) & 0x7FC0 == 0x7FC0
+
+
+def test_bf16_add_double_rounding_is_innocuous(oracle_lib):
+    """The pages describe the add both as one binary32 add rounded to bf16 and
+    as a bf16 add; binary32's 24 bits make the two the same. Checked against
+    the exact sum rounded once."""
+    from oracle.brute import bf_value, rnbf
+
+    rng = np.random.default_rng(14)
+    for _ in range(20000):
+        a = int(rng.integers(0, 0x7F00)) | (int(rng.integers(0, 2)) << 15)
+        scale = int(rng.integers(-12, 3))
+        b = int(rng.integers(max(0, 0x3F80 + scale * 0x80 - 0x200), 0x3F80 + scale * 0x80 + 0x200))
+        b |= int(rng.integers(0, 2)) << 15
+        got = oracle_lib.cache_value(a, b, 1.0, 0.0)
+        want = rnbf(Fraction(bf_value(a)) + Fraction(bf_value(b)))
+        assert oracle_lib.bf16_to_f32(got) == want, (hex(a), hex(b))
+
+
+def test_bias_is_sequential_fp32_dot_within_gamma(oracle_lib):
+    from oracle.brute import bf_value, bias as brute_bias, rnbf
+
+    rng = np.random.default_rng(15)
+    from markov_draft_sampling_step_amd.workloads import to_bf16_bits
+
+    for R in (16, 32, 256):
+        for _ in range(60):
+            e = to_bf16_bits(rng.standard_normal(R).astype(np.float32) * 0.02)
+            w = to_bf16_bits(rng.standard_normal(R).astype(np.float32) * 0.02)
+            b, s64, sabs = oracle_lib.bias(e, w)
+            exact = sum(Fraction(bf_value(int(x))) * Fraction(bf_value(int(y))) for x, y in zip(e, w))
+            u = Fraction(1, 2 ** 24)
+            gamma = (R * u) / (1 - R * u)
+            # the binary32 sum is within gamma * sum|p| of the exact sum,
+            # and the bias is that sum rounded once to bf16
+            lo, hi = exact - gamma * Fraction(sabs), exact + gamma * Fraction(sabs)
+            bv = oracle_lib.bf16_to_f32(b)
+            assert rnbf(lo) <= bv <= rnbf(hi)
+            assert abs(s64 - float(exact)) <= 1e-12 * max(1.0, sabs)
+            if R <= 32:
+                assert bv == brute_bias(e, w)
+
+
+def test_softcap_properties(oracle_lib):
+    from oracle.brute import bf_value
+
+    rng = np.random.default_rng(16)
+    for _ in range(3000):
+        a = int(rng.integers(0, 0x7F00)) | (int(rng.integers(0, 2)) << 15)
+        b = int(rng.integers(0x3000, 0x3D00)) | (int(rng.integers(0, 2)) << 15)
+        c = oracle_lib.cache_value(a, b, 1.0, 30.0)
+        v = oracle_lib.bf16_to_f32(c)
+        assert abs(v) <= 30.0
+        cn = oracle_lib.cache_value(a ^ 0x8000, b ^ 0x8000, 1.0, 30.0)
+        assert oracle_lib.bf16_to_f32(cn) == -v               # odd
+        x = bf_value(oracle_lib.cache_value(a, b, 1.0, 0.0))
+        if abs(x) < 0.5:
+            assert abs(v - x) <= abs(x) * 2 ** -7 + 1e-30     # tanh(z) ~ z
+
+
+def test_w1_clamp(oracle_lib):
+    V = 1000
+    assert oracle_lib.w1_row(3, V) == 3
+    assert oracle_lib.w1_row(V - 1, V) == V - 1
+    assert oracle_lib.w1_row(V, V) == V - 1
+    assert oracle_lib.w1_row(-1, V) == V - 1
+    assert oracle_lib.w1_row(-(2 ** 63), V) == V - 1
+
+
+# -- total order -------------------------------------------------------------------------
+
+def test_total_order_cases(oracle_lib):
+    nan, inf = float("nan"), float("inf")
+    b = oracle_lib.before
+    assert b(nan, 5, 1e30, 1) and not b(1e30, 1, nan, 5)
+    assert b(nan, 1, nan, 2) and not b(nan, 2, nan, 1)
+    assert b(2.0, 9, 1.0, 0) and not b(1.0, 0, 2.0, 9)
+    assert b(1.0, 3, 1.0, 4) and not b(1.0, 4, 1.0, 3)
+    assert b(-0.0, 3, 0.0, 4) and b(0.0, 3, -0.0, 4) and not b(0.0, 4, -0.0, 3)
+    assert b(inf, 7, 3.0, 1) and b(-inf, 1, -inf, 2) and b(3.0, 9, -inf, 1)
+
+
+def test_argmax_equals_numpy(oracle_lib):
+    rng = np.random.default_rng(17)
+    for trial in range(400):
+        n = int(rng.integers(1, 300))
+        x = rng.integers(-4, 5, size=n).astype(np.float32)   # many ties
+        if trial % 3 == 0:
+            x[rng.integers(0, n, size=int(rng.integers(1, 3)))] = np.nan
+        if trial % 5 == 0:
+            x[rng.integers(0, n)] = -0.0
+        assert oracle_lib.argmax(x) == int(np.argmax(x))
+
+
+def test_block_invariance_of_argmax(oracle_lib):
+    """A two-level argmax (blocks, then a shuffled pass over the block
+    winners) gives the same id at every block size: the order is total."""
+    rng = np.random.default_rng(18)
+    for trial in range(40):
+        n = 1000
+        x = rng.integers(-3, 4, size=n).astype(np.float32)
+        if trial % 4 == 0:
+            x[rng.integers(0, n, size=2)] = np.nan
+        want = oracle_lib.argmax(x)
+        for B in (1, 3, 64, 256, 1000):
+            winners = []
+            for s in range(0, n, B):
+                w = s + oracle_lib.argmax(x[s:s + B])
+                winners.append(w)
+            rng.shuffle(winners)
+            best = winners[0]
+            for w in winners[1:]:
+                if oracle_lib.before(float(x[w]), w, float(x[best]), best):
+                    best = w
+            assert best == want, (B, trial)
+
+
+# -- whole steps ----------------------------------------------------------------------------
+
+def _tiny_case(rng, V, R, rows, k, T_choices, softcap, inject):
+    from markov_draft_sampling_step_amd.workloads import to_bf16_bits
+
+    w1 = to_bf16_bits(rng.standard_normal((V, R)).astype(np.float32) * 0.3)
+    w2 = to_bf16_bits(rng.standard_normal((V, R)).astype(np.float32) * 0.3)
+    base = to_bf16_bits(rng.standard_normal((rows, k, V)).astype(np.float32) * 2)
+    if inject and V >= 2:
+        for r in range(rows):
+            s = int(rng.integers(0, k))
+            t1, t2 = sorted(rng.choice(V, size=2, replace=False))
+            base[r, s, t1] = base[r, s, t2] = 0x4280 if r % 2 == 0 else 0x7FC0
+    prev = rng.integers(-2, V + 2, size=rows).astype(np.int64)
+    seeds = rng.integers(0, 2 ** 40, size=rows).astype(np.int64)
+    pos = (rng.integers(0, 5000, size=rows)[:, None] + np.arange(k)[None, :]).astype(np.int64)
+    temp = np.array([rng.choice(T_choices) for _ in range(rows)], dtype=np.float32)
+    return w1, w2, base, prev, seeds, pos, temp, 1.0, softcap
+
+
+@pytest.mark.slow
+def test_oracle_matches_brute_force_on_tiny_inputs(oracle_lib):
+    """C oracle and the pure-Python brute force are bit-identical (cache and
+    tokens, step after step) on tiny vocabularies, with ties and NaNs."""
+    from oracle import brute
+
+    rng = np.random.default_rng(19)
+    cases = []
+    for V in (1, 2, 3, 7, 64, 257):
+        for R in (16, 32):
+            cases.append((V, R, 1 if V > 64 else 3, 2 if V > 64 else 3))
+    for i, (V, R, rows, k) in enumerate(cases):
+        softcap = 30.0 if i % 3 == 1 else 0.0
+        w1, w2, base, prev, seeds, pos, temp, mult, cap = _tiny_case(
+            rng, V, R, rows, k, (0.0, 1.0, 0.7, 2.0), softcap, inject=(i % 2 == 0))
+        cache, tokens = oracle_lib.sample_sequential(base, w1, w2, prev, seeds, pos, temp,
+                                                     mult, cap)
+        feed = [int(p) for p in prev]
+        for s in range(k):
+            for r in range(rows):
+                c_b, _, t_b = brute.step(base[r, s], w1, w2, feed[r], int(seeds[r]),
+                                         int(pos[r, s]), s, float(temp[r]), mult, cap)
+                for v in range(V):
+                    assert same_bf16(cache[r, s, v], c_b[v]), (V, R, r, s, v)
+                assert tokens[r, s] == t_b, (V, R, r, s)
+                feed[r] = t_b
+
+
+def test_temperature_zero_token_is_numpy_argmax_of_cache(oracle_lib):
+    rng = np.random.default_rng(20)
+    w1, w2, base, prev, seeds, pos, temp, mult, cap = _tiny_case(
+        rng, 500, 16, 6, 3, (0.0,), 0.0, inject=True)
+    cache, tokens = oracle_lib.sample_sequential(base, w1, w2, prev, seeds, pos, temp)
+    from markov_draft_sampling_step_amd.workloads import bf16_bits_to_f32
+
+    for r in range(6):
+        for s in range(3):
+            assert tokens[r, s] == int(np.argmax(bf16_bits_to_f32(cache[r, s])))
+
+
+def test_tiny_temperature_reduces_to_argmax(oracle_lib):
+    """At T = 1e-6 the noise (within [-2.9, 22.9]) cannot reorder two cache
+    values more than 26 T apart: the token is the plain argmax there."""
+    from markov_draft_sampling_step_amd.workloads import bf16_bits_to_f32
+
+    rng = np.random.default_rng(21)
+    w1, w2, base, prev, seeds, pos, temp, mult, cap = _tiny_case(
+        rng, 400, 16, 8, 2, (1e-6,), 0.0, inject=False)
+    cache, tokens = oracle_lib.sample_sequential(base, w1, w2, prev, seeds, pos, temp)
+    checked = 0
+    for r in range(8):
+        for s in range(2):
+            c = bf16_bits_to_f32(cache[r, s]).astype(np.float64)
+            top = np.sort(c)[::-1]
+            if top[0] - top[1] > 26e-6:
+                assert tokens[r, s] == int(np.argmax(c))
+                checked += 1
+    assert checked > 0
+
+
+def _chi2(counts, probs):
+    from scipy.stats import chisquare
+
+    n = counts.sum()
+    return chisquare(counts, n * probs).pvalue
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7, 2.0])
+@pytest.mark.parametrize("vary", ["seed", "position", "step"])
+def test_gumbel_max_law_chi_square(oracle_lib, T, vary):
+    """Over many independent noise draws the sampled token follows
+    softmax(l / T) (the Gumbel-max law), and not softmax(l / 1.1T)."""
+    logits = np.array([0.0, 1.0, -1.0, 2.0, 0.5, -0.5, 1.5, -2.0], dtype=np.float32)
+    V, R = 8, 16
+    N = 200000 if vary == "seed" else 40000
+    from markov_draft_sampling_step_amd.workloads import to_bf16_bits
+
+    base = np.tile(to_bf16_bits(logits), (N, 1))
+    w1 = np.zeros((V, R), dtype=np.uint16)
+    w2 = np.zeros((V, R), dtype=np.uint16)
+    prev = np.zeros(N, dtype=np.int64)
+    idx = np.arange(N, dtype=np.int64)
+    seeds = idx * 7919 + 17 if vary == "seed" else np.full(N, 99, dtype=np.int64)
+    pos = idx + 1 if vary == "position" else np.full(N, 1234, dtype=np.int64)
+    temp = np.full(N, T, dtype=np.float32)
+    if vary == "step":
+        # one row per call, same seed and position; only the step index differs
+        counts = np.zeros(V, dtype=np.int64)
+        one = np.ones(1, dtype=np.float32) * np.float32(T)
+        for s in range(20000):
+            out = oracle_lib.step(base[:1], w1, w2, prev[:1], np.array([5], np.int64),
+                                  np.array([77], np.int64), s, one)
+            counts[out["tokens"][0]] += 1
+    else:
+        out = oracle_lib.step(base, w1, w2, prev, seeds, pos, 0, temp, threads=4)
+        counts = np.bincount(out["tokens"], minlength=V)
+    lf = logits.astype(np.float64)
+
+    def softmax(t):
+        z = np.exp(lf / t - (lf / t).max())
+        return z / z.sum()
+
+    assert _chi2(counts, softmax(T)) > 1e-3
+    assert _chi2(counts, softmax(1.1 * T)) < 1e-3
+
+
+# -- the tolerance ------------------------------------------------------------------------
+
+def test_decided_rules(oracle_lib):
+    V = 64
+    cache = np.full(V, 0x3F80, dtype=np.uint16)   # all 1.0
+    cache[10] = cache[20] = 0x4280                 # tie at 64.0
+    ok, w = oracle_lib.decided(cache, cache, 0.0, 1, 0, 5, literal=False)
+    assert ok and w == 10                          # exact tie, realized: decided
+    ok, w = oracle_lib.decided(cache, cache, 0.0, 1, 0, 5, literal=True)
+    assert not ok and w == 10                      # literal 1-ulp band: undecided
+    nan_cache = cache.copy()
+    nan_cache[30] = nan_cache[40] = 0x7FC0
+    ok, w = oracle_lib.decided(nan_cache, nan_cache, 1.0, 1, 0, 5)
+    assert ok and w == 30                          # structural NaN
+    other = nan_cache.copy()
+    other[30] = 0x4280
+    ok, _ = oracle_lib.decided(nan_cache, other, 1.0, 1, 0, 5)
+    assert not ok                                  # NaN on one side only
+    far = cache.copy()
+    far[5] = 0x4300                                # 128.0 alone on top
+    ok, w = oracle_lib.decided(far, far, 1.0, 1, 0, 5, literal=True)
+    assert ok and w == 5
