@@ -1,0 +1,157 @@
+/*
+ * markov.h -- C ABI of the MI355X (gfx950) DSpark sequential Markov
+ * draft-sampling step.
+ *
+ * What one call computes (the pages' definition):
+ *   For each draft step s = 0..k-1 and request row r, with t the token that
+ *   feeds the step (prev[r] at s = 0, else the token step s-1 sampled):
+ *     emb   = w1[min_u64(t, V-1)]                          gather, clamped
+ *     b[v]  = bf16( sum_j emb[j] * w2[v][j] )              fp32 dot, one rounding
+ *     x[v]  = bf16( base[r][s][v] + b[v] )                 fp32 add, to bf16
+ *     c[v]  = bf16( cap > 0 ? cap*tanh(mult*x*RN32(1/cap)) : mult*x )
+ *     cache[r][s][v] = c[v]
+ *     key[v] = T != 0 ? RN32(RN32(c/T) - log(-log1m(u)))  :  c
+ *              u from MurmurHash3(seed, step, position, v)
+ *     tokens[r][s] = the first NaN key, else the lowest id of the largest key
+ *   Sources (vLLM API pages): "vllm.models.kimi_k3.nvidia.specialized_decode.
+ *   drafter.markov" (module docstring: the exactness paragraph; `_gumbel_key`,
+ *   `_loop_rest`), "vllm.models.muse_spark.nvidia.specialized_decode.cutedsl.
+ *   draft.markov" (module docstring; `_logit`, `_gumbel`, `_murmur_prefix`,
+ *   `_combine`, `_w1_row`, `markov_step`), "vllm.models.deepseek_v41.amd.ops.
+ *   fused_markov" (module docstring).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers are HIP device memory owned by the
+ *     caller; the library never frees or keeps them. `stream` is a hipStream_t
+ *     (NULL = the default stream).
+ *   - Nothing is allocated and no host synchronisation happens inside
+ *     markov_sample_sequential; it only enqueues kernels on `stream`, so it
+ *     can be captured into a HIP graph.
+ *   - Errors are detected on the host only and returned as a negative
+ *     MARKOV_ERR_* code (0 = success); nothing is enqueued on an error.
+ *     Device data is never validated: an out-of-range token reads the last
+ *     w1 row (the pages' `_w1_row` clamp), NaN logits flow through the total
+ *     order, and a NaN temperature makes every key NaN.
+ */
+#ifndef MARKOV_H_
+#define MARKOV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* markov_stream_t; /* a hipStream_t */
+
+/* Shape of one loop. rows: request rows; vocab: V (a multiple of 8);
+ * rank: R, a power of two in [16, 512] (the gate of the kimi_k3 page's
+ * `why_not`); mult: the output multiplier; softcap: the soft cap, <= 0 for
+ * none (the muse_spark page's `_logit` output transform). */
+typedef struct markov_shape {
+  int32_t rows;
+  int32_t vocab;
+  int32_t rank;
+  float mult;
+  float softcap;
+} markov_shape_t;
+
+enum {
+  MARKOV_OK = 0,
+  MARKOV_ERR_NULL = -1,        /* a required pointer is NULL */
+  MARKOV_ERR_SHAPE = -2,       /* rows < 1, vocab < 1 or not a multiple of 8, k < 1 */
+  MARKOV_ERR_RANK = -3,        /* rank not a power of two in [16, 512] */
+  MARKOV_ERR_ALIGN = -4,       /* a bf16 array not 16-byte aligned */
+  MARKOV_ERR_ROWS = -5,        /* rows above what the rank's LDS budget holds */
+  MARKOV_ERR_WORKSPACE = -6,   /* workspace smaller than markov_workspace_bytes */
+  MARKOV_ERR_HIP = -7,         /* a HIP runtime call failed */
+  MARKOV_ERR_VOCAB = -8        /* vocab above 2^31 - 1 */
+};
+
+/* The most rows one call takes at a given rank (the embedding rows are
+ * staged in LDS: rows * rank * 2 bytes must fit in 128 KiB). */
+int32_t markov_max_rows(int32_t rank);
+
+/* Bytes of device workspace one loop of this shape needs: per-row packed
+ * (key, id) maxima and the arrival counter. Independent of k. */
+size_t markov_workspace_bytes(const markov_shape_t* shape, int32_t k);
+
+/* Zero a workspace once after allocating it (enqueued on `stream`). Every
+ * call of markov_sample_sequential leaves it zeroed again, so it is reused
+ * as is; it must not be shared by two calls in flight at once. */
+int markov_workspace_init(void* workspace, size_t bytes, markov_stream_t stream);
+
+/* NULL when this shape and k are supported, else why not (a static string);
+ * mirrors the pages' fallback gates (kimi_k3 `why_not`, deepseek_v41
+ * `_why_not`) for what a call can check. */
+const char* markov_why_not(const markov_shape_t* shape, int32_t k);
+
+/*
+ * The k-step loop: one kernel launch per draft step on `stream`.
+ *   base_logits  device, bf16 [rows, k, V] contiguous        (read)
+ *   w1, w2       device, bf16 [V, R] contiguous row-major    (read)
+ *   prev         device, int64 [rows]: the token feeding step 0 (read)
+ *   seeds        device, int64 [rows]: per-request seed      (read)
+ *   positions    device, int64 [rows, k]: sample position of each step;
+ *                the noise hashes positions[r][s] - 1 + 2^30 (read)
+ *   k            number of draft steps, >= 1
+ *   temperature  device, fp32 [rows]; 0 (or -0) means plain argmax (read)
+ *   cache        device, bf16 [rows, k, V] contiguous        (write)
+ *   tokens       device, int64 [rows, k] contiguous          (write)
+ *   stream       hipStream_t
+ *   shape        host pointer (rows, V, R, mult, softcap)
+ *   workspace    device, zeroed once by markov_workspace_init
+ *   workspace_bytes  its size, >= markov_workspace_bytes(shape, k)
+ * base_logits, w1, w2 and cache must be 16-byte aligned; cache must not
+ * overlap base_logits.
+ */
+int markov_sample_sequential(const void* base_logits, const void* w1, const void* w2,
+                             const int64_t* prev, const int64_t* seeds,
+                             const int64_t* positions, int32_t k, const float* temperature,
+                             void* cache, int64_t* tokens, markov_stream_t stream,
+                             const markov_shape_t* shape, void* workspace,
+                             size_t workspace_bytes);
+
+/* A readable name of a status code (static string). */
+const char* markov_status_string(int status);
+
+/* ---- test-only entry points ------------------------------------------- */
+
+/* markov_sample_sequential with the exact key taken at every element (no
+ * pruning by the cheap key estimate); the tokens must be the same. */
+int markov_debug_sample_exact(const void* base_logits, const void* w1, const void* w2,
+                              const int64_t* prev, const int64_t* seeds,
+                              const int64_t* positions, int32_t k, const float* temperature,
+                              void* cache, int64_t* tokens, markov_stream_t stream,
+                              const markov_shape_t* shape, void* workspace,
+                              size_t workspace_bytes);
+
+/*
+ * The bias alone, through the step kernel's own contraction path:
+ * bias[r][v] = bf16(sum_j w1[min_u64(tok[r], V-1)][j] * w2[v][j]).
+ *   w1, w2 device bf16 [V, R]; tok device int64 [rows]; bias device bf16
+ *   [rows, V] (write). Same error rules as markov_sample_sequential.
+ */
+int markov_debug_bias(const void* w1, const void* w2, const int64_t* tok, void* bias,
+                      const markov_shape_t* shape, markov_stream_t stream);
+
+/*
+ * The Gumbel key of n (logit, token id) pairs of one row at one step, as
+ * the step kernel computes it: key_exact (the key the kernel's argmax
+ * uses), key_fast and margin (its cheap estimate and the bound the kernel
+ * trusts, |key_fast - key_exact| <= margin, to skip exact keys that cannot
+ * win). All arrays device, length n; logits fp32, ids uint32, outputs fp32.
+ */
+int markov_debug_gumbel(const float* logits, const uint32_t* ids, int64_t n, float temperature,
+                        int64_t seed, int32_t step, int64_t position, float* key_exact,
+                        float* key_fast, float* margin, markov_stream_t stream);
+
+/* RN bf16 of n binary32 values with the kernel's conversion (test-only). */
+int markov_debug_bf16_round(const float* in, uint16_t* out, int64_t n, markov_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MARKOV_H_ */

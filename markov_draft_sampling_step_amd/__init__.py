@@ -1,2 +1,212 @@
-"""MI355X-native DSpark sequential Markov draft-sampling step (placeholder;
-the binding is added with the HIP library)."""
+"""MI355X-native DSpark sequential Markov draft-sampling step.
+
+A thin ctypes binding over ``libmarkov.so`` (HIP kernels for gfx950 behind
+the C ABI in ``include/markov.h``). The functions here marshal arguments
+only: every step of the computation runs in the library's kernels, and the
+binding raises if the library is missing -- there is no CPU path.
+
+PyTorch serves for device memory and streams: tensors are passed by
+``data_ptr()`` and the stream defaults to torch's current stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libmarkov.so")
+
+OK = 0
+ERRORS = {
+    -1: "MARKOV_ERR_NULL", -2: "MARKOV_ERR_SHAPE", -3: "MARKOV_ERR_RANK",
+    -4: "MARKOV_ERR_ALIGN", -5: "MARKOV_ERR_ROWS", -6: "MARKOV_ERR_WORKSPACE",
+    -7: "MARKOV_ERR_HIP", -8: "MARKOV_ERR_VOCAB",
+}
+
+
+class MarkovError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        name = ERRORS.get(status, str(status))
+        super().__init__(f"{what}: {name} ({status_string(status)})" if what else name)
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int32), ("vocab", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("mult", ctypes.c_float), ("softcap", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "markov_max_rows": (ctypes.c_int32, [ctypes.c_int32]),
+    "markov_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32]),
+    "markov_workspace_init": (ctypes.c_int, [_P, ctypes.c_size_t, _P]),
+    "markov_why_not": (ctypes.c_char_p, [ctypes.POINTER(Shape), ctypes.c_int32]),
+    "markov_sample_sequential": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
+                                                _P, _P, ctypes.POINTER(Shape), _P,
+                                                ctypes.c_size_t]),
+    "markov_debug_sample_exact": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
+                                                 _P, _P, ctypes.POINTER(Shape), _P,
+                                                 ctypes.c_size_t]),
+    "markov_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "markov_debug_bias": (ctypes.c_int, [_P, _P, _P, _P, ctypes.POINTER(Shape), _P]),
+    "markov_debug_gumbel": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_float,
+                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, _P,
+                                           _P, _P, _P]),
+    "markov_debug_bf16_round": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise ImportError(
+                f"{LIBRARY} is missing: build it first (python -c 'import __graft_entry__ as g; "
+                "g.build()'); there is no CPU fallback")
+        handle = ctypes.CDLL(LIBRARY)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().markov_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise MarkovError(status, what)
+
+
+def make_shape(rows: int, vocab: int, rank: int, mult: float = 1.0, softcap: float = 0.0):
+    return Shape(int(rows), int(vocab), int(rank), float(mult), float(softcap))
+
+
+def max_rows(rank: int) -> int:
+    return int(lib().markov_max_rows(int(rank)))
+
+
+def workspace_bytes(rows: int, vocab: int, rank: int, k: int, mult: float = 1.0,
+                    softcap: float = 0.0) -> int:
+    sh = make_shape(rows, vocab, rank, mult, softcap)
+    return int(lib().markov_workspace_bytes(ctypes.byref(sh), int(k)))
+
+
+def why_not(rows: int, vocab: int, rank: int, k: int, mult: float = 1.0,
+            softcap: float = 0.0) -> str | None:
+    sh = make_shape(rows, vocab, rank, mult, softcap)
+    r = lib().markov_why_not(ctypes.byref(sh), int(k))
+    return None if r is None else r.decode()
+
+
+# -- tensors ---------------------------------------------------------------------
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name, shape=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def new_workspace(rows: int, vocab: int, rank: int, k: int, device="cuda", stream=None):
+    """Allocate and zero a workspace for this shape (a uint8 tensor)."""
+    import torch
+
+    n = workspace_bytes(rows, vocab, rank, k)
+    if n == 0:
+        raise MarkovError(-2, "workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    _check(lib().markov_workspace_init(ctypes.c_void_p(ws.data_ptr()), n, _stream_ptr(stream)),
+           "markov_workspace_init")
+    return ws
+
+
+def sample_sequential(base_logits, w1, w2, prev, seeds, positions, temperature, cache, tokens,
+                      workspace, mult: float = 1.0, softcap: float = 0.0, stream=None,
+                      exact: bool = False):
+    """markov_sample_sequential: base_logits/cache bf16 [rows, k, V], w1/w2 bf16
+    [V, R], prev/seeds int64 [rows], positions/tokens int64 [rows, k],
+    temperature fp32 [rows], workspace from ``new_workspace``. ``exact`` runs
+    the test-only variant that takes the exact key at every element."""
+    import torch
+
+    rows, k, V = base_logits.shape
+    R = w1.shape[1]
+    sh = make_shape(rows, V, R, mult, softcap)
+    args = (
+        _dev(base_logits, torch.bfloat16, "base_logits"),
+        _dev(w1, torch.bfloat16, "w1", (V, R)),
+        _dev(w2, torch.bfloat16, "w2", (V, R)),
+        _dev(prev, torch.int64, "prev", (rows,)),
+        _dev(seeds, torch.int64, "seeds", (rows,)),
+        _dev(positions, torch.int64, "positions", (rows, k)),
+        ctypes.c_int32(k),
+        _dev(temperature, torch.float32, "temperature", (rows,)),
+        _dev(cache, torch.bfloat16, "cache", (rows, k, V)),
+        _dev(tokens, torch.int64, "tokens", (rows, k)),
+        _stream_ptr(stream),
+        ctypes.byref(sh),
+        _dev(workspace, torch.uint8, "workspace"),
+        ctypes.c_size_t(workspace.numel()),
+    )
+    fn = lib().markov_debug_sample_exact if exact else lib().markov_sample_sequential
+    _check(fn(*args), "markov_sample_sequential")
+
+
+def debug_bias(w1, w2, tok, bias, stream=None):
+    import torch
+
+    V, R = w1.shape
+    rows = tok.shape[0]
+    sh = make_shape(rows, V, R)
+    _check(lib().markov_debug_bias(_dev(w1, torch.bfloat16, "w1"), _dev(w2, torch.bfloat16, "w2"),
+                                   _dev(tok, torch.int64, "tok"),
+                                   _dev(bias, torch.bfloat16, "bias", (rows, V)),
+                                   ctypes.byref(sh), _stream_ptr(stream)), "markov_debug_bias")
+
+
+def debug_gumbel(logits, ids, temperature: float, seed: int, step: int, position: int,
+                 key_exact, key_fast, margin, stream=None):
+    import torch
+
+    n = logits.numel()
+    _check(lib().markov_debug_gumbel(
+        _dev(logits, torch.float32, "logits"), _dev(ids, torch.int32, "ids"), n,
+        float(temperature), int(seed), int(step), int(position),
+        _dev(key_exact, torch.float32, "key_exact"), _dev(key_fast, torch.float32, "key_fast"),
+        _dev(margin, torch.float32, "margin"), _stream_ptr(stream)), "markov_debug_gumbel")
+
+
+def debug_bf16_round(x, out, stream=None):
+    import torch
+
+    _check(lib().markov_debug_bf16_round(_dev(x, torch.float32, "x"), _dev(out, torch.int16, "out"),
+                                         x.numel(), _stream_ptr(stream)),
+           "markov_debug_bf16_round")

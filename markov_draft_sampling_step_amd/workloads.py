@@ -158,3 +158,42 @@ def make(name: str, V: int | None = None, rows: int | None = None, k: int | None
                     seeds=seeds, positions=np.ascontiguousarray(positions),
                     temperature=temperature, mult=mult, softcap=softcap,
                     tie_rows=sorted(tie_rows), nan_rows=sorted(nan_rows), injected=injected)
+
+
+def to_device(w: Workload, device="cuda") -> dict:
+    """The workload's arrays as device tensors (bf16 bit patterns become
+    torch.bfloat16), plus empty outputs and a zeroed workspace."""
+    import torch
+
+    from . import new_workspace
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    def plain(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    return dict(
+        base=bf(w.base), w1=bf(w.w1), w2=bf(w.w2), prev=plain(w.prev), seeds=plain(w.seeds),
+        positions=plain(w.positions), temperature=plain(w.temperature),
+        cache=torch.empty((w.rows, w.k, w.V), dtype=torch.bfloat16, device=device),
+        tokens=torch.empty((w.rows, w.k), dtype=torch.int64, device=device),
+        workspace=new_workspace(w.rows, w.V, w.R, w.k, device=device),
+    )
+
+
+def run(w: Workload, d: dict, stream=None, exact: bool = False):
+    """One k-step loop of workload `w` on the device tensors `d`."""
+    from . import sample_sequential
+
+    sample_sequential(d["base"], d["w1"], d["w2"], d["prev"], d["seeds"], d["positions"],
+                      d["temperature"], d["cache"], d["tokens"], d["workspace"], w.mult,
+                      w.softcap, stream=stream, exact=exact)
+
+
+def fetch(d: dict):
+    """(cache uint16 [rows, k, V], tokens int64 [rows, k]) back on the host."""
+    import torch
+
+    cache = d["cache"].view(torch.int16).cpu().numpy().view(np.uint16)
+    return cache, d["tokens"].cpu().numpy()

@@ -1,0 +1,102 @@
+"""Parity check of a device result against the oracle.
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check). Given a workload and the
+cache / tokens a device run produced, recompute every checked row-step with
+the oracle, teacher-forced: step s of row r is fed the device's own token of
+step s-1, so every step is compared from the same state.
+
+The bar (the tolerance the definition admits, see ``oracle_decided``):
+  * cache: each element equal up to one bf16 ulp (or both NaN);
+  * tokens: equal on every decided row-step (realized reading); undecided
+    row-steps are counted, and the device token must lie in the near-tie set
+    (its oracle key within the perturbation band of the best key).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """One bf16 ulp at |x| (binary64), 2^-133 at zero."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(a)
+    u = np.ldexp(1.0, e - 8)
+    return np.where(a == 0, 2.0 ** -133, u)
+
+
+def compare_cache(cg: np.ndarray, co: np.ndarray):
+    """(elements beyond one bf16 ulp, elements that differ at all)."""
+    g = bf16_to_f32(cg).astype(np.float64)
+    o = bf16_to_f32(co).astype(np.float64)
+    gn, on = np.isnan(g), np.isnan(o)
+    both_nan = gn & on
+    one_nan = gn ^ on
+    diff = np.where(both_nan, 0.0, np.abs(g - o))
+    tol = ulp_bf16(np.maximum(np.abs(np.nan_to_num(g)), np.abs(np.nan_to_num(o))))
+    beyond = one_nan | (~both_nan & (diff > tol))
+    differ = one_nan | (~both_nan & (diff != 0))
+    return int(beyond.sum()), int(differ.sum())
+
+
+def check_loop(w, cache_g: np.ndarray, tokens_g: np.ndarray, rows=None, steps=None,
+               threads: int = 8, literal: bool = True) -> dict:
+    """Teacher-forced comparison of a device loop with the oracle.
+
+    w: a Workload; cache_g uint16 [rows, k, V]; tokens_g int64 [rows, k].
+    rows / steps: subsets to check (default all).
+    """
+    rows = list(range(w.rows)) if rows is None else list(rows)
+    steps = list(range(w.k)) if steps is None else list(steps)
+    rows_a = np.array(rows, dtype=np.int64)
+    rep = dict(row_steps=0, cache_beyond=0, cache_differ=0, cache_elems=0, decided=0,
+               undecided=0, decided_literal=0, token_mismatch=[], undecided_cases=[],
+               near_tie_violations=[])
+    for s in steps:
+        feed = w.prev[rows_a] if s == 0 else tokens_g[rows_a, s - 1]
+        out = oracle.step(np.ascontiguousarray(w.base[rows_a, s]), w.w1, w.w2, feed,
+                          w.seeds[rows_a], w.positions[rows_a, s], s, w.temperature[rows_a],
+                          w.mult, w.softcap, want_keys=True, threads=threads)
+        co = out["cache"]
+        cg = np.ascontiguousarray(cache_g[rows_a, s])
+        beyond, differ = compare_cache(cg, co)
+        rep["cache_beyond"] += beyond
+        rep["cache_differ"] += differ
+        rep["cache_elems"] += co.size
+        for i, r in enumerate(rows):
+            rep["row_steps"] += 1
+            T = float(w.temperature[r])
+            ok, win = oracle.decided(co[i], cg[i], T, int(w.seeds[r]), s,
+                                     int(w.positions[r, s]), literal=False)
+            assert win == int(out["tokens"][i])
+            if literal:
+                ok_l, _ = oracle.decided(co[i], co[i], T, int(w.seeds[r]), s,
+                                         int(w.positions[r, s]), literal=True)
+                rep["decided_literal"] += int(ok_l)
+            gt = int(tokens_g[r, s])
+            if ok:
+                rep["decided"] += 1
+                if gt != win:
+                    rep["token_mismatch"].append((r, s, gt, win))
+            else:
+                rep["undecided"] += 1
+                rep["undecided_cases"].append((r, s, gt, win))
+                keys = out["keys"][i]
+                kb, kg = float(keys[win]), float(keys[gt]) if 0 <= gt < w.V else float("nan")
+                band = 4.0 * (abs(kb) + 1.0) * 2.0 ** -20 + (2.0 ** -6 / max(abs(T), 1e-30) if T else 1.0)
+                if not (np.isnan(kb) or (kb - kg) <= band):
+                    rep["near_tie_violations"].append((r, s, gt, win, kb, kg))
+    return rep
+
+
+def assert_parity(rep: dict, max_undecided_frac: float = 0.02):
+    assert rep["cache_beyond"] == 0, f"cache beyond one bf16 ulp: {rep['cache_beyond']}"
+    assert not rep["token_mismatch"], f"token mismatches on decided row-steps: {rep['token_mismatch'][:10]}"
+    assert not rep["near_tie_violations"], f"undecided tokens outside the tie band: {rep['near_tie_violations'][:5]}"
+    assert rep["undecided"] <= max(1, max_undecided_frac * rep["row_steps"]), rep["undecided_cases"][:10]

@@ -1,0 +1,108 @@
+"""The C ABI library, on the host: it loads, exports every entry point its
+header declares, and the host-side checks return the documented errors.
+No call here reaches the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import markov_draft_sampling_step_amd as m
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "markov.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m.LIBRARY):
+        from markov_draft_sampling_step_amd import build
+
+        build.build()
+    return m.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(markov_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("markov_sample_sequential", "markov_workspace_bytes", "markov_workspace_init",
+                     "markov_why_not", "markov_status_string", "markov_debug_bias"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    handle = ctypes.CDLL(m.LIBRARY)
+    missing = [n for n in declared_functions() if not hasattr(handle, n)]
+    assert not missing, missing
+
+
+def test_status_strings(lib):
+    assert m.status_string(0) == "ok"
+    for code in m.ERRORS:
+        assert m.status_string(code) != "unknown status"
+
+
+def test_max_rows_and_workspace(lib):
+    assert m.max_rows(256) == 256
+    assert m.max_rows(512) == 128
+    assert m.max_rows(32) == 1024
+    assert m.max_rows(48) == 0
+    assert m.workspace_bytes(64, 163840, 256, 5) >= 64 * 8 + 4
+    assert m.workspace_bytes(0, 163840, 256, 5) == 0
+    assert m.workspace_bytes(4, 100, 256, 5) == 0        # vocab not a multiple of 8
+
+
+@pytest.mark.parametrize("rows,V,R,k,why", [
+    (0, 4096, 32, 3, "no requests"),
+    (2, 4096, 32, 0, "no draft steps"),
+    (2, 4100, 32, 3, "vocabulary"),
+    (2, 4096, 48, 3, "rank"),
+    (2, 4096, 1024, 3, "rank"),
+    (257, 4096, 256, 3, "LDS"),
+    (2, 4096, 32, 3, None),
+    (256, 163840, 256, 8, None),
+])
+def test_why_not(lib, rows, V, R, k, why):
+    r = m.why_not(rows, V, R, k)
+    if why is None:
+        assert r is None
+    else:
+        assert r is not None and why in r
+
+
+def _call(lib, shape, ptrs, k=3, ws_bytes=4096):
+    P = ctypes.c_void_p
+    return lib.markov_sample_sequential(P(ptrs[0]), P(ptrs[1]), P(ptrs[2]), P(ptrs[3]),
+                                        P(ptrs[4]), P(ptrs[5]), k, P(ptrs[6]), P(ptrs[7]),
+                                        P(ptrs[8]), None, ctypes.byref(shape), P(ptrs[9]),
+                                        ws_bytes)
+
+
+def test_host_errors_before_any_device_work(lib):
+    good = [0x10000 * (i + 1) for i in range(10)]          # never dereferenced
+    sh = m.make_shape(2, 4096, 32)
+    assert _call(lib, m.make_shape(0, 4096, 32), good) == -2
+    assert _call(lib, m.make_shape(2, 4100, 32), good) == -2
+    assert _call(lib, sh, good, k=0) == -2
+    assert _call(lib, m.make_shape(2, 4096, 40), good) == -3
+    assert _call(lib, m.make_shape(300, 4096, 256), good) == -5
+    for i in range(10):
+        bad = list(good)
+        bad[i] = 0
+        assert _call(lib, sh, bad) == -1, i
+    for i in (0, 1, 2, 7):                                  # bf16 arrays
+        bad = list(good)
+        bad[i] += 2
+        assert _call(lib, sh, bad) == -4, i
+    assert _call(lib, sh, good, ws_bytes=8) == -6
+    P = ctypes.c_void_p
+    assert lib.markov_debug_bias(P(good[0]), P(good[1]), P(good[2]), P(good[3]),
+                                 ctypes.byref(m.make_shape(2, 4096, 33)), None) == -3
+    assert lib.markov_debug_gumbel(None, None, 4, ctypes.c_float(1.0), 1, 0, 1, None, None, None,
+                                   None) == -1

@@ -1,0 +1,248 @@
+"""Parity of the HIP path with the oracle, through the C ABI, on the GPU.
+
+Every case runs the device loop, then recomputes each checked row-step with
+the oracle teacher-forced by the device's own previous token. The bar:
+cache within one bf16 ulp of the oracle; tokens equal on every decided
+row-step (see ``oracle_decided``); undecided row-steps counted and kept
+within the near-tie set.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import markov_draft_sampling_step_amd as m  # noqa: E402
+from markov_draft_sampling_step_amd import workloads  # noqa: E402
+from oracle import parity  # noqa: E402
+
+THREADS = min(16, os.cpu_count() or 4)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.lib()
+    return torch.device("cuda:0")
+
+
+def run_and_check(w, dev, rows=None, exact=False, max_undecided_frac=0.02):
+    say(f"case {w.name} V={w.V} R={w.R} rows={w.rows} k={w.k} exact={exact}")
+    d = workloads.to_device(w, dev)
+    workloads.run(w, d, exact=exact)
+    torch.cuda.synchronize()
+    cg, tg = workloads.fetch(d)
+    rep = parity.check_loop(w, cg, tg, rows=rows, threads=THREADS)
+    say(f"  row-steps {rep['row_steps']} decided {rep['decided']} (literal {rep['decided_literal']}) "
+        f"undecided {rep['undecided']} cache differing {rep['cache_differ']}/{rep['cache_elems']}")
+    parity.assert_parity(rep, max_undecided_frac)
+    return cg, tg, rep
+
+
+def custom(V, R, rows, k, seed, temps=(1.0,), softcap=0.0, mult=1.0, inject=True, prev_oob=True):
+    """A shrunk workload with mixed temperatures, injected ties and NaNs and
+    out-of-range feed tokens."""
+    w = workloads.make("tiny", V=V, R=R, rows=rows, k=k, data_seed=seed)
+    rng = np.random.default_rng(seed + 1000)
+    w.name = f"custom{seed}"
+    w.w1 = workloads.to_bf16_bits(rng.standard_normal((V, R)).astype(np.float32) * 0.05)
+    w.w2 = workloads.to_bf16_bits(rng.standard_normal((V, R)).astype(np.float32) * 0.05)
+    w.base = workloads.to_bf16_bits(rng.standard_normal((rows, k, V)).astype(np.float32) * 3)
+    w.temperature = np.array([temps[r % len(temps)] for r in range(rows)], dtype=np.float32)
+    w.seeds = rng.integers(-(2 ** 62), 2 ** 62, size=rows).astype(np.int64)
+    P = rng.integers(0, 1 << 20, size=rows).astype(np.int64)
+    w.positions = np.ascontiguousarray(P[:, None] + np.arange(k)[None, :])
+    w.prev = rng.integers(0, V, size=rows).astype(np.int64)
+    if prev_oob and rows >= 2:
+        w.prev[0] = -5
+        w.prev[1] = V + 17
+    if inject and V >= 4:
+        for r in range(0, rows, 3):
+            for s in range(k):
+                t1, t2 = sorted(int(t) for t in rng.choice(V, size=2, replace=False))
+                val = 0x4280 if r % 2 == 0 else workloads.BF16_NAN
+                w.base[r, s, t1] = w.base[r, s, t2] = val
+    w.mult, w.softcap = mult, softcap
+    return w
+
+
+# -- pieces -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("V,R,rows", [(1000, 32, 19), (264, 16, 3), (2056, 64, 33), (1032, 512, 5),
+                                      (4096, 256, 70)])
+def test_bias_contraction_matches_oracle(dev, V, R, rows):
+    import oracle
+
+    say(f"bias V={V} R={R} rows={rows}")
+    rng = np.random.default_rng(V + R + rows)
+    w1 = workloads.to_bf16_bits(rng.standard_normal((V, R)).astype(np.float32) * 0.05)
+    w2 = workloads.to_bf16_bits(rng.standard_normal((V, R)).astype(np.float32) * 0.05)
+    tok = rng.integers(-3, V + 3, size=rows).astype(np.int64)
+    bw1 = torch.from_numpy(w1.view(np.int16)).to(dev).view(torch.bfloat16)
+    bw2 = torch.from_numpy(w2.view(np.int16)).to(dev).view(torch.bfloat16)
+    ttok = torch.from_numpy(tok).to(dev)
+    bias = torch.empty((rows, V), dtype=torch.bfloat16, device=dev)
+    m.debug_bias(bw1, bw2, ttok, bias)
+    torch.cuda.synchronize()
+    bg = bias.view(torch.int16).cpu().numpy().view(np.uint16)
+    # oracle: sequential fp32 dot per element
+    out = oracle.step(np.zeros((rows, V), np.uint16), w1, w2, tok, np.zeros(rows, np.int64),
+                      np.zeros(rows, np.int64), 0, np.zeros(rows, np.float32), want_bias=True,
+                      threads=THREADS)
+    bo = out["bias"]
+    g = parity.bf16_to_f32(bg).astype(np.float64)
+    o = parity.bf16_to_f32(bo).astype(np.float64)
+    tol = parity.ulp_bf16(np.maximum(np.abs(g), np.abs(o)))
+    bad = np.abs(g - o) > tol
+    # where cancellation leaves more than an ulp, fall back on the order-free
+    # bound: the device value is a bf16 rounding of some sum within gamma_R of
+    # the exact one
+    if bad.any():
+        idx = np.argwhere(bad)
+        for r, v in idx[:2000]:
+            row = oracle.w1_row(int(tok[r]), V)
+            _, s64, sabs = oracle.bias(w1[row], w2[v])
+            gam = R * 2.0 ** -24 / (1 - R * 2.0 ** -24)
+            lo, hi = s64 - gam * sabs, s64 + gam * sabs
+            assert parity.bf16_to_f32(np.array([oracle.bf16_round(lo)]))[0] <= g[r, v] <= \
+                parity.bf16_to_f32(np.array([oracle.bf16_round(hi)]))[0], (r, v, g[r, v], o[r, v])
+    say(f"  bias elements differing {int((g != o).sum())}/{g.size}, beyond one ulp {int(bad.sum())}")
+
+
+def test_bf16_conversion_matches_oracle(dev):
+    import oracle
+
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    # exact ties and near-ties in every binade, subnormals, extremes
+    e = np.arange(0, 255, dtype=np.uint32)
+    for low in (0x8000, 0x7FFF, 0x8001, 0x18000, 0x0000):
+        bits = np.concatenate([bits, (e << 23) | np.uint32(low), (e << 23) | np.uint32(low) | np.uint32(1 << 31)])
+    bits = np.concatenate([bits, np.array([0x7F7FFFFF, 0x7F7F8000, 0x7F800000, 0xFF800000, 0x7FC00000,
+                                           0x00000001, 0x80000001, 0x007FFFFF], dtype=np.uint32)])
+    x = bits.view(np.float32)
+    xt = torch.from_numpy(x).to(dev)
+    out = torch.empty(x.size, dtype=torch.int16, device=dev)
+    m.debug_bf16_round(xt, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    idx = np.arange(x.size)[:: max(1, x.size // 200000)]
+    for i in idx:
+        xi = float(x[i])
+        if np.isnan(xi):
+            assert (got[i] & 0x7F80) == 0x7F80 and (got[i] & 0x7F) != 0
+            continue
+        assert got[i] == oracle.bf16_round(xi), (hex(int(bits[i])), hex(int(got[i])))
+
+
+def test_gumbel_exact_key_and_margin(dev):
+    import oracle
+
+    n = 1 << 22
+    rng = np.random.default_rng(9)
+    ids = rng.integers(0, 2 ** 32, size=n, dtype=np.uint64).astype(np.uint32)
+    logits = parity.bf16_to_f32(workloads.to_bf16_bits(rng.standard_normal(n).astype(np.float32) * 4))
+    for T, seed, step, pos in ((1.0, 12345, 0, 4096), (0.7, -(2 ** 60) + 3, 3, 17), (0.8, 7, 7, 1)):
+        lt = torch.from_numpy(logits).to(dev)
+        it = torch.from_numpy(ids.view(np.int32)).to(dev)
+        kx = torch.empty(n, dtype=torch.float32, device=dev)
+        kf = torch.empty_like(kx)
+        mg = torch.empty_like(kx)
+        m.debug_gumbel(lt, it, T, seed, step, pos, kx, kf, mg)
+        torch.cuda.synchronize()
+        kx, kf, mg = kx.cpu().numpy(), kf.cpu().numpy(), mg.cpu().numpy()
+        err = np.abs(kf.astype(np.float64) - kx.astype(np.float64))
+        assert np.all(err <= mg), (T, float(err.max()), int(np.argmax(err - mg)))
+        say(f"  T={T}: max |fast-exact| {err.max():.3g}, margin min {mg.min():.3g}")
+        # exact keys bit-equal to the oracle's (sampled)
+        sel = rng.choice(n, size=20000, replace=False)
+        mism = 0
+        for i in sel:
+            h = oracle.noise_hash(seed, step, pos, int(ids[i]))
+            ko = oracle.gumbel_key(float(logits[i]), T, h)
+            if np.float32(ko).view(np.uint32) != np.float32(kx[i]).view(np.uint32):
+                mism += 1
+        assert mism <= 2, mism   # only a binary64 log within an ulp of a rounding midpoint may differ
+
+
+# -- loops ----------------------------------------------------------------------------
+
+def test_tiny(dev):
+    run_and_check(workloads.make("tiny"), dev)
+
+
+@pytest.mark.parametrize("args", [
+    dict(V=1000, R=32, rows=19, k=3, seed=1, temps=(1.0, 0.0, 0.7)),
+    dict(V=264, R=16, rows=3, k=2, seed=2, temps=(2.0,)),
+    dict(V=8, R=16, rows=1, k=2, seed=3, temps=(1.0,), inject=False),
+    dict(V=2056, R=64, rows=33, k=4, seed=4, temps=(0.0, 1.0), softcap=30.0),
+    dict(V=1032, R=512, rows=5, k=2, seed=5, temps=(1.5, -0.0, 0.5), mult=0.5),
+    dict(V=4104, R=128, rows=70, k=2, seed=6, temps=(1.0, float("nan"), 0.0)),
+    dict(V=1016, R=256, rows=256, k=2, seed=7, temps=(0.0, 1.0)),
+])
+def test_ragged_and_edge_shapes(dev, args):
+    w = custom(**args)
+    run_and_check(w, dev)
+
+
+def test_exact_and_pruned_agree_small(dev):
+    w = custom(V=2056, R=64, rows=33, k=4, seed=11, temps=(0.0, 1.0, 0.3))
+    cg1, tg1, _ = run_and_check(w, dev)
+    cg2, tg2, _ = run_and_check(w, dev, exact=True)
+    assert np.array_equal(tg1, tg2)
+    assert np.array_equal(cg1, cg2)
+
+
+def test_workspace_reuse_is_deterministic(dev):
+    w = custom(V=1000, R=32, rows=19, k=3, seed=12, temps=(1.0, 0.0))
+    d = workloads.to_device(w, dev)
+    workloads.run(w, d)
+    c1, t1 = workloads.fetch(d)
+    for _ in range(3):
+        workloads.run(w, d)
+    c2, t2 = workloads.fetch(d)
+    assert np.array_equal(t1, t2) and np.array_equal(c1, c2)
+    ws = d["workspace"].cpu().numpy()
+    assert not ws.any(), "workspace must be left zeroed"
+
+
+@pytest.mark.parametrize("name", ["single", "small", "large"])
+def test_full_config(dev, name):
+    run_and_check(workloads.make(name), dev)
+
+
+def test_full_stress_sampled_rows(dev):
+    w = workloads.make("stress")
+    rng = np.random.default_rng(0)
+    rows = sorted(set(w.tie_rows) | set(w.nan_rows) | set(int(r) for r in rng.choice(w.rows, 36, replace=False)))
+    cg, tg, rep = run_and_check(w, dev, rows=rows)
+    for r in w.nan_rows:
+        for (s, t1, t2) in w.injected[r]:
+            assert tg[r, s] == t1, (r, s)
+    for r in w.tie_rows:
+        if w.temperature[r] == 0:
+            for (s, t1, t2) in w.injected[r]:
+                assert tg[r, s] == t1, (r, s)
+
+
+@pytest.mark.parametrize("name", ["large", "stress"])
+def test_exact_and_pruned_agree_full(dev, name):
+    w = workloads.make(name)
+    d = workloads.to_device(w, dev)
+    workloads.run(w, d)
+    c1, t1 = workloads.fetch(d)
+    workloads.run(w, d, exact=True)
+    c2, t2 = workloads.fetch(d)
+    assert np.array_equal(t1, t2)
+    assert np.array_equal(c1, c2)
