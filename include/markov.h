@@ -113,6 +113,18 @@ int markov_sample_sequential(const void* base_logits, const void* w1, const void
                              const markov_shape_t* shape, void* workspace,
                              size_t workspace_bytes);
 
+/*
+ * Step `step` (0 <= step < k) of the same loop alone: one kernel launch that
+ * feeds on prev (step 0) or on tokens[:, step-1], and writes cache[:, step, :]
+ * and tokens[:, step]. Arguments and errors as markov_sample_sequential;
+ * calling it for step = 0..k-1 in order is that loop.
+ */
+int markov_sample_step(const void* base_logits, const void* w1, const void* w2,
+                       const int64_t* prev, const int64_t* seeds, const int64_t* positions,
+                       int32_t k, int32_t step, const float* temperature, void* cache,
+                       int64_t* tokens, markov_stream_t stream, const markov_shape_t* shape,
+                       void* workspace, size_t workspace_bytes);
+
 /* A readable name of a status code (static string). */
 const char* markov_status_string(int status);
 

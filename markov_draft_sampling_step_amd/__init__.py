@@ -49,6 +49,9 @@ _SIGS = {
     "markov_debug_sample_exact": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
                                                  _P, _P, ctypes.POINTER(Shape), _P,
                                                  ctypes.c_size_t]),
+    "markov_sample_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                          _P, _P, _P, _P, ctypes.POINTER(Shape), _P,
+                                          ctypes.c_size_t]),
     "markov_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "markov_debug_bias": (ctypes.c_int, [_P, _P, _P, _P, ctypes.POINTER(Shape), _P]),
     "markov_debug_gumbel": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_float,
@@ -150,11 +153,12 @@ def new_workspace(rows: int, vocab: int, rank: int, k: int, device="cuda", strea
 
 def sample_sequential(base_logits, w1, w2, prev, seeds, positions, temperature, cache, tokens,
                       workspace, mult: float = 1.0, softcap: float = 0.0, stream=None,
-                      exact: bool = False):
+                      exact: bool = False, step: int | None = None):
     """markov_sample_sequential: base_logits/cache bf16 [rows, k, V], w1/w2 bf16
     [V, R], prev/seeds int64 [rows], positions/tokens int64 [rows, k],
     temperature fp32 [rows], workspace from ``new_workspace``. ``exact`` runs
-    the test-only variant that takes the exact key at every element."""
+    the test-only variant that takes the exact key at every element; ``step``
+    runs that one step of the loop alone (markov_sample_step)."""
     import torch
 
     rows, k, V = base_logits.shape
@@ -176,6 +180,10 @@ def sample_sequential(base_logits, w1, w2, prev, seeds, positions, temperature, 
         _dev(workspace, torch.uint8, "workspace"),
         ctypes.c_size_t(workspace.numel()),
     )
+    if step is not None:
+        args = args[:7] + (ctypes.c_int32(step),) + args[7:]
+        _check(lib().markov_sample_step(*args), "markov_sample_step")
+        return
     fn = lib().markov_debug_sample_exact if exact else lib().markov_sample_sequential
     _check(fn(*args), "markov_sample_sequential")
 
@@ -210,3 +218,57 @@ def debug_bf16_round(x, out, stream=None):
     _check(lib().markov_debug_bf16_round(_dev(x, torch.float32, "x"), _dev(out, torch.int16, "out"),
                                          x.numel(), _stream_ptr(stream)),
            "markov_debug_bf16_round")
+
+
+class PreparedCall:
+    """A loop (or one step) with its arguments marshalled once, for tight
+    launch loops and graph capture. Calling it enqueues the kernels on the
+    stream it was prepared for."""
+
+    def __init__(self, fn, args, stream_index, what):
+        self._fn, self._args, self._si, self._what = fn, list(args), stream_index, what
+
+    def on(self, stream):
+        c = PreparedCall(self._fn, self._args, self._si, self._what)
+        c._args[self._si] = _stream_ptr(stream)
+        return c
+
+    def __call__(self):
+        _check(self._fn(*self._args), self._what)
+
+
+def prepare(w, d, step: int | None = None, exact: bool = False, stream=None) -> PreparedCall:
+    """Marshal the arguments of workload `w` on device tensors `d` (see
+    ``workloads.to_device``) once."""
+    import torch
+
+    rows, k, V, R = w.rows, w.k, w.V, w.R
+    sh = make_shape(rows, V, R, w.mult, w.softcap)
+    args = [
+        _dev(d["base"], torch.bfloat16, "base_logits", (rows, k, V)),
+        _dev(d["w1"], torch.bfloat16, "w1", (V, R)),
+        _dev(d["w2"], torch.bfloat16, "w2", (V, R)),
+        _dev(d["prev"], torch.int64, "prev", (rows,)),
+        _dev(d["seeds"], torch.int64, "seeds", (rows,)),
+        _dev(d["positions"], torch.int64, "positions", (rows, k)),
+        ctypes.c_int32(k),
+        _dev(d["temperature"], torch.float32, "temperature", (rows,)),
+        _dev(d["cache"], torch.bfloat16, "cache", (rows, k, V)),
+        _dev(d["tokens"], torch.int64, "tokens", (rows, k)),
+        _stream_ptr(stream),
+        sh,
+        _dev(d["workspace"], torch.uint8, "workspace"),
+        ctypes.c_size_t(d["workspace"].numel()),
+    ]
+    args[11] = ctypes.byref(sh)
+    keep = sh
+    si = 10
+    if step is not None:
+        args.insert(7, ctypes.c_int32(step))
+        si = 11
+        call = PreparedCall(lib().markov_sample_step, args, si, "markov_sample_step")
+    else:
+        fn = lib().markov_debug_sample_exact if exact else lib().markov_sample_sequential
+        call = PreparedCall(fn, args, si, "markov_sample_sequential")
+    call._keep = keep
+    return call

@@ -567,9 +567,10 @@ Workspace ws_layout(void* w, int rows) {
 }
 
 int launch_steps(int mode, const void* base, const void* w1, const void* w2, const int64_t* prev,
-                 const int64_t* seeds, const int64_t* positions, int32_t k,
-                 const float* temperature, void* cache, int64_t* tokens, void* bias_out,
-                 markov_stream_t stream, const markov_shape_t* sh, void* workspace) {
+                 const int64_t* seeds, const int64_t* positions, int32_t k, int32_t s_begin,
+                 int32_t s_end, const float* temperature, void* cache, int64_t* tokens,
+                 void* bias_out, markov_stream_t stream, const markov_shape_t* sh,
+                 void* workspace) {
   StepFn fn = mode == MODE_SAMPLE ? pick_kernel<MODE_SAMPLE>(sh->rank)
             : mode == MODE_SAMPLE_EXACT ? pick_kernel<MODE_SAMPLE_EXACT>(sh->rank)
                                         : pick_kernel<MODE_BIAS>(sh->rank);
@@ -605,7 +606,7 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   a.has_cap = sh->softcap > 0.0f;
   a.cap = sh->softcap;
   a.inv_cap = a.has_cap ? 1.0f / sh->softcap : 0.0f;
-  for (int s = 0; s < k; ++s) {
+  for (int s = s_begin; s < s_end; ++s) {
     a.step = s;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(BLOCK), lds, (hipStream_t)stream, a);
     if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
@@ -615,18 +616,20 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
 
 int sample_common(int mode, const void* base_logits, const void* w1, const void* w2,
                   const int64_t* prev, const int64_t* seeds, const int64_t* positions, int32_t k,
-                  const float* temperature, void* cache, int64_t* tokens, markov_stream_t stream,
-                  const markov_shape_t* shape, void* workspace, size_t workspace_bytes) {
+                  int32_t s_begin, int32_t s_end, const float* temperature, void* cache,
+                  int64_t* tokens, markov_stream_t stream, const markov_shape_t* shape,
+                  void* workspace, size_t workspace_bytes) {
   int rc = check_shape(shape, k);
   if (rc) return rc;
+  if (s_begin < 0 || s_end > k || s_begin >= s_end) return MARKOV_ERR_SHAPE;
   if (!base_logits || !w1 || !w2 || !prev || !seeds || !positions || !temperature || !cache ||
       !tokens || !workspace)
     return MARKOV_ERR_NULL;
   if (!aligned16(base_logits) || !aligned16(w1) || !aligned16(w2) || !aligned16(cache))
     return MARKOV_ERR_ALIGN;
   if (workspace_bytes < ws_bytes(shape->rows)) return MARKOV_ERR_WORKSPACE;
-  return launch_steps(mode, base_logits, w1, w2, prev, seeds, positions, k, temperature, cache,
-                      tokens, nullptr, stream, shape, workspace);
+  return launch_steps(mode, base_logits, w1, w2, prev, seeds, positions, k, s_begin, s_end,
+                      temperature, cache, tokens, nullptr, stream, shape, workspace);
 }
 
 }  // namespace
@@ -662,8 +665,18 @@ int markov_sample_sequential(const void* base_logits, const void* w1, const void
                              void* cache, int64_t* tokens, markov_stream_t stream,
                              const markov_shape_t* shape, void* workspace,
                              size_t workspace_bytes) {
-  return sample_common(MODE_SAMPLE, base_logits, w1, w2, prev, seeds, positions, k, temperature,
-                       cache, tokens, stream, shape, workspace, workspace_bytes);
+  return sample_common(MODE_SAMPLE, base_logits, w1, w2, prev, seeds, positions, k, 0, k,
+                       temperature, cache, tokens, stream, shape, workspace, workspace_bytes);
+}
+
+int markov_sample_step(const void* base_logits, const void* w1, const void* w2,
+                       const int64_t* prev, const int64_t* seeds, const int64_t* positions,
+                       int32_t k, int32_t step, const float* temperature, void* cache,
+                       int64_t* tokens, markov_stream_t stream, const markov_shape_t* shape,
+                       void* workspace, size_t workspace_bytes) {
+  return sample_common(MODE_SAMPLE, base_logits, w1, w2, prev, seeds, positions, k, step,
+                       step + 1, temperature, cache, tokens, stream, shape, workspace,
+                       workspace_bytes);
 }
 
 int markov_debug_sample_exact(const void* base_logits, const void* w1, const void* w2,
@@ -672,7 +685,7 @@ int markov_debug_sample_exact(const void* base_logits, const void* w1, const voi
                               void* cache, int64_t* tokens, markov_stream_t stream,
                               const markov_shape_t* shape, void* workspace,
                               size_t workspace_bytes) {
-  return sample_common(MODE_SAMPLE_EXACT, base_logits, w1, w2, prev, seeds, positions, k,
+  return sample_common(MODE_SAMPLE_EXACT, base_logits, w1, w2, prev, seeds, positions, k, 0, k,
                        temperature, cache, tokens, stream, shape, workspace, workspace_bytes);
 }
 
@@ -697,8 +710,8 @@ int markov_debug_bias(const void* w1, const void* w2, const int64_t* tok, void* 
   if (rc) return rc;
   if (!w1 || !w2 || !tok || !bias) return MARKOV_ERR_NULL;
   if (!aligned16(w1) || !aligned16(w2) || !aligned16(bias)) return MARKOV_ERR_ALIGN;
-  return launch_steps(MODE_BIAS, nullptr, w1, w2, tok, nullptr, nullptr, 1, nullptr, nullptr,
-                      nullptr, bias, stream, shape, nullptr);
+  return launch_steps(MODE_BIAS, nullptr, w1, w2, tok, nullptr, nullptr, 1, 0, 1, nullptr,
+                      nullptr, nullptr, bias, stream, shape, nullptr);
 }
 
 int markov_debug_gumbel(const float* logits, const uint32_t* ids, int64_t n, float temperature,

@@ -246,3 +246,30 @@ def test_exact_and_pruned_agree_full(dev, name):
     c2, t2 = workloads.fetch(d)
     assert np.array_equal(t1, t2)
     assert np.array_equal(c1, c2)
+
+
+def test_graph_replay_matches_eager(dev):
+    """The loop captured as a HIP graph: every replay, with eager work and
+    synchronisations between replays, gives the eager result."""
+    w = custom(V=2056, R=64, rows=33, k=4, seed=21, temps=(0.0, 1.0, 0.7), softcap=30.0)
+    d = workloads.to_device(w, dev)
+    workloads.run(w, d)
+    torch.cuda.synchronize()
+    c_ref, t_ref = workloads.fetch(d)
+    call = m.prepare(w, d)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        call.on(side)()
+    for i in range(4):
+        d["cache"].zero_()
+        d["tokens"].fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        c, t = workloads.fetch(d)
+        assert np.array_equal(t, t_ref), i
+        assert np.array_equal(c, c_ref), i
+        workloads.run(w, d)          # eager work between replays
+        torch.cuda.synchronize()
+    assert not d["workspace"].cpu().numpy().any()
