@@ -132,6 +132,15 @@ const char* markov_status_string(int status);
 
 /* markov_sample_sequential with the exact key taken at every element (no
  * pruning by the cheap key estimate); the tokens must be the same. */
+int markov_debug_sample_fallback(const void* base_logits, const void* w1, const void* w2,
+                                 const int64_t* prev, const int64_t* seeds,
+                                 const int64_t* positions, int32_t k, const float* temperature,
+                                 void* cache, int64_t* tokens, markov_stream_t stream,
+                                 const markov_shape_t* shape, void* workspace,
+                                 size_t workspace_bytes);
+/* (markov_debug_sample_fallback above: every noisy row of every workgroup
+ * takes the exact re-read path that near-ties and non-finite estimates
+ * take; the tokens must be the same.) */
 int markov_debug_sample_exact(const void* base_logits, const void* w1, const void* w2,
                               const int64_t* prev, const int64_t* seeds,
                               const int64_t* positions, int32_t k, const float* temperature,

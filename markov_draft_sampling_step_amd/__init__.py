@@ -49,6 +49,9 @@ _SIGS = {
     "markov_debug_sample_exact": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
                                                  _P, _P, ctypes.POINTER(Shape), _P,
                                                  ctypes.c_size_t]),
+    "markov_debug_sample_fallback": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
+                                                    _P, _P, _P, ctypes.POINTER(Shape), _P,
+                                                    ctypes.c_size_t]),
     "markov_sample_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                           _P, _P, _P, _P, ctypes.POINTER(Shape), _P,
                                           ctypes.c_size_t]),
@@ -153,12 +156,13 @@ def new_workspace(rows: int, vocab: int, rank: int, k: int, device="cuda", strea
 
 def sample_sequential(base_logits, w1, w2, prev, seeds, positions, temperature, cache, tokens,
                       workspace, mult: float = 1.0, softcap: float = 0.0, stream=None,
-                      exact: bool = False, step: int | None = None):
+                      exact: bool = False, step: int | None = None, fallback: bool = False):
     """markov_sample_sequential: base_logits/cache bf16 [rows, k, V], w1/w2 bf16
     [V, R], prev/seeds int64 [rows], positions/tokens int64 [rows, k],
     temperature fp32 [rows], workspace from ``new_workspace``. ``exact`` runs
-    the test-only variant that takes the exact key at every element; ``step``
-    runs that one step of the loop alone (markov_sample_step)."""
+    the test-only variant that takes the exact key at every element,
+    ``fallback`` the one that sends every noisy row through the exact re-read
+    path; ``step`` runs that one step of the loop alone (markov_sample_step)."""
     import torch
 
     rows, k, V = base_logits.shape
@@ -184,7 +188,8 @@ def sample_sequential(base_logits, w1, w2, prev, seeds, positions, temperature, 
         args = args[:7] + (ctypes.c_int32(step),) + args[7:]
         _check(lib().markov_sample_step(*args), "markov_sample_step")
         return
-    fn = lib().markov_debug_sample_exact if exact else lib().markov_sample_sequential
+    fn = (lib().markov_debug_sample_exact if exact else
+          lib().markov_debug_sample_fallback if fallback else lib().markov_sample_sequential)
     _check(fn(*args), "markov_sample_sequential")
 
 
@@ -237,7 +242,8 @@ class PreparedCall:
         _check(self._fn(*self._args), self._what)
 
 
-def prepare(w, d, step: int | None = None, exact: bool = False, stream=None) -> PreparedCall:
+def prepare(w, d, step: int | None = None, exact: bool = False, stream=None,
+            fallback: bool = False) -> PreparedCall:
     """Marshal the arguments of workload `w` on device tensors `d` (see
     ``workloads.to_device``) once."""
     import torch
@@ -268,7 +274,8 @@ def prepare(w, d, step: int | None = None, exact: bool = False, stream=None) -> 
         si = 11
         call = PreparedCall(lib().markov_sample_step, args, si, "markov_sample_step")
     else:
-        fn = lib().markov_debug_sample_exact if exact else lib().markov_sample_sequential
+        fn = (lib().markov_debug_sample_exact if exact else
+              lib().markov_debug_sample_fallback if fallback else lib().markov_sample_sequential)
         call = PreparedCall(fn, args, si, "markov_sample_sequential")
     call._keep = keep
     return call

@@ -39,10 +39,11 @@ constexpr int NONE = 0x7fffffff;       // id of "no element yet"
 constexpr int LDS_EMB_MAX = 128 * 1024;
 constexpr int ROWS_CAP = 1024;
 
-enum Mode { MODE_SAMPLE = 0, MODE_SAMPLE_EXACT = 1, MODE_BIAS = 2 };
+enum Mode { MODE_SAMPLE = 0, MODE_SAMPLE_EXACT = 1, MODE_BIAS = 2, MODE_SAMPLE_FALLBACK = 3 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct StepArgs {
   const uint16_t* base;
@@ -54,8 +55,7 @@ struct StepArgs {
   const float* temperature;
   uint16_t* cache;
   int64_t* tokens;
-  unsigned long long* slots;
-  unsigned int* counter;
+  unsigned long long* slots;  // [3][rows] packed winners, step s uses s % 3
   uint16_t* bias_out;
   int rows, V, R, k, step, nslabs;
   float mult, inv_cap, cap;
@@ -208,88 +208,201 @@ __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *(const uint4*
 
 // ---------------------------------------------------------------- the step
 
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// The winner slot of a row decodes to its token id.
+__device__ __forceinline__ int64_t slot_token(unsigned long long w) {
+  return (int64_t)(uint32_t)(~(uint32_t)w);
+}
+
+// Merge rules of the per-row states. ORDER: the exact (key, id) under the
+// total order. TOP2: (v1, id1, l1) is the element with the largest upper
+// bound v1 of its key, v2 the largest upper bound among all other elements.
+struct RowState {
+  float v1, v2, l1;
+  int id1;
+};
+
+__device__ __forceinline__ void merge_order(RowState& a, const RowState& b) {
+  if (before(b.v1, b.id1, a.v1, a.id1)) {
+    a.v1 = b.v1;
+    a.id1 = b.id1;
+    a.l1 = b.l1;
+  }
+}
+
+__device__ __forceinline__ void merge_top2(RowState& a, const RowState& b) {
+  const bool bw = (b.v1 > a.v1) || (b.v1 == a.v1 && b.id1 < a.id1);
+  const float lose = bw ? a.v1 : b.v1;
+  const float win2 = bw ? b.v2 : a.v2;
+  a.v2 = fmaxf(lose, win2);
+  if (bw) {
+    a.v1 = b.v1;
+    a.id1 = b.id1;
+    a.l1 = b.l1;
+  }
+}
+
+// Upper bound of an exact key from its estimate, less the constant part of
+// the margin (added back at the decision): key <= hi + 1e-3.
+__device__ __forceinline__ float upper_of(float ka) { return __builtin_fmaf(fabsf(ka), 0x1p-18f, ka); }
+
+// Lower bound of the exact key of the element whose upper bound is v1:
+// key >= v1 - 2 * margin, with margin = 1e-3 + |ka| 2^-18 (rounded up).
+__device__ __forceinline__ float lower_of_upper(float v1) {
+  return v1 - 2.5e-3f - fabsf(v1) * 0x1p-16f;
+}
+
+template <int KB>
+__device__ __forceinline__ void load_w2_tile(const uint16_t* w2, int V, int R, int tok0, int m, int g,
+                                             bool kzero, bf16x8_t* A0, bf16x8_t* A1) {
+  const int t0 = tok0 + 8 * (m >> 2) + (m & 3);
+  const int ta = t0 < V ? t0 : V - 1, tb = t0 + 4 < V ? t0 + 4 : V - 1;
+  const uint16_t* pa = w2 + (size_t)ta * R;
+  const uint16_t* pb = w2 + (size_t)tb * R;
+#pragma unroll
+  for (int i = 0; i < KB; ++i) {
+    if (kzero) {
+      A0[i] = (bf16x8_t){};
+      A1[i] = (bf16x8_t){};
+    } else {
+      const int ch = 4 * i + g;
+      A0[i] = __builtin_nontemporal_load((const bf16x8_t*)(pa + ch * 8));
+      A1[i] = __builtin_nontemporal_load((const bf16x8_t*)(pb + ch * 8));
+    }
+  }
+}
+
+constexpr int PF = 4;  // base-logit prefetch depth, in 16-row blocks
+
 template <int KB, int MODE>
 __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
+  constexpr bool DB = KB <= 8;                  // double-buffer the w2 tile in registers
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
-  const int rows = a.rows, rows_pad = (rows + 15) & ~15, R = a.R, V = a.V, s = a.step;
+  const int rows = a.rows, rp = (rows + 15) & ~15, R = a.R, V = a.V, s = a.step, K = a.k;
   const int cpr = R >> 3;                       // 16-byte chunks per embedding row
   const int swz = (cpr < 8 ? cpr : 8) - 1;
+  const int G = gridDim.x;
 
   uint16_t* emb = (uint16_t*)lds;
-  uint32_t* row_prefix = (uint32_t*)(lds + (size_t)rows_pad * R * 2);
-  float* row_T = (float*)(row_prefix + rows_pad);
-  float* row_rcp = row_T + rows_pad;
-  int* row_src = (int*)(row_rcp + rows_pad);
-  float* best_key = (float*)(row_src + rows_pad);  // [NW][rows_pad]
-  int* best_id = (int*)(best_key + NW * rows_pad);
-  int* flag = best_id + NW * rows_pad;
+  int* n_row = (int*)(lds + (size_t)rp * R * 2);  // LDS row n -> request row
+  int* n_src = n_row + rp;                         // its w1 row
+  float* n_T = (float*)(n_src + rp);
+  float* n_rcp = n_T + rp;
+  uint32_t* n_prefix = (uint32_t*)(n_rcp + rp);
+  float* st_v1 = (float*)(n_prefix + rp);          // [NW][rp] running row states
+  float* st_v2 = st_v1 + NW * rp;
+  float* st_l = st_v2 + NW * rp;
+  int* st_id = (int*)(st_l + NW * rp);
+  int* sp_cnt = st_id + NW * rp;                   // [rp] elements whose estimate is not finite
+  int* fb_list = sp_cnt + rp;                      // [rp] rows that take the exact fallback
+  int* misc = fb_list + rp;                        // chunk counts [2][16], fallback count
 
-  // 1. per-row set-up: the token feeding this step, clamped; temperature;
-  //    the hash prefix; empty running winners.
-  for (int r = tid; r < rows_pad; r += BLOCK) {
-    if (r < rows) {
-      int64_t t = (MODE == MODE_BIAS || s == 0) ? a.prev[r] : a.tokens[(int64_t)r * a.k + s - 1];
-      uint64_t ut = (uint64_t)t, last = (uint64_t)(V - 1);
-      row_src[r] = (int)(ut < last ? ut : last);
-      if (MODE != MODE_BIAS) {
-        float T = a.temperature[r];
-        row_T[r] = T;
-        row_rcp[r] = 1.0f / T;
-        row_prefix[r] = row_prefix_of(a.seeds[r], s, a.positions[(int64_t)r * a.k + s]);
+  unsigned long long* slots_cur = a.slots ? a.slots + (size_t)(s % 3) * rows : nullptr;
+  const unsigned long long* slots_prev = a.slots ? a.slots + (size_t)((s + 2) % 3) * rows : nullptr;
+  unsigned long long* slots_next = a.slots ? a.slots + (size_t)((s + 1) % 3) * rows : nullptr;
+
+  // 1. rows: the token feeding this step (decoded from the previous step's
+  //    winner slots), temperature, hash prefix. Noisy rows are placed first
+  //    so that 16-row blocks are of one kind.
+  const int nchunks = (rows + 63) >> 6;
+  for (int c = wave; c < nchunks; c += NW) {
+    const int r = c * 64 + lane;
+    const bool valid = r < rows;
+    const float T = (MODE != MODE_BIAS && valid) ? a.temperature[r] : 0.0f;
+    const bool noisy = valid && !(T == 0.0f);
+    const uint64_t bn = __ballot(noisy), bz = __ballot(valid && !noisy);
+    if (lane == 0) {
+      misc[c] = __builtin_popcountll(bn);
+      misc[16 + c] = __builtin_popcountll(bz);
+    }
+  }
+  for (int n = rows + tid; n < rp; n += BLOCK) {
+    n_row[n] = -1;
+    n_src[n] = 0;
+    n_T[n] = 0.0f;
+    n_rcp[n] = 0.0f;
+    n_prefix[n] = 0u;
+  }
+  for (int i = tid; i < NW * rp; i += BLOCK) {
+    st_v1[i] = -INFINITY;
+    st_v2[i] = -INFINITY;
+    st_l[i] = 0.0f;
+    st_id[i] = NONE;
+  }
+  for (int n = tid; n < rp; n += BLOCK) sp_cnt[n] = 0;
+  if (tid == 0) misc[32] = 0;
+  __syncthreads();
+  int total_noisy = 0;
+  for (int c = 0; c < nchunks; ++c) total_noisy += misc[c];
+  for (int c = wave; c < nchunks; c += NW) {
+    const int r = c * 64 + lane;
+    const bool valid = r < rows;
+    float T = 0.0f;
+    int64_t t = 0;
+    if (valid) {
+      if (MODE != MODE_BIAS) T = a.temperature[r];
+      t = (MODE == MODE_BIAS || s == 0) ? a.prev[r] : slot_token(slots_prev[r]);
+    }
+    const bool noisy = valid && !(T == 0.0f);
+    const uint64_t bn = __ballot(noisy), bz = __ballot(valid && !noisy);
+    int pre_n = 0, pre_z = 0;
+    for (int c2 = 0; c2 < c; ++c2) {
+      pre_n += misc[c2];
+      pre_z += misc[16 + c2];
+    }
+    if (valid) {
+      const int pos = MODE == MODE_BIAS ? r
+                    : noisy ? pre_n + (int)lanes_below(bn)
+                            : total_noisy + pre_z + (int)lanes_below(bz);
+      const uint64_t ut = (uint64_t)t, last = (uint64_t)(V - 1);
+      n_row[pos] = r;
+      n_src[pos] = (int)(ut < last ? ut : last);
+      n_T[pos] = T;
+      n_rcp[pos] = 1.0f / T;
+      n_prefix[pos] = MODE == MODE_BIAS ? 0u : row_prefix_of(a.seeds[r], s, a.positions[(int64_t)r * K + s]);
+      if (MODE != MODE_BIAS && blockIdx.x == 0) {
+        if (s > 0) a.tokens[(int64_t)r * K + s - 1] = t;   // the previous step's token
+        slots_next[r] = 0ull;                             // next step's slots start empty
       }
-    } else {
-      row_src[r] = -1;
-      row_T[r] = 0.0f;
-      row_rcp[r] = 0.0f;
-      row_prefix[r] = 0u;
-    }
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      best_key[w * rows_pad + r] = -INFINITY;
-      best_id[w * rows_pad + r] = NONE;
     }
   }
   __syncthreads();
 
-  // 2. gather the rows' embeddings into LDS (padding rows are zero).
-  for (int c = tid; c < rows_pad * cpr; c += BLOCK) {
-    int n = c / cpr, ch = c - n * cpr;
-    int src = row_src[n];
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (src >= 0) v = ld16(a.w1 + (size_t)src * R + ch * 8);
-    *(uint4*)(emb + (size_t)n * R + ((ch ^ (n & swz)) * 8)) = v;
+  // 2. gather the embeddings straight into LDS (16-byte chunks, swizzled);
+  //    padding rows read row 0 and are never used.
+  {
+    const int total = rp * cpr;
+    for (int j = wave; j * 64 < total; j += NW) {
+      const int p = j * 64 + lane;
+      if (p < total) {
+        const int n = p / cpr, cs = p - n * cpr;
+        const uint16_t* src = a.w1 + (size_t)n_src[n] * R + ((cs ^ (n & swz)) * 8);
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (__attribute__((address_space(3))) void*)(emb + (size_t)j * 512),
+                                         16, 0, 0);
+      }
+    }
   }
+
+  const int nrb = rp >> 4;
+  const bool kzero = (R == 16) && (g >= 2);
+  bf16x8_t Ac0[KB], Ac1[KB], An0[KB], An1[KB];
+  int slab = blockIdx.x;
+  load_w2_tile<KB>(a.w2, V, R, slab * SLAB + wave * TOK_PER_WAVE, m, g, kzero, Ac0, Ac1);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  const int nrb = rows_pad >> 4;
-  const bool kzero = (R == 16) && (g >= 2);     // rank 16 fills half a K=32 block
-
-  for (int slab = blockIdx.x; slab < a.nslabs; slab += gridDim.x) {
+  const float mult = a.mult, cap = a.cap, inv_cap = a.inv_cap;
+  for (; slab < a.nslabs; slab += G) {
+    const int nxt = slab + G;
+    if (DB && nxt < a.nslabs)
+      load_w2_tile<KB>(a.w2, V, R, nxt * SLAB + wave * TOK_PER_WAVE, m, g, kzero, An0, An1);
     const int tok0 = slab * SLAB + wave * TOK_PER_WAVE;
-    if (tok0 >= V) continue;                    // wave-uniform: past the vocabulary
-
-    // A operands: M-tile 0 row mm holds token tok0 + 8(mm/4) + mm%4, M-tile 1
-    // the same + 4; K chunk (4i + g) of the row feeds k-block i, lane group g.
-    bf16x8_t A0[KB], A1[KB];
-    {
-      const int t0 = tok0 + 8 * (m >> 2) + (m & 3);
-      const int ta = t0 < V ? t0 : V - 1, tb = t0 + 4 < V ? t0 + 4 : V - 1;
-      const uint16_t* pa = a.w2 + (size_t)ta * R;
-      const uint16_t* pb = a.w2 + (size_t)tb * R;
-#pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        if (kzero) {
-          A0[i] = (bf16x8_t){};
-          A1[i] = (bf16x8_t){};
-        } else {
-          const int ch = 4 * i + g;
-          A0[i] = *(const bf16x8_t*)(pa + ch * 8);
-          A1[i] = *(const bf16x8_t*)(pb + ch * 8);
-        }
-      }
-    }
     const int tg = tok0 + 8 * g;                // this lane's 8 tokens: tg .. tg+7
     const bool tok_ok = tg < V;
     uint32_t kw[8];
@@ -297,162 +410,246 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kw[e] = mm_token_word((uint32_t)(tg + e));
     }
-
-    for (int rb = 0; rb < nrb; ++rb) {
-      const int n = rb * 16 + m;                // this lane's row
-      f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    // base prefetch ring
+    u32x4_t bq[PF];
 #pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        bf16x8_t B;
-        if (kzero) {
-          B = (bf16x8_t){};
-        } else {
-          const int ch = 4 * i + g;
-          B = *(const bf16x8_t*)(emb + (size_t)n * R + ((ch ^ (n & swz)) * 8));
+    for (int j = 0; j < PF; ++j) {
+      bq[j] = (u32x4_t){0u, 0u, 0u, 0u};
+      const int n = j * 16 + m;
+      if (MODE != MODE_BIAS && j < nrb && tok_ok && n < rows)
+        bq[j] = __builtin_nontemporal_load(
+            (const u32x4_t*)(a.base + ((size_t)n_row[n] * K + s) * (size_t)V + tg));
+    }
+    for (int rb0 = 0; rb0 < nrb; rb0 += PF) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int rb = rb0 + j;
+        if (rb >= nrb) break;
+        const int n = rb * 16 + m;
+        f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+          bf16x8_t B;
+          if (kzero) {
+            B = (bf16x8_t){};
+          } else {
+            const int ch = 4 * i + g;
+            B = *(const bf16x8_t*)(emb + (size_t)n * R + ((ch ^ (n & swz)) * 8));
+          }
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ac0[i], B, c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ac1[i], B, c1, 0, 0, 0);
         }
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[i], B, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[i], B, c1, 0, 0, 0);
-      }
-      const bool active = (n < rows) && tok_ok;
-      // bias rounded once to bf16, two per word, tokens tg .. tg+7
-      uint32_t bw[4];
-      bw[0] = pack_bf16(c0[0], c0[1]);
-      bw[1] = pack_bf16(c0[2], c0[3]);
-      bw[2] = pack_bf16(c1[0], c1[1]);
-      bw[3] = pack_bf16(c1[2], c1[3]);
-
-      if (MODE == MODE_BIAS) {
-        if (active) *(uint4*)(a.bias_out + (size_t)n * V + tg) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-        continue;
-      }
-
-      const float T = row_T[n], rcpT = row_rcp[n];
-      const uint32_t prefix = row_prefix[n];
-      const bool noisy = !(T == 0.0f);
-      float l[8];
-      uint32_t h[8];
-      float lo_max = -INFINITY;
-      float lane_key = -INFINITY;
-      int lane_id = NONE;
-      uint32_t cand = 0u;
-      float hi_e[8];
-      if (active) {
-        const size_t off = ((size_t)n * a.k + s) * (size_t)V + tg;
-        const uint4 bv = ld16(a.base + off);
+        const bool active = (n < rows) && tok_ok;
+        uint32_t bw[4];
+        bw[0] = pack_bf16(c0[0], c0[1]);
+        bw[1] = pack_bf16(c0[2], c0[3]);
+        bw[2] = pack_bf16(c1[0], c1[1]);
+        bw[3] = pack_bf16(c1[2], c1[3]);
+        if (MODE == MODE_BIAS) {
+          if (active)
+            *(uint4*)(a.bias_out + (size_t)n_row[n] * V + tg) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+          continue;
+        }
+        const u32x4_t bv = bq[j];
+        {
+          const int n2 = (rb + PF) * 16 + m;
+          if (rb + PF < nrb && tok_ok && n2 < rows)
+            bq[j] = __builtin_nontemporal_load(
+                (const u32x4_t*)(a.base + ((size_t)n_row[n2] * K + s) * (size_t)V + tg));
+        }
+        const float T = n_T[n], rcpT = n_rcp[n];
+        const uint32_t prefix = n_prefix[n];
+        const bool noisy = !(T == 0.0f);
+        const bool top2 = noisy && MODE != MODE_SAMPLE_EXACT;
+        // logits: bf16 add (one binary32 add, rounded), multiplier, soft cap
         const uint32_t bwd[4] = {bv.x, bv.y, bv.z, bv.w};
+        float l[8];
         uint32_t cw[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          // bf16 add: one binary32 add, rounded to bf16
-          uint32_t xp = pack_bf16(bf_lo(bwd[q]) + bf_lo(bw[q]), bf_hi(bwd[q]) + bf_hi(bw[q]));
-          float y0 = a.mult * bf_lo(xp), y1 = a.mult * bf_hi(xp);
+          const uint32_t xp = pack_bf16(bf_lo(bwd[q]) + bf_lo(bw[q]), bf_hi(bwd[q]) + bf_hi(bw[q]));
+          float y0 = mult * bf_lo(xp), y1 = mult * bf_hi(xp);
           if (a.has_cap) {
-            y0 = a.cap * tanhf(y0 * a.inv_cap);
-            y1 = a.cap * tanhf(y1 * a.inv_cap);
+            y0 = cap * tanhf(y0 * inv_cap);
+            y1 = cap * tanhf(y1 * inv_cap);
           }
           cw[q] = pack_bf16(y0, y1);
           l[2 * q] = bf_lo(cw[q]);
           l[2 * q + 1] = bf_hi(cw[q]);
         }
-        *(uint4*)(a.cache + off) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        if (active)
+          __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]},
+                                      (u32x4_t*)(a.cache + ((size_t)n_row[n] * K + s) * (size_t)V + tg));
 
-        if (!noisy) {
+        RowState st = {-INFINITY, -INFINITY, 0.0f, NONE};
+        if (__any(active && top2)) {
+          if (active && top2) {
+            uint32_t spm = 0u;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (before(l[e], tg + e, lane_key, lane_id)) { lane_key = l[e]; lane_id = tg + e; }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            h[e] = mm_finish(prefix, kw[e]);
-            if (MODE == MODE_SAMPLE_EXACT) {
-              hi_e[e] = __builtin_nanf("");     // every element is a candidate
-            } else {
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t h = mm_finish(prefix, kw[e]);
               float mg;
-              float ka = key_fast(l[e], rcpT, h[e], &mg);
-              if (__builtin_isfinite(ka) && fabsf(ka) < 1e37f) {
-                lo_max = fmaxf(lo_max, ka - mg);
-                hi_e[e] = ka + mg;
+              const float ka = key_fast(l[e], rcpT, h, &mg);
+              const bool ok = fabsf(ka) < 1e37f;
+              const float hx = ok ? upper_of(ka) : -INFINITY;
+              spm |= (ok ? 0u : 1u) << e;
+              // elements arrive in rising id: a tie keeps the earlier as top
+              if (hx > st.v1) {
+                st.v2 = st.v1;
+                st.v1 = hx;
+                st.id1 = tg + e;
+                st.l1 = l[e];
               } else {
-                hi_e[e] = __builtin_nanf("");   // always a candidate
+                st.v2 = fmaxf(st.v2, hx);
+              }
+            }
+            if (spm) atomicAdd(&sp_cnt[n], __builtin_popcount(spm));
+          }
+        }
+        if (__any(active && !top2)) {
+          if (active && !top2) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float key = l[e];
+              if (noisy) key = key_exact(l[e], T, mm_finish(prefix, kw[e]));
+              if (before(key, tg + e, st.v1, st.id1)) {
+                st.v1 = key;
+                st.id1 = tg + e;
+                st.l1 = l[e];
               }
             }
           }
         }
-      }
-      // the row's best lower bound over its 4 lanes (32 tokens)
-      lo_max = fmaxf(lo_max, __shfl_xor(lo_max, 16));
-      lo_max = fmaxf(lo_max, __shfl_xor(lo_max, 32));
-      const float Bk = best_key[wave * rows_pad + n];
-      const int Bi = best_id[wave * rows_pad + n];
-      if (active && noisy) {
-        const bool b_none = (Bi == NONE), b_nan = __builtin_isnan(Bk);
+        // the row's 4 lanes, then the wave's running state for the row
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          bool c;
-          if (__builtin_isnan(hi_e[e])) c = b_none || !b_nan;
-          else c = hi_e[e] >= lo_max && (b_none || (!b_nan && hi_e[e] > Bk));
-          cand |= (c ? 1u : 0u) << e;
+        for (int sh = 16; sh <= 32; sh <<= 1) {
+          RowState o;
+          o.v1 = __shfl_xor(st.v1, sh);
+          o.v2 = __shfl_xor(st.v2, sh);
+          o.l1 = __shfl_xor(st.l1, sh);
+          o.id1 = __shfl_xor(st.id1, sh);
+          if (top2) merge_top2(st, o);
+          else merge_order(st, o);
+        }
+        if (g == 0 && n < rows) {
+          const int i = wave * rp + n;
+          RowState o = {st_v1[i], st_v2[i], st_l[i], st_id[i]};
+          if (top2) merge_top2(st, o);
+          else merge_order(st, o);
+          st_v1[i] = st.v1;
+          st_v2[i] = st.v2;
+          st_l[i] = st.l1;
+          st_id[i] = st.id1;
         }
       }
-      // exact keys of the candidates, one per lane per round
-      while (__any(cand != 0u)) {
-        if (cand != 0u) {
-          const int e = __builtin_ctz(cand);
-          cand &= cand - 1u;
-          const float le = pick8(l, e);
-          const uint32_t he = pick8(h, e);
-          const float kx = key_exact(le, T, he);
-          if (before(kx, tg + e, lane_key, lane_id)) { lane_key = kx; lane_id = tg + e; }
-        }
-      }
-      // the row's winner over its 4 lanes, then into the wave's running best
+    }
+    if (DB) {
 #pragma unroll
-      for (int sh = 16; sh <= 32; sh <<= 1) {
-        float ok = __shfl_xor(lane_key, sh);
-        int oi = __shfl_xor(lane_id, sh);
-        if (before(ok, oi, lane_key, lane_id)) { lane_key = ok; lane_id = oi; }
+      for (int i = 0; i < KB; ++i) {
+        Ac0[i] = An0[i];
+        Ac1[i] = An1[i];
       }
-      if (g == 0 && n < rows && before(lane_key, lane_id, Bk, Bi)) {
-        best_key[wave * rows_pad + n] = lane_key;
-        best_id[wave * rows_pad + n] = lane_id;
-      }
+    } else if (nxt < a.nslabs) {
+      load_w2_tile<KB>(a.w2, V, R, nxt * SLAB + wave * TOK_PER_WAVE, m, g, kzero, Ac0, Ac1);
     }
   }
   if (MODE == MODE_BIAS) return;
 
-  // 3. this workgroup's winner per row -> one packed atomicMax per row.
+  // 3. this workgroup's winner per row: one exact key for the top element
+  //    of a noisy row unless another element's bound reaches it (or an
+  //    estimate was not finite), in which case the row goes to the exact
+  //    fallback below; then one packed atomicMax per row.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int r = tid; r < rows; r += BLOCK) {
-    float bk = best_key[r];
-    int bi = best_id[r];
+  for (int n = tid; n < rows; n += BLOCK) {
+    const float T = n_T[n];
+    const bool noisy = !(T == 0.0f);
+    const bool top2 = noisy && MODE != MODE_SAMPLE_EXACT;
+    RowState st = {st_v1[n], st_v2[n], st_l[n], st_id[n]};
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
-      float k2 = best_key[w * rows_pad + r];
-      int i2 = best_id[w * rows_pad + r];
-      if (before(k2, i2, bk, bi)) { bk = k2; bi = i2; }
+      const int i = w * rp + n;
+      RowState o = {st_v1[i], st_v2[i], st_l[i], st_id[i]};
+      if (top2) merge_top2(st, o);
+      else merge_order(st, o);
     }
-    if (bi != NONE)
-      __hip_atomic_fetch_max(a.slots + r, pack_winner(bk, bi), __ATOMIC_RELAXED,
+    float key = st.v1;
+    if (top2) {
+      const bool near = st.id1 != NONE && st.v2 >= lower_of_upper(st.v1);
+      if (near || sp_cnt[n] > 0 || MODE == MODE_SAMPLE_FALLBACK) {
+        fb_list[atomicAdd(&misc[32], 1)] = n;
+        continue;
+      }
+      key = key_exact(st.l1, T, mm_finish(n_prefix[n], mm_token_word((uint32_t)st.id1)));
+    }
+    if (st.id1 != NONE)
+      __hip_atomic_fetch_max(slots_cur + n_row[n], pack_winner(key, st.id1), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   }
-  // 4. arrival: release this workgroup's maxima; the last to arrive acquires
-  //    them all, writes the step's tokens and re-zeroes slots and counter.
-  __threadfence();
   __syncthreads();
-  if (tid == 0) {
-    unsigned int ticket = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (ticket == gridDim.x - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (*flag) {
-    __threadfence();
-    for (int r = tid; r < rows; r += BLOCK) {
-      unsigned long long w = __hip_atomic_load(a.slots + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      a.tokens[(int64_t)r * a.k + s] = (int64_t)(uint32_t)(~(uint32_t)w);
-      __hip_atomic_store(a.slots + r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // 4. exact fallback: the whole workgroup re-reads the row's cached logits
+  //    over its own slabs and takes every exact key.
+  const int nfb = misc[32];
+  float* red_v = st_v1;  // reuse: [BLOCK / 64] partials
+  int* red_i = st_id;
+  for (int f = 0; f < nfb; ++f) {
+    const int n = fb_list[f];
+    const int r = n_row[n];
+    const float T = n_T[n];
+    const uint32_t prefix = n_prefix[n];
+    float bv = -INFINITY;
+    int bi = NONE;
+    const int per_wg = ((a.nslabs - blockIdx.x + G - 1) / G) * SLAB;
+    for (int i = tid; i < per_wg; i += BLOCK) {
+      const int t = (blockIdx.x + (i / SLAB) * G) * SLAB + (i % SLAB);
+      if (t < V) {
+        const float l = bf_lo((uint32_t)a.cache[((size_t)r * K + s) * (size_t)V + t]);
+        const float key = key_exact(l, T, mm_finish(prefix, mm_token_word((uint32_t)t)));
+        if (before(key, t, bv, bi)) {
+          bv = key;
+          bi = t;
+        }
+      }
     }
-    if (tid == 0) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const float ov = __shfl_xor(bv, sh);
+      const int oi = __shfl_xor(bi, sh);
+      if (before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    __syncthreads();
+    if (lane == 0) {
+      red_v[wave] = bv;
+      red_i[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < NW; ++w)
+        if (before(red_v[w], red_i[w], bv, bi)) {
+          bv = red_v[w];
+          bi = red_i[w];
+        }
+      if (bi != NONE)
+        __hip_atomic_fetch_max(slots_cur + r, pack_winner(bv, bi), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// After the last step: its winners become tokens[:, k-1], and all three
+// slot buffers are left zeroed for the next call.
+__global__ __launch_bounds__(BLOCK) void markov_finish_kernel(unsigned long long* slots, int64_t* tokens,
+                                                              int rows, int k) {
+  for (int r = threadIdx.x; r < rows; r += BLOCK) {
+    const unsigned long long w = slots[(size_t)((k - 1) % 3) * rows + r];
+    tokens[(int64_t)r * k + k - 1] = slot_token(w);
+    slots[r] = 0ull;
+    slots[(size_t)rows + r] = 0ull;
+    slots[(size_t)2 * rows + r] = 0ull;
   }
 }
 
@@ -496,15 +693,22 @@ StepFn pick_kernel(int R) {
 
 bool pow2_rank(int R) { return R >= 16 && R <= 512 && (R & (R - 1)) == 0; }
 
-int32_t max_rows_of(int32_t R) {
-  if (!pow2_rank(R)) return 0;
-  int32_t by_lds = LDS_EMB_MAX / (R * 2);
-  return by_lds < ROWS_CAP ? by_lds : ROWS_CAP;
-}
-
+// LDS of one workgroup: the embeddings, per-row data (5 words), the waves'
+// running row states (4 words each), the special counts and fallback list,
+// and a small misc area.
 size_t lds_bytes(int rows, int R) {
   size_t rp = (size_t)((rows + 15) & ~15);
-  return rp * R * 2 + rp * 4 * 4 + (size_t)NW * rp * 8 + 16;
+  return rp * R * 2 + rp * 5 * 4 + (size_t)NW * rp * 16 + rp * 8 + 64 * 4;
+}
+
+constexpr size_t LDS_MAX = 160 * 1024;
+
+int32_t max_rows_of(int32_t R) {
+  if (!pow2_rank(R)) return 0;
+  int32_t best = 0;
+  for (int32_t rows = 16; rows <= ROWS_CAP; rows += 16)
+    if ((size_t)rows * R * 2 <= (size_t)LDS_EMB_MAX && lds_bytes(rows, R) <= LDS_MAX) best = rows;
+  return best;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -523,7 +727,7 @@ struct LaunchCache {
   size_t lds;
   int grid_cap;
 };
-LaunchCache g_cache[32];
+LaunchCache g_cache[64];
 int g_cache_n = 0;
 
 // Workgroups to launch: as many as are resident at once (occupancy at this
@@ -547,24 +751,12 @@ int launch_grid(StepFn fn, size_t lds, int nslabs, int* grid) {
     return MARKOV_ERR_HIP;
   if (occ < 1) return MARKOV_ERR_ROWS;
   int cap = cus * occ;
-  if (g_cache_n < 32) g_cache[g_cache_n++] = LaunchCache{fn, dev, lds, cap};
+  if (g_cache_n < 64) g_cache[g_cache_n++] = LaunchCache{fn, dev, lds, cap};
   *grid = nslabs < cap ? nslabs : cap;
   return MARKOV_OK;
 }
 
-struct Workspace {
-  unsigned long long* slots;
-  unsigned int* counter;
-};
-
-size_t ws_bytes(int rows) { return (size_t)rows * 8 + 256; }
-
-Workspace ws_layout(void* w, int rows) {
-  Workspace out;
-  out.slots = (unsigned long long*)w;
-  out.counter = (unsigned int*)((unsigned char*)w + (size_t)rows * 8);
-  return out;
-}
+size_t ws_bytes(int rows) { return (size_t)rows * 8 * 3; }
 
 int launch_steps(int mode, const void* base, const void* w1, const void* w2, const int64_t* prev,
                  const int64_t* seeds, const int64_t* positions, int32_t k, int32_t s_begin,
@@ -573,7 +765,8 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
                  void* workspace) {
   StepFn fn = mode == MODE_SAMPLE ? pick_kernel<MODE_SAMPLE>(sh->rank)
             : mode == MODE_SAMPLE_EXACT ? pick_kernel<MODE_SAMPLE_EXACT>(sh->rank)
-                                        : pick_kernel<MODE_BIAS>(sh->rank);
+            : mode == MODE_SAMPLE_FALLBACK ? pick_kernel<MODE_SAMPLE_FALLBACK>(sh->rank)
+                                           : pick_kernel<MODE_BIAS>(sh->rank);
   if (!fn) return MARKOV_ERR_RANK;
   const size_t lds = lds_bytes(sh->rows, sh->rank);
   const int nslabs = (sh->vocab + SLAB - 1) / SLAB;
@@ -592,11 +785,7 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   a.cache = (uint16_t*)cache;
   a.tokens = tokens;
   a.bias_out = (uint16_t*)bias_out;
-  if (workspace) {
-    Workspace ws = ws_layout(workspace, sh->rows);
-    a.slots = ws.slots;
-    a.counter = ws.counter;
-  }
+  a.slots = (unsigned long long*)workspace;
   a.rows = sh->rows;
   a.V = sh->vocab;
   a.R = sh->rank;
@@ -609,6 +798,11 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   for (int s = s_begin; s < s_end; ++s) {
     a.step = s;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(BLOCK), lds, (hipStream_t)stream, a);
+    if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
+  }
+  if (mode != MODE_BIAS && s_end == k) {
+    hipLaunchKernelGGL(markov_finish_kernel, dim3(1), dim3(BLOCK), 0, (hipStream_t)stream,
+                       a.slots, tokens, sh->rows, k);
     if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   }
   return MARKOV_OK;
@@ -677,6 +871,16 @@ int markov_sample_step(const void* base_logits, const void* w1, const void* w2,
   return sample_common(MODE_SAMPLE, base_logits, w1, w2, prev, seeds, positions, k, step,
                        step + 1, temperature, cache, tokens, stream, shape, workspace,
                        workspace_bytes);
+}
+
+int markov_debug_sample_fallback(const void* base_logits, const void* w1, const void* w2,
+                                 const int64_t* prev, const int64_t* seeds,
+                                 const int64_t* positions, int32_t k, const float* temperature,
+                                 void* cache, int64_t* tokens, markov_stream_t stream,
+                                 const markov_shape_t* shape, void* workspace,
+                                 size_t workspace_bytes) {
+  return sample_common(MODE_SAMPLE_FALLBACK, base_logits, w1, w2, prev, seeds, positions, k, 0, k,
+                       temperature, cache, tokens, stream, shape, workspace, workspace_bytes);
 }
 
 int markov_debug_sample_exact(const void* base_logits, const void* w1, const void* w2,

@@ -182,14 +182,15 @@ def to_device(w: Workload, device="cuda") -> dict:
     )
 
 
-def run(w: Workload, d: dict, stream=None, exact: bool = False, step: int | None = None):
+def run(w: Workload, d: dict, stream=None, exact: bool = False, step: int | None = None,
+        fallback: bool = False):
     """One k-step loop of workload `w` on the device tensors `d` (or its one
     step `step`)."""
     from . import sample_sequential
 
     sample_sequential(d["base"], d["w1"], d["w2"], d["prev"], d["seeds"], d["positions"],
                       d["temperature"], d["cache"], d["tokens"], d["workspace"], w.mult,
-                      w.softcap, stream=stream, exact=exact, step=step)
+                      w.softcap, stream=stream, exact=exact, step=step, fallback=fallback)
 
 
 def fetch(d: dict):

@@ -37,10 +37,10 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run_and_check(w, dev, rows=None, exact=False, max_undecided_frac=0.02):
-    say(f"case {w.name} V={w.V} R={w.R} rows={w.rows} k={w.k} exact={exact}")
+def run_and_check(w, dev, rows=None, exact=False, max_undecided_frac=0.02, fallback=False):
+    say(f"case {w.name} V={w.V} R={w.R} rows={w.rows} k={w.k} exact={exact} fallback={fallback}")
     d = workloads.to_device(w, dev)
-    workloads.run(w, d, exact=exact)
+    workloads.run(w, d, exact=exact, fallback=fallback)
     torch.cuda.synchronize()
     cg, tg = workloads.fetch(d)
     rep = parity.check_loop(w, cg, tg, rows=rows, threads=THREADS)
@@ -200,8 +200,9 @@ def test_exact_and_pruned_agree_small(dev):
     w = custom(V=2056, R=64, rows=33, k=4, seed=11, temps=(0.0, 1.0, 0.3))
     cg1, tg1, _ = run_and_check(w, dev)
     cg2, tg2, _ = run_and_check(w, dev, exact=True)
-    assert np.array_equal(tg1, tg2)
-    assert np.array_equal(cg1, cg2)
+    cg3, tg3, _ = run_and_check(w, dev, fallback=True)
+    assert np.array_equal(tg1, tg2) and np.array_equal(tg1, tg3)
+    assert np.array_equal(cg1, cg2) and np.array_equal(cg1, cg3)
 
 
 def test_workspace_reuse_is_deterministic(dev):
@@ -244,8 +245,10 @@ def test_exact_and_pruned_agree_full(dev, name):
     c1, t1 = workloads.fetch(d)
     workloads.run(w, d, exact=True)
     c2, t2 = workloads.fetch(d)
-    assert np.array_equal(t1, t2)
-    assert np.array_equal(c1, c2)
+    workloads.run(w, d, fallback=True)
+    c3, t3 = workloads.fetch(d)
+    assert np.array_equal(t1, t2) and np.array_equal(t1, t3)
+    assert np.array_equal(c1, c2) and np.array_equal(c1, c3)
 
 
 def test_graph_replay_matches_eager(dev):
