@@ -275,13 +275,38 @@ __device__ __forceinline__ void load_w2_tile(const uint16_t* w2, int V, int R, i
   }
 }
 
-constexpr int PF = 4;  // base-logit prefetch depth, in 16-row blocks
+// tanh for the soft cap: an odd minimax polynomial z + z^3 P(z^2) below
+// |z| = 0.625 (fitted here for binary32 Horner evaluation, within 0.7 ulp),
+// else 1 - 2 / (e^{2|z|} + 1) with the hardware exp2 and reciprocal (about
+// 2 ulp). The cache rounds the result to bf16.
+__device__ __forceinline__ float tanh_fast(float z) {
+  const float az = fabsf(z);
+  const float t = z * z;
+  float p = 0x1.18dc88p-9f;
+  p = __builtin_fmaf(p, t, -0x1.0bf272p-7f);
+  p = __builtin_fmaf(p, t, 0x1.638a82p-6f);
+  p = __builtin_fmaf(p, t, -0x1.b9ee7p-5f);
+  p = __builtin_fmaf(p, t, 0x1.111066p-3f);
+  p = __builtin_fmaf(p, t, -0x1.555554p-2f);
+  const float ys = __builtin_fmaf(t * z, p, z);
+  const float e = __builtin_amdgcn_exp2f(az * 2.88539008177792681f);
+  const float r = __builtin_amdgcn_rcpf(e + 1.0f);
+  const float yl = __builtin_copysignf(__builtin_fmaf(-2.0f, r, 1.0f), z);
+  return az < 0.625f ? ys : yl;
+}
 
-template <int KB, int MODE>
-__global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
+constexpr int PF = 2;  // base-logit prefetch depth, in this wave's row blocks
+
+// Waves: 4 token waves (32 tokens each, a 128-token slab) times RG row
+// groups; row block rb belongs to row group rb % RG. The row groups share the
+// workgroup's LDS copy of the embeddings.
+template <int KB, int MODE, int RG>
+__global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
+  constexpr int NWV = 4 * RG;                   // waves per workgroup
+  constexpr int NTH = 64 * NWV;
   extern __shared__ __align__(16) unsigned char lds[];
-  constexpr bool DB = KB <= 8;                  // double-buffer the w2 tile in registers
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wt = wave & 3, wr = wave >> 2;
   const int g = lane >> 4, m = lane & 15;
   const int rows = a.rows, rp = (rows + 15) & ~15, R = a.R, V = a.V, s = a.step, K = a.k;
   const int cpr = R >> 3;                       // 16-byte chunks per embedding row
@@ -294,11 +319,10 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
   float* n_T = (float*)(n_src + rp);
   float* n_rcp = n_T + rp;
   uint32_t* n_prefix = (uint32_t*)(n_rcp + rp);
-  float* st_v1 = (float*)(n_prefix + rp);          // [NW][rp] running row states
-  float* st_v2 = st_v1 + NW * rp;
-  float* st_l = st_v2 + NW * rp;
-  int* st_id = (int*)(st_l + NW * rp);
-  int* sp_cnt = st_id + NW * rp;                   // [rp] elements whose estimate is not finite
+  float* st_v1 = (float*)(n_prefix + rp);          // [4][rp] running row states, by token wave
+  float* st_v2 = st_v1 + 4 * rp;
+  int* st_id = (int*)(st_v2 + 4 * rp);
+  int* sp_cnt = st_id + 4 * rp;                    // [rp] elements whose estimate is not finite
   int* fb_list = sp_cnt + rp;                      // [rp] rows that take the exact fallback
   int* misc = fb_list + rp;                        // chunk counts [2][16], fallback count
 
@@ -310,7 +334,7 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
   //    winner slots), temperature, hash prefix. Noisy rows are placed first
   //    so that 16-row blocks are of one kind.
   const int nchunks = (rows + 63) >> 6;
-  for (int c = wave; c < nchunks; c += NW) {
+  for (int c = wave; c < nchunks; c += NWV) {
     const int r = c * 64 + lane;
     const bool valid = r < rows;
     const float T = (MODE != MODE_BIAS && valid) ? a.temperature[r] : 0.0f;
@@ -321,25 +345,24 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
       misc[16 + c] = __builtin_popcountll(bz);
     }
   }
-  for (int n = rows + tid; n < rp; n += BLOCK) {
+  for (int n = rows + tid; n < rp; n += NTH) {
     n_row[n] = -1;
     n_src[n] = 0;
     n_T[n] = 0.0f;
     n_rcp[n] = 0.0f;
     n_prefix[n] = 0u;
   }
-  for (int i = tid; i < NW * rp; i += BLOCK) {
+  for (int i = tid; i < 4 * rp; i += NTH) {
     st_v1[i] = -INFINITY;
     st_v2[i] = -INFINITY;
-    st_l[i] = 0.0f;
     st_id[i] = NONE;
   }
-  for (int n = tid; n < rp; n += BLOCK) sp_cnt[n] = 0;
+  for (int n = tid; n < rp; n += NTH) sp_cnt[n] = 0;
   if (tid == 0) misc[32] = 0;
   __syncthreads();
   int total_noisy = 0;
   for (int c = 0; c < nchunks; ++c) total_noisy += misc[c];
-  for (int c = wave; c < nchunks; c += NW) {
+  for (int c = wave; c < nchunks; c += NWV) {
     const int r = c * 64 + lane;
     const bool valid = r < rows;
     float T = 0.0f;
@@ -377,7 +400,7 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
   //    padding rows read row 0 and are never used.
   {
     const int total = rp * cpr;
-    for (int j = wave; j * 64 < total; j += NW) {
+    for (int j = wave; j * 64 < total; j += NWV) {
       const int p = j * 64 + lane;
       if (p < total) {
         const int n = p / cpr, cs = p - n * cpr;
@@ -390,19 +413,17 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
   }
 
   const int nrb = rp >> 4;
+  const int my_nrb = nrb > wr ? (nrb - wr + RG - 1) / RG : 0;  // row blocks of this row group
   const bool kzero = (R == 16) && (g >= 2);
-  bf16x8_t Ac0[KB], Ac1[KB], An0[KB], An1[KB];
-  int slab = blockIdx.x;
-  load_w2_tile<KB>(a.w2, V, R, slab * SLAB + wave * TOK_PER_WAVE, m, g, kzero, Ac0, Ac1);
+  bf16x8_t Ac0[KB], Ac1[KB];
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   const float mult = a.mult, cap = a.cap, inv_cap = a.inv_cap;
-  for (; slab < a.nslabs; slab += G) {
-    const int nxt = slab + G;
-    if (DB && nxt < a.nslabs)
-      load_w2_tile<KB>(a.w2, V, R, nxt * SLAB + wave * TOK_PER_WAVE, m, g, kzero, An0, An1);
-    const int tok0 = slab * SLAB + wave * TOK_PER_WAVE;
+  for (int slab = blockIdx.x; slab < a.nslabs; slab += G) {
+    const int tok0 = slab * SLAB + wt * TOK_PER_WAVE;
+    if (tok0 >= V || my_nrb == 0) continue;     // wave-uniform
+    load_w2_tile<KB>(a.w2, V, R, tok0, m, g, kzero, Ac0, Ac1);
     const int tg = tok0 + 8 * g;                // this lane's 8 tokens: tg .. tg+7
     const bool tok_ok = tg < V;
     uint32_t kw[8];
@@ -410,21 +431,22 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kw[e] = mm_token_word((uint32_t)(tg + e));
     }
-    // base prefetch ring
+    // base prefetch ring over this wave's row blocks rb = wr + i * RG
     u32x4_t bq[PF];
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       bq[j] = (u32x4_t){0u, 0u, 0u, 0u};
-      const int n = j * 16 + m;
-      if (MODE != MODE_BIAS && j < nrb && tok_ok && n < rows)
+      const int n = (wr + j * RG) * 16 + m;
+      if (MODE != MODE_BIAS && j < my_nrb && tok_ok && n < rows)
         bq[j] = __builtin_nontemporal_load(
             (const u32x4_t*)(a.base + ((size_t)n_row[n] * K + s) * (size_t)V + tg));
     }
-    for (int rb0 = 0; rb0 < nrb; rb0 += PF) {
+    for (int i0 = 0; i0 < my_nrb; i0 += PF) {
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
-        const int rb = rb0 + j;
-        if (rb >= nrb) break;
+        const int ii = i0 + j;
+        if (ii >= my_nrb) break;
+        const int rb = wr + ii * RG;
         const int n = rb * 16 + m;
         f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -452,8 +474,8 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
         }
         const u32x4_t bv = bq[j];
         {
-          const int n2 = (rb + PF) * 16 + m;
-          if (rb + PF < nrb && tok_ok && n2 < rows)
+          const int n2 = (rb + PF * RG) * 16 + m;
+          if (ii + PF < my_nrb && tok_ok && n2 < rows)
             bq[j] = __builtin_nontemporal_load(
                 (const u32x4_t*)(a.base + ((size_t)n_row[n2] * K + s) * (size_t)V + tg));
         }
@@ -470,8 +492,8 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
           const uint32_t xp = pack_bf16(bf_lo(bwd[q]) + bf_lo(bw[q]), bf_hi(bwd[q]) + bf_hi(bw[q]));
           float y0 = mult * bf_lo(xp), y1 = mult * bf_hi(xp);
           if (a.has_cap) {
-            y0 = cap * tanhf(y0 * inv_cap);
-            y1 = cap * tanhf(y1 * inv_cap);
+            y0 = cap * tanh_fast(y0 * inv_cap);
+            y1 = cap * tanh_fast(y1 * inv_cap);
           }
           cw[q] = pack_bf16(y0, y1);
           l[2 * q] = bf_lo(cw[q]);
@@ -481,7 +503,8 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
           __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]},
                                       (u32x4_t*)(a.cache + ((size_t)n_row[n] * K + s) * (size_t)V + tg));
 
-        RowState st = {-INFINITY, -INFINITY, 0.0f, NONE};
+        float v1 = -INFINITY, v2 = -INFINITY;
+        int id1 = NONE;
         if (__any(active && top2)) {
           if (active && top2) {
             uint32_t spm = 0u;
@@ -494,14 +517,10 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
               const float hx = ok ? upper_of(ka) : -INFINITY;
               spm |= (ok ? 0u : 1u) << e;
               // elements arrive in rising id: a tie keeps the earlier as top
-              if (hx > st.v1) {
-                st.v2 = st.v1;
-                st.v1 = hx;
-                st.id1 = tg + e;
-                st.l1 = l[e];
-              } else {
-                st.v2 = fmaxf(st.v2, hx);
-              }
+              const bool up = hx > v1;
+              v2 = up ? v1 : fmaxf(v2, hx);
+              v1 = up ? hx : v1;
+              id1 = up ? tg + e : id1;
             }
             if (spm) atomicAdd(&sp_cnt[n], __builtin_popcount(spm));
           }
@@ -512,67 +531,58 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
             for (int e = 0; e < 8; ++e) {
               float key = l[e];
               if (noisy) key = key_exact(l[e], T, mm_finish(prefix, kw[e]));
-              if (before(key, tg + e, st.v1, st.id1)) {
-                st.v1 = key;
-                st.id1 = tg + e;
-                st.l1 = l[e];
+              if (before(key, tg + e, v1, id1)) {
+                v1 = key;
+                id1 = tg + e;
               }
             }
           }
         }
-        // the row's 4 lanes, then the wave's running state for the row
+        // the row's 4 lanes, then the token wave's running state for the row
+        RowState st = {v1, v2, 0.0f, id1};
 #pragma unroll
         for (int sh = 16; sh <= 32; sh <<= 1) {
           RowState o;
           o.v1 = __shfl_xor(st.v1, sh);
           o.v2 = __shfl_xor(st.v2, sh);
-          o.l1 = __shfl_xor(st.l1, sh);
+          o.l1 = 0.0f;
           o.id1 = __shfl_xor(st.id1, sh);
           if (top2) merge_top2(st, o);
           else merge_order(st, o);
         }
         if (g == 0 && n < rows) {
-          const int i = wave * rp + n;
-          RowState o = {st_v1[i], st_v2[i], st_l[i], st_id[i]};
+          const int i = wt * rp + n;
+          RowState o = {st_v1[i], st_v2[i], 0.0f, st_id[i]};
           if (top2) merge_top2(st, o);
           else merge_order(st, o);
           st_v1[i] = st.v1;
           st_v2[i] = st.v2;
-          st_l[i] = st.l1;
           st_id[i] = st.id1;
         }
       }
-    }
-    if (DB) {
-#pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        Ac0[i] = An0[i];
-        Ac1[i] = An1[i];
-      }
-    } else if (nxt < a.nslabs) {
-      load_w2_tile<KB>(a.w2, V, R, nxt * SLAB + wave * TOK_PER_WAVE, m, g, kzero, Ac0, Ac1);
     }
   }
   if (MODE == MODE_BIAS) return;
 
   // 3. this workgroup's winner per row: one exact key for the top element
-  //    of a noisy row unless another element's bound reaches it (or an
-  //    estimate was not finite), in which case the row goes to the exact
-  //    fallback below; then one packed atomicMax per row.
+  //    of a noisy row (its cached logit read back) unless another element's
+  //    bound reaches it (or an estimate was not finite), in which case the
+  //    row goes to the exact fallback below; then one packed atomicMax per row.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int n = tid; n < rows; n += BLOCK) {
+  for (int n = tid; n < rows; n += NTH) {
     const float T = n_T[n];
     const bool noisy = !(T == 0.0f);
     const bool top2 = noisy && MODE != MODE_SAMPLE_EXACT;
-    RowState st = {st_v1[n], st_v2[n], st_l[n], st_id[n]};
+    RowState st = {st_v1[n], st_v2[n], 0.0f, st_id[n]};
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
+    for (int w = 1; w < 4; ++w) {
       const int i = w * rp + n;
-      RowState o = {st_v1[i], st_v2[i], st_l[i], st_id[i]};
+      RowState o = {st_v1[i], st_v2[i], 0.0f, st_id[i]};
       if (top2) merge_top2(st, o);
       else merge_order(st, o);
     }
+    const int r = n_row[n];
     float key = st.v1;
     if (top2) {
       const bool near = st.id1 != NONE && st.v2 >= lower_of_upper(st.v1);
@@ -580,10 +590,11 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
         fb_list[atomicAdd(&misc[32], 1)] = n;
         continue;
       }
-      key = key_exact(st.l1, T, mm_finish(n_prefix[n], mm_token_word((uint32_t)st.id1)));
+      const float l1 = bf_lo((uint32_t)a.cache[((size_t)r * K + s) * (size_t)V + st.id1]);
+      key = key_exact(l1, T, mm_finish(n_prefix[n], mm_token_word((uint32_t)st.id1)));
     }
     if (st.id1 != NONE)
-      __hip_atomic_fetch_max(slots_cur + n_row[n], pack_winner(key, st.id1), __ATOMIC_RELAXED,
+      __hip_atomic_fetch_max(slots_cur + r, pack_winner(key, st.id1), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
@@ -591,7 +602,7 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
   // 4. exact fallback: the whole workgroup re-reads the row's cached logits
   //    over its own slabs and takes every exact key.
   const int nfb = misc[32];
-  float* red_v = st_v1;  // reuse: [BLOCK / 64] partials
+  float* red_v = st_v1;  // reuse: [NWV] partials
   int* red_i = st_id;
   for (int f = 0; f < nfb; ++f) {
     const int n = fb_list[f];
@@ -601,7 +612,7 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
     float bv = -INFINITY;
     int bi = NONE;
     const int per_wg = ((a.nslabs - blockIdx.x + G - 1) / G) * SLAB;
-    for (int i = tid; i < per_wg; i += BLOCK) {
+    for (int i = tid; i < per_wg; i += NTH) {
       const int t = (blockIdx.x + (i / SLAB) * G) * SLAB + (i % SLAB);
       if (t < V) {
         const float l = bf_lo((uint32_t)a.cache[((size_t)r * K + s) * (size_t)V + t]);
@@ -628,7 +639,7 @@ __global__ __launch_bounds__(BLOCK) void markov_step_kernel(StepArgs a) {
     }
     __syncthreads();
     if (tid == 0) {
-      for (int w = 1; w < NW; ++w)
+      for (int w = 1; w < NWV; ++w)
         if (before(red_v[w], red_i[w], bv, bi)) {
           bv = red_v[w];
           bi = red_i[w];
@@ -678,17 +689,33 @@ __global__ void debug_bf16_kernel(const float* in, uint16_t* out, int64_t n) {
 
 typedef void (*StepFn)(StepArgs);
 
-template <int MODE>
-StepFn pick_kernel(int R) {
+template <int MODE, int RG>
+StepFn pick_rank(int R) {
   switch (R) {
     case 16:
-    case 32: return markov_step_kernel<1, MODE>;
-    case 64: return markov_step_kernel<2, MODE>;
-    case 128: return markov_step_kernel<4, MODE>;
-    case 256: return markov_step_kernel<8, MODE>;
-    case 512: return markov_step_kernel<16, MODE>;
+    case 32: return markov_step_kernel<1, MODE, RG>;
+    case 64: return markov_step_kernel<2, MODE, RG>;
+    case 128: return markov_step_kernel<4, MODE, RG>;
+    case 256: return markov_step_kernel<8, MODE, RG>;
+    case 512: return markov_step_kernel<16, MODE, RG>;
   }
   return nullptr;
+}
+
+template <int MODE>
+StepFn pick_kernel(int R, int RG) {
+  return RG == 4 ? pick_rank<MODE, 4>(R) : RG == 2 ? pick_rank<MODE, 2>(R) : pick_rank<MODE, 1>(R);
+}
+
+// Row groups per workgroup: when one workgroup's LDS (mostly the
+// embeddings) leaves room for a single workgroup per CU, more waves share it
+// (two row groups; four where the rank is small enough to keep the w2 tile in
+// few registers).
+size_t lds_bytes(int rows, int R);
+
+int row_groups(int rows, int R) {
+  if (lds_bytes(rows, R) <= 80 * 1024) return 1;
+  return R <= 64 ? 4 : 2;
 }
 
 bool pow2_rank(int R) { return R >= 16 && R <= 512 && (R & (R - 1)) == 0; }
@@ -698,7 +725,7 @@ bool pow2_rank(int R) { return R >= 16 && R <= 512 && (R & (R - 1)) == 0; }
 // and a small misc area.
 size_t lds_bytes(int rows, int R) {
   size_t rp = (size_t)((rows + 15) & ~15);
-  return rp * R * 2 + rp * 5 * 4 + (size_t)NW * rp * 16 + rp * 8 + 64 * 4;
+  return rp * R * 2 + rp * 5 * 4 + (size_t)4 * rp * 12 + rp * 8 + 64 * 4;
 }
 
 constexpr size_t LDS_MAX = 160 * 1024;
@@ -732,7 +759,7 @@ int g_cache_n = 0;
 
 // Workgroups to launch: as many as are resident at once (occupancy at this
 // LDS size times the CU count), never more than there are slabs.
-int launch_grid(StepFn fn, size_t lds, int nslabs, int* grid) {
+int launch_grid(StepFn fn, size_t lds, int block, int nslabs, int* grid) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MARKOV_ERR_HIP;
   for (int i = 0; i < g_cache_n; ++i) {
@@ -747,7 +774,7 @@ int launch_grid(StepFn fn, size_t lds, int nslabs, int* grid) {
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MARKOV_ERR_HIP;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)fn, BLOCK, lds) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)fn, block, lds) != hipSuccess)
     return MARKOV_ERR_HIP;
   if (occ < 1) return MARKOV_ERR_ROWS;
   int cap = cus * occ;
@@ -763,15 +790,17 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
                  int32_t s_end, const float* temperature, void* cache, int64_t* tokens,
                  void* bias_out, markov_stream_t stream, const markov_shape_t* sh,
                  void* workspace) {
-  StepFn fn = mode == MODE_SAMPLE ? pick_kernel<MODE_SAMPLE>(sh->rank)
-            : mode == MODE_SAMPLE_EXACT ? pick_kernel<MODE_SAMPLE_EXACT>(sh->rank)
-            : mode == MODE_SAMPLE_FALLBACK ? pick_kernel<MODE_SAMPLE_FALLBACK>(sh->rank)
-                                           : pick_kernel<MODE_BIAS>(sh->rank);
+  const int rg = row_groups(sh->rows, sh->rank);
+  StepFn fn = mode == MODE_SAMPLE ? pick_kernel<MODE_SAMPLE>(sh->rank, rg)
+            : mode == MODE_SAMPLE_EXACT ? pick_kernel<MODE_SAMPLE_EXACT>(sh->rank, rg)
+            : mode == MODE_SAMPLE_FALLBACK ? pick_kernel<MODE_SAMPLE_FALLBACK>(sh->rank, rg)
+                                           : pick_kernel<MODE_BIAS>(sh->rank, rg);
   if (!fn) return MARKOV_ERR_RANK;
   const size_t lds = lds_bytes(sh->rows, sh->rank);
   const int nslabs = (sh->vocab + SLAB - 1) / SLAB;
+  const int block = 256 * rg;
   int grid = 0;
-  int rc = launch_grid(fn, lds, nslabs, &grid);
+  int rc = launch_grid(fn, lds, block, nslabs, &grid);
   if (rc) return rc;
   StepArgs a;
   memset(&a, 0, sizeof(a));
@@ -797,7 +826,7 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   a.inv_cap = a.has_cap ? 1.0f / sh->softcap : 0.0f;
   for (int s = s_begin; s < s_end; ++s) {
     a.step = s;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(BLOCK), lds, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(block), lds, (hipStream_t)stream, a);
     if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   }
   if (mode != MODE_BIAS && s_end == k) {
