@@ -57,7 +57,7 @@ struct StepArgs {
   int64_t* tokens;
   unsigned long long* slots;  // [3][rows] packed winners, step s uses s % 3
   uint16_t* bias_out;
-  int rows, V, R, k, step, nslabs;
+  int rows, V, R, k, step, nslabs, mode;
   float mult, inv_cap, cap;
   int has_cap;
 };
@@ -101,7 +101,7 @@ __device__ __forceinline__ uint32_t mm_token_word(uint32_t id) {
 __device__ __forceinline__ uint32_t mm_finish(uint32_t prefix, uint32_t token_word) {
   uint32_t h = prefix ^ token_word;
   h = rotl32(h, 13);
-  h = h * 5u + 0xe6546b64u;
+  h = (h << 2) + h + 0xe6546b64u;   // h * 5 + c
   h ^= 16u;                       // message length in bytes
   h ^= h >> 16;
   h *= 0x85ebca6bu;
@@ -154,24 +154,27 @@ __device__ __noinline__ float key_exact(float l, float T, uint32_t h) {
   return q - lb;
 }
 
-// Cheap key estimate and its error margin. y = -log(1 - u) by a 4-term
-// series below u = 1/16 (truncation < 4e-6 relative), else by the hardware
-// log2; the outer log by the hardware log2. |key_fast - key_exact| stays far
-// inside `margin` (1e-3 absolute plus 2^-18 relative), which the tests check
-// against the exact key over the hash range.
+// Cheap key estimate. The uniform is taken with one conversion (within
+// 2^-23 relative of the exact one); y2 = -log2(1 - u) by u (1 + u/2) / ln 2
+// below u = 2^-10, else by the hardware log2 of max(1 - u, 2^-24); then
+// key ~ l / T - ln(y2 ln 2) = l rcp(T) + (-ln ln 2) - ln2 log2(y2).
+// |key_fast - key_exact| <= 1e-3 + |key_fast| 2^-18 (the margin the kernel
+// trusts; the tests check it against the exact key over many hashes): the
+// estimate's own error is below 1e-4 plus a few ulps of |l / T| <= |key| + 23.
 constexpr float LN2F = 0.693147180559945309f;
+constexpr float LOG2EF = 1.44269504088896341f;
+constexpr float NEG_LN_LN2 = 0.366512920581664327f;
 
-__device__ __forceinline__ float key_fast(float l, float rcpT, uint32_t h, float* margin) {
-  float u = uniform_of(h);
-  float ys = u * __builtin_fmaf(u, __builtin_fmaf(u, __builtin_fmaf(u, 0.25f, 1.0f / 3.0f), 0.5f), 1.0f);
-  float yl = -LN2F * __builtin_amdgcn_logf(fmaxf(1.0f - u, 0x1p-24f));
-  float y = u < 0.0625f ? ys : yl;
-  float g = -LN2F * __builtin_amdgcn_logf(y);
-  float q = l * rcpT;
-  float ka = q + g;
-  *margin = 1e-3f + (fabsf(q) + fabsf(ka)) * 0x1p-18f;
-  return ka;
+__device__ __forceinline__ float key_fast(float l, float rcpT, uint32_t h) {
+  const float u = __builtin_fmaf((float)h, 0x1p-32f, 0x1p-33f);
+  const float ys = u * __builtin_fmaf(u, 0.5f * LOG2EF, LOG2EF);
+  const float yl = -__builtin_amdgcn_logf(fmaxf(1.0f - u, 0x1p-24f));
+  const float y2 = u < 0x1p-10f ? ys : yl;
+  const float qc = __builtin_fmaf(l, rcpT, NEG_LN_LN2);
+  return __builtin_fmaf(-LN2F, __builtin_amdgcn_logf(y2), qc);
 }
+
+__device__ __forceinline__ float fast_margin(float ka) { return __builtin_fmaf(fabsf(ka), 0x1p-18f, 1e-3f); }
 
 // The total order of every argmax here: a NaN beats every non-NaN, lower
 // id among NaNs; otherwise the larger value, and equal values (so -0 == +0)
@@ -279,8 +282,7 @@ __device__ __forceinline__ void load_w2_tile(const uint16_t* w2, int V, int R, i
 // |z| = 0.625 (fitted here for binary32 Horner evaluation, within 0.7 ulp),
 // else 1 - 2 / (e^{2|z|} + 1) with the hardware exp2 and reciprocal (about
 // 2 ulp). The cache rounds the result to bf16.
-__device__ __forceinline__ float tanh_fast(float z) {
-  const float az = fabsf(z);
+__device__ __forceinline__ float tanh_poly(float z) {
   const float t = z * z;
   float p = 0x1.18dc88p-9f;
   p = __builtin_fmaf(p, t, -0x1.0bf272p-7f);
@@ -288,40 +290,88 @@ __device__ __forceinline__ float tanh_fast(float z) {
   p = __builtin_fmaf(p, t, -0x1.b9ee7p-5f);
   p = __builtin_fmaf(p, t, 0x1.111066p-3f);
   p = __builtin_fmaf(p, t, -0x1.555554p-2f);
-  const float ys = __builtin_fmaf(t * z, p, z);
+  return __builtin_fmaf(t * z, p, z);
+}
+
+__device__ __forceinline__ float tanh_fast(float z) {
+  const float az = fabsf(z);
   const float e = __builtin_amdgcn_exp2f(az * 2.88539008177792681f);
   const float r = __builtin_amdgcn_rcpf(e + 1.0f);
   const float yl = __builtin_copysignf(__builtin_fmaf(-2.0f, r, 1.0f), z);
-  return az < 0.625f ? ys : yl;
+  return az < 0.625f ? tanh_poly(z) : yl;
 }
 
-constexpr int PF = 2;  // base-logit prefetch depth, in this wave's row blocks
+// Per-lane view of one of the wave's row blocks, kept in registers for the
+// whole step: the row's offset into base/cache, 1/T, the hash prefix, its
+// kind, and the running state of this lane's elements of the row.
+
+// Per LDS row n, one 16-byte record: rk = row * k + step (the row's slice of
+// base / cache starts at rk * V), 1/T, the hash prefix and T.
+struct RowInfo {
+  int rk;
+  float rcp;
+  uint32_t prefix;
+  float T;
+};
+typedef RowInfo RowInfoReg;
+struct LaneRow {
+  float v1, v2, l1;
+  int id1;
+  RowInfoReg info;   // the row's constants, when kept in registers
+};
+constexpr int PFD = 2;  // base logits are requested this many row blocks ahead
+
+// The bias of one 16-row block for the wave's 32 tokens: lane (g, m) gets
+// row n = 16 rb + m, tokens tg .. tg+3 in c0 and tg+4 .. tg+7 in c1.
+template <int KB>
+__device__ __forceinline__ void block_bias(const bf16x8_t* A0, const bf16x8_t* A1, const uint16_t* emb,
+                                           int n, int R, int g, int swz, bool kzero, f32x4_t& c0,
+                                           f32x4_t& c1) {
+  c0 = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  c1 = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < KB; ++i) {
+    bf16x8_t B;
+    if (kzero) {
+      B = (bf16x8_t){};
+    } else {
+      const int ch = 4 * i + g;
+      B = *(const bf16x8_t*)(emb + (size_t)n * R + ((ch ^ (n & swz)) * 8));
+    }
+    c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[i], B, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[i], B, c1, 0, 0, 0);
+  }
+}
 
 // Waves: 4 token waves (32 tokens each, a 128-token slab) times RG row
-// groups; row block rb belongs to row group rb % RG. The row groups share the
-// workgroup's LDS copy of the embeddings.
-template <int KB, int MODE, int RG>
+// groups; the wave's row blocks are rb = wr + j RG, j < MRB (unrolled, so
+// their state lives in registers). Row groups share the workgroup's LDS copy
+// of the embeddings.
+template <int KB, int RG, int MRB, bool EXACT>
 __global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
   constexpr int NWV = 4 * RG;                   // waves per workgroup
   constexpr int NTH = 64 * NWV;
   extern __shared__ __align__(16) unsigned char lds[];
+  const int mode = a.mode;
+  const bool bias_mode = mode == MODE_BIAS;
+  constexpr bool exact_mode = EXACT;   // the test-only exact-everywhere variant
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wt = wave & 3, wr = wave >> 2;
   const int g = lane >> 4, m = lane & 15;
-  const int rows = a.rows, rp = (rows + 15) & ~15, R = a.R, V = a.V, s = a.step, K = a.k;
+  const int R = KB >= 2 ? 32 * KB : a.R;         // the rank is fixed by KB from 64 up
+  const int rows = a.rows, rp = (rows + 15) & ~15, V = a.V, s = a.step, K = a.k;
   const int cpr = R >> 3;                       // 16-byte chunks per embedding row
-  const int swz = (cpr < 8 ? cpr : 8) - 1;
+  const int swz = (cpr < 16 ? cpr : 16) - 1;   // a 16-lane LDS pass reads 16 distinct chunks
   const int G = gridDim.x;
 
   uint16_t* emb = (uint16_t*)lds;
-  int* n_row = (int*)(lds + (size_t)rp * R * 2);  // LDS row n -> request row
+  RowInfo* n_info = (RowInfo*)(lds + (size_t)rp * R * 2);  // by LDS row n
+  int* n_row = (int*)(n_info + rp);                // LDS row n -> request row
   int* n_src = n_row + rp;                         // its w1 row
-  float* n_T = (float*)(n_src + rp);
-  float* n_rcp = n_T + rp;
-  uint32_t* n_prefix = (uint32_t*)(n_rcp + rp);
-  float* st_v1 = (float*)(n_prefix + rp);          // [4][rp] running row states, by token wave
+  float* st_v1 = (float*)(n_src + rp);             // [4][rp] row states, by token wave
   float* st_v2 = st_v1 + 4 * rp;
-  int* st_id = (int*)(st_v2 + 4 * rp);
+  float* st_l = st_v2 + 4 * rp;
+  int* st_id = (int*)(st_l + 4 * rp);
   int* sp_cnt = st_id + 4 * rp;                    // [rp] elements whose estimate is not finite
   int* fb_list = sp_cnt + rp;                      // [rp] rows that take the exact fallback
   int* misc = fb_list + rp;                        // chunk counts [2][16], fallback count
@@ -337,7 +387,7 @@ __global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
   for (int c = wave; c < nchunks; c += NWV) {
     const int r = c * 64 + lane;
     const bool valid = r < rows;
-    const float T = (MODE != MODE_BIAS && valid) ? a.temperature[r] : 0.0f;
+    const float T = (!bias_mode && valid) ? a.temperature[r] : 0.0f;
     const bool noisy = valid && !(T == 0.0f);
     const uint64_t bn = __ballot(noisy), bz = __ballot(valid && !noisy);
     if (lane == 0) {
@@ -346,16 +396,9 @@ __global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
     }
   }
   for (int n = rows + tid; n < rp; n += NTH) {
-    n_row[n] = -1;
+    n_row[n] = 0;
     n_src[n] = 0;
-    n_T[n] = 0.0f;
-    n_rcp[n] = 0.0f;
-    n_prefix[n] = 0u;
-  }
-  for (int i = tid; i < 4 * rp; i += NTH) {
-    st_v1[i] = -INFINITY;
-    st_v2[i] = -INFINITY;
-    st_id[i] = NONE;
+    n_info[n] = RowInfo{s, 0.0f, 0u, 0.0f};
   }
   for (int n = tid; n < rp; n += NTH) sp_cnt[n] = 0;
   if (tid == 0) misc[32] = 0;
@@ -368,8 +411,8 @@ __global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
     float T = 0.0f;
     int64_t t = 0;
     if (valid) {
-      if (MODE != MODE_BIAS) T = a.temperature[r];
-      t = (MODE == MODE_BIAS || s == 0) ? a.prev[r] : slot_token(slots_prev[r]);
+      if (!bias_mode) T = a.temperature[r];
+      t = (bias_mode || s == 0) ? a.prev[r] : slot_token(slots_prev[r]);
     }
     const bool noisy = valid && !(T == 0.0f);
     const uint64_t bn = __ballot(noisy), bz = __ballot(valid && !noisy);
@@ -379,16 +422,16 @@ __global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
       pre_z += misc[16 + c2];
     }
     if (valid) {
-      const int pos = MODE == MODE_BIAS ? r
+      const int pos = bias_mode ? r
                     : noisy ? pre_n + (int)lanes_below(bn)
                             : total_noisy + pre_z + (int)lanes_below(bz);
       const uint64_t ut = (uint64_t)t, last = (uint64_t)(V - 1);
       n_row[pos] = r;
       n_src[pos] = (int)(ut < last ? ut : last);
-      n_T[pos] = T;
-      n_rcp[pos] = 1.0f / T;
-      n_prefix[pos] = MODE == MODE_BIAS ? 0u : row_prefix_of(a.seeds[r], s, a.positions[(int64_t)r * K + s]);
-      if (MODE != MODE_BIAS && blockIdx.x == 0) {
+      n_info[pos] = RowInfo{r * K + s, 1.0f / T,
+                            bias_mode ? 0u : row_prefix_of(a.seeds[r], s, a.positions[(int64_t)r * K + s]),
+                            T};
+      if (!bias_mode && blockIdx.x == 0) {
         if (s > 0) a.tokens[(int64_t)r * K + s - 1] = t;   // the previous step's token
         slots_next[r] = 0ull;                             // next step's slots start empty
       }
@@ -412,173 +455,244 @@ __global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
     }
   }
 
+  // this lane's rows, one per row block of the wave
   const int nrb = rp >> 4;
-  const int my_nrb = nrb > wr ? (nrb - wr + RG - 1) / RG : 0;  // row blocks of this row group
-  const bool kzero = (R == 16) && (g >= 2);
-  bf16x8_t Ac0[KB], Ac1[KB];
+  const int my_nrb = nrb > wr ? (nrb - wr + RG - 1) / RG : 0;
+  // small row-block counts keep each row's constants in registers (they feed
+  // the base-logit addresses); large ones read them from LDS per tile
+  constexpr bool ROWREG = MRB <= 4;
+  LaneRow lr[MRB];
+#pragma unroll
+  for (int j = 0; j < MRB; ++j) {
+    if (ROWREG) {
+      const int n = (wr + j * RG) * 16 + m;
+      lr[j].info = n_info[j < my_nrb ? n : 0];
+    }
+    lr[j].v1 = -INFINITY;
+    lr[j].v2 = -INFINITY;
+    lr[j].l1 = 0.0f;
+    lr[j].id1 = NONE;
+  }
+  const bool kzero = (KB == 1) && (R == 16) && (g >= 2);
+  bf16x8_t A0[KB], A1[KB];
+  int slab = blockIdx.x;
+  if (my_nrb > 0) load_w2_tile<KB>(a.w2, V, R, slab * SLAB + wt * TOK_PER_WAVE, m, g, kzero, A0, A1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  // D: row blocks whose contraction is issued ahead of the current epilogue;
+  // once the slab's last contraction is out, the next slab's w2 tile is
+  // requested, so it streams in under the remaining epilogues.
+#ifndef MARKOV_AHEAD
+#define MARKOV_AHEAD 1
+#endif
+#ifndef MARKOV_XSLAB
+#define MARKOV_XSLAB 0
+#endif
+  constexpr int D = MRB - 1 < MARKOV_AHEAD ? MRB - 1 : MARKOV_AHEAD;
   const float mult = a.mult, cap = a.cap, inv_cap = a.inv_cap;
-  for (int slab = blockIdx.x; slab < a.nslabs; slab += G) {
-    const int tok0 = slab * SLAB + wt * TOK_PER_WAVE;
-    if (tok0 >= V || my_nrb == 0) continue;     // wave-uniform
-    load_w2_tile<KB>(a.w2, V, R, tok0, m, g, kzero, Ac0, Ac1);
-    const int tg = tok0 + 8 * g;                // this lane's 8 tokens: tg .. tg+7
-    const bool tok_ok = tg < V;
-    uint32_t kw[8];
-    if (MODE != MODE_BIAS) {
+  u32x4_t bq[MRB];
+  if (my_nrb > 0) {
+    for (; slab < a.nslabs; slab += G) {
+      if (!MARKOV_XSLAB || slab == (int)blockIdx.x) {
+        const int tg0 = slab * SLAB + wt * TOK_PER_WAVE + 8 * g;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kw[e] = mm_token_word((uint32_t)(tg + e));
-    }
-    // base prefetch ring over this wave's row blocks rb = wr + i * RG
-    u32x4_t bq[PF];
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      bq[j] = (u32x4_t){0u, 0u, 0u, 0u};
-      const int n = (wr + j * RG) * 16 + m;
-      if (MODE != MODE_BIAS && j < my_nrb && tok_ok && n < rows)
-        bq[j] = __builtin_nontemporal_load(
-            (const u32x4_t*)(a.base + ((size_t)n_row[n] * K + s) * (size_t)V + tg));
-    }
-    for (int i0 = 0; i0 < my_nrb; i0 += PF) {
-#pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int ii = i0 + j;
-        if (ii >= my_nrb) break;
-        const int rb = wr + ii * RG;
-        const int n = rb * 16 + m;
-        f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < KB; ++i) {
-          bf16x8_t B;
-          if (kzero) {
-            B = (bf16x8_t){};
-          } else {
-            const int ch = 4 * i + g;
-            B = *(const bf16x8_t*)(emb + (size_t)n * R + ((ch ^ (n & swz)) * 8));
-          }
-          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ac0[i], B, c0, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ac1[i], B, c1, 0, 0, 0);
+        for (int j = 0; j < MRB; ++j) {
+          bq[j] = (u32x4_t){0u, 0u, 0u, 0u};
+          const int n = (wr + j * RG) * 16 + m;
+          if (!bias_mode && j < PFD && j < my_nrb && n < rows && tg0 < V)
+            bq[j] = __builtin_nontemporal_load(
+                (const u32x4_t*)(a.base + (size_t)(ROWREG ? lr[j].info.rk : n_info[n].rk) * V + tg0));
         }
-        const bool active = (n < rows) && tok_ok;
+      }
+      const int tok0 = slab * SLAB + wt * TOK_PER_WAVE;
+      const int nxt = slab + G;
+      const int tg = tok0 + 8 * g;              // this lane's 8 tokens: tg .. tg+7
+      const int tgn = tg + G * SLAB;            // the same lane's tokens in the next slab
+      const bool tok_ok = tg < V, tokn_ok = nxt < a.nslabs && tgn < V;
+      if (tok0 >= V) continue;                  // wave-uniform: the last slab's tail
+      uint32_t kw[8];
+      if (!bias_mode) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kw[e] = mm_token_word((uint32_t)(tg + e));
+      }
+      f32x4_t cb0[MRB], cb1[MRB];
+      bool a_out = false;                       // next slab's tile requested
+#pragma unroll
+      for (int j = 0; j < D; ++j)
+        if (j < my_nrb) block_bias<KB>(A0, A1, emb, (wr + j * RG) * 16 + m, R, g, swz, kzero, cb0[j], cb1[j]);
+      if (my_nrb <= D && nxt < a.nslabs) {
+        load_w2_tile<KB>(a.w2, V, R, nxt * SLAB + wt * TOK_PER_WAVE, m, g, kzero, A0, A1);
+        a_out = true;
+      }
+#pragma unroll
+      for (int j = 0; j < MRB; ++j) {
+        if (j >= my_nrb) break;
+        const int n = (wr + j * RG) * 16 + m;
+        if (j + D < MRB && j + D < my_nrb) {
+          block_bias<KB>(A0, A1, emb, n + D * RG * 16, R, g, swz, kzero, cb0[j + D], cb1[j + D]);
+          if (j + D == my_nrb - 1 && nxt < a.nslabs) {
+            load_w2_tile<KB>(a.w2, V, R, nxt * SLAB + wt * TOK_PER_WAVE, m, g, kzero, A0, A1);
+            a_out = true;
+          }
+        }
+        // base logits PFD row blocks ahead, into the next slab past the end
+        if (!bias_mode) {
+          if (j + PFD < MRB) {
+            const int n2 = n + PFD * RG * 16;
+            if (n2 < rows && tok_ok && j + PFD < my_nrb)
+              bq[j + PFD] = __builtin_nontemporal_load(
+                  (const u32x4_t*)(a.base + (size_t)(ROWREG ? lr[j + PFD].info.rk : n_info[n2].rk) * V + tg));
+          }
+        }
+        const RowInfo info = ROWREG ? lr[j].info : n_info[n];
+        const f32x4_t c0 = cb0[j], c1 = cb1[j];
+        const bool valid = n < rows;
+        const bool active = valid && tok_ok;
+        const bool noisy = !(info.T == 0.0f);
+        const bool top2 = noisy && !exact_mode;
         uint32_t bw[4];
         bw[0] = pack_bf16(c0[0], c0[1]);
         bw[1] = pack_bf16(c0[2], c0[3]);
         bw[2] = pack_bf16(c1[0], c1[1]);
         bw[3] = pack_bf16(c1[2], c1[3]);
-        if (MODE == MODE_BIAS) {
+        if (bias_mode) {
           if (active)
             *(uint4*)(a.bias_out + (size_t)n_row[n] * V + tg) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-          continue;
-        }
-        const u32x4_t bv = bq[j];
-        {
-          const int n2 = (rb + PF * RG) * 16 + m;
-          if (ii + PF < my_nrb && tok_ok && n2 < rows)
-            bq[j] = __builtin_nontemporal_load(
-                (const u32x4_t*)(a.base + ((size_t)n_row[n2] * K + s) * (size_t)V + tg));
-        }
-        const float T = n_T[n], rcpT = n_rcp[n];
-        const uint32_t prefix = n_prefix[n];
-        const bool noisy = !(T == 0.0f);
-        const bool top2 = noisy && MODE != MODE_SAMPLE_EXACT;
-        // logits: bf16 add (one binary32 add, rounded), multiplier, soft cap
-        const uint32_t bwd[4] = {bv.x, bv.y, bv.z, bv.w};
-        float l[8];
-        uint32_t cw[4];
+        } else {
+          const u32x4_t bv = bq[j];
+          // this slot is free again: the next slab's logits for the same row
+          if (MARKOV_XSLAB && j < PFD) {
+            bq[j] = (u32x4_t){0u, 0u, 0u, 0u};
+            if (valid && tokn_ok && (my_nrb > PFD || j + PFD >= my_nrb))
+              bq[j] = __builtin_nontemporal_load((const u32x4_t*)(a.base + (size_t)info.rk * V + tgn));
+          }
+          // logits: bf16 add (one binary32 add, rounded), multiplier, soft cap
+          const uint32_t bwd[4] = {bv.x, bv.y, bv.z, bv.w};
+          float l[8];
+          uint32_t cw[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t xp = pack_bf16(bf_lo(bwd[q]) + bf_lo(bw[q]), bf_hi(bwd[q]) + bf_hi(bw[q]));
-          float y0 = mult * bf_lo(xp), y1 = mult * bf_hi(xp);
+          for (int q = 0; q < 4; ++q)
+            cw[q] = pack_bf16(bf_lo(bwd[q]) + bf_lo(bw[q]), bf_hi(bwd[q]) + bf_hi(bw[q]));
           if (a.has_cap) {
-            y0 = cap * tanh_fast(y0 * inv_cap);
-            y1 = cap * tanh_fast(y1 * inv_cap);
-          }
-          cw[q] = pack_bf16(y0, y1);
-          l[2 * q] = bf_lo(cw[q]);
-          l[2 * q + 1] = bf_hi(cw[q]);
-        }
-        if (active)
-          __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]},
-                                      (u32x4_t*)(a.cache + ((size_t)n_row[n] * K + s) * (size_t)V + tg));
-
-        float v1 = -INFINITY, v2 = -INFINITY;
-        int id1 = NONE;
-        if (__any(active && top2)) {
-          if (active && top2) {
-            uint32_t spm = 0u;
+            float z[8];
+            float zmax = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t h = mm_finish(prefix, kw[e]);
-              float mg;
-              const float ka = key_fast(l[e], rcpT, h, &mg);
-              const bool ok = fabsf(ka) < 1e37f;
-              const float hx = ok ? upper_of(ka) : -INFINITY;
-              spm |= (ok ? 0u : 1u) << e;
-              // elements arrive in rising id: a tie keeps the earlier as top
-              const bool up = hx > v1;
-              v2 = up ? v1 : fmaxf(v2, hx);
-              v1 = up ? hx : v1;
-              id1 = up ? tg + e : id1;
+            for (int q = 0; q < 4; ++q) {
+              z[2 * q] = (mult * bf_lo(cw[q])) * inv_cap;
+              z[2 * q + 1] = (mult * bf_hi(cw[q])) * inv_cap;
+              zmax = fmaxf(zmax, fmaxf(fabsf(z[2 * q]), fabsf(z[2 * q + 1])));
             }
-            if (spm) atomicAdd(&sp_cnt[n], __builtin_popcount(spm));
-          }
-        }
-        if (__any(active && !top2)) {
-          if (active && !top2) {
+            if (__any(!(zmax < 0.625f))) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              float key = l[e];
-              if (noisy) key = key_exact(l[e], T, mm_finish(prefix, kw[e]));
-              if (before(key, tg + e, v1, id1)) {
-                v1 = key;
-                id1 = tg + e;
+              for (int q = 0; q < 4; ++q)
+                cw[q] = pack_bf16(cap * tanh_fast(z[2 * q]), cap * tanh_fast(z[2 * q + 1]));
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                cw[q] = pack_bf16(cap * tanh_poly(z[2 * q]), cap * tanh_poly(z[2 * q + 1]));
+            }
+          } else if (mult != 1.0f) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              cw[q] = pack_bf16(mult * bf_lo(cw[q]), mult * bf_hi(cw[q]));
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            l[2 * q] = bf_lo(cw[q]);
+            l[2 * q + 1] = bf_hi(cw[q]);
+          }
+          if (active)
+            __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]},
+                                        (u32x4_t*)(a.cache + (size_t)info.rk * V + tg));
+
+          if (__any(active && top2)) {
+            if (active && top2) {
+              bool special = false;
+              float v1 = lr[j].v1, v2 = lr[j].v2;
+              int eb = -1;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t h = mm_finish(info.prefix, kw[e]);
+                const float ka = key_fast(l[e], info.rcp, h);
+                const bool bad = !(fabsf(ka) < 1e37f);
+                special = special || bad;
+                const float hx = bad ? -INFINITY : upper_of(ka);
+                // elements arrive in rising id: a tie keeps the earlier as top
+                eb = hx > v1 ? e : eb;
+                v2 = __builtin_amdgcn_fmed3f(v1, v2, hx);
+                v1 = fmaxf(v1, hx);
+              }
+              lr[j].v1 = v1;
+              lr[j].v2 = v2;
+              if (eb >= 0) {
+                lr[j].id1 = tg + eb;
+                lr[j].l1 = pick8(l, eb);
+              }
+              if (special) atomicAdd(&sp_cnt[n], 1);
+            }
+          }
+          // keep each row block's live ranges to itself
+          if (__any(active && !top2)) {
+            if (active && !top2) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                float key = l[e];
+                if (noisy) key = key_exact(l[e], info.T, mm_finish(info.prefix, kw[e]));
+                if (before(key, tg + e, lr[j].v1, lr[j].id1)) {
+                  lr[j].v1 = key;
+                  lr[j].id1 = tg + e;
+                }
               }
             }
           }
         }
-        // the row's 4 lanes, then the token wave's running state for the row
-        RowState st = {v1, v2, 0.0f, id1};
-#pragma unroll
-        for (int sh = 16; sh <= 32; sh <<= 1) {
-          RowState o;
-          o.v1 = __shfl_xor(st.v1, sh);
-          o.v2 = __shfl_xor(st.v2, sh);
-          o.l1 = 0.0f;
-          o.id1 = __shfl_xor(st.id1, sh);
-          if (top2) merge_top2(st, o);
-          else merge_order(st, o);
-        }
-        if (g == 0 && n < rows) {
-          const int i = wt * rp + n;
-          RowState o = {st_v1[i], st_v2[i], 0.0f, st_id[i]};
-          if (top2) merge_top2(st, o);
-          else merge_order(st, o);
-          st_v1[i] = st.v1;
-          st_v2[i] = st.v2;
-          st_id[i] = st.id1;
-        }
+        if (MRB >= 8) __builtin_amdgcn_sched_barrier(0);
       }
+      if (!a_out && nxt < a.nslabs)
+        load_w2_tile<KB>(a.w2, V, R, nxt * SLAB + wt * TOK_PER_WAVE, m, g, kzero, A0, A1);
     }
   }
-  if (MODE == MODE_BIAS) return;
+  if (bias_mode) return;
 
-  // 3. this workgroup's winner per row: one exact key for the top element
-  //    of a noisy row (its cached logit read back) unless another element's
-  //    bound reaches it (or an estimate was not finite), in which case the
-  //    row goes to the exact fallback below; then one packed atomicMax per row.
-  __builtin_amdgcn_s_waitcnt(0);
+  // 3. each row's state: this lane's, merged over the row's 4 lanes, stored
+  //    per token wave, then merged over the token waves; one exact key for
+  //    the top element of a noisy row (its cached logit read back) unless
+  //    another element's bound reaches it (or an estimate was not finite),
+  //    in which case the row goes to the exact fallback below; then one
+  //    packed atomicMax per row.
+#pragma unroll
+  for (int j = 0; j < MRB; ++j) {
+    if (j >= my_nrb) break;
+    RowState st = {lr[j].v1, lr[j].v2, lr[j].l1, lr[j].id1};
+#pragma unroll
+    for (int sh = 16; sh <= 32; sh <<= 1) {
+      RowState o;
+      o.v1 = __shfl_xor(st.v1, sh);
+      o.v2 = __shfl_xor(st.v2, sh);
+      o.l1 = __shfl_xor(st.l1, sh);
+      o.id1 = __shfl_xor(st.id1, sh);
+      if (!(n_info[(wr + j * RG) * 16 + m].T == 0.0f) && !exact_mode) merge_top2(st, o);
+      else merge_order(st, o);
+    }
+    const int n = (wr + j * RG) * 16 + m;
+    if (g == 0 && n < rp) {
+      st_v1[wt * rp + n] = st.v1;
+      st_v2[wt * rp + n] = st.v2;
+      st_l[wt * rp + n] = st.l1;
+      st_id[wt * rp + n] = st.id1;
+    }
+  }
   __syncthreads();
   for (int n = tid; n < rows; n += NTH) {
-    const float T = n_T[n];
+    const float T = n_info[n].T;
     const bool noisy = !(T == 0.0f);
-    const bool top2 = noisy && MODE != MODE_SAMPLE_EXACT;
-    RowState st = {st_v1[n], st_v2[n], 0.0f, st_id[n]};
+    const bool top2 = noisy && !exact_mode;
+    RowState st = {st_v1[n], st_v2[n], st_l[n], st_id[n]};
 #pragma unroll
     for (int w = 1; w < 4; ++w) {
       const int i = w * rp + n;
-      RowState o = {st_v1[i], st_v2[i], 0.0f, st_id[i]};
+      RowState o = {st_v1[i], st_v2[i], st_l[i], st_id[i]};
       if (top2) merge_top2(st, o);
       else merge_order(st, o);
     }
@@ -586,12 +700,11 @@ __global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
     float key = st.v1;
     if (top2) {
       const bool near = st.id1 != NONE && st.v2 >= lower_of_upper(st.v1);
-      if (near || sp_cnt[n] > 0 || MODE == MODE_SAMPLE_FALLBACK) {
+      if (near || sp_cnt[n] > 0 || mode == MODE_SAMPLE_FALLBACK) {
         fb_list[atomicAdd(&misc[32], 1)] = n;
         continue;
       }
-      const float l1 = bf_lo((uint32_t)a.cache[((size_t)r * K + s) * (size_t)V + st.id1]);
-      key = key_exact(l1, T, mm_finish(n_prefix[n], mm_token_word((uint32_t)st.id1)));
+      key = key_exact(st.l1, T, mm_finish(n_info[n].prefix, mm_token_word((uint32_t)st.id1)));
     }
     if (st.id1 != NONE)
       __hip_atomic_fetch_max(slots_cur + r, pack_winner(key, st.id1), __ATOMIC_RELAXED,
@@ -602,13 +715,17 @@ __global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
   // 4. exact fallback: the whole workgroup re-reads the row's cached logits
   //    over its own slabs and takes every exact key.
   const int nfb = misc[32];
+  if (nfb > 0) {
+    __builtin_amdgcn_s_waitcnt(0);   // this workgroup's cache stores, re-read below
+    __syncthreads();
+  }
   float* red_v = st_v1;  // reuse: [NWV] partials
   int* red_i = st_id;
   for (int f = 0; f < nfb; ++f) {
     const int n = fb_list[f];
     const int r = n_row[n];
-    const float T = n_T[n];
-    const uint32_t prefix = n_prefix[n];
+    const float T = n_info[n].T;
+    const uint32_t prefix = n_info[n].prefix;
     float bv = -INFINITY;
     int bi = NONE;
     const int per_wg = ((a.nslabs - blockIdx.x + G - 1) / G) * SLAB;
@@ -673,9 +790,9 @@ __global__ void debug_gumbel_kernel(const float* logits, const uint32_t* ids, in
   if (i >= n) return;
   uint32_t h = mm_finish(row_prefix_of(seed, step, position), mm_token_word(ids[i]));
   float l = logits[i];
-  float margin;
-  kf[i] = key_fast(l, 1.0f / T, h, &margin);
-  mg[i] = margin;
+  const float ka = key_fast(l, 1.0f / T, h);
+  kf[i] = ka;
+  mg[i] = fast_margin(ka);
   kx[i] = !(T == 0.0f) ? key_exact(l, T, h) : l;
 }
 
@@ -689,33 +806,66 @@ __global__ void debug_bf16_kernel(const float* in, uint16_t* out, int64_t n) {
 
 typedef void (*StepFn)(StepArgs);
 
-template <int MODE, int RG>
-StepFn pick_rank(int R) {
-  switch (R) {
-    case 16:
-    case 32: return markov_step_kernel<1, MODE, RG>;
-    case 64: return markov_step_kernel<2, MODE, RG>;
-    case 128: return markov_step_kernel<4, MODE, RG>;
-    case 256: return markov_step_kernel<8, MODE, RG>;
-    case 512: return markov_step_kernel<16, MODE, RG>;
+// Row groups per workgroup: when one workgroup's LDS (mostly the
+// embeddings) leaves room for a single workgroup per CU, more waves share it
+// (two row groups; four where the rank is small enough to keep the w2 tile in
+// few registers). MRB: the most row blocks one wave handles.
+size_t lds_bytes(int rows, int R);
+
+struct Plan {
+  int rg, mrb;
+};
+
+Plan plan_of(int rows, int R) {
+  const int nrb = (rows + 15) / 16;
+  int rg = 1;
+  if (lds_bytes(rows, R) > 80 * 1024) rg = 2;
+#ifdef MARKOV_FORCE_RG
+  if (nrb >= MARKOV_FORCE_RG) rg = MARKOV_FORCE_RG;
+#endif
+  const int need = (nrb + rg - 1) / rg;
+  int mrb = 1;
+  while (mrb < need) mrb *= 2;
+  return Plan{rg, mrb};
+}
+
+template <int KB, bool EX>
+StepFn pick_plan(Plan p) {
+  if (p.rg == 1) {
+    switch (p.mrb) {
+      case 1: return markov_step_kernel<KB, 1, 1, EX>;
+      case 2: return markov_step_kernel<KB, 1, 2, EX>;
+      case 4: return markov_step_kernel<KB, 1, 4, EX>;
+      case 8: return markov_step_kernel<KB, 1, 8, EX>;
+    }
+  } else if (p.rg == 2) {
+    switch (p.mrb) {
+      case 1: return markov_step_kernel<KB, 2, 1, EX>;
+      case 2: return markov_step_kernel<KB, 2, 2, EX>;
+      case 4: return markov_step_kernel<KB, 2, 4, EX>;
+      case 8: return markov_step_kernel<KB, 2, 8, EX>;
+      case 16: return KB <= 2 ? markov_step_kernel<KB <= 2 ? KB : 1, 2, 16, EX> : nullptr;
+      case 32: return KB == 1 ? markov_step_kernel<1, 2, 32, EX> : nullptr;
+    }
   }
   return nullptr;
 }
 
-template <int MODE>
-StepFn pick_kernel(int R, int RG) {
-  return RG == 4 ? pick_rank<MODE, 4>(R) : RG == 2 ? pick_rank<MODE, 2>(R) : pick_rank<MODE, 1>(R);
+template <bool EX>
+StepFn pick_rank(int R, Plan p) {
+  switch (R) {
+    case 16:
+    case 32: return pick_plan<1, EX>(p);
+    case 64: return pick_plan<2, EX>(p);
+    case 128: return pick_plan<4, EX>(p);
+    case 256: return pick_plan<8, EX>(p);
+    case 512: return pick_plan<16, EX>(p);
+  }
+  return nullptr;
 }
 
-// Row groups per workgroup: when one workgroup's LDS (mostly the
-// embeddings) leaves room for a single workgroup per CU, more waves share it
-// (two row groups; four where the rank is small enough to keep the w2 tile in
-// few registers).
-size_t lds_bytes(int rows, int R);
-
-int row_groups(int rows, int R) {
-  if (lds_bytes(rows, R) <= 80 * 1024) return 1;
-  return R <= 64 ? 4 : 2;
+StepFn pick_kernel(int R, Plan p, bool exact = false) {
+  return exact ? pick_rank<true>(R, p) : pick_rank<false>(R, p);
 }
 
 bool pow2_rank(int R) { return R >= 16 && R <= 512 && (R & (R - 1)) == 0; }
@@ -725,7 +875,7 @@ bool pow2_rank(int R) { return R >= 16 && R <= 512 && (R & (R - 1)) == 0; }
 // and a small misc area.
 size_t lds_bytes(int rows, int R) {
   size_t rp = (size_t)((rows + 15) & ~15);
-  return rp * R * 2 + rp * 5 * 4 + (size_t)4 * rp * 12 + rp * 8 + 64 * 4;
+  return rp * R * 2 + rp * 6 * 4 + (size_t)4 * rp * 16 + rp * 8 + 64 * 4;
 }
 
 constexpr size_t LDS_MAX = 160 * 1024;
@@ -734,7 +884,9 @@ int32_t max_rows_of(int32_t R) {
   if (!pow2_rank(R)) return 0;
   int32_t best = 0;
   for (int32_t rows = 16; rows <= ROWS_CAP; rows += 16)
-    if ((size_t)rows * R * 2 <= (size_t)LDS_EMB_MAX && lds_bytes(rows, R) <= LDS_MAX) best = rows;
+    if ((size_t)rows * R * 2 <= (size_t)LDS_EMB_MAX && lds_bytes(rows, R) <= LDS_MAX &&
+        pick_kernel(R, plan_of(rows, R)) != nullptr)
+      best = rows;
   return best;
 }
 
@@ -778,6 +930,12 @@ int launch_grid(StepFn fn, size_t lds, int block, int nslabs, int* grid) {
     return MARKOV_ERR_HIP;
   if (occ < 1) return MARKOV_ERR_ROWS;
   int cap = cus * occ;
+#ifndef MARKOV_GRID_PER_CU
+#define MARKOV_GRID_PER_CU 2
+#endif
+  // at most two resident workgroups per CU: each workgroup's prologue
+  // (embedding gather) and per-row atomics are a fixed cost
+  if (occ > MARKOV_GRID_PER_CU) cap = cus * MARKOV_GRID_PER_CU;
   if (g_cache_n < 64) g_cache[g_cache_n++] = LaunchCache{fn, dev, lds, cap};
   *grid = nslabs < cap ? nslabs : cap;
   return MARKOV_OK;
@@ -790,12 +948,10 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
                  int32_t s_end, const float* temperature, void* cache, int64_t* tokens,
                  void* bias_out, markov_stream_t stream, const markov_shape_t* sh,
                  void* workspace) {
-  const int rg = row_groups(sh->rows, sh->rank);
-  StepFn fn = mode == MODE_SAMPLE ? pick_kernel<MODE_SAMPLE>(sh->rank, rg)
-            : mode == MODE_SAMPLE_EXACT ? pick_kernel<MODE_SAMPLE_EXACT>(sh->rank, rg)
-            : mode == MODE_SAMPLE_FALLBACK ? pick_kernel<MODE_SAMPLE_FALLBACK>(sh->rank, rg)
-                                           : pick_kernel<MODE_BIAS>(sh->rank, rg);
-  if (!fn) return MARKOV_ERR_RANK;
+  const Plan plan = plan_of(sh->rows, sh->rank);
+  const int rg = plan.rg;
+  StepFn fn = pick_kernel(sh->rank, plan, mode == MODE_SAMPLE_EXACT);
+  if (!fn) return MARKOV_ERR_ROWS;
   const size_t lds = lds_bytes(sh->rows, sh->rank);
   const int nslabs = (sh->vocab + SLAB - 1) / SLAB;
   const int block = 256 * rg;
@@ -820,6 +976,7 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   a.R = sh->rank;
   a.k = k;
   a.nslabs = nslabs;
+  a.mode = mode;
   a.mult = sh->mult;
   a.has_cap = sh->softcap > 0.0f;
   a.cap = sh->softcap;

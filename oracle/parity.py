@@ -24,11 +24,10 @@ def bf16_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def ulp_bf16(x: np.ndarray) -> np.ndarray:
-    """One bf16 ulp at |x| (binary64), 2^-133 at zero."""
+    """One bf16 ulp at |x| (binary64); 2^-133 throughout the subnormal range."""
     a = np.abs(np.asarray(x, dtype=np.float64))
     _, e = np.frexp(a)
-    u = np.ldexp(1.0, e - 8)
-    return np.where(a == 0, 2.0 ** -133, u)
+    return np.maximum(np.ldexp(1.0, e - 8), 2.0 ** -133)
 
 
 def compare_cache(cg: np.ndarray, co: np.ndarray):
@@ -36,12 +35,13 @@ def compare_cache(cg: np.ndarray, co: np.ndarray):
     g = bf16_to_f32(cg).astype(np.float64)
     o = bf16_to_f32(co).astype(np.float64)
     gn, on = np.isnan(g), np.isnan(o)
-    both_nan = gn & on
+    same = (gn & on) | (g == o)                    # equal values, infinities included
     one_nan = gn ^ on
-    diff = np.where(both_nan, 0.0, np.abs(g - o))
+    with np.errstate(invalid="ignore"):
+        diff = np.where(same | one_nan, 0.0, np.abs(g - o))
     tol = ulp_bf16(np.maximum(np.abs(np.nan_to_num(g)), np.abs(np.nan_to_num(o))))
-    beyond = one_nan | (~both_nan & (diff > tol))
-    differ = one_nan | (~both_nan & (diff != 0))
+    beyond = one_nan | (~same & ~(diff <= tol))
+    differ = ~same
     return int(beyond.sum()), int(differ.sum())
 
 

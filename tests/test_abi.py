@@ -51,7 +51,10 @@ def test_status_strings(lib):
 def test_max_rows_and_workspace(lib):
     assert m.max_rows(256) == 256
     assert m.max_rows(512) == 128
-    assert m.max_rows(32) == 1024
+    mr32 = m.max_rows(32)                                  # LDS-bound: 160 KiB per workgroup
+    assert 1000 <= mr32 <= 1024 and mr32 % 16 == 0
+    assert m.why_not(mr32, 4096, 32, 3) is None
+    assert m.why_not(mr32 + 1, 4096, 32, 3) is not None
     assert m.max_rows(48) == 0
     assert m.workspace_bytes(64, 163840, 256, 5) >= 64 * 8 + 4
     assert m.workspace_bytes(0, 163840, 256, 5) == 0

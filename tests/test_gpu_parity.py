@@ -276,3 +276,36 @@ def test_graph_replay_matches_eager(dev):
         workloads.run(w, d)          # eager work between replays
         torch.cuda.synchronize()
     assert not d["workspace"].cpu().numpy().any()
+
+
+@pytest.mark.parametrize("mult,softcap", [(1.0, 30.0), (0.75, 30.0), (1.0, 0.5), (1.25, 0.0)])
+def test_transform_exhaustive_over_bf16(dev, mult, softcap):
+    """Every finite bf16 base logit through the kernel with a zero bias: the
+    cached value is the oracle's transform of it (multiplier, soft cap,
+    rounding) within one bf16 ulp, and the mismatch count is reported."""
+    import oracle
+
+    vals = np.array([b for b in range(0x10000) if (b & 0x7F80) != 0x7F80], dtype=np.uint16)
+    V = (len(vals) // 8) * 8
+    vals = vals[:V]
+    R = 16
+    w = workloads.make("tiny", V=V, R=R, rows=1, k=1, data_seed=77)
+    w.name = "transform"
+    w.w1 = np.zeros((V, R), dtype=np.uint16)
+    w.w2 = np.zeros((V, R), dtype=np.uint16)
+    w.base = vals.reshape(1, 1, V).copy()
+    w.temperature = np.zeros(1, dtype=np.float32)
+    w.mult, w.softcap = mult, softcap
+    d = workloads.to_device(w, dev)
+    workloads.run(w, d)
+    torch.cuda.synchronize()
+    cg, tg = workloads.fetch(d)
+    co = np.array([oracle.cache_value(int(b), 0, mult, softcap) for b in vals], dtype=np.uint16)
+    beyond, differ = parity.compare_cache(cg[0, 0], co)
+    say(f"  transform mult={mult} cap={softcap}: differing {differ}/{V}, beyond one ulp {beyond}")
+    bad = np.nonzero(cg[0, 0] != co)[0][:12]
+    for i in bad:
+        say(f"    base {vals[i]:#06x} ({parity.bf16_to_f32(vals[i:i+1])[0]:.6g}) gpu {cg[0, 0, i]:#06x} oracle {co[i]:#06x}")
+    assert beyond == 0
+    assert differ <= V // 1000
+    assert tg[0, 0] == int(np.argmax(parity.bf16_to_f32(cg[0, 0])))
