@@ -1,24 +1,31 @@
 #!/usr/bin/env python3
 """Throughput of the Markov draft-sampling loop on one MI355X.
 
-One bench "step" is one k-step loop (markov_sample_sequential: k kernel
-launches, one per draft step) over the workload's synthetic inputs, which
-are resident in HBM before timing starts. `value` is draft steps per second
-(k per loop); the line also carries µs per loop, the roofline of the step
-kernel and the CPU oracle's rate on a bounded sample.
+One bench "step" is one k-step loop (markov_sample_sequential: one step
+kernel per draft step plus one small finishing kernel) over the workload's
+synthetic inputs, which are resident in HBM before timing starts. `value` is
+draft steps per second (k per loop) of the headline mode, plain launches
+(eager); the same loop captured once as a HIP graph and replayed is reported
+beside it (on this part a replay measures no faster than the eager loop). The line also carries the step kernel's roofline and the CPU
+oracle's rate on a bounded sample.
 
 Roofline: the step kernel's algorithmic HBM bytes per launch are
 2VR (the w2 table) + 4 rows V (the base slice read, the cache slice
 written) + 2 rows R (the rows' w1 rows); its average duration comes from
-HIP events around each launch on the launching stream, over a second timed
-pass of the same loops launched one step at a time.
+HIP events recorded around each step-kernel launch on the launching stream,
+in a timed pass of eager loops. Measured DRAM traffic (rocprofv3 FETCH_SIZE
+and WRITE_SIZE, scaled by the same counters on a plain copy) is read from
+the committed profile summary and reported only while the kernel source is
+the one it was measured on.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +34,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft steps/s + µs per k-step loop, V=163840 R=256; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "markov_draft_sampling_step_amd", "csrc", "markov.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "markov_step_kernel_{cfg}_traffic.txt")
 
 
 def parse():
@@ -36,31 +45,84 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="large",
                     choices=["tiny", "single", "small", "large", "stress"])
-    ap.add_argument("--graph", action="store_true", help="replay the loop as a HIP graph")
+    ap.add_argument("--graph", action="store_true",
+                    help="headline from replays of the loop captured as a HIP graph")
+    ap.add_argument("--eager", action="store_true",
+                    help="plain launches only (no graph capture at all)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time loops with a 1 GiB write between them (MALL evicted)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=None,
-                    help="json file with measured HBM bytes per launch (from rocprofv3 counters)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-time budget of the CPU oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run 3 plain device copies (markov_copy_kernel) of MIB MiB, the "
+                         "reference for the DRAM byte counters")
     return ap.parse_args()
 
 
-def cpu_baseline(w):
-    """The oracle (plain C, untuned) on a bounded sample: step 0 of the
-    workload for every row, i.e. one draft step, on the host's cores."""
-    import numpy as np
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
+
+def measured_traffic(cfg: str):
+    """DRAM bytes per step-kernel launch from the committed counter summary,
+    or None when there is none or the kernel source changed since."""
+    path = TRAFFIC_SUMMARY.format(cfg=cfg)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch\s*=\s*(\d+)", text)
+    h = re.search(r"kernel_source_sha256\s*=\s*([0-9a-f]{64})", text)
+    if not m or not h or h.group(1) != source_digest():
+        return None
+    return int(m.group(1))
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle (plain C, untuned) on a bounded sample: whole k-step loops
+    over every row of the workload, repeated until the wall-time budget is
+    spent, on the host's cores (its OpenMP loop runs over rows)."""
     import oracle
 
     threads = max(1, min(16, os.cpu_count() or 1))
+    used = min(threads, w.rows)
     if not os.path.exists(oracle.LIBRARY):
         oracle.build()
+    loops = 0
     t0 = time.perf_counter()
-    oracle.step(np.ascontiguousarray(w.base[:, 0]), w.w1, w.w2, w.prev, w.seeds,
-                w.positions[:, 0], 0, w.temperature, w.mult, w.softcap, threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": round(1.0 / dt, 4), "unit": "draft steps/s", "cores": threads,
+    while True:
+        oracle.sample_sequential(w.base, w.w1, w.w2, w.prev, w.seeds, w.positions,
+                                 w.temperature, w.mult, w.softcap, threads=threads)
+        loops += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or loops >= 1000:
+            break
+    return {"value": round(loops * w.k / dt, 4), "unit": "draft steps/s", "cores": used,
             "kind": "oracle",
-            "sample": f"one draft step (step 0, all {w.rows} rows, V={w.V}) of the {w.name} "
-                      f"workload, {threads} OpenMP threads, {dt:.2f} s wall"}
+            "sample": f"{loops} whole {w.k}-step loop(s) of the {w.name} workload (all {w.rows} "
+                      f"rows, V={w.V}), {used} OpenMP thread(s) over rows, {dt:.2f} s wall"}
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    i = min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))
+    return xs[i]
+
+
+def time_loops(torch, launch, stream, n):
+    """n loops back to back: (wall µs per loop, per-loop event µs)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / n * 1e6
+    return wall, [a.elapsed_time(b) * 1e3 for a, b in evs]
 
 
 def main():
@@ -78,61 +140,76 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 2
+        src = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            m.debug_copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     w = workloads.make(args.config)
     d = workloads.to_device(w, dev)
     call = m.prepare(w, d)
     step_calls = [m.prepare(w, d, step=s) for s in range(w.k)]
-    stream = torch.cuda.current_stream()
+    launches = w.k + 1                       # k step kernels and the finishing kernel
 
     for _ in range(max(1, args.warmup)):
         call()
     torch.cuda.synchronize()
 
     graph = None
-    if args.graph:
-        graph = torch.cuda.CUDAGraph()
+    if not args.eager:
         side = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=side):
             call.on(side)()
-        for _ in range(2):
+        for _ in range(max(1, args.warmup)):
             graph.replay()
         torch.cuda.synchronize()
 
-    # pass 1: the headline, K loops back to back
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if graph is not None:
-        for _ in range(args.steps):
-            graph.replay()
-    else:
-        for _ in range(args.steps):
-            call()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    loop_us = dt / args.steps * 1e6
-    value = args.steps * w.k / dt
+    # the timed loops: graph replays (unless --eager) and eager launches, K each
+    g_wall, g_ev = time_loops(torch, graph.replay, stream, args.steps) if graph else (None, None)
+    e_wall, e_ev = time_loops(torch, call, stream, args.steps)
+    head_wall, head_ev = (g_wall, g_ev) if (graph and args.graph) else (e_wall, e_ev)
+    value = w.k / (head_wall * 1e-6)
 
-    # pass 2: the step kernel's duration, HIP events around each launch
+    # the step kernel alone: events around each step-kernel launch of eager
+    # loops (the last step's launch also carries the finishing kernel, so it
+    # is left out of the average)
     n2 = max(1, min(args.steps, 50))
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n2 * w.k)]
+    timed = [s for s in range(w.k) if s < w.k - 1] or [0]
+    evs = []
     torch.cuda.synchronize()
-    i = 0
     for _ in range(n2):
         for s in range(w.k):
-            evs[i][0].record(stream)
-            step_calls[s]()
-            evs[i][1].record(stream)
-            i += 1
+            if s in timed:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                step_calls[s]()
+                b.record(stream)
+                evs.append((a, b))
+            else:
+                step_calls[s]()
     torch.cuda.synchronize()
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
-    kern_us = sum(kern_ms) / len(kern_ms) * 1e3
+    kern_us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
     bytes_step = w.bytes_per_step()
     achieved = bytes_step / (kern_us * 1e-6) / 1e9
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get(args.config)
+    cold = None
+    if args.cold:
+        junk = torch.empty(1 << 29, dtype=torch.float16, device=dev)
+        ts = []
+        for _ in range(min(args.steps, 20)):
+            junk.fill_(1.0)
+            torch.cuda.synchronize()
+            _, ev = time_loops(torch, graph.replay if (graph and args.graph) else call, stream, 1)
+            ts += ev
+        cold = round(percentile(ts, 0.5), 2)
+        del junk
 
     out = {
         "metric": METRIC,
@@ -141,8 +218,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(dt / args.steps * 1e3, 4),
-        "us_per_loop": round(loop_us, 2),
+        "ms_per_step": round(head_wall * 1e-3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -151,14 +227,21 @@ def main():
         "config": {"workload": f"{w.name}: V={w.V} R={w.R} rows={w.rows} k={w.k}"
                                f"{' softcap=%g' % w.softcap if w.softcap > 0 else ''}",
                    "V": w.V, "R": w.R, "rows": w.rows, "k": w.k,
-                   "launches_per_loop": w.k, "mode": "graph" if graph is not None else "eager"},
+                   "launches_per_loop": launches,
+                   "mode": "graph" if (graph and args.graph) else "eager"},
+        "us_per_loop": round(head_wall, 2),
+        "us_per_loop_p10_p50_p90": [round(percentile(head_ev, q), 2) for q in (0.1, 0.5, 0.9)],
+        "us_per_loop_graph": round(g_wall, 2) if graph else None,
+        "us_per_loop_eager": round(e_wall, 2),
+        "us_per_loop_cold": cold,
+        "draft_tokens_per_s": round(w.rows * value, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel_us": round(kern_us, 3),
-                     "bytes_per_launch": bytes_step},
+                     "traffic": measured_traffic(args.config), "kernel_us": round(kern_us, 3),
+                     "bytes_per_launch": bytes_step, "kernel": "markov_step_kernel"},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -168,6 +168,14 @@ int markov_debug_gumbel(const float* logits, const uint32_t* ids, int64_t n, flo
                         int64_t seed, int32_t step, int64_t position, float* key_exact,
                         float* key_fast, float* margin, markov_stream_t stream);
 
+/*
+ * A plain device copy of `bytes` bytes (a multiple of 16; src and dst
+ * device, 16-byte aligned, not overlapping). It reads and writes exactly
+ * `bytes` each and serves to calibrate DRAM byte counters; it is not part of
+ * the sampling path.
+ */
+int markov_debug_copy(const void* src, void* dst, int64_t bytes, markov_stream_t stream);
+
 /* RN bf16 of n binary32 values with the kernel's conversion (test-only). */
 int markov_debug_bf16_round(const float* in, uint16_t* out, int64_t n, markov_stream_t stream);
 

@@ -61,6 +61,7 @@ _SIGS = {
                                            ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, _P,
                                            _P, _P, _P]),
     "markov_debug_bf16_round": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
+    "markov_debug_copy": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
 }
 
 _lib = None
@@ -223,6 +224,15 @@ def debug_bf16_round(x, out, stream=None):
     _check(lib().markov_debug_bf16_round(_dev(x, torch.float32, "x"), _dev(out, torch.int16, "out"),
                                          x.numel(), _stream_ptr(stream)),
            "markov_debug_bf16_round")
+
+
+def debug_copy(src, dst, stream=None):
+    """A plain device copy of src into dst (same byte size; counter calibration)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("debug_copy: src and dst differ in size")
+    _check(lib().markov_debug_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                   n, _stream_ptr(stream)), "markov_debug_copy")
 
 
 class PreparedCall:

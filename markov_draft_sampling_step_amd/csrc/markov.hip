@@ -802,6 +802,16 @@ __global__ void debug_bf16_kernel(const float* in, uint16_t* out, int64_t n) {
   out[i] = (uint16_t)(pack_bf16(in[i], 0.0f) & 0xffffu);
 }
 
+// A plain copy, 16 bytes per lane per iteration over a grid-stride loop:
+// the calibration reference for the DRAM byte counters (it reads and writes
+// exactly `n16` * 16 bytes).
+__global__ __launch_bounds__(256) void markov_copy_kernel(const u32x4_t* __restrict__ src,
+                                                          u32x4_t* __restrict__ dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
+}
+
 // ---------------------------------------------------------------- host side
 
 typedef void (*StepFn)(StepArgs);
@@ -1114,6 +1124,23 @@ int markov_debug_gumbel(const float* logits, const uint32_t* ids, int64_t n, flo
   const int64_t blocks = (n + tb - 1) / tb;
   debug_gumbel_kernel<<<dim3((unsigned)blocks), tb, 0, (hipStream_t)stream>>>(
       logits, ids, n, temperature, seed, step, position, key_exact_out, key_fast_out, margin);
+  if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
+  return MARKOV_OK;
+}
+
+int markov_debug_copy(const void* src, void* dst, int64_t bytes, markov_stream_t stream) {
+  if (!src || !dst) return MARKOV_ERR_NULL;
+  if (bytes < 0 || (bytes & 15)) return MARKOV_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return MARKOV_ERR_ALIGN;
+  if (bytes == 0) return MARKOV_OK;
+  const int64_t n16 = bytes / 16;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t want = (n16 + 255) / 256;
+  const int64_t blocks = want < (int64_t)cus * 8 ? want : (int64_t)cus * 8;
+  markov_copy_kernel<<<dim3((unsigned)blocks), 256, 0, (hipStream_t)stream>>>(
+      (const u32x4_t*)src, (u32x4_t*)dst, n16);
   if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   return MARKOV_OK;
 }

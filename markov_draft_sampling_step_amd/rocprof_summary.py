@@ -1,0 +1,102 @@
+"""Short text summaries of rocprofv3 CSV output.
+
+  python -m markov_draft_sampling_step_amd.rocprof_summary stats DIR
+      per-kernel calls / average / min / max duration from *_kernel_stats.csv
+
+  python -m markov_draft_sampling_step_amd.rocprof_summary traffic \\
+      --fetch DIR --write DIR --copy-bytes N [--kernel markov_step_kernel]
+      DRAM bytes per dispatch of the kernel from two --pmc runs (FETCH_SIZE,
+      then WRITE_SIZE; the counters read KiB), each scaled by the factor that
+      makes the same counter read exactly N bytes on markov_copy_kernel
+      (which reads N bytes and writes N bytes).
+
+The summaries are plain text meant to be committed; they restate the figures
+the CSVs hold and print the kernel source's sha256 so that a later reader
+can tell whether the measured kernel is still the current one.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(HERE, "csrc", "markov.hip")
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise SystemExit(f"no file matches {pattern}")
+    return hits[0]
+
+
+def stats(d: str) -> str:
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_stats.csv")))))
+    out = [f"{'kernel':48s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s} "
+           f"{'total %':>8s}"]
+    for r in rows:
+        out.append(f"{r['Name'][:48]:48s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.3f} "
+                   f"{float(r['MinNs']) / 1e3:10.3f} {float(r['MaxNs']) / 1e3:10.3f} "
+                   f"{float(r['Percentage']):8.2f}")
+    return "\n".join(out)
+
+
+def _counter(d: str, counter: str, name_part: str) -> list[float]:
+    path = _one(os.path.join(d, "**", "*counter_collection.csv"))
+    vals = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+            vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"{path}: no {counter} rows for a kernel named *{name_part}*")
+    return vals
+
+
+def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, kernel: str) -> str:
+    cf = statistics.median(_counter(fetch_dir, "FETCH_SIZE", "markov_copy_kernel"))
+    cw = statistics.median(_counter(write_dir, "WRITE_SIZE", "markov_copy_kernel"))
+    kf = _counter(fetch_dir, "FETCH_SIZE", kernel)
+    kw = _counter(write_dir, "WRITE_SIZE", kernel)
+    f_scale = copy_bytes / cf            # bytes per counter unit, reads
+    w_scale = copy_bytes / cw            # bytes per counter unit, writes
+    rd = statistics.mean(kf) * f_scale
+    wr = statistics.mean(kw) * w_scale
+    digest = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    return "\n".join([
+        f"copy calibration: markov_copy_kernel of {copy_bytes} bytes reads FETCH_SIZE={cf:.1f}, "
+        f"WRITE_SIZE={cw:.1f} (KiB) -> {f_scale:.2f} and {w_scale:.2f} bytes per counter unit "
+        f"(1024 would be exact KiB)",
+        f"{kernel}: {len(kf)} dispatches (FETCH_SIZE run), {len(kw)} (WRITE_SIZE run); "
+        f"FETCH_SIZE mean {statistics.mean(kf):.1f} min {min(kf):.1f} max {max(kf):.1f}; "
+        f"WRITE_SIZE mean {statistics.mean(kw):.1f} min {min(kw):.1f} max {max(kw):.1f}",
+        f"read bytes per launch  = {rd:.0f}",
+        f"write bytes per launch = {wr:.0f}",
+        f"traffic_bytes_per_launch = {rd + wr:.0f}",
+        f"kernel_source_sha256 = {digest}",
+    ])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("dir")
+    b = sub.add_parser("traffic")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--copy-bytes", type=int, required=True)
+    b.add_argument("--kernel", default="markov_step_kernel")
+    args = ap.parse_args()
+    if args.cmd == "stats":
+        print(stats(args.dir))
+    else:
+        print(traffic(args.fetch, args.write, args.copy_bytes, args.kernel))
+
+
+if __name__ == "__main__":
+    main()
