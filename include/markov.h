@@ -69,17 +69,19 @@ enum {
   MARKOV_ERR_VOCAB = -8        /* vocab above 2^31 - 1 */
 };
 
-/* The most rows one call takes at a given rank (the embedding rows are
- * staged in LDS: rows * rank * 2 bytes must fit in 128 KiB). */
+/* The most rows one call takes at a given rank (at most 512; the embedding
+ * rows are staged in LDS next to per-row data, within 160 KiB). */
 int32_t markov_max_rows(int32_t rank);
 
-/* Bytes of device workspace one loop of this shape needs: per-row packed
- * (key, id) maxima and the arrival counter. Independent of k. */
+/* Bytes of device workspace one loop of this shape needs: the noise bound
+ * table (8448 bytes) and three per-row arrays of packed (key, id) maxima.
+ * Independent of k. */
 size_t markov_workspace_bytes(const markov_shape_t* shape, int32_t k);
 
-/* Zero a workspace once after allocating it (enqueued on `stream`). Every
- * call of markov_sample_sequential leaves it zeroed again, so it is reused
- * as is; it must not be shared by two calls in flight at once. */
+/* Prepare a workspace once after allocating it (enqueued on `stream`): the
+ * noise bound table is copied in and the rest zeroed. Every call of
+ * markov_sample_sequential leaves it so again, so it is reused as is; it
+ * must not be shared by two calls in flight at once. 16-byte aligned. */
 int markov_workspace_init(void* workspace, size_t bytes, markov_stream_t stream);
 
 /* NULL when this shape and k are supported, else why not (a static string);
@@ -115,8 +117,10 @@ int markov_sample_sequential(const void* base_logits, const void* w1, const void
 
 /*
  * Step `step` (0 <= step < k) of the same loop alone: one kernel launch that
- * feeds on prev (step 0) or on tokens[:, step-1], and writes cache[:, step, :]
- * and tokens[:, step]. Arguments and errors as markov_sample_sequential;
+ * feeds on prev (step 0) or on the previous step's winners (kept in the
+ * workspace), writes cache[:, step, :] and tokens[:, step-1]; for the last
+ * step (step = k-1) a second, small launch also writes tokens[:, k-1] and
+ * re-zeroes the workspace. Arguments and errors as markov_sample_sequential;
  * calling it for step = 0..k-1 in order is that loop.
  */
 int markov_sample_step(const void* base_logits, const void* w1, const void* w2,
@@ -158,23 +162,16 @@ int markov_debug_bias(const void* w1, const void* w2, const int64_t* tok, void* 
                       const markov_shape_t* shape, markov_stream_t stream);
 
 /*
- * The Gumbel key of n (logit, token id) pairs of one row at one step, as
- * the step kernel computes it: key_exact (the key the kernel's argmax
- * uses), key_fast and margin (its cheap estimate and the bound the kernel
- * trusts, |key_fast - key_exact| <= margin, to skip exact keys that cannot
- * win). All arrays device, length n; logits fp32, ids uint32, outputs fp32.
+ * The Gumbel key of n (logit, token id) pairs of one row at one step:
+ * key_exact is the key the kernel's argmax uses; key_upper is the kernel's
+ * cheap upper bound of it (the noise bound table lookup plus the logit term),
+ * key_exact <= key_upper for every input with a finite bound. `workspace` is
+ * a workspace prepared by markov_workspace_init (it holds the table). All
+ * arrays device, length n; logits fp32, ids uint32, outputs fp32.
  */
 int markov_debug_gumbel(const float* logits, const uint32_t* ids, int64_t n, float temperature,
-                        int64_t seed, int32_t step, int64_t position, float* key_exact,
-                        float* key_fast, float* margin, markov_stream_t stream);
-
-/*
- * A plain device copy of `bytes` bytes (a multiple of 16; src and dst
- * device, 16-byte aligned, not overlapping). It reads and writes exactly
- * `bytes` each and serves to calibrate DRAM byte counters; it is not part of
- * the sampling path.
- */
-int markov_debug_copy(const void* src, void* dst, int64_t bytes, markov_stream_t stream);
+                        int64_t seed, int32_t step, int64_t position, const void* workspace,
+                        float* key_exact, float* key_upper, markov_stream_t stream);
 
 /* RN bf16 of n binary32 values with the kernel's conversion (test-only). */
 int markov_debug_bf16_round(const float* in, uint16_t* out, int64_t n, markov_stream_t stream);

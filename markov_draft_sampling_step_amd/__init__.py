@@ -62,6 +62,7 @@ _SIGS = {
                                            _P, _P, _P]),
     "markov_debug_bf16_round": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
     "markov_debug_copy": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
+    "markov_debug_noise_table": (ctypes.c_int32, [_P, ctypes.c_int32]),
 }
 
 _lib = None
@@ -207,15 +208,18 @@ def debug_bias(w1, w2, tok, bias, stream=None):
 
 
 def debug_gumbel(logits, ids, temperature: float, seed: int, step: int, position: int,
-                 key_exact, key_fast, margin, stream=None):
+                 workspace, key_exact, key_upper, stream=None):
+    """Exact keys and the kernel's upper bounds of (logit, id) pairs of one
+    row at one step; `workspace` from ``new_workspace``."""
     import torch
 
     n = logits.numel()
     _check(lib().markov_debug_gumbel(
         _dev(logits, torch.float32, "logits"), _dev(ids, torch.int32, "ids"), n,
         float(temperature), int(seed), int(step), int(position),
-        _dev(key_exact, torch.float32, "key_exact"), _dev(key_fast, torch.float32, "key_fast"),
-        _dev(margin, torch.float32, "margin"), _stream_ptr(stream)), "markov_debug_gumbel")
+        _dev(workspace, torch.uint8, "workspace"),
+        _dev(key_exact, torch.float32, "key_exact"), _dev(key_upper, torch.float32, "key_upper"),
+        _stream_ptr(stream)), "markov_debug_gumbel")
 
 
 def debug_bf16_round(x, out, stream=None):
@@ -224,6 +228,17 @@ def debug_bf16_round(x, out, stream=None):
     _check(lib().markov_debug_bf16_round(_dev(x, torch.float32, "x"), _dev(out, torch.int16, "out"),
                                          x.numel(), _stream_ptr(stream)),
            "markov_debug_bf16_round")
+
+
+def debug_noise_table():
+    """The noise bound table (host numpy float32 array of 2050 entries)."""
+    import numpy as np
+
+    out = np.zeros(2050, dtype=np.float32)
+    n = lib().markov_debug_noise_table(out.ctypes.data_as(ctypes.c_void_p), out.size)
+    if n != out.size:
+        raise MarkovError(int(n) if n < 0 else -2, "markov_debug_noise_table")
+    return out
 
 
 def debug_copy(src, dst, stream=None):

@@ -1,43 +1,54 @@
 // MI355X (gfx950, CDNA4) DSpark sequential Markov draft-sampling step.
 //
-// One kernel launch per draft step. Every workgroup owns vocabulary slabs of
-// SLAB tokens (persistently, grid-strided) and all request rows:
+// One kernel launch per draft step; one 8-wave workgroup per CU. The
+// vocabulary is cut into 128-token slabs (four 32-token units, one per
+// SIMD); a workgroup owns the slabs blockIdx.x + G i, and the two waves on
+// each SIMD take every other one of them, so every SIMD gets the same share
+// of the vocabulary. Each wave handles all request rows of its units:
 //   * the rows' Markov embeddings w1[prev] sit in LDS (16-byte chunks,
 //     XOR-swizzled by row so the MFMA operand reads hit distinct banks);
-//   * each wave streams its 32 tokens' w2 rows from HBM once per step,
-//     straight into v_mfma_f32_16x16x32_bf16 A operands (16-byte loads);
-//     tokens sit on the MFMA's M side, in an order chosen so that after the
-//     MFMA each lane holds 8 consecutive tokens of one row, so the base read
-//     and the cache write are 16-byte vectors with no LDS transpose;
+//   * each wave streams its unit's w2 rows from HBM once per step, straight
+//     into v_mfma_f32_16x16x32_bf16 A operands (16-byte loads, issued before
+//     anything else at kernel start and again as soon as a unit's last
+//     contraction has issued); tokens sit on the MFMA's M side in an order
+//     that leaves each lane with 8 consecutive tokens of one row, so the
+//     base read and the cache write are 16-byte vectors with no transpose;
 //   * the epilogue (bf16 bias, bf16 add, multiplier / soft cap, cache store)
-//     and the Gumbel noise run in registers; a cheap noise estimate with a
-//     proven error margin decides which elements can still win, and only
-//     those get the exact key (binary64 logs, IEEE division);
+//     and the Gumbel noise run in registers. The noise is bounded, not
+//     computed: MurmurHash3 gives h, and a 2050-entry table in LDS, indexed
+//     by the exponent and top 6 mantissa bits of float(h), holds an upper
+//     bound of the noise over each bucket of h. A lane keeps the largest two
+//     bounds of its row; the workgroup takes one exact key (binary64 logs,
+//     IEEE division) per row, for the element with the largest bound, and
+//     only re-scans a row when another bound reaches that key;
 //   * per-row winners go out as one packed (order-preserving key, ~id)
-//     64-bit atomicMax per row per workgroup; the last workgroup to arrive
-//     writes tokens[:, step] and re-zeroes the slots and the counter.
+//     64-bit atomicMax per row per workgroup; the next step's kernel decodes
+//     them (no fences: the kernel boundary orders the steps).
 //
 // The definition followed is stated in include/markov.h, with the pages it
 // comes from (vLLM Markov-drafter API pages: kimi_k3 `_gumbel_key` and the
 // module's exactness paragraph; muse_spark cutedsl `_logit`, `_gumbel`,
-// `_murmur_prefix`, `_combine`, `_w1_row`, `_StepKernel.kernel`).
+// `_murmur_prefix`, `_combine`, `_w1_row`, `markov_step`).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "markov.h"
 
 namespace {
 
-constexpr int NW = 4;                  // waves per workgroup
-constexpr int BLOCK = 64 * NW;         // threads per workgroup
+constexpr int NWV = 8;                 // waves per workgroup (two per SIMD)
+constexpr int NTH = 64 * NWV;          // threads per workgroup
 constexpr int TOK_PER_WAVE = 32;       // two 16-token MFMA M tiles
-constexpr int SLAB = NW * TOK_PER_WAVE;
+constexpr int SLAB = 4 * TOK_PER_WAVE; // one unit per SIMD
 constexpr int NONE = 0x7fffffff;       // id of "no element yet"
-constexpr int LDS_EMB_MAX = 128 * 1024;
-constexpr int ROWS_CAP = 1024;
+constexpr int ROWS_CAP = NTH;          // the prologue gives every row one thread
+constexpr int MRB_MAX = 8;             // row blocks one wave keeps in registers
+constexpr size_t LDS_MAX = 160 * 1024;
 
 enum Mode { MODE_SAMPLE = 0, MODE_SAMPLE_EXACT = 1, MODE_BIAS = 2, MODE_SAMPLE_FALLBACK = 3 };
 
@@ -56,6 +67,7 @@ struct StepArgs {
   uint16_t* cache;
   int64_t* tokens;
   unsigned long long* slots;  // [3][rows] packed winners, step s uses s % 3
+  const float* gtable;        // the noise bound table (in the workspace)
   uint16_t* bias_out;
   int rows, V, R, k, step, nslabs, mode;
   float mult, inv_cap, cap;
@@ -98,10 +110,18 @@ __device__ __forceinline__ uint32_t mm_token_word(uint32_t id) {
   return k * MM_C2;
 }
 
+// h * 5 + c as a shift-add and an add (two full-rate ops; left to itself
+// the compiler picks a 64-bit multiply-add)
+__device__ __forceinline__ uint32_t times5_plus(uint32_t h, uint32_t c) {
+  uint32_t r;
+  asm("v_lshl_add_u32 %0, %1, 2, %1" : "=v"(r) : "v"(h));
+  return r + c;
+}
+
 __device__ __forceinline__ uint32_t mm_finish(uint32_t prefix, uint32_t token_word) {
   uint32_t h = prefix ^ token_word;
   h = rotl32(h, 13);
-  h = (h << 2) + h + 0xe6546b64u;   // h * 5 + c
+  h = times5_plus(h, 0xe6546b64u);
   h ^= 16u;                       // message length in bytes
   h ^= h >> 16;
   h *= 0x85ebca6bu;
@@ -146,7 +166,7 @@ __device__ __forceinline__ float log1m_exact(float u) {
   return (float)log((double)x);
 }
 
-__device__ __noinline__ float key_exact(float l, float T, uint32_t h) {
+__device__ __forceinline__ float key_exact(float l, float T, uint32_t h) {
   float u = uniform_of(h);
   float L = log1m_exact(u);
   float lb = (float)log((double)(-L));
@@ -154,27 +174,31 @@ __device__ __noinline__ float key_exact(float l, float T, uint32_t h) {
   return q - lb;
 }
 
-// Cheap key estimate. The uniform is taken with one conversion (within
-// 2^-23 relative of the exact one); y2 = -log2(1 - u) by u (1 + u/2) / ln 2
-// below u = 2^-10, else by the hardware log2 of max(1 - u, 2^-24); then
-// key ~ l / T - ln(y2 ln 2) = l rcp(T) + (-ln ln 2) - ln2 log2(y2).
-// |key_fast - key_exact| <= 1e-3 + |key_fast| 2^-18 (the margin the kernel
-// trusts; the tests check it against the exact key over many hashes): the
-// estimate's own error is below 1e-4 plus a few ulps of |l / T| <= |key| + 23.
-constexpr float LN2F = 0.693147180559945309f;
-constexpr float LOG2EF = 1.44269504088896341f;
-constexpr float NEG_LN_LN2 = 0.366512920581664327f;
+// Noise bound table. Bucket b of h: b = 0 for h = 0, else
+// (bits(float(h)) >> 17) - 8127, i.e. the exponent and the top 6 mantissa
+// bits of the nearest binary32 to h (1 .. 2049; 2049 is h rounding to
+// 2^32). gtable[b] is at least the largest noise -lb of any h in the bucket
+// plus 3e-5 (the host builds it in binary64 at the bucket's smallest h; the
+// noise falls as h grows). The kernel's upper bound of an exact key is then
+//   hi = fma(l, RN(1/T), gtable[b]),  up = fma(|hi|, 2^-19, hi)
+// (2^-19 |hi| covers the roundings of l / T, of the key and of hi, and the
+// 3-bit id the kernel packs into up's low bits; 3e-5 covers the
+// definition's own binary32 roundings of L and lb).
+constexpr int GT_BASE = 8127;
+constexpr int GT_N = 2050;
+constexpr int GT_PAD = 2112;              // stored entries: 528 chunks of 16 bytes
+constexpr uint32_t GT_BYTES = GT_PAD * 4;
 
-__device__ __forceinline__ float key_fast(float l, float rcpT, uint32_t h) {
-  const float u = __builtin_fmaf((float)h, 0x1p-32f, 0x1p-33f);
-  const float ys = u * __builtin_fmaf(u, 0.5f * LOG2EF, LOG2EF);
-  const float yl = -__builtin_amdgcn_logf(fmaxf(1.0f - u, 0x1p-24f));
-  const float y2 = u < 0x1p-10f ? ys : yl;
-  const float qc = __builtin_fmaf(l, rcpT, NEG_LN_LN2);
-  return __builtin_fmaf(-LN2F, __builtin_amdgcn_logf(y2), qc);
+// byte offset of h's table entry
+__device__ __forceinline__ uint32_t gt_offset(uint32_t h) {
+  const uint32_t fb = __float_as_uint((float)h);
+  return __builtin_elementwise_sub_sat((fb >> 15) & ~3u, (uint32_t)(GT_BASE * 4));
 }
 
-__device__ __forceinline__ float fast_margin(float ka) { return __builtin_fmaf(fabsf(ka), 0x1p-18f, 1e-3f); }
+__device__ __forceinline__ float key_upper(float l, float rcpT, float gh) {
+  const float hi = __builtin_fmaf(l, rcpT, gh);
+  return __builtin_fmaf(fabsf(hi), 0x1p-19f, hi);
+}
 
 // The total order of every argmax here: a NaN beats every non-NaN, lower
 // id among NaNs; otherwise the larger value, and equal values (so -0 == +0)
@@ -199,85 +223,22 @@ __device__ __forceinline__ unsigned long long pack_winner(float v, int id) {
   return ((unsigned long long)o << 32) | (unsigned long long)(uint32_t)(~(uint32_t)id);
 }
 
-template <typename T8>
-__device__ __forceinline__ T8 pick8(const T8* v, int e) {
-  T8 r = v[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) r = (e == i) ? v[i] : r;
-  return r;
-}
-
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *(const uint4*)p; }
-
-// ---------------------------------------------------------------- the step
-
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
 // The winner slot of a row decodes to its token id.
 __device__ __forceinline__ int64_t slot_token(unsigned long long w) {
   return (int64_t)(uint32_t)(~(uint32_t)w);
 }
 
-// Merge rules of the per-row states. ORDER: the exact (key, id) under the
-// total order. TOP2: (v1, id1, l1) is the element with the largest upper
-// bound v1 of its key, v2 the largest upper bound among all other elements.
-struct RowState {
-  float v1, v2, l1;
-  int id1;
-};
-
-__device__ __forceinline__ void merge_order(RowState& a, const RowState& b) {
-  if (before(b.v1, b.id1, a.v1, a.id1)) {
-    a.v1 = b.v1;
-    a.id1 = b.id1;
-    a.l1 = b.l1;
-  }
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__device__ __forceinline__ void merge_top2(RowState& a, const RowState& b) {
-  const bool bw = (b.v1 > a.v1) || (b.v1 == a.v1 && b.id1 < a.id1);
-  const float lose = bw ? a.v1 : b.v1;
-  const float win2 = bw ? b.v2 : a.v2;
-  a.v2 = fmaxf(lose, win2);
-  if (bw) {
-    a.v1 = b.v1;
-    a.id1 = b.id1;
-    a.l1 = b.l1;
-  }
+// A cache word written by another wave of this workgroup (agent-coherent load).
+__device__ __forceinline__ uint32_t load_cache_word(const uint16_t* cache, size_t elem_even) {
+  return __hip_atomic_load((const uint32_t*)(cache + elem_even), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Upper bound of an exact key from its estimate, less the constant part of
-// the margin (added back at the decision): key <= hi + 1e-3.
-__device__ __forceinline__ float upper_of(float ka) { return __builtin_fmaf(fabsf(ka), 0x1p-18f, ka); }
-
-// Lower bound of the exact key of the element whose upper bound is v1:
-// key >= v1 - 2 * margin, with margin = 1e-3 + |ka| 2^-18 (rounded up).
-__device__ __forceinline__ float lower_of_upper(float v1) {
-  return v1 - 2.5e-3f - fabsf(v1) * 0x1p-16f;
-}
-
-template <int KB>
-__device__ __forceinline__ void load_w2_tile(const uint16_t* w2, int V, int R, int tok0, int m, int g,
-                                             bool kzero, bf16x8_t* A0, bf16x8_t* A1) {
-  const int t0 = tok0 + 8 * (m >> 2) + (m & 3);
-  const int ta = t0 < V ? t0 : V - 1, tb = t0 + 4 < V ? t0 + 4 : V - 1;
-  const uint16_t* pa = w2 + (size_t)ta * R;
-  const uint16_t* pb = w2 + (size_t)tb * R;
-#pragma unroll
-  for (int i = 0; i < KB; ++i) {
-    if (kzero) {
-      A0[i] = (bf16x8_t){};
-      A1[i] = (bf16x8_t){};
-    } else {
-      const int ch = 4 * i + g;
-      A0[i] = __builtin_nontemporal_load((const bf16x8_t*)(pa + ch * 8));
-      A1[i] = __builtin_nontemporal_load((const bf16x8_t*)(pb + ch * 8));
-    }
-  }
-}
-
+// ---------------------------------------------------------------- output transform
 // tanh for the soft cap: an odd minimax polynomial z + z^3 P(z^2) below
 // |z| = 0.625 (fitted here for binary32 Horner evaluation, within 0.7 ulp),
 // else 1 - 2 / (e^{2|z|} + 1) with the hardware exp2 and reciprocal (about
@@ -301,25 +262,37 @@ __device__ __forceinline__ float tanh_fast(float z) {
   return az < 0.625f ? tanh_poly(z) : yl;
 }
 
-// Per-lane view of one of the wave's row blocks, kept in registers for the
-// whole step: the row's offset into base/cache, 1/T, the hash prefix, its
-// kind, and the running state of this lane's elements of the row.
+// ---------------------------------------------------------------- tiles
 
-// Per LDS row n, one 16-byte record: rk = row * k + step (the row's slice of
-// base / cache starts at rk * V), 1/T, the hash prefix and T.
-struct RowInfo {
-  int rk;
-  float rcp;
-  uint32_t prefix;
-  float T;
-};
-typedef RowInfo RowInfoReg;
-struct LaneRow {
-  float v1, v2, l1;
-  int id1;
-  RowInfoReg info;   // the row's constants, when kept in registers
-};
-constexpr int PFD = 2;  // base logits are requested this many row blocks ahead
+// The w2 rows of one 32-token unit as MFMA A operands: lane (g, m) holds
+// k-chunks 4i + g of tokens t0 = tok0 + 8 (m >> 2) + (m & 3) (A0) and t0 + 4
+// (A1); tokens past the vocabulary read its last row (never stored).
+// STREAM: the tile is read once (nontemporal); else a second wave reads the
+// same tile soon after and should find it in L2.
+template <int KB, bool STREAM>
+__device__ __forceinline__ void load_w2_tile(const uint16_t* w2, int V, int R, int tok0, int m, int g,
+                                             bool kzero, bf16x8_t* A0, bf16x8_t* A1) {
+  const int t0 = tok0 + 8 * (m >> 2) + (m & 3);
+  const int ta = t0 < V ? t0 : V - 1, tb = t0 + 4 < V ? t0 + 4 : V - 1;
+  const uint16_t* pa = w2 + (size_t)ta * R;
+  const uint16_t* pb = w2 + (size_t)tb * R;
+#pragma unroll
+  for (int i = 0; i < KB; ++i) {
+    if (kzero) {
+      A0[i] = (bf16x8_t){};
+      A1[i] = (bf16x8_t){};
+    } else {
+      const int ch = 4 * i + g;
+      if (STREAM) {
+        A0[i] = __builtin_nontemporal_load((const bf16x8_t*)(pa + ch * 8));
+        A1[i] = __builtin_nontemporal_load((const bf16x8_t*)(pb + ch * 8));
+      } else {
+        A0[i] = *(const bf16x8_t*)(pa + ch * 8);
+        A1[i] = *(const bf16x8_t*)(pb + ch * 8);
+      }
+    }
+  }
+}
 
 // The bias of one 16-row block for the wave's 32 tokens: lane (g, m) gets
 // row n = 16 rb + m, tokens tg .. tg+3 in c0 and tg+4 .. tg+7 in c1.
@@ -343,104 +316,190 @@ __device__ __forceinline__ void block_bias(const bf16x8_t* A0, const bf16x8_t* A
   }
 }
 
-// Waves: 4 token waves (32 tokens each, a 128-token slab) times RG row
-// groups; the wave's row blocks are rb = wr + j RG, j < MRB (unrolled, so
-// their state lives in registers). Row groups share the workgroup's LDS copy
-// of the embeddings.
+// Per LDS row n, one 16-byte record: rk = row * k + step (the row's slice of
+// base / cache starts at rk * V), 1/T, the hash prefix and T.
+struct RowInfo {
+  int rk;
+  float rcp;
+  uint32_t prefix;
+  float T;
+};
+
+// Merge rules of the per-row states. ORDER: the exact (key, id) under the
+// total order. TOP2: (v1, id) is the element with the largest upper bound
+// v1, v2 the largest upper bound among all other elements. sp: some element
+// had a non-finite estimate (noisy rows) or a NaN / -inf logit (T = 0 rows).
+struct RowState {
+  float v1, v2;
+  int id;
+  int sp;
+};
+
+__device__ __forceinline__ void merge_order(RowState& a, const RowState& b) {
+  if (before(b.v1, b.id, a.v1, a.id)) {
+    a.v1 = b.v1;
+    a.id = b.id;
+  }
+  a.sp |= b.sp;
+}
+
+__device__ __forceinline__ void merge_top2(RowState& a, const RowState& b) {
+  const bool bw = (b.v1 > a.v1) || (b.v1 == a.v1 && b.id < a.id);
+  const float lose = bw ? a.v1 : b.v1;
+  const float win2 = bw ? b.v2 : a.v2;
+  a.v2 = fmaxf(lose, win2);
+  if (bw) {
+    a.v1 = b.v1;
+    a.id = b.id;
+  }
+  a.sp |= b.sp;
+}
+
+// LDS layout (bytes), the table first so that its reads need no base:
+//   [0, GT_BYTES)   noise bound table
+//   region0         embeddings [rp][R] bf16; after the slab loop the waves'
+//                   row states [4][NWV][rp] (v1, v2, id, sp)
+//   info [rp] RowInfo, n_row [rp], n_src [rp], fb_row [rp], fb_thr [rp],
+//   misc [64] (per-wave row counts, fallback count)
+__host__ __device__ __forceinline__ size_t region0_bytes(int rp, int R) {
+  const size_t e = (size_t)rp * R * 2, st = (size_t)NWV * rp * 16;
+  return e > st ? e : st;
+}
+
+__host__ __device__ __forceinline__ size_t lds_total(int rp, int R) {
+  return GT_BYTES + region0_bytes(rp, R) + (size_t)rp * 16 + (size_t)rp * 16 + 64 * 4;
+}
+
+// ---------------------------------------------------------------- the step
+//
+// KB = R / 32 (1 for R = 16 with half the chunks zero), RG row groups (1,
+// or 2 for more than 8 row blocks: then the two waves of a SIMD split the
+// rows, both take every slab of the workgroup and read its w2 tiles through
+// L2), MRB = row blocks per wave (a power of two, the wave's real count may
+// be lower), EXACT = the test-only variant that takes the exact key of
+// every element.
 template <int KB, int RG, int MRB, bool EXACT>
-__global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
-  constexpr int NWV = 4 * RG;                   // waves per workgroup
-  constexpr int NTH = 64 * NWV;
+__global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
+  constexpr int NB = MRB == 1 ? 2 : 1;                   // w2 tiles in flight per wave
+  constexpr int D = MRB - 1 < 3 ? MRB - 1 : 3;           // row blocks contracted ahead
+  constexpr int PFD = MRB == 1 ? 1 : 2;                  // base logits prefetched ahead
+  constexpr int S = RG == 1 ? 2 : 1;                     // waves splitting one SIMD's slabs
+  constexpr bool ROWREG = MRB <= 4;                      // row constants in registers
   extern __shared__ __align__(16) unsigned char lds[];
   const int mode = a.mode;
   const bool bias_mode = mode == MODE_BIAS;
-  constexpr bool exact_mode = EXACT;   // the test-only exact-everywhere variant
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wt = wave & 3, wr = wave >> 2;
+  const int tw = wave & 3;
+  const int sub = RG == 1 ? wave >> 2 : 0;
+  const int wr = RG == 1 ? 0 : wave >> 2;
   const int g = lane >> 4, m = lane & 15;
-  const int R = KB >= 2 ? 32 * KB : a.R;         // the rank is fixed by KB from 64 up
+  const int R = KB >= 2 ? 32 * KB : a.R;
   const int rows = a.rows, rp = (rows + 15) & ~15, V = a.V, s = a.step, K = a.k;
-  const int cpr = R >> 3;                       // 16-byte chunks per embedding row
-  const int swz = (cpr < 16 ? cpr : 16) - 1;   // a 16-lane LDS pass reads 16 distinct chunks
-  const int G = gridDim.x;
+  const int nslabs = a.nslabs, G = gridDim.x;
+  const int cpr = R >> 3;
+  const int swz = (cpr < 16 ? cpr : 16) - 1;
+  const int nrb = rp >> 4;
+  const int my_nrb = nrb > wr ? (nrb - wr + RG - 1) / RG : 0;
+  const int slab_step = G * S;
+  const int slab0 = blockIdx.x + G * sub;
+  const bool kzero = (KB == 1) && (R == 16) && (g >= 2);
 
-  uint16_t* emb = (uint16_t*)lds;
-  RowInfo* n_info = (RowInfo*)(lds + (size_t)rp * R * 2);  // by LDS row n
-  int* n_row = (int*)(n_info + rp);                // LDS row n -> request row
-  int* n_src = n_row + rp;                         // its w1 row
-  float* st_v1 = (float*)(n_src + rp);             // [4][rp] row states, by token wave
-  float* st_v2 = st_v1 + 4 * rp;
-  float* st_l = st_v2 + 4 * rp;
-  int* st_id = (int*)(st_l + 4 * rp);
-  int* sp_cnt = st_id + 4 * rp;                    // [rp] elements whose estimate is not finite
-  int* fb_list = sp_cnt + rp;                      // [rp] rows that take the exact fallback
-  int* misc = fb_list + rp;                        // chunk counts [2][16], fallback count
+  const float* gtab = (const float*)lds;
+  uint16_t* emb = (uint16_t*)(lds + GT_BYTES);
+  const size_t r0 = region0_bytes(rp, R);
+  RowInfo* n_info = (RowInfo*)(lds + GT_BYTES + r0);
+  int* n_row = (int*)(n_info + rp);
+  int* n_src = n_row + rp;
+  int* fb_row = n_src + rp;
+  float* fb_thr = (float*)(fb_row + rp);
+  int* misc = (int*)(fb_thr + rp);
 
-  unsigned long long* slots_cur = a.slots ? a.slots + (size_t)(s % 3) * rows : nullptr;
-  const unsigned long long* slots_prev = a.slots ? a.slots + (size_t)((s + 2) % 3) * rows : nullptr;
-  unsigned long long* slots_next = a.slots ? a.slots + (size_t)((s + 1) % 3) * rows : nullptr;
+  unsigned long long* slots_cur = nullptr;
+  const unsigned long long* slots_prev = nullptr;
+  unsigned long long* slots_next = nullptr;
+  if (!bias_mode) {
+    slots_cur = a.slots + (size_t)(s % 3) * rows;
+    slots_prev = a.slots + (size_t)((s + 2) % 3) * rows;
+    slots_next = a.slots + (size_t)((s + 1) % 3) * rows;
+  }
 
-  // 1. rows: the token feeding this step (decoded from the previous step's
-  //    winner slots), temperature, hash prefix. Noisy rows are placed first
-  //    so that 16-row blocks are of one kind.
-  const int nchunks = (rows + 63) >> 6;
-  for (int c = wave; c < nchunks; c += NWV) {
-    const int r = c * 64 + lane;
-    const bool valid = r < rows;
-    const float T = (!bias_mode && valid) ? a.temperature[r] : 0.0f;
-    const bool noisy = valid && !(T == 0.0f);
-    const uint64_t bn = __ballot(noisy), bz = __ballot(valid && !noisy);
-    if (lane == 0) {
-      misc[c] = __builtin_popcountll(bn);
-      misc[16 + c] = __builtin_popcountll(bz);
+  // 0. this thread's request row: everything it needs in one round trip
+  const int r = tid;
+  const bool valid = r < rows;
+  float T = 0.0f;
+  int64_t tok = 0, seed = 0, pos = 0;
+  if (valid) {
+    if (!bias_mode) {
+      T = a.temperature[r];
+      seed = a.seeds[r];
+      pos = a.positions[(int64_t)r * K + s];
+    }
+    tok = (bias_mode || s == 0) ? a.prev[r] : slot_token(slots_prev[r]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 1. the wave's first w2 tiles: they depend on nothing above
+  bf16x8_t A0[NB][KB], A1[NB][KB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int sl = slab0 + nb * slab_step;
+    if (my_nrb > 0 && sl < nslabs)
+      load_w2_tile<KB, RG == 1>(a.w2, V, R, sl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[nb], A1[nb]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // the noise bound table, straight into LDS
+  if (!bias_mode) {
+    for (int j = wave; j * 64 * 16 < (int)GT_BYTES; j += NWV) {
+      const int p = j * 64 + lane;
+      if (p * 16 < (int)GT_BYTES)
+        __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.gtable + (size_t)p * 16),
+                                         (__attribute__((address_space(3))) void*)(lds + (size_t)j * 1024),
+                                         16, 0, 0);
     }
   }
-  for (int n = rows + tid; n < rp; n += NTH) {
-    n_row[n] = 0;
-    n_src[n] = 0;
-    n_info[n] = RowInfo{s, 0.0f, 0u, 0.0f};
+
+  // 2. rows: noisy rows first, so that 16-row blocks are of one kind
+  const bool noisy_r = valid && !bias_mode && !(T == 0.0f);
+  const uint64_t bn = __ballot(noisy_r), bz = __ballot(valid && !noisy_r);
+  if (lane == 0) {
+    misc[wave] = __builtin_popcountll(bn);
+    misc[8 + wave] = __builtin_popcountll(bz);
   }
-  for (int n = tid; n < rp; n += NTH) sp_cnt[n] = 0;
-  if (tid == 0) misc[32] = 0;
+  if (tid == 0) misc[16] = 0;
   __syncthreads();
-  int total_noisy = 0;
-  for (int c = 0; c < nchunks; ++c) total_noisy += misc[c];
-  for (int c = wave; c < nchunks; c += NWV) {
-    const int r = c * 64 + lane;
-    const bool valid = r < rows;
-    float T = 0.0f;
-    int64_t t = 0;
-    if (valid) {
-      if (!bias_mode) T = a.temperature[r];
-      t = (bias_mode || s == 0) ? a.prev[r] : slot_token(slots_prev[r]);
-    }
-    const bool noisy = valid && !(T == 0.0f);
-    const uint64_t bn = __ballot(noisy), bz = __ballot(valid && !noisy);
-    int pre_n = 0, pre_z = 0;
-    for (int c2 = 0; c2 < c; ++c2) {
-      pre_n += misc[c2];
-      pre_z += misc[16 + c2];
-    }
-    if (valid) {
-      const int pos = bias_mode ? r
-                    : noisy ? pre_n + (int)lanes_below(bn)
-                            : total_noisy + pre_z + (int)lanes_below(bz);
-      const uint64_t ut = (uint64_t)t, last = (uint64_t)(V - 1);
-      n_row[pos] = r;
-      n_src[pos] = (int)(ut < last ? ut : last);
-      n_info[pos] = RowInfo{r * K + s, 1.0f / T,
-                            bias_mode ? 0u : row_prefix_of(a.seeds[r], s, a.positions[(int64_t)r * K + s]),
-                            T};
-      if (!bias_mode && blockIdx.x == 0) {
-        if (s > 0) a.tokens[(int64_t)r * K + s - 1] = t;   // the previous step's token
-        slots_next[r] = 0ull;                             // next step's slots start empty
+  {
+    int pre_n = 0, pre_z = 0, tot_n = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const int cn = misc[w], cz = misc[8 + w];
+      tot_n += cn;
+      if (w < wave) {
+        pre_n += cn;
+        pre_z += cz;
       }
     }
+    if (valid) {
+      const int n = bias_mode ? r
+                  : noisy_r ? pre_n + (int)lanes_below(bn)
+                            : tot_n + pre_z + (int)lanes_below(bz);
+      const uint64_t ut = (uint64_t)tok, last = (uint64_t)(V - 1);
+      n_row[n] = r;
+      n_src[n] = (int)(ut < last ? ut : last);
+      n_info[n] = RowInfo{r * K + s, 1.0f / T, bias_mode ? 0u : row_prefix_of(seed, s, pos), T};
+      if (!bias_mode && blockIdx.x == 0) {
+        if (s > 0) a.tokens[(int64_t)r * K + s - 1] = tok;   // the previous step's token
+        slots_next[r] = 0ull;                               // next step's slots start empty
+      }
+    } else if (r < rp) {
+      n_row[r] = 0;
+      n_src[r] = 0;
+      n_info[r] = RowInfo{0, 0.0f, 0u, 0.0f};
+    }
   }
   __syncthreads();
 
-  // 2. gather the embeddings straight into LDS (16-byte chunks, swizzled);
-  //    padding rows read row 0 and are never used.
+  // 3. the embeddings, straight into LDS (16-byte chunks, swizzled);
+  //    padding rows read row 0 and are never used
   {
     const int total = rp * cpr;
     for (int j = wave; j * 64 < total; j += NWV) {
@@ -455,285 +514,340 @@ __global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
     }
   }
 
-  // this lane's rows, one per row block of the wave
-  const int nrb = rp >> 4;
-  const int my_nrb = nrb > wr ? (nrb - wr + RG - 1) / RG : 0;
-  // small row-block counts keep each row's constants in registers (they feed
-  // the base-logit addresses); large ones read them from LDS per tile
-  constexpr bool ROWREG = MRB <= 4;
-  LaneRow lr[MRB];
+  // this lane's rows: one per row block of the wave (n = 16 (wr + RG j) + m)
+  RowInfo ri[ROWREG ? MRB : 1];
+  if (ROWREG) {
+#pragma unroll
+    for (int j = 0; j < (ROWREG ? MRB : 1); ++j) ri[j] = n_info[j < my_nrb ? 16 * (wr + RG * j) + m : 0];
+  }
+  auto rk_of = [&](int j) -> int {
+    return ROWREG ? ri[ROWREG ? j : 0].rk : n_info[16 * (wr + RG * j) + m].rk;
+  };
+  // base logits of block j of the unit in slab sl, for this lane's 8 tokens
+  auto fetch_base = [&](int j, int sl, u32x4_t& dst) {
+    const int n = 16 * (wr + RG * j) + m;
+    const int tgt = sl * SLAB + tw * TOK_PER_WAVE + 8 * g;
+    dst = (u32x4_t){0u, 0u, 0u, 0u};
+    if (j < my_nrb && n < rows && sl < nslabs && tgt < V)
+      dst = __builtin_nontemporal_load((const u32x4_t*)(a.base + (size_t)rk_of(j) * V + tgt));
+  };
+  u32x4_t bq[MRB];
+  if (!bias_mode) {
+#pragma unroll
+    for (int j = 0; j < PFD && j < MRB; ++j) fetch_base(j, slab0, bq[j]);
+  }
+
+  float v1[MRB], v2[MRB];
+  int idt[MRB];
+  bool sp[MRB];
 #pragma unroll
   for (int j = 0; j < MRB; ++j) {
-    if (ROWREG) {
-      const int n = (wr + j * RG) * 16 + m;
-      lr[j].info = n_info[j < my_nrb ? n : 0];
-    }
-    lr[j].v1 = -INFINITY;
-    lr[j].v2 = -INFINITY;
-    lr[j].l1 = 0.0f;
-    lr[j].id1 = NONE;
+    v1[j] = -INFINITY;
+    v2[j] = -INFINITY;
+    idt[j] = NONE;
+    sp[j] = false;
   }
-  const bool kzero = (KB == 1) && (R == 16) && (g >= 2);
-  bf16x8_t A0[KB], A1[KB];
-  int slab = blockIdx.x;
-  if (my_nrb > 0) load_w2_tile<KB>(a.w2, V, R, slab * SLAB + wt * TOK_PER_WAVE, m, g, kzero, A0, A1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // D: row blocks whose contraction is issued ahead of the current epilogue;
-  // once the slab's last contraction is out, the next slab's w2 tile is
-  // requested, so it streams in under the remaining epilogues.
-#ifndef MARKOV_AHEAD
-#define MARKOV_AHEAD 1
-#endif
-#ifndef MARKOV_XSLAB
-#define MARKOV_XSLAB 0
-#endif
-  constexpr int D = MRB - 1 < MARKOV_AHEAD ? MRB - 1 : MARKOV_AHEAD;
   const float mult = a.mult, cap = a.cap, inv_cap = a.inv_cap;
-  u32x4_t bq[MRB];
-  if (my_nrb > 0) {
-    for (; slab < a.nslabs; slab += G) {
-      if (!MARKOV_XSLAB || slab == (int)blockIdx.x) {
-        const int tg0 = slab * SLAB + wt * TOK_PER_WAVE + 8 * g;
+  const bool has_cap = a.has_cap != 0;
+
+  // one 32-token unit (slab `sl`) with w2 tile buffer BUF
+  auto unit = [&](auto bufc, int sl) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int tok0 = sl * SLAB + tw * TOK_PER_WAVE;
+    const int tg = tok0 + 8 * g;               // this lane's 8 tokens: tg .. tg+7
+    const bool tok_ok = tg < V;
+    const int nsl = sl + NB * slab_step;       // the slab whose tile goes into this buffer next
+    const int psl = sl + slab_step;            // the next slab (base logit prefetch)
+    uint32_t kw[8];
+    if (!bias_mode) {
+      uint32_t kc = (uint32_t)tg * MM_C1;
 #pragma unroll
-        for (int j = 0; j < MRB; ++j) {
-          bq[j] = (u32x4_t){0u, 0u, 0u, 0u};
-          const int n = (wr + j * RG) * 16 + m;
-          if (!bias_mode && j < PFD && j < my_nrb && n < rows && tg0 < V)
-            bq[j] = __builtin_nontemporal_load(
-                (const u32x4_t*)(a.base + (size_t)(ROWREG ? lr[j].info.rk : n_info[n].rk) * V + tg0));
-        }
+      for (int e = 0; e < 8; ++e) {
+        kw[e] = rotl32(kc, 15) * MM_C2;
+        kc += MM_C1;
       }
-      const int tok0 = slab * SLAB + wt * TOK_PER_WAVE;
-      const int nxt = slab + G;
-      const int tg = tok0 + 8 * g;              // this lane's 8 tokens: tg .. tg+7
-      const int tgn = tg + G * SLAB;            // the same lane's tokens in the next slab
-      const bool tok_ok = tg < V, tokn_ok = nxt < a.nslabs && tgn < V;
-      if (tok0 >= V) continue;                  // wave-uniform: the last slab's tail
-      uint32_t kw[8];
+    }
+    f32x4_t cb0[MRB], cb1[MRB];
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j < my_nrb)
+        block_bias<KB>(A0[BUF], A1[BUF], emb, 16 * (wr + RG * j) + m, R, g, swz, kzero, cb0[j], cb1[j]);
+    if (D > 0 && my_nrb <= D && nsl < nslabs)
+      load_w2_tile<KB, RG == 1>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF], A1[BUF]);
+#pragma unroll
+    for (int j = 0; j < MRB; ++j) {
+      const int n = 16 * (wr + RG * j) + m;
+      // the contraction of block j + D (of block j itself when D == 0); once
+      // the unit's last one has issued, this buffer's next tile
+      if (D == 0) {
+        if (j < my_nrb) {
+          block_bias<KB>(A0[BUF], A1[BUF], emb, n, R, g, swz, kzero, cb0[j], cb1[j]);
+          if (j == my_nrb - 1 && nsl < nslabs)
+            load_w2_tile<KB, RG == 1>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF], A1[BUF]);
+        }
+      } else if (j + D < MRB && j + D < my_nrb) {
+        block_bias<KB>(A0[BUF], A1[BUF], emb, n + 16 * RG * D, R, g, swz, kzero, cb0[j + D], cb1[j + D]);
+        if (j + D == my_nrb - 1 && nsl < nslabs)
+          load_w2_tile<KB, RG == 1>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF], A1[BUF]);
+      }
+      const u32x4_t bv = bq[j];
+      // base logits PFD blocks ahead, into the next slab past this one's end
       if (!bias_mode) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kw[e] = mm_token_word((uint32_t)(tg + e));
+        if (j + PFD < MRB) fetch_base(j + PFD, sl, bq[j + PFD < MRB ? j + PFD : 0]);
+        else fetch_base(j + PFD - MRB, psl, bq[j + PFD >= MRB ? j + PFD - MRB : 0]);
       }
-      f32x4_t cb0[MRB], cb1[MRB];
-      bool a_out = false;                       // next slab's tile requested
-#pragma unroll
-      for (int j = 0; j < D; ++j)
-        if (j < my_nrb) block_bias<KB>(A0, A1, emb, (wr + j * RG) * 16 + m, R, g, swz, kzero, cb0[j], cb1[j]);
-      if (my_nrb <= D && nxt < a.nslabs) {
-        load_w2_tile<KB>(a.w2, V, R, nxt * SLAB + wt * TOK_PER_WAVE, m, g, kzero, A0, A1);
-        a_out = true;
+      if (j >= my_nrb) continue;
+
+      const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[n];
+      const bool active = n < rows && tok_ok;
+      const bool noisy = !(info.T == 0.0f);
+      const f32x4_t c0 = cb0[j], c1 = cb1[j];
+      uint32_t bw[4];
+      bw[0] = pack_bf16(c0[0], c0[1]);
+      bw[1] = pack_bf16(c0[2], c0[3]);
+      bw[2] = pack_bf16(c1[0], c1[1]);
+      bw[3] = pack_bf16(c1[2], c1[3]);
+      if (bias_mode) {
+        if (active)
+          *(uint4*)(a.bias_out + (size_t)n_row[n] * V + tg) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+        continue;
       }
+      // logits: bf16 add (one binary32 add, rounded), multiplier, soft cap
+      const uint32_t bwd[4] = {bv.x, bv.y, bv.z, bv.w};
+      uint32_t cw[4];
 #pragma unroll
-      for (int j = 0; j < MRB; ++j) {
-        if (j >= my_nrb) break;
-        const int n = (wr + j * RG) * 16 + m;
-        if (j + D < MRB && j + D < my_nrb) {
-          block_bias<KB>(A0, A1, emb, n + D * RG * 16, R, g, swz, kzero, cb0[j + D], cb1[j + D]);
-          if (j + D == my_nrb - 1 && nxt < a.nslabs) {
-            load_w2_tile<KB>(a.w2, V, R, nxt * SLAB + wt * TOK_PER_WAVE, m, g, kzero, A0, A1);
-            a_out = true;
-          }
+      for (int q = 0; q < 4; ++q)
+        cw[q] = pack_bf16(bf_lo(bwd[q]) + bf_lo(bw[q]), bf_hi(bwd[q]) + bf_hi(bw[q]));
+      if (has_cap) {
+        float z[8];
+        float zmax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          z[2 * q] = (mult * bf_lo(cw[q])) * inv_cap;
+          z[2 * q + 1] = (mult * bf_hi(cw[q])) * inv_cap;
+          zmax = fmaxf(zmax, fmaxf(fabsf(z[2 * q]), fabsf(z[2 * q + 1])));
         }
-        // base logits PFD row blocks ahead, into the next slab past the end
-        if (!bias_mode) {
-          if (j + PFD < MRB) {
-            const int n2 = n + PFD * RG * 16;
-            if (n2 < rows && tok_ok && j + PFD < my_nrb)
-              bq[j + PFD] = __builtin_nontemporal_load(
-                  (const u32x4_t*)(a.base + (size_t)(ROWREG ? lr[j + PFD].info.rk : n_info[n2].rk) * V + tg));
-          }
-        }
-        const RowInfo info = ROWREG ? lr[j].info : n_info[n];
-        const f32x4_t c0 = cb0[j], c1 = cb1[j];
-        const bool valid = n < rows;
-        const bool active = valid && tok_ok;
-        const bool noisy = !(info.T == 0.0f);
-        const bool top2 = noisy && !exact_mode;
-        uint32_t bw[4];
-        bw[0] = pack_bf16(c0[0], c0[1]);
-        bw[1] = pack_bf16(c0[2], c0[3]);
-        bw[2] = pack_bf16(c1[0], c1[1]);
-        bw[3] = pack_bf16(c1[2], c1[3]);
-        if (bias_mode) {
-          if (active)
-            *(uint4*)(a.bias_out + (size_t)n_row[n] * V + tg) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-        } else {
-          const u32x4_t bv = bq[j];
-          // this slot is free again: the next slab's logits for the same row
-          if (MARKOV_XSLAB && j < PFD) {
-            bq[j] = (u32x4_t){0u, 0u, 0u, 0u};
-            if (valid && tokn_ok && (my_nrb > PFD || j + PFD >= my_nrb))
-              bq[j] = __builtin_nontemporal_load((const u32x4_t*)(a.base + (size_t)info.rk * V + tgn));
-          }
-          // logits: bf16 add (one binary32 add, rounded), multiplier, soft cap
-          const uint32_t bwd[4] = {bv.x, bv.y, bv.z, bv.w};
-          float l[8];
-          uint32_t cw[4];
+        if (__any(!(zmax < 0.625f))) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            cw[q] = pack_bf16(bf_lo(bwd[q]) + bf_lo(bw[q]), bf_hi(bwd[q]) + bf_hi(bw[q]));
-          if (a.has_cap) {
-            float z[8];
-            float zmax = 0.0f;
+            cw[q] = pack_bf16(cap * tanh_fast(z[2 * q]), cap * tanh_fast(z[2 * q + 1]));
+        } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              z[2 * q] = (mult * bf_lo(cw[q])) * inv_cap;
-              z[2 * q + 1] = (mult * bf_hi(cw[q])) * inv_cap;
-              zmax = fmaxf(zmax, fmaxf(fabsf(z[2 * q]), fabsf(z[2 * q + 1])));
-            }
-            if (__any(!(zmax < 0.625f))) {
+          for (int q = 0; q < 4; ++q)
+            cw[q] = pack_bf16(cap * tanh_poly(z[2 * q]), cap * tanh_poly(z[2 * q + 1]));
+        }
+      } else if (mult != 1.0f) {
 #pragma unroll
-              for (int q = 0; q < 4; ++q)
-                cw[q] = pack_bf16(cap * tanh_fast(z[2 * q]), cap * tanh_fast(z[2 * q + 1]));
-            } else {
+        for (int q = 0; q < 4; ++q) cw[q] = pack_bf16(mult * bf_lo(cw[q]), mult * bf_hi(cw[q]));
+      }
+      float l[8];
 #pragma unroll
-              for (int q = 0; q < 4; ++q)
-                cw[q] = pack_bf16(cap * tanh_poly(z[2 * q]), cap * tanh_poly(z[2 * q + 1]));
-            }
-          } else if (mult != 1.0f) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              cw[q] = pack_bf16(mult * bf_lo(cw[q]), mult * bf_hi(cw[q]));
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            l[2 * q] = bf_lo(cw[q]);
-            l[2 * q + 1] = bf_hi(cw[q]);
-          }
-          if (active)
-            __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]},
-                                        (u32x4_t*)(a.cache + (size_t)info.rk * V + tg));
+      for (int q = 0; q < 4; ++q) {
+        l[2 * q] = bf_lo(cw[q]);
+        l[2 * q + 1] = bf_hi(cw[q]);
+      }
+      if (active)
+        __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]},
+                                    (u32x4_t*)(a.cache + (size_t)info.rk * V + tg));
 
-          if (__any(active && top2)) {
-            if (active && top2) {
-              bool special = false;
-              float v1 = lr[j].v1, v2 = lr[j].v2;
-              int eb = -1;
+      if (EXACT) {
+        if (active) {
 #pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const uint32_t h = mm_finish(info.prefix, kw[e]);
-                const float ka = key_fast(l[e], info.rcp, h);
-                const bool bad = !(fabsf(ka) < 1e37f);
-                special = special || bad;
-                const float hx = bad ? -INFINITY : upper_of(ka);
-                // elements arrive in rising id: a tie keeps the earlier as top
-                eb = hx > v1 ? e : eb;
-                v2 = __builtin_amdgcn_fmed3f(v1, v2, hx);
-                v1 = fmaxf(v1, hx);
-              }
-              lr[j].v1 = v1;
-              lr[j].v2 = v2;
-              if (eb >= 0) {
-                lr[j].id1 = tg + eb;
-                lr[j].l1 = pick8(l, eb);
-              }
-              if (special) atomicAdd(&sp_cnt[n], 1);
-            }
-          }
-          // keep each row block's live ranges to itself
-          if (__any(active && !top2)) {
-            if (active && !top2) {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                float key = l[e];
-                if (noisy) key = key_exact(l[e], info.T, mm_finish(info.prefix, kw[e]));
-                if (before(key, tg + e, lr[j].v1, lr[j].id1)) {
-                  lr[j].v1 = key;
-                  lr[j].id1 = tg + e;
-                }
-              }
+          for (int e = 0; e < 8; ++e) {
+            float key = l[e];
+            if (noisy) key = key_exact(l[e], info.T, mm_finish(info.prefix, kw[e]));
+            if (before(key, tg + e, v1[j], idt[j])) {
+              v1[j] = key;
+              idt[j] = tg + e;
             }
           }
         }
-        if (MRB >= 8) __builtin_amdgcn_sched_barrier(0);
+        continue;
       }
-      if (!a_out && nxt < a.nslabs)
-        load_w2_tile<KB>(a.w2, V, R, nxt * SLAB + wt * TOK_PER_WAVE, m, g, kzero, A0, A1);
+      // noisy rows: the two largest upper bounds, the element's index in the
+      // tile packed into the bound's low 3 bits
+      if (__any(active && noisy)) {
+        if (active && noisy) {
+          float x1 = v1[j], x2 = v2[j];
+          const float x1b = x1;
+          bool spx = false;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t h = mm_finish(info.prefix, kw[e]);
+            const float gh = *(const float*)((const unsigned char*)gtab + gt_offset(h));
+            const float up = key_upper(l[e], info.rcp, gh);
+            spx = spx || __builtin_amdgcn_class(up, 0x207);       // NaN or infinite
+            const float pk = __uint_as_float((__float_as_uint(up) & ~7u) | (uint32_t)e);
+            x2 = __builtin_amdgcn_fmed3f(x1, x2, pk);
+            x1 = __builtin_amdgcn_fmed3f(x1, pk, INFINITY);
+          }
+          if (x1 != x1b) idt[j] = tg;
+          v1[j] = x1;
+          v2[j] = x2;
+          sp[j] = sp[j] || spx;
+        }
+      }
+      // temperature-0 rows: the exact largest logit, the earliest on ties
+      // (elements arrive in rising id); v2 holds its index in the tile
+      if (__any(active && !noisy)) {
+        if (active && !noisy) {
+          float x1 = v1[j];
+          const float x1b = x1;
+          uint32_t e1 = __float_as_uint(v2[j]);
+          bool spx = false;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            spx = spx || __builtin_amdgcn_class(l[e], 0x007);   // NaN or -inf
+            const bool gt = l[e] > x1;
+            x1 = gt ? l[e] : x1;
+            e1 = gt ? (uint32_t)e : e1;
+          }
+          if (x1 != x1b) idt[j] = tg;
+          v1[j] = x1;
+          v2[j] = __uint_as_float(e1);
+          sp[j] = sp[j] || spx;
+        }
+      }
+    }
+  };
+
+  if (my_nrb > 0) {
+    int sl = slab0;
+    if (NB == 1) {
+      for (; sl < nslabs && sl * SLAB + tw * TOK_PER_WAVE < V; sl += slab_step)
+        unit(std::integral_constant<int, 0>{}, sl);
+    } else {
+      while (sl < nslabs && sl * SLAB + tw * TOK_PER_WAVE < V) {
+        unit(std::integral_constant<int, 0>{}, sl);
+        sl += slab_step;
+        if (!(sl < nslabs && sl * SLAB + tw * TOK_PER_WAVE < V)) break;
+        unit(std::integral_constant<int, NB - 1>{}, sl);
+        sl += slab_step;
+      }
     }
   }
   if (bias_mode) return;
 
-  // 3. each row's state: this lane's, merged over the row's 4 lanes, stored
-  //    per token wave, then merged over the token waves; one exact key for
-  //    the top element of a noisy row (its cached logit read back) unless
-  //    another element's bound reaches it (or an estimate was not finite),
-  //    in which case the row goes to the exact fallback below; then one
-  //    packed atomicMax per row.
+  // 4. each row's state: this lane's, merged over the row's 4 lanes, stored
+  //    per wave (over the embeddings, once every wave is past its last
+  //    contraction), merged over the waves; then per row either the packed
+  //    atomicMax of its certified winner or the fallback list.
+  RowState fin[MRB];
 #pragma unroll
   for (int j = 0; j < MRB; ++j) {
     if (j >= my_nrb) break;
-    RowState st = {lr[j].v1, lr[j].v2, lr[j].l1, lr[j].id1};
+    const int n = 16 * (wr + RG * j) + m;
+    const bool noisy = !((ROWREG ? ri[ROWREG ? j : 0].T : n_info[n].T) == 0.0f);
+    RowState st;
+    st.v1 = v1[j];
+    st.v2 = v2[j];
+    st.sp = sp[j] ? 1 : 0;
+    if (EXACT) st.id = idt[j];
+    else if (idt[j] == NONE) st.id = NONE;
+    else st.id = idt[j] + (int)((noisy ? __float_as_uint(v1[j]) : __float_as_uint(v2[j])) & 7u);
+    const bool top2 = noisy && !EXACT;
 #pragma unroll
     for (int sh = 16; sh <= 32; sh <<= 1) {
       RowState o;
       o.v1 = __shfl_xor(st.v1, sh);
       o.v2 = __shfl_xor(st.v2, sh);
-      o.l1 = __shfl_xor(st.l1, sh);
-      o.id1 = __shfl_xor(st.id1, sh);
-      if (!(n_info[(wr + j * RG) * 16 + m].T == 0.0f) && !exact_mode) merge_top2(st, o);
+      o.id = __shfl_xor(st.id, sh);
+      o.sp = __shfl_xor(st.sp, sh);
+      if (top2) merge_top2(st, o);
       else merge_order(st, o);
     }
-    const int n = (wr + j * RG) * 16 + m;
-    if (g == 0 && n < rp) {
-      st_v1[wt * rp + n] = st.v1;
-      st_v2[wt * rp + n] = st.v2;
-      st_l[wt * rp + n] = st.l1;
-      st_id[wt * rp + n] = st.id1;
+    fin[j] = st;
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's cache stores, read back below
+  __syncthreads();
+  float* st_v1 = (float*)emb;
+  float* st_v2 = st_v1 + NWV * rp;
+  int* st_id = (int*)(st_v2 + NWV * rp);
+  int* st_sp = st_id + NWV * rp;
+#pragma unroll
+  for (int j = 0; j < MRB; ++j) {
+    if (j >= my_nrb) break;
+    const int n = 16 * (wr + RG * j) + m;
+    if (g == 0) {
+      st_v1[wave * rp + n] = fin[j].v1;
+      st_v2[wave * rp + n] = fin[j].v2;
+      st_id[wave * rp + n] = fin[j].id;
+      st_sp[wave * rp + n] = fin[j].sp;
     }
   }
   __syncthreads();
   for (int n = tid; n < rows; n += NTH) {
-    const float T = n_info[n].T;
-    const bool noisy = !(T == 0.0f);
-    const bool top2 = noisy && !exact_mode;
-    RowState st = {st_v1[n], st_v2[n], st_l[n], st_id[n]};
-#pragma unroll
-    for (int w = 1; w < 4; ++w) {
+    const RowInfo info = n_info[n];
+    const bool noisy = !(info.T == 0.0f);
+    const bool top2 = noisy && !EXACT;
+    const int w0 = RG == 1 ? 0 : 4 * ((n >> 4) & 1);
+    const int w1n = RG == 1 ? NWV : w0 + 4;
+    RowState st = {st_v1[w0 * rp + n], st_v2[w0 * rp + n], st_id[w0 * rp + n], st_sp[w0 * rp + n]};
+    for (int w = w0 + 1; w < w1n; ++w) {
       const int i = w * rp + n;
-      RowState o = {st_v1[i], st_v2[i], st_l[i], st_id[i]};
+      RowState o = {st_v1[i], st_v2[i], st_id[i], st_sp[i]};
       if (top2) merge_top2(st, o);
       else merge_order(st, o);
     }
     const int r = n_row[n];
     float key = st.v1;
-    if (top2) {
-      const bool near = st.id1 != NONE && st.v2 >= lower_of_upper(st.v1);
-      if (near || sp_cnt[n] > 0 || mode == MODE_SAMPLE_FALLBACK) {
-        fb_list[atomicAdd(&misc[32], 1)] = n;
-        continue;
+    bool fb = !EXACT && (st.sp != 0 || (mode == MODE_SAMPLE_FALLBACK && noisy));
+    float thr = -INFINITY;
+    if (!fb && top2 && st.id != NONE) {
+      const size_t e = (size_t)info.rk * V + st.id;
+      const uint32_t wd = load_cache_word(a.cache, e & ~(size_t)1);
+      const float l1 = (e & 1) ? bf_hi(wd) : bf_lo(wd);
+      key = key_exact(l1, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)st.id)));
+      if (!(key > st.v2)) {
+        fb = true;
+        thr = key;
       }
-      key = key_exact(st.l1, T, mm_finish(n_info[n].prefix, mm_token_word((uint32_t)st.id1)));
     }
-    if (st.id1 != NONE)
-      __hip_atomic_fetch_max(slots_cur + r, pack_winner(key, st.id1), __ATOMIC_RELAXED,
+    if (fb) {
+      const int i = atomicAdd(&misc[16], 1);
+      fb_row[i] = n;
+      fb_thr[i] = thr;
+    } else if (st.id != NONE) {
+      __hip_atomic_fetch_max(slots_cur + r, pack_winner(key, st.id), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __syncthreads();
 
-  // 4. exact fallback: the whole workgroup re-reads the row's cached logits
-  //    over its own slabs and takes every exact key.
-  const int nfb = misc[32];
-  if (nfb > 0) {
-    __builtin_amdgcn_s_waitcnt(0);   // this workgroup's cache stores, re-read below
-    __syncthreads();
-  }
-  float* red_v = st_v1;  // reuse: [NWV] partials
-  int* red_i = st_id;
-  for (int f = 0; f < nfb; ++f) {
-    const int n = fb_list[f];
+  // 5. fallback rows, one per wave at a time: the wave re-reads the row's
+  //    cached logits over the workgroup's slabs and takes the exact key of
+  //    every element whose bound reaches the threshold (all of them for a
+  //    row with a non-finite estimate).
+  const int nfb = misc[16];
+  const int wg_slabs = (int)blockIdx.x < nslabs ? (nslabs - (int)blockIdx.x + G - 1) / G : 0;
+  for (int f = wave; f < nfb; f += NWV) {
+    const int n = fb_row[f];
+    const float thr = fb_thr[f];
+    const RowInfo info = n_info[n];
+    const bool noisy = !(info.T == 0.0f);
     const int r = n_row[n];
-    const float T = n_info[n].T;
-    const uint32_t prefix = n_info[n].prefix;
     float bv = -INFINITY;
     int bi = NONE;
-    const int per_wg = ((a.nslabs - blockIdx.x + G - 1) / G) * SLAB;
-    for (int i = tid; i < per_wg; i += NTH) {
-      const int t = (blockIdx.x + (i / SLAB) * G) * SLAB + (i % SLAB);
-      if (t < V) {
-        const float l = bf_lo((uint32_t)a.cache[((size_t)r * K + s) * (size_t)V + t]);
-        const float key = key_exact(l, T, mm_finish(prefix, mm_token_word((uint32_t)t)));
+    for (int q = lane; q < wg_slabs * (SLAB / 2); q += 64) {
+      const int t0 = ((int)blockIdx.x + (q / (SLAB / 2)) * G) * SLAB + 2 * (q % (SLAB / 2));
+      if (t0 >= V) continue;
+      const uint32_t wd = load_cache_word(a.cache, (size_t)info.rk * V + t0);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int t = t0 + e;
+        const float l = e ? bf_hi(wd) : bf_lo(wd);
+        float key = l;
+        if (noisy) {
+          const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
+          if (!(thr == -INFINITY)) {
+            const float gh = *(const float*)((const unsigned char*)gtab + gt_offset(h));
+            if (key_upper(l, info.rcp, gh) < thr) continue;
+          }
+          key = key_exact(l, info.T, h);
+        }
         if (before(key, t, bv, bi)) {
           bv = key;
           bi = t;
@@ -749,30 +863,17 @@ __global__ __launch_bounds__(256 * RG) void markov_step_kernel(StepArgs a) {
         bi = oi;
       }
     }
-    __syncthreads();
-    if (lane == 0) {
-      red_v[wave] = bv;
-      red_i[wave] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 1; w < NWV; ++w)
-        if (before(red_v[w], red_i[w], bv, bi)) {
-          bv = red_v[w];
-          bi = red_i[w];
-        }
-      if (bi != NONE)
-        __hip_atomic_fetch_max(slots_cur + r, pack_winner(bv, bi), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (lane == 0 && bi != NONE)
+      __hip_atomic_fetch_max(slots_cur + r, pack_winner(bv, bi), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // After the last step: its winners become tokens[:, k-1], and all three
 // slot buffers are left zeroed for the next call.
-__global__ __launch_bounds__(BLOCK) void markov_finish_kernel(unsigned long long* slots, int64_t* tokens,
-                                                              int rows, int k) {
-  for (int r = threadIdx.x; r < rows; r += BLOCK) {
+__global__ __launch_bounds__(256) void markov_finish_kernel(unsigned long long* slots, int64_t* tokens,
+                                                            int rows, int k) {
+  for (int r = threadIdx.x; r < rows; r += 256) {
     const unsigned long long w = slots[(size_t)((k - 1) % 3) * rows + r];
     tokens[(int64_t)r * k + k - 1] = slot_token(w);
     slots[r] = 0ull;
@@ -784,15 +885,13 @@ __global__ __launch_bounds__(BLOCK) void markov_finish_kernel(unsigned long long
 // ---------------------------------------------------------------- test kernels
 
 __global__ void debug_gumbel_kernel(const float* logits, const uint32_t* ids, int64_t n, float T,
-                                    int64_t seed, int step, int64_t position, float* kx, float* kf,
-                                    float* mg) {
+                                    int64_t seed, int step, int64_t position, const float* gtable,
+                                    float* kx, float* ku) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   uint32_t h = mm_finish(row_prefix_of(seed, step, position), mm_token_word(ids[i]));
   float l = logits[i];
-  const float ka = key_fast(l, 1.0f / T, h);
-  kf[i] = ka;
-  mg[i] = fast_margin(ka);
+  ku[i] = key_upper(l, 1.0f / T, gtable[gt_offset(h) / 4]);
   kx[i] = !(T == 0.0f) ? key_exact(l, T, h) : l;
 }
 
@@ -814,25 +913,54 @@ __global__ __launch_bounds__(256) void markov_copy_kernel(const u32x4_t* __restr
 
 // ---------------------------------------------------------------- host side
 
-typedef void (*StepFn)(StepArgs);
+// The noise bound table (see gt_offset), built once in binary64: entry b
+// bounds the noise -log(-L(u)) of every h in bucket b from above by its
+// value at the bucket's smallest h (the noise falls as h, hence u, grows),
+// plus 3e-5, rounded up to binary32.
+float g_table[GT_PAD];
+bool g_table_ready = false;
 
-// Row groups per workgroup: when one workgroup's LDS (mostly the
-// embeddings) leaves room for a single workgroup per CU, more waves share it
-// (two row groups; four where the rank is small enough to keep the w2 tile in
-// few registers). MRB: the most row blocks one wave handles.
-size_t lds_bytes(int rows, int R);
+float up_to_float(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = nextafterf(f, INFINITY);
+  return f;
+}
+
+void build_table() {
+  if (g_table_ready) return;
+  for (int b = 0; b < GT_N; ++b) {
+    double hlo = 0.0;
+    if (b > 0) {
+      const uint32_t fb = (uint32_t)(b + GT_BASE) << 17;
+      float F;
+      memcpy(&F, &fb, 4);
+      // the smallest h whose nearest binary32 is F or above: below 2^24 every
+      // integer is exact, above it h reaches at least the midpoint between
+      // F's predecessor and F (taken rounded down)
+      const double Fd = (double)F;
+      hlo = Fd <= 0x1p24 ? ceil(Fd) : floor(0.5 * ((double)nextafterf(F, 0.0f) + Fd));
+    }
+    const float u = (float)((hlo + 0.5) * 0x1p-32);     // the page's uniform, RN32
+    const double L = u >= 1.0f ? log(0x1p-24) : log1p(-(double)u);
+    const double g = -log(-L);
+    g_table[b] = up_to_float(g + 3e-5);
+  }
+  for (int b = GT_N; b < GT_PAD; ++b) g_table[b] = g_table[GT_N - 1];
+  g_table_ready = true;
+}
+
+typedef void (*StepFn)(StepArgs);
 
 struct Plan {
   int rg, mrb;
 };
 
-Plan plan_of(int rows, int R) {
+// Row blocks: each wave handles all of them (up to 8), else the two waves
+// of a SIMD split them (row groups; past 16 row blocks a wave keeps 16 and
+// spills registers).
+Plan plan_of(int rows) {
   const int nrb = (rows + 15) / 16;
-  int rg = 1;
-  if (lds_bytes(rows, R) > 80 * 1024) rg = 2;
-#ifdef MARKOV_FORCE_RG
-  if (nrb >= MARKOV_FORCE_RG) rg = MARKOV_FORCE_RG;
-#endif
+  const int rg = nrb > MRB_MAX ? 2 : 1;
   const int need = (nrb + rg - 1) / rg;
   int mrb = 1;
   while (mrb < need) mrb *= 2;
@@ -850,12 +978,10 @@ StepFn pick_plan(Plan p) {
     }
   } else if (p.rg == 2) {
     switch (p.mrb) {
-      case 1: return markov_step_kernel<KB, 2, 1, EX>;
-      case 2: return markov_step_kernel<KB, 2, 2, EX>;
-      case 4: return markov_step_kernel<KB, 2, 4, EX>;
       case 8: return markov_step_kernel<KB, 2, 8, EX>;
-      case 16: return KB <= 2 ? markov_step_kernel<KB <= 2 ? KB : 1, 2, 16, EX> : nullptr;
-      case 32: return KB == 1 ? markov_step_kernel<1, 2, 32, EX> : nullptr;
+      case 16:
+        if constexpr (KB <= 8) return markov_step_kernel<KB, 2, 16, EX>;
+        break;
     }
   }
   return nullptr;
@@ -880,23 +1006,13 @@ StepFn pick_kernel(int R, Plan p, bool exact = false) {
 
 bool pow2_rank(int R) { return R >= 16 && R <= 512 && (R & (R - 1)) == 0; }
 
-// LDS of one workgroup: the embeddings, per-row data (5 words), the waves'
-// running row states (4 words each), the special counts and fallback list,
-// and a small misc area.
-size_t lds_bytes(int rows, int R) {
-  size_t rp = (size_t)((rows + 15) & ~15);
-  return rp * R * 2 + rp * 6 * 4 + (size_t)4 * rp * 16 + rp * 8 + 64 * 4;
-}
-
-constexpr size_t LDS_MAX = 160 * 1024;
+size_t lds_bytes(int rows, int R) { return lds_total((rows + 15) & ~15, R); }
 
 int32_t max_rows_of(int32_t R) {
   if (!pow2_rank(R)) return 0;
   int32_t best = 0;
   for (int32_t rows = 16; rows <= ROWS_CAP; rows += 16)
-    if ((size_t)rows * R * 2 <= (size_t)LDS_EMB_MAX && lds_bytes(rows, R) <= LDS_MAX &&
-        pick_kernel(R, plan_of(rows, R)) != nullptr)
-      best = rows;
+    if (lds_bytes(rows, R) <= LDS_MAX && pick_kernel(R, plan_of(rows)) != nullptr) best = rows;
   return best;
 }
 
@@ -914,59 +1030,51 @@ struct LaunchCache {
   StepFn fn;
   int device;
   size_t lds;
-  int grid_cap;
+  int cus;
 };
 LaunchCache g_cache[64];
 int g_cache_n = 0;
 
-// Workgroups to launch: as many as are resident at once (occupancy at this
-// LDS size times the CU count), never more than there are slabs.
-int launch_grid(StepFn fn, size_t lds, int block, int nslabs, int* grid) {
+// Workgroups to launch: one per CU (the kernel is sized for one resident
+// 8-wave workgroup), never more than there are slab pairs (one slab for each
+// of a SIMD's two waves).
+int launch_grid(StepFn fn, size_t lds, int nslabs, int S, int* grid) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MARKOV_ERR_HIP;
-  for (int i = 0; i < g_cache_n; ++i) {
-    if (g_cache[i].fn == fn && g_cache[i].device == dev && g_cache[i].lds == lds) {
-      *grid = nslabs < g_cache[i].grid_cap ? nslabs : g_cache[i].grid_cap;
-      return MARKOV_OK;
-    }
+  int cus = 0;
+  for (int i = 0; i < g_cache_n; ++i)
+    if (g_cache[i].fn == fn && g_cache[i].device == dev && g_cache[i].lds == lds) cus = g_cache[i].cus;
+  if (cus == 0) {
+    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+        hipSuccess)
+      return MARKOV_ERR_HIP;
+    int occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MARKOV_ERR_HIP;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)fn, NTH, lds) != hipSuccess)
+      return MARKOV_ERR_HIP;
+    if (occ < 1 || cus < 1) return MARKOV_ERR_ROWS;
+    if (g_cache_n < 64) g_cache[g_cache_n++] = LaunchCache{fn, dev, lds, cus};
   }
-  if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-      hipSuccess)
-    return MARKOV_ERR_HIP;
-  int cus = 0, occ = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return MARKOV_ERR_HIP;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)fn, block, lds) != hipSuccess)
-    return MARKOV_ERR_HIP;
-  if (occ < 1) return MARKOV_ERR_ROWS;
-  int cap = cus * occ;
-#ifndef MARKOV_GRID_PER_CU
-#define MARKOV_GRID_PER_CU 2
-#endif
-  // at most two resident workgroups per CU: each workgroup's prologue
-  // (embedding gather) and per-row atomics are a fixed cost
-  if (occ > MARKOV_GRID_PER_CU) cap = cus * MARKOV_GRID_PER_CU;
-  if (g_cache_n < 64) g_cache[g_cache_n++] = LaunchCache{fn, dev, lds, cap};
-  *grid = nslabs < cap ? nslabs : cap;
+  const int want = (nslabs + S - 1) / S;
+  *grid = want < cus ? want : cus;
   return MARKOV_OK;
 }
 
-size_t ws_bytes(int rows) { return (size_t)rows * 8 * 3; }
+size_t ws_bytes(int rows) { return (size_t)GT_BYTES + (size_t)rows * 8 * 3; }
 
 int launch_steps(int mode, const void* base, const void* w1, const void* w2, const int64_t* prev,
                  const int64_t* seeds, const int64_t* positions, int32_t k, int32_t s_begin,
                  int32_t s_end, const float* temperature, void* cache, int64_t* tokens,
                  void* bias_out, markov_stream_t stream, const markov_shape_t* sh,
                  void* workspace) {
-  const Plan plan = plan_of(sh->rows, sh->rank);
-  const int rg = plan.rg;
+  const Plan plan = plan_of(sh->rows);
   StepFn fn = pick_kernel(sh->rank, plan, mode == MODE_SAMPLE_EXACT);
   if (!fn) return MARKOV_ERR_ROWS;
   const size_t lds = lds_bytes(sh->rows, sh->rank);
   const int nslabs = (sh->vocab + SLAB - 1) / SLAB;
-  const int block = 256 * rg;
   int grid = 0;
-  int rc = launch_grid(fn, lds, block, nslabs, &grid);
+  int rc = launch_grid(fn, lds, nslabs, plan.rg == 1 ? 2 : 1, &grid);
   if (rc) return rc;
   StepArgs a;
   memset(&a, 0, sizeof(a));
@@ -980,7 +1088,10 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   a.cache = (uint16_t*)cache;
   a.tokens = tokens;
   a.bias_out = (uint16_t*)bias_out;
-  a.slots = (unsigned long long*)workspace;
+  if (workspace) {
+    a.gtable = (const float*)workspace;
+    a.slots = (unsigned long long*)((unsigned char*)workspace + GT_BYTES);
+  }
   a.rows = sh->rows;
   a.V = sh->vocab;
   a.R = sh->rank;
@@ -993,12 +1104,12 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   a.inv_cap = a.has_cap ? 1.0f / sh->softcap : 0.0f;
   for (int s = s_begin; s < s_end; ++s) {
     a.step = s;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(block), lds, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(NTH), lds, (hipStream_t)stream, a);
     if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   }
   if (mode != MODE_BIAS && s_end == k) {
-    hipLaunchKernelGGL(markov_finish_kernel, dim3(1), dim3(BLOCK), 0, (hipStream_t)stream,
-                       a.slots, tokens, sh->rows, k);
+    hipLaunchKernelGGL(markov_finish_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, a.slots,
+                       tokens, sh->rows, k);
     if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   }
   return MARKOV_OK;
@@ -1015,7 +1126,8 @@ int sample_common(int mode, const void* base_logits, const void* w1, const void*
   if (!base_logits || !w1 || !w2 || !prev || !seeds || !positions || !temperature || !cache ||
       !tokens || !workspace)
     return MARKOV_ERR_NULL;
-  if (!aligned16(base_logits) || !aligned16(w1) || !aligned16(w2) || !aligned16(cache))
+  if (!aligned16(base_logits) || !aligned16(w1) || !aligned16(w2) || !aligned16(cache) ||
+      !aligned16(workspace))
     return MARKOV_ERR_ALIGN;
   if (workspace_bytes < ws_bytes(shape->rows)) return MARKOV_ERR_WORKSPACE;
   return launch_steps(mode, base_logits, w1, w2, prev, seeds, positions, k, s_begin, s_end,
@@ -1035,7 +1147,15 @@ size_t markov_workspace_bytes(const markov_shape_t* shape, int32_t k) {
 
 int markov_workspace_init(void* workspace, size_t bytes, markov_stream_t stream) {
   if (!workspace) return MARKOV_ERR_NULL;
-  if (hipMemsetAsync(workspace, 0, bytes, (hipStream_t)stream) != hipSuccess) return MARKOV_ERR_HIP;
+  if (!aligned16(workspace)) return MARKOV_ERR_ALIGN;
+  if (bytes < ws_bytes(1)) return MARKOV_ERR_WORKSPACE;
+  build_table();
+  if (hipMemcpyAsync(workspace, g_table, GT_BYTES, hipMemcpyHostToDevice, (hipStream_t)stream) !=
+      hipSuccess)
+    return MARKOV_ERR_HIP;
+  if (hipMemsetAsync((unsigned char*)workspace + GT_BYTES, 0, bytes - GT_BYTES, (hipStream_t)stream) !=
+      hipSuccess)
+    return MARKOV_ERR_HIP;
   return MARKOV_OK;
 }
 
@@ -1095,7 +1215,7 @@ const char* markov_status_string(int status) {
     case MARKOV_ERR_NULL: return "a required pointer is NULL";
     case MARKOV_ERR_SHAPE: return "bad shape (rows, vocab or k)";
     case MARKOV_ERR_RANK: return "rank not a power of two in [16, 512]";
-    case MARKOV_ERR_ALIGN: return "a bf16 array is not 16-byte aligned";
+    case MARKOV_ERR_ALIGN: return "a bf16 array or the workspace is not 16-byte aligned";
     case MARKOV_ERR_ROWS: return "more rows than the rank's LDS budget holds";
     case MARKOV_ERR_WORKSPACE: return "workspace too small";
     case MARKOV_ERR_HIP: return "HIP runtime error";
@@ -1115,17 +1235,26 @@ int markov_debug_bias(const void* w1, const void* w2, const int64_t* tok, void* 
 }
 
 int markov_debug_gumbel(const float* logits, const uint32_t* ids, int64_t n, float temperature,
-                        int64_t seed, int32_t step, int64_t position, float* key_exact_out,
-                        float* key_fast_out, float* margin, markov_stream_t stream) {
-  if (!logits || !ids || !key_exact_out || !key_fast_out || !margin) return MARKOV_ERR_NULL;
+                        int64_t seed, int32_t step, int64_t position, const void* workspace,
+                        float* key_exact_out, float* key_upper_out, markov_stream_t stream) {
+  if (!logits || !ids || !workspace || !key_exact_out || !key_upper_out) return MARKOV_ERR_NULL;
   if (n < 0) return MARKOV_ERR_SHAPE;
   if (n == 0) return MARKOV_OK;
   const int tb = 256;
   const int64_t blocks = (n + tb - 1) / tb;
   debug_gumbel_kernel<<<dim3((unsigned)blocks), tb, 0, (hipStream_t)stream>>>(
-      logits, ids, n, temperature, seed, step, position, key_exact_out, key_fast_out, margin);
+      logits, ids, n, temperature, seed, step, position, (const float*)workspace, key_exact_out,
+      key_upper_out);
   if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   return MARKOV_OK;
+}
+
+int32_t markov_debug_noise_table(float* out, int32_t n) {
+  if (!out) return MARKOV_ERR_NULL;
+  build_table();
+  const int32_t c = n < GT_N ? n : GT_N;
+  for (int32_t i = 0; i < c; ++i) out[i] = g_table[i];
+  return c;
 }
 
 int markov_debug_copy(const void* src, void* dst, int64_t bytes, markov_stream_t stream) {

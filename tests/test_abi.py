@@ -49,14 +49,19 @@ def test_status_strings(lib):
 
 
 def test_max_rows_and_workspace(lib):
-    assert m.max_rows(256) == 256
-    assert m.max_rows(512) == 128
-    mr32 = m.max_rows(32)                                  # LDS-bound: 160 KiB per workgroup
-    assert 1000 <= mr32 <= 1024 and mr32 % 16 == 0
-    assert m.why_not(mr32, 4096, 32, 3) is None
-    assert m.why_not(mr32 + 1, 4096, 32, 3) is not None
+    # LDS-bound at R = 256 and 512 (160 KiB per workgroup), else the
+    # one-thread-per-row prologue's 512
+    assert m.max_rows(256) == 272
+    assert m.max_rows(512) == 144
+    for R in (16, 32, 64, 128):
+        assert m.max_rows(R) == 512
     assert m.max_rows(48) == 0
-    assert m.workspace_bytes(64, 163840, 256, 5) >= 64 * 8 + 4
+    for R in (16, 64, 256, 512):
+        mr = m.max_rows(R)
+        assert m.why_not(mr, 4096, R, 3) is None
+        assert "LDS" in m.why_not(mr + 1, 4096, R, 3)
+    # the noise bound table (8448 bytes) and three per-row slot arrays
+    assert m.workspace_bytes(64, 163840, 256, 5) == 8448 + 64 * 8 * 3
     assert m.workspace_bytes(0, 163840, 256, 5) == 0
     assert m.workspace_bytes(4, 100, 256, 5) == 0        # vocab not a multiple of 8
 
@@ -67,7 +72,8 @@ def test_max_rows_and_workspace(lib):
     (2, 4100, 32, 3, "vocabulary"),
     (2, 4096, 48, 3, "rank"),
     (2, 4096, 1024, 3, "rank"),
-    (257, 4096, 256, 3, "LDS"),
+    (273, 4096, 256, 3, "LDS"),
+    (513, 4096, 32, 3, "LDS"),
     (2, 4096, 32, 3, None),
     (256, 163840, 256, 8, None),
 ])
@@ -79,7 +85,7 @@ def test_why_not(lib, rows, V, R, k, why):
         assert r is not None and why in r
 
 
-def _call(lib, shape, ptrs, k=3, ws_bytes=4096):
+def _call(lib, shape, ptrs, k=3, ws_bytes=1 << 16):
     P = ctypes.c_void_p
     return lib.markov_sample_sequential(P(ptrs[0]), P(ptrs[1]), P(ptrs[2]), P(ptrs[3]),
                                         P(ptrs[4]), P(ptrs[5]), k, P(ptrs[6]), P(ptrs[7]),
@@ -95,6 +101,7 @@ def test_host_errors_before_any_device_work(lib):
     assert _call(lib, sh, good, k=0) == -2
     assert _call(lib, m.make_shape(2, 4096, 40), good) == -3
     assert _call(lib, m.make_shape(300, 4096, 256), good) == -5
+    assert _call(lib, sh, good, ws_bytes=8448 + 2 * 24 - 1) == -6
     for i in range(10):
         bad = list(good)
         bad[i] = 0
@@ -109,3 +116,6 @@ def test_host_errors_before_any_device_work(lib):
                                  ctypes.byref(m.make_shape(2, 4096, 33)), None) == -3
     assert lib.markov_debug_gumbel(None, None, 4, ctypes.c_float(1.0), 1, 0, 1, None, None, None,
                                    None) == -1
+    bad = list(good)
+    bad[9] += 8                                             # workspace must be 16-byte aligned
+    assert _call(lib, sh, bad, ws_bytes=1 << 16) == -4
