@@ -72,6 +72,7 @@ struct StepArgs {
   int rows, V, R, k, step, nslabs, mode;
   float mult, inv_cap, cap;
   int has_cap;
+  float inf;                  // +infinity, opaque to the compiler (see the noise loop)
 };
 
 // ---------------------------------------------------------------- numbers
@@ -79,11 +80,12 @@ struct StepArgs {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Two binary32 -> one word of two bf16 (round to nearest even; the hardware
-// conversion v_cvt_pk_bf16_f32), `a` in the low half.
+// Two binary32 -> one word of two bf16 (round to nearest even; one
+// hardware v_cvt_pk_bf16_f32), `a` in the low half.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // ---------------------------------------------------------------- noise hash
@@ -232,6 +234,23 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Workgroup barrier for LDS data only: this wave's LDS operations are
+// complete, then all waves meet. (__syncthreads also waits for every
+// outstanding global load, which would hold the prologue up on the w2 tiles
+// already in flight.) The asm keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N vector memory operations of this wave are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // A cache word written by another wave of this workgroup (agent-coherent load).
 __device__ __forceinline__ uint32_t load_cache_word(const uint16_t* cache, size_t elem_even) {
   return __hip_atomic_load((const uint32_t*)(cache + elem_even), __ATOMIC_RELAXED,
@@ -355,8 +374,8 @@ __device__ __forceinline__ void merge_top2(RowState& a, const RowState& b) {
   a.sp |= b.sp;
 }
 
-// LDS layout (bytes), the table first so that its reads need no base:
-//   [0, GT_BYTES)   noise bound table
+// LDS: the noise bound table is a static array (its address is a constant,
+// so the table reads need no base register); the rest is dynamic:
 //   region0         embeddings [rp][R] bf16; after the slab loop the waves'
 //                   row states [4][NWV][rp] (v1, v2, id, sp)
 //   info [rp] RowInfo, n_row [rp], n_src [rp], fb_row [rp], fb_thr [rp],
@@ -366,9 +385,11 @@ __host__ __device__ __forceinline__ size_t region0_bytes(int rp, int R) {
   return e > st ? e : st;
 }
 
-__host__ __device__ __forceinline__ size_t lds_total(int rp, int R) {
-  return GT_BYTES + region0_bytes(rp, R) + (size_t)rp * 16 + (size_t)rp * 16 + 64 * 4;
+__host__ __device__ __forceinline__ size_t lds_dynamic(int rp, int R) {
+  return region0_bytes(rp, R) + (size_t)rp * 16 + (size_t)rp * 16 + 64 * 4;
 }
+
+__host__ __device__ __forceinline__ size_t lds_total(int rp, int R) { return GT_BYTES + lds_dynamic(rp, R); }
 
 // ---------------------------------------------------------------- the step
 //
@@ -377,15 +398,15 @@ __host__ __device__ __forceinline__ size_t lds_total(int rp, int R) {
 // rows, both take every slab of the workgroup and read its w2 tiles through
 // L2), MRB = row blocks per wave (a power of two, the wave's real count may
 // be lower), EXACT = the test-only variant that takes the exact key of
-// every element.
+// every element. One launch runs step a.step.
 template <int KB, int RG, int MRB, bool EXACT>
 __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   constexpr int NB = MRB == 1 ? 2 : 1;                   // w2 tiles in flight per wave
   constexpr int D = MRB - 1 < 3 ? MRB - 1 : 3;           // row blocks contracted ahead
-  constexpr int PFD = MRB == 1 ? 1 : 2;                  // base logits prefetched ahead
   constexpr int S = RG == 1 ? 2 : 1;                     // waves splitting one SIMD's slabs
   constexpr bool ROWREG = MRB <= 4;                      // row constants in registers
   extern __shared__ __align__(16) unsigned char lds[];
+  __shared__ __align__(16) float gtab[GT_PAD];
   const int mode = a.mode;
   const bool bias_mode = mode == MODE_BIAS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -394,7 +415,8 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   const int wr = RG == 1 ? 0 : wave >> 2;
   const int g = lane >> 4, m = lane & 15;
   const int R = KB >= 2 ? 32 * KB : a.R;
-  const int rows = a.rows, rp = (rows + 15) & ~15, V = a.V, s = a.step, K = a.k;
+  const int rows = a.rows, rp = (rows + 15) & ~15, V = a.V, K = a.k;
+  const int s = a.step;
   const int nslabs = a.nslabs, G = gridDim.x;
   const int cpr = R >> 3;
   const int swz = (cpr < 16 ? cpr : 16) - 1;
@@ -403,27 +425,24 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   const int slab_step = G * S;
   const int slab0 = blockIdx.x + G * sub;
   const bool kzero = (KB == 1) && (R == 16) && (g >= 2);
+  // this wave's units per step: slabs slab0 + i slab_step whose 32 tokens
+  // start inside the vocabulary
+  int lim = (V - tw * TOK_PER_WAVE + SLAB - 1) / SLAB;
+  lim = lim < nslabs ? lim : nslabs;
+  const int U = (my_nrb > 0 && slab0 < lim) ? (lim - slab0 + slab_step - 1) / slab_step : 0;
 
-  const float* gtab = (const float*)lds;
-  uint16_t* emb = (uint16_t*)(lds + GT_BYTES);
+
+  uint16_t* emb = (uint16_t*)lds;
   const size_t r0 = region0_bytes(rp, R);
-  RowInfo* n_info = (RowInfo*)(lds + GT_BYTES + r0);
+  RowInfo* n_info = (RowInfo*)(lds + r0);
   int* n_row = (int*)(n_info + rp);
   int* n_src = n_row + rp;
   int* fb_row = n_src + rp;
   float* fb_thr = (float*)(fb_row + rp);
   int* misc = (int*)(fb_thr + rp);
 
-  unsigned long long* slots_cur = nullptr;
-  const unsigned long long* slots_prev = nullptr;
-  unsigned long long* slots_next = nullptr;
-  if (!bias_mode) {
-    slots_cur = a.slots + (size_t)(s % 3) * rows;
-    slots_prev = a.slots + (size_t)((s + 2) % 3) * rows;
-    slots_next = a.slots + (size_t)((s + 1) % 3) * rows;
-  }
-
-  // 0. this thread's request row: everything it needs in one round trip
+  // 0. this thread's request row: everything the first step needs, in one
+  //    round trip
   const int r = tid;
   const bool valid = r < rows;
   float T = 0.0f;
@@ -434,39 +453,42 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       seed = a.seeds[r];
       pos = a.positions[(int64_t)r * K + s];
     }
-    tok = (bias_mode || s == 0) ? a.prev[r] : slot_token(slots_prev[r]);
+    tok = (bias_mode || s == 0) ? a.prev[r] : slot_token(a.slots[(size_t)((s + 2) % 3) * rows + r]);
   }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 1. the wave's first w2 tiles: they depend on nothing above
-  bf16x8_t A0[NB][KB], A1[NB][KB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int sl = slab0 + nb * slab_step;
-    if (my_nrb > 0 && sl < nslabs)
-      load_w2_tile<KB, RG == 1>(a.w2, V, R, sl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[nb], A1[nb]);
-  }
-  __builtin_amdgcn_sched_barrier(0);
   // the noise bound table, straight into LDS
   if (!bias_mode) {
     for (int j = wave; j * 64 * 16 < (int)GT_BYTES; j += NWV) {
       const int p = j * 64 + lane;
       if (p * 16 < (int)GT_BYTES)
         __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.gtable + (size_t)p * 16),
-                                         (__attribute__((address_space(3))) void*)(lds + (size_t)j * 1024),
+                                         (__attribute__((address_space(3))) void*)(gtab + (size_t)j * 256),
                                          16, 0, 0);
     }
   }
-
-  // 2. rows: noisy rows first, so that 16-row blocks are of one kind
+  wait_vm<0>();   // row data and table (nothing else is in flight yet)
+  // everything the row set-up needs from them, before the tile loads below
+  // (whose wait would otherwise precede the first use of a row register)
   const bool noisy_r = valid && !bias_mode && !(T == 0.0f);
   const uint64_t bn = __ballot(noisy_r), bz = __ballot(valid && !noisy_r);
+  const float rcp_r = 1.0f / T;
+  const uint32_t prefix_r = (valid && !bias_mode) ? row_prefix_of(seed, s, pos) : 0u;
+  const int tok32 = (int)tok;
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 1. the wave's first w2 tile: it depends on nothing above, and stays in
+  //    flight through the row set-up (a wave without units reads clamped rows)
+  bf16x8_t A0[NB][KB], A1[NB][KB];
+  load_w2_tile<KB, RG == 1>(a.w2, V, R, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE, m, g, kzero,
+                            A0[0], A1[0]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. rows: noisy rows first, so that 16-row blocks are of one kind
   if (lane == 0) {
     misc[wave] = __builtin_popcountll(bn);
     misc[8 + wave] = __builtin_popcountll(bz);
   }
   if (tid == 0) misc[16] = 0;
-  __syncthreads();
+  lds_barrier();
   {
     int pre_n = 0, pre_z = 0, tot_n = 0;
 #pragma unroll
@@ -479,16 +501,17 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       }
     }
     if (valid) {
-      const int n = bias_mode ? r
-                  : noisy_r ? pre_n + (int)lanes_below(bn)
-                            : tot_n + pre_z + (int)lanes_below(bz);
+      const int pos_n = bias_mode ? r
+                      : noisy_r ? pre_n + (int)lanes_below(bn)
+                                : tot_n + pre_z + (int)lanes_below(bz);
+      n_row[pos_n] = r;
+      // the feeding token (any int64 at step 0, clamped as unsigned)
       const uint64_t ut = (uint64_t)tok, last = (uint64_t)(V - 1);
-      n_row[n] = r;
-      n_src[n] = (int)(ut < last ? ut : last);
-      n_info[n] = RowInfo{r * K + s, 1.0f / T, bias_mode ? 0u : row_prefix_of(seed, s, pos), T};
+      n_src[pos_n] = (int)(ut < last ? ut : last);
+      n_info[pos_n] = RowInfo{r * K + s, rcp_r, prefix_r, T};
       if (!bias_mode && blockIdx.x == 0) {
-        if (s > 0) a.tokens[(int64_t)r * K + s - 1] = tok;   // the previous step's token
-        slots_next[r] = 0ull;                               // next step's slots start empty
+        if (s > 0) a.tokens[(int64_t)r * K + s - 1] = (int64_t)(uint32_t)tok32;   // previous step's
+        a.slots[(size_t)((s + 1) % 3) * rows + r] = 0ull;            // next step's slots start empty
       }
     } else if (r < rp) {
       n_row[r] = 0;
@@ -496,9 +519,42 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       n_info[r] = RowInfo{0, 0.0f, 0u, 0.0f};
     }
   }
-  __syncthreads();
 
-  // 3. the embeddings, straight into LDS (16-byte chunks, swizzled);
+  u32x4_t bq[MRB];
+  RowInfo ri[ROWREG ? MRB : 1];
+  auto rk_of = [&](int j) -> int {
+    return ROWREG ? ri[ROWREG ? j : 0].rk : n_info[16 * (wr + RG * j) + m].rk;
+  };
+  // base logits of block j of the unit in slab sl, for this lane's 8 tokens
+  auto fetch_base = [&](int j, int sl, u32x4_t& dst) {
+    const int n = 16 * (wr + RG * j) + m;
+    const int tgt = sl * SLAB + tw * TOK_PER_WAVE + 8 * g;
+    dst = (u32x4_t){0u, 0u, 0u, 0u};
+    if (j < my_nrb && n < rows && tgt < V)
+      dst = __builtin_nontemporal_load((const u32x4_t*)(a.base + (size_t)rk_of(j) * V + tgt));
+  };
+
+  const float mult = a.mult, cap = a.cap, inv_cap = a.inv_cap;
+  const bool has_cap = a.has_cap != 0;
+  const bool mult1 = mult == 1.0f;
+  const float pinf = a.inf;
+  float v1[MRB], v2[MRB];
+  int idt[MRB];
+  bool sp[MRB];
+
+  unsigned long long* slots_cur = bias_mode ? nullptr : a.slots + (size_t)(s % 3) * rows;
+  lds_barrier();
+  if (ROWREG) {
+#pragma unroll
+    for (int j = 0; j < (ROWREG ? MRB : 1); ++j) ri[j] = n_info[j < my_nrb ? 16 * (wr + RG * j) + m : 0];
+  }
+  // base logits of the first unit
+  if (!bias_mode && U > 0) {
+#pragma unroll
+    for (int j = 0; j < MRB; ++j) fetch_base(j, slab0, bq[j]);
+  }
+
+  // 4. the embeddings, straight into LDS (16-byte chunks, swizzled);
   //    padding rows read row 0 and are never used
   {
     const int total = rp * cpr;
@@ -513,33 +569,14 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       }
     }
   }
+  // the second tile in flight (two-tile waves), issued after the gather so
+  // that waiting for the gather does not wait for it
+  __builtin_amdgcn_sched_barrier(0);
+  if (NB == 2)
+    load_w2_tile<KB, RG == 1>(a.w2, V, R, (U > 1 ? slab0 + slab_step : 0) * SLAB + tw * TOK_PER_WAVE, m,
+                              g, kzero, A0[NB - 1], A1[NB - 1]);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // this lane's rows: one per row block of the wave (n = 16 (wr + RG j) + m)
-  RowInfo ri[ROWREG ? MRB : 1];
-  if (ROWREG) {
-#pragma unroll
-    for (int j = 0; j < (ROWREG ? MRB : 1); ++j) ri[j] = n_info[j < my_nrb ? 16 * (wr + RG * j) + m : 0];
-  }
-  auto rk_of = [&](int j) -> int {
-    return ROWREG ? ri[ROWREG ? j : 0].rk : n_info[16 * (wr + RG * j) + m].rk;
-  };
-  // base logits of block j of the unit in slab sl, for this lane's 8 tokens
-  auto fetch_base = [&](int j, int sl, u32x4_t& dst) {
-    const int n = 16 * (wr + RG * j) + m;
-    const int tgt = sl * SLAB + tw * TOK_PER_WAVE + 8 * g;
-    dst = (u32x4_t){0u, 0u, 0u, 0u};
-    if (j < my_nrb && n < rows && sl < nslabs && tgt < V)
-      dst = __builtin_nontemporal_load((const u32x4_t*)(a.base + (size_t)rk_of(j) * V + tgt));
-  };
-  u32x4_t bq[MRB];
-  if (!bias_mode) {
-#pragma unroll
-    for (int j = 0; j < PFD && j < MRB; ++j) fetch_base(j, slab0, bq[j]);
-  }
-
-  float v1[MRB], v2[MRB];
-  int idt[MRB];
-  bool sp[MRB];
 #pragma unroll
   for (int j = 0; j < MRB; ++j) {
     v1[j] = -INFINITY;
@@ -547,20 +584,21 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     idt[j] = NONE;
     sp[j] = false;
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // everything but the second tile: the embeddings (every wave's, hence
+  // the barrier), the first tile and base logits
+  wait_vm<NB == 2 ? 2 * KB : 0>();
+  lds_barrier();
 
-  const float mult = a.mult, cap = a.cap, inv_cap = a.inv_cap;
-  const bool has_cap = a.has_cap != 0;
-
-  // one 32-token unit (slab `sl`) with w2 tile buffer BUF
-  auto unit = [&](auto bufc, int sl) {
+  // one 32-token unit (the wave's unit i, slab `sl`) with w2 tile buffer BUF
+  auto unit = [&](auto bufc, int i, int sl) {
     constexpr int BUF = decltype(bufc)::value;
     const int tok0 = sl * SLAB + tw * TOK_PER_WAVE;
     const int tg = tok0 + 8 * g;               // this lane's 8 tokens: tg .. tg+7
     const bool tok_ok = tg < V;
-    const int nsl = sl + NB * slab_step;       // the slab whose tile goes into this buffer next
-    const int psl = sl + slab_step;            // the next slab (base logit prefetch)
+    const bool ntile = i + NB < U;             // the unit whose tile goes into this buffer next
+    const int nsl = sl + NB * slab_step;
+    const bool pnext = i + 1 < U;              // the next unit (base logit prefetch)
+    const int psl = sl + slab_step;
     uint32_t kw[8];
     if (!bias_mode) {
       uint32_t kc = (uint32_t)tg * MM_C1;
@@ -575,30 +613,31 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     for (int j = 0; j < D; ++j)
       if (j < my_nrb)
         block_bias<KB>(A0[BUF], A1[BUF], emb, 16 * (wr + RG * j) + m, R, g, swz, kzero, cb0[j], cb1[j]);
-    if (D > 0 && my_nrb <= D && nsl < nslabs)
+    if (D > 0 && my_nrb <= D && ntile)
       load_w2_tile<KB, RG == 1>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF], A1[BUF]);
 #pragma unroll
     for (int j = 0; j < MRB; ++j) {
       const int n = 16 * (wr + RG * j) + m;
-      // the contraction of block j + D (of block j itself when D == 0); once
-      // the unit's last one has issued, this buffer's next tile
+      // the contraction of block j + D (of block j itself when D == 0);
+      // once the unit's last one has issued, this buffer's next tile
       if (D == 0) {
         if (j < my_nrb) {
           block_bias<KB>(A0[BUF], A1[BUF], emb, n, R, g, swz, kzero, cb0[j], cb1[j]);
-          if (j == my_nrb - 1 && nsl < nslabs)
-            load_w2_tile<KB, RG == 1>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF], A1[BUF]);
+          if (j == my_nrb - 1 && ntile)
+            load_w2_tile<KB, RG == 1>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF],
+                                      A1[BUF]);
         }
       } else if (j + D < MRB && j + D < my_nrb) {
         block_bias<KB>(A0[BUF], A1[BUF], emb, n + 16 * RG * D, R, g, swz, kzero, cb0[j + D], cb1[j + D]);
-        if (j + D == my_nrb - 1 && nsl < nslabs)
-          load_w2_tile<KB, RG == 1>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF], A1[BUF]);
+        if (j + D == my_nrb - 1 && ntile)
+          load_w2_tile<KB, RG == 1>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF],
+                                    A1[BUF]);
       }
       const u32x4_t bv = bq[j];
-      // base logits PFD blocks ahead, into the next slab past this one's end
-      if (!bias_mode) {
-        if (j + PFD < MRB) fetch_base(j + PFD, sl, bq[j + PFD < MRB ? j + PFD : 0]);
-        else fetch_base(j + PFD - MRB, psl, bq[j + PFD >= MRB ? j + PFD - MRB : 0]);
-      }
+      // block j of the next unit (a whole unit ahead: earlier requests
+      // would queue behind the next tile, vector memory completing in
+      // issue order)
+      if (!bias_mode && pnext) fetch_base(j, psl, bq[j]);
       if (j >= my_nrb) continue;
 
       const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[n];
@@ -626,8 +665,8 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         float zmax = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          z[2 * q] = (mult * bf_lo(cw[q])) * inv_cap;
-          z[2 * q + 1] = (mult * bf_hi(cw[q])) * inv_cap;
+          z[2 * q] = (mult1 ? bf_lo(cw[q]) : mult * bf_lo(cw[q])) * inv_cap;
+          z[2 * q + 1] = (mult1 ? bf_hi(cw[q]) : mult * bf_hi(cw[q])) * inv_cap;
           zmax = fmaxf(zmax, fmaxf(fabsf(z[2 * q]), fabsf(z[2 * q + 1])));
         }
         if (__any(!(zmax < 0.625f))) {
@@ -667,22 +706,27 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         }
         continue;
       }
-      // noisy rows: the two largest upper bounds, the element's index in the
-      // tile packed into the bound's low 3 bits
+      // noisy rows: the two largest upper bounds, the element's index in
+      // the tile packed into the bound's low 3 bits
       if (__any(active && noisy)) {
         if (active && noisy) {
           float x1 = v1[j], x2 = v2[j];
           const float x1b = x1;
           bool spx = false;
+          // all 8 table reads in flight before the first is used
+          uint32_t off[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) off[e] = gt_offset(mm_finish(info.prefix, kw[e]));
+          float gh[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gh[e] = gtab[off[e] >> 2];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const uint32_t h = mm_finish(info.prefix, kw[e]);
-            const float gh = *(const float*)((const unsigned char*)gtab + gt_offset(h));
-            const float up = key_upper(l[e], info.rcp, gh);
+            const float up = key_upper(l[e], info.rcp, gh[e]);
             spx = spx || __builtin_amdgcn_class(up, 0x207);       // NaN or infinite
             const float pk = __uint_as_float((__float_as_uint(up) & ~7u) | (uint32_t)e);
             x2 = __builtin_amdgcn_fmed3f(x1, x2, pk);
-            x1 = __builtin_amdgcn_fmed3f(x1, pk, INFINITY);
+            x1 = __builtin_amdgcn_fmed3f(x1, pk, pinf);   // max, no canonicalising
           }
           if (x1 != x1b) idt[j] = tg;
           v1[j] = x1;
@@ -714,24 +758,14 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     }
   };
 
-  if (my_nrb > 0) {
-    int sl = slab0;
-    if (NB == 1) {
-      for (; sl < nslabs && sl * SLAB + tw * TOK_PER_WAVE < V; sl += slab_step)
-        unit(std::integral_constant<int, 0>{}, sl);
-    } else {
-      while (sl < nslabs && sl * SLAB + tw * TOK_PER_WAVE < V) {
-        unit(std::integral_constant<int, 0>{}, sl);
-        sl += slab_step;
-        if (!(sl < nslabs && sl * SLAB + tw * TOK_PER_WAVE < V)) break;
-        unit(std::integral_constant<int, NB - 1>{}, sl);
-        sl += slab_step;
-      }
-    }
+  // the wave's units (a two-tile wave alternates its buffers)
+  for (int i = 0; i < U; i += NB) {
+    unit(std::integral_constant<int, 0>{}, i, slab0 + i * slab_step);
+    if (NB == 2 && i + 1 < U) unit(std::integral_constant<int, NB - 1>{}, i + 1, slab0 + (i + 1) * slab_step);
   }
   if (bias_mode) return;
 
-  // 4. each row's state: this lane's, merged over the row's 4 lanes, stored
+  // 5. each row's state: this lane's, merged over the row's 4 lanes, stored
   //    per wave (over the embeddings, once every wave is past its last
   //    contraction), merged over the waves; then per row either the packed
   //    atomicMax of its certified winner or the fallback list.
@@ -778,6 +812,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       st_sp[wave * rp + n] = fin[j].sp;
     }
   }
+  if (tid == 0) misc[16] = 0;
   __syncthreads();
   for (int n = tid; n < rows; n += NTH) {
     const RowInfo info = n_info[n];
@@ -792,7 +827,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       if (top2) merge_top2(st, o);
       else merge_order(st, o);
     }
-    const int r = n_row[n];
+    const int rr = n_row[n];
     float key = st.v1;
     bool fb = !EXACT && (st.sp != 0 || (mode == MODE_SAMPLE_FALLBACK && noisy));
     float thr = -INFINITY;
@@ -811,13 +846,13 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       fb_row[i] = n;
       fb_thr[i] = thr;
     } else if (st.id != NONE) {
-      __hip_atomic_fetch_max(slots_cur + r, pack_winner(key, st.id), __ATOMIC_RELAXED,
+      __hip_atomic_fetch_max(slots_cur + rr, pack_winner(key, st.id), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   __syncthreads();
 
-  // 5. fallback rows, one per wave at a time: the wave re-reads the row's
+  // 6. fallback rows, one per wave at a time: the wave re-reads the row's
   //    cached logits over the workgroup's slabs and takes the exact key of
   //    every element whose bound reaches the threshold (all of them for a
   //    row with a non-finite estimate).
@@ -828,7 +863,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     const float thr = fb_thr[f];
     const RowInfo info = n_info[n];
     const bool noisy = !(info.T == 0.0f);
-    const int r = n_row[n];
+    const int rr = n_row[n];
     float bv = -INFINITY;
     int bi = NONE;
     for (int q = lane; q < wg_slabs * (SLAB / 2); q += 64) {
@@ -843,7 +878,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         if (noisy) {
           const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
           if (!(thr == -INFINITY)) {
-            const float gh = *(const float*)((const unsigned char*)gtab + gt_offset(h));
+            const float gh = gtab[gt_offset(h) >> 2];
             if (key_upper(l, info.rcp, gh) < thr) continue;
           }
           key = key_exact(l, info.T, h);
@@ -864,9 +899,10 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       }
     }
     if (lane == 0 && bi != NONE)
-      __hip_atomic_fetch_max(slots_cur + r, pack_winner(bv, bi), __ATOMIC_RELAXED,
+      __hip_atomic_fetch_max(slots_cur + rr, pack_winner(bv, bi), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   }
+
 }
 
 // After the last step: its winners become tokens[:, k-1], and all three
@@ -945,7 +981,7 @@ void build_table() {
     const double g = -log(-L);
     g_table[b] = up_to_float(g + 3e-5);
   }
-  for (int b = GT_N; b < GT_PAD; ++b) g_table[b] = g_table[GT_N - 1];
+  for (int b = GT_N; b < GT_PAD; ++b) g_table[b] = 0.0f;   // unused
   g_table_ready = true;
 }
 
@@ -1000,6 +1036,7 @@ StepFn pick_rank(int R, Plan p) {
   return nullptr;
 }
 
+// exact: the test-only exact-everywhere variant
 StepFn pick_kernel(int R, Plan p, bool exact = false) {
   return exact ? pick_rank<true>(R, p) : pick_rank<false>(R, p);
 }
@@ -1007,6 +1044,7 @@ StepFn pick_kernel(int R, Plan p, bool exact = false) {
 bool pow2_rank(int R) { return R >= 16 && R <= 512 && (R & (R - 1)) == 0; }
 
 size_t lds_bytes(int rows, int R) { return lds_total((rows + 15) & ~15, R); }
+size_t lds_dyn_bytes(int rows, int R) { return lds_dynamic((rows + 15) & ~15, R); }
 
 int32_t max_rows_of(int32_t R) {
   if (!pow2_rank(R)) return 0;
@@ -1071,7 +1109,7 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   const Plan plan = plan_of(sh->rows);
   StepFn fn = pick_kernel(sh->rank, plan, mode == MODE_SAMPLE_EXACT);
   if (!fn) return MARKOV_ERR_ROWS;
-  const size_t lds = lds_bytes(sh->rows, sh->rank);
+  const size_t lds = lds_dyn_bytes(sh->rows, sh->rank);
   const int nslabs = (sh->vocab + SLAB - 1) / SLAB;
   int grid = 0;
   int rc = launch_grid(fn, lds, nslabs, plan.rg == 1 ? 2 : 1, &grid);
@@ -1102,6 +1140,7 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   a.has_cap = sh->softcap > 0.0f;
   a.cap = sh->softcap;
   a.inv_cap = a.has_cap ? 1.0f / sh->softcap : 0.0f;
+  a.inf = INFINITY;
   for (int s = s_begin; s < s_end; ++s) {
     a.step = s;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(NTH), lds, (hipStream_t)stream, a);

@@ -283,6 +283,31 @@ def test_workspace_reuse_is_deterministic(dev):
     assert not ws[8448:].any(), "slots must be left zeroed"
 
 
+@pytest.mark.parametrize("args", [
+    dict(V=4104, R=128, rows=70, k=3, seed=31, temps=(1.0, 0.0, 0.6)),
+    dict(V=1000, R=32, rows=19, k=4, seed=32, temps=(0.0, 1.0)),
+    dict(V=2056, R=256, rows=160, k=3, seed=33, temps=(1.0, 0.0), softcap=30.0),
+])
+def test_loop_equals_step_by_step_calls(dev, args):
+    """markov_sample_sequential and markov_sample_step called for each step
+    in turn give the same bits."""
+    w = custom(**args)
+    d = workloads.to_device(w, dev)
+    workloads.run(w, d)
+    torch.cuda.synchronize()
+    c1, t1 = workloads.fetch(d)
+    d["cache"].zero_()
+    d["tokens"].fill_(-1)
+    for s in range(w.k):
+        workloads.run(w, d, step=s)
+    torch.cuda.synchronize()
+    c2, t2 = workloads.fetch(d)
+    assert np.array_equal(t1, t2)
+    assert np.array_equal(c1, c2)
+    assert not d["workspace"].cpu().numpy()[8448:].any()
+    say(f"  {w.name}: loop == steps")
+
+
 @pytest.mark.parametrize("name", ["single", "small", "large"])
 def test_full_config(dev, name):
     run_and_check(workloads.make(name), dev)
