@@ -286,9 +286,10 @@ __device__ __forceinline__ float tanh_fast(float z) {
 // The w2 rows of one 32-token unit as MFMA A operands: lane (g, m) holds
 // k-chunks 4i + g of tokens t0 = tok0 + 8 (m >> 2) + (m & 3) (A0) and t0 + 4
 // (A1); tokens past the vocabulary read its last row (never stored).
-// STREAM: the tile is read once (nontemporal); else a second wave reads the
-// same tile soon after and should find it in L2.
-template <int KB, bool STREAM>
+// Ordinary (not nontemporal) loads: the table is read again by the next
+// step, and unmarked lines of it stay in the memory-side cache between steps
+// (measured: a nontemporal tile stream made the step about 5% slower).
+template <int KB>
 __device__ __forceinline__ void load_w2_tile(const uint16_t* w2, int V, int R, int tok0, int m, int g,
                                              bool kzero, bf16x8_t* A0, bf16x8_t* A1) {
   const int t0 = tok0 + 8 * (m >> 2) + (m & 3);
@@ -302,13 +303,8 @@ __device__ __forceinline__ void load_w2_tile(const uint16_t* w2, int V, int R, i
       A1[i] = (bf16x8_t){};
     } else {
       const int ch = 4 * i + g;
-      if (STREAM) {
-        A0[i] = __builtin_nontemporal_load((const bf16x8_t*)(pa + ch * 8));
-        A1[i] = __builtin_nontemporal_load((const bf16x8_t*)(pb + ch * 8));
-      } else {
-        A0[i] = *(const bf16x8_t*)(pa + ch * 8);
-        A1[i] = *(const bf16x8_t*)(pb + ch * 8);
-      }
+      A0[i] = *(const bf16x8_t*)(pa + ch * 8);
+      A1[i] = *(const bf16x8_t*)(pb + ch * 8);
     }
   }
 }
@@ -478,7 +474,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   // 1. the wave's first w2 tile: it depends on nothing above, and stays in
   //    flight through the row set-up (a wave without units reads clamped rows)
   bf16x8_t A0[NB][KB], A1[NB][KB];
-  load_w2_tile<KB, RG == 1>(a.w2, V, R, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE, m, g, kzero,
+  load_w2_tile<KB>(a.w2, V, R, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE, m, g, kzero,
                             A0[0], A1[0]);
   __builtin_amdgcn_sched_barrier(0);
 
@@ -531,7 +527,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     const int tgt = sl * SLAB + tw * TOK_PER_WAVE + 8 * g;
     dst = (u32x4_t){0u, 0u, 0u, 0u};
     if (j < my_nrb && n < rows && tgt < V)
-      dst = __builtin_nontemporal_load((const u32x4_t*)(a.base + (size_t)rk_of(j) * V + tgt));
+      dst = *(const u32x4_t*)(a.base + (size_t)rk_of(j) * V + tgt);
   };
 
   const float mult = a.mult, cap = a.cap, inv_cap = a.inv_cap;
@@ -573,7 +569,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   // that waiting for the gather does not wait for it
   __builtin_amdgcn_sched_barrier(0);
   if (NB == 2)
-    load_w2_tile<KB, RG == 1>(a.w2, V, R, (U > 1 ? slab0 + slab_step : 0) * SLAB + tw * TOK_PER_WAVE, m,
+    load_w2_tile<KB>(a.w2, V, R, (U > 1 ? slab0 + slab_step : 0) * SLAB + tw * TOK_PER_WAVE, m,
                               g, kzero, A0[NB - 1], A1[NB - 1]);
   __builtin_amdgcn_sched_barrier(0);
 
@@ -614,7 +610,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       if (j < my_nrb)
         block_bias<KB>(A0[BUF], A1[BUF], emb, 16 * (wr + RG * j) + m, R, g, swz, kzero, cb0[j], cb1[j]);
     if (D > 0 && my_nrb <= D && ntile)
-      load_w2_tile<KB, RG == 1>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF], A1[BUF]);
+      load_w2_tile<KB>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF], A1[BUF]);
 #pragma unroll
     for (int j = 0; j < MRB; ++j) {
       const int n = 16 * (wr + RG * j) + m;
@@ -624,13 +620,13 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         if (j < my_nrb) {
           block_bias<KB>(A0[BUF], A1[BUF], emb, n, R, g, swz, kzero, cb0[j], cb1[j]);
           if (j == my_nrb - 1 && ntile)
-            load_w2_tile<KB, RG == 1>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF],
+            load_w2_tile<KB>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF],
                                       A1[BUF]);
         }
       } else if (j + D < MRB && j + D < my_nrb) {
         block_bias<KB>(A0[BUF], A1[BUF], emb, n + 16 * RG * D, R, g, swz, kzero, cb0[j + D], cb1[j + D]);
         if (j + D == my_nrb - 1 && ntile)
-          load_w2_tile<KB, RG == 1>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF],
+          load_w2_tile<KB>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF],
                                     A1[BUF]);
       }
       const u32x4_t bv = bq[j];
