@@ -48,6 +48,7 @@ constexpr int SLAB = 4 * TOK_PER_WAVE; // one unit per SIMD
 constexpr int NONE = 0x7fffffff;       // id of "no element yet"
 constexpr int ROWS_CAP = NTH;          // the prologue gives every row one thread
 constexpr int MRB_MAX = 8;             // row blocks one wave keeps in registers
+constexpr int FB_BATCH = 8;            // cache words in flight per lane in a fallback scan
 constexpr size_t LDS_MAX = 160 * 1024;
 
 enum Mode { MODE_SAMPLE = 0, MODE_SAMPLE_EXACT = 1, MODE_BIAS = 2, MODE_SAMPLE_FALLBACK = 3 };
@@ -862,26 +863,37 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     const int rr = n_row[n];
     float bv = -INFINITY;
     int bi = NONE;
-    for (int q = lane; q < wg_slabs * (SLAB / 2); q += 64) {
-      const int t0 = ((int)blockIdx.x + (q / (SLAB / 2)) * G) * SLAB + 2 * (q % (SLAB / 2));
-      if (t0 >= V) continue;
-      const uint32_t wd = load_cache_word(a.cache, (size_t)info.rk * V + t0);
+    // the lane's words, FB_BATCH loads in flight at a time
+    const int nq = wg_slabs * (SLAB / 2);
+    for (int q0 = 0; q0 < nq; q0 += 64 * FB_BATCH) {
+      uint32_t wd[FB_BATCH];
+      int t0[FB_BATCH];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int t = t0 + e;
-        const float l = e ? bf_hi(wd) : bf_lo(wd);
-        float key = l;
-        if (noisy) {
-          const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
-          if (!(thr == -INFINITY)) {
-            const float gh = gtab[gt_offset(h) >> 2];
-            if (key_upper(l, info.rcp, gh) < thr) continue;
+      for (int b = 0; b < FB_BATCH; ++b) {
+        const int q = q0 + 64 * b + lane;
+        t0[b] = q < nq ? ((int)blockIdx.x + (q / (SLAB / 2)) * G) * SLAB + 2 * (q % (SLAB / 2)) : V;
+        wd[b] = t0[b] < V ? load_cache_word(a.cache, (size_t)info.rk * V + t0[b]) : 0u;
+      }
+#pragma unroll
+      for (int b = 0; b < FB_BATCH; ++b) {
+        if (t0[b] >= V) continue;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int t = t0[b] + e;
+          const float l = e ? bf_hi(wd[b]) : bf_lo(wd[b]);
+          float key = l;
+          if (noisy) {
+            const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
+            if (!(thr == -INFINITY)) {
+              const float gh = gtab[gt_offset(h) >> 2];
+              if (key_upper(l, info.rcp, gh) < thr) continue;
+            }
+            key = key_exact(l, info.T, h);
           }
-          key = key_exact(l, info.T, h);
-        }
-        if (before(key, t, bv, bi)) {
-          bv = key;
-          bi = t;
+          if (before(key, t, bv, bi)) {
+            bv = key;
+            bi = t;
+          }
         }
       }
     }
