@@ -49,6 +49,7 @@ constexpr int NONE = 0x7fffffff;       // id of "no element yet"
 constexpr int ROWS_CAP = NTH;          // the prologue gives every row one thread
 constexpr int MRB_MAX = 8;             // row blocks one wave keeps in registers
 constexpr int FB_BATCH = 8;            // cache words in flight per lane in a fallback scan
+constexpr int WAIT_VM0 = 0x0F70;       // s_waitcnt vmcnt(0), the other counters free (gfx9 encoding)
 constexpr size_t LDS_MAX = 160 * 1024;
 
 enum Mode { MODE_SAMPLE = 0, MODE_SAMPLE_EXACT = 1, MODE_BIAS = 2, MODE_SAMPLE_FALLBACK = 3 };
@@ -450,9 +451,19 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       seed = a.seeds[r];
       pos = a.positions[(int64_t)r * K + s];
     }
-    tok = (bias_mode || s == 0) ? a.prev[r] : slot_token(a.slots[(size_t)((s + 2) % 3) * rows + r]);
+    // the feeding token: prev at step 0, else the previous step's winner slot
+    // (one load from either address, decoded after the wait below)
+    const bool from_prev = bias_mode || s == 0;
+    tok = *(from_prev ? a.prev + r : (const int64_t*)(a.slots + (size_t)((s + 2) % 3) * rows + r));
   }
-  // the noise bound table, straight into LDS
+  // the row data, waited for before the table copy is issued: a wait the
+  // compiler sees, so that no later use of a row register waits for the copy;
+  // the empty asm keeps every use of the four values (the row hash) below it,
+  // so that all four loads are issued before the one wait
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+  asm volatile("" : "+v"(T), "+v"(seed), "+v"(pos), "+v"(tok));
+  // the noise bound table, straight into LDS: waited for with the first tile
+  // (before the unit loop), in flight through the row set-up
   if (!bias_mode) {
     for (int j = wave; j * 64 * 16 < (int)GT_BYTES; j += NWV) {
       const int p = j * 64 + lane;
@@ -462,13 +473,13 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
                                          16, 0, 0);
     }
   }
-  wait_vm<0>();   // row data and table (nothing else is in flight yet)
-  // everything the row set-up needs from them, before the tile loads below
-  // (whose wait would otherwise precede the first use of a row register)
+  // everything the row set-up needs from the row data, before the tile loads
+  // below
   const bool noisy_r = valid && !bias_mode && !(T == 0.0f);
   const uint64_t bn = __ballot(noisy_r), bz = __ballot(valid && !noisy_r);
   const float rcp_r = 1.0f / T;
   const uint32_t prefix_r = (valid && !bias_mode) ? row_prefix_of(seed, s, pos) : 0u;
+  if (!(bias_mode || s == 0)) tok = slot_token((unsigned long long)tok);
   const int tok32 = (int)tok;
   __builtin_amdgcn_sched_barrier(0);
 
@@ -874,6 +885,12 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         t0[b] = q < nq ? ((int)blockIdx.x + (q / (SLAB / 2)) * G) * SLAB + 2 * (q % (SLAB / 2)) : V;
         wd[b] = t0[b] < V ? load_cache_word(a.cache, (size_t)info.rk * V + t0[b]) : 0u;
       }
+      // with a threshold: the elements whose bound reaches it, the first two
+      // of the lane's kept aside and their exact keys taken together below
+      int nc = 0, ct0 = 0, ct1 = 0;
+      float cl0 = 0.0f, cl1 = 0.0f;
+      uint32_t ch0 = 0u, ch1 = 0u;
+      const bool screen = noisy && !(thr == -INFINITY);
 #pragma unroll
       for (int b = 0; b < FB_BATCH; ++b) {
         if (t0[b] >= V) continue;
@@ -881,18 +898,59 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         for (int e = 0; e < 2; ++e) {
           const int t = t0[b] + e;
           const float l = e ? bf_hi(wd[b]) : bf_lo(wd[b]);
-          float key = l;
-          if (noisy) {
+          if (screen) {
             const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
-            if (!(thr == -INFINITY)) {
-              const float gh = gtab[gt_offset(h) >> 2];
-              if (key_upper(l, info.rcp, gh) < thr) continue;
+            const float gh = gtab[gt_offset(h) >> 2];
+            if (!(key_upper(l, info.rcp, gh) < thr)) {
+              if (nc == 0) {
+                ct0 = t;
+                cl0 = l;
+                ch0 = h;
+              } else if (nc == 1) {
+                ct1 = t;
+                cl1 = l;
+                ch1 = h;
+              }
+              ++nc;
             }
-            key = key_exact(l, info.T, h);
+          } else {
+            const float key = noisy ? key_exact(l, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)t))) : l;
+            if (before(key, t, bv, bi)) {
+              bv = key;
+              bi = t;
+            }
           }
-          if (before(key, t, bv, bi)) {
-            bv = key;
-            bi = t;
+        }
+      }
+      if (nc > 0) {
+        const float key = key_exact(cl0, info.T, ch0);
+        if (before(key, ct0, bv, bi)) {
+          bv = key;
+          bi = ct0;
+        }
+      }
+      if (nc > 1) {
+        const float key = key_exact(cl1, info.T, ch1);
+        if (before(key, ct1, bv, bi)) {
+          bv = key;
+          bi = ct1;
+        }
+      }
+      if (nc > 2) {   // rare: every candidate of the batch, again
+#pragma unroll
+        for (int b = 0; b < FB_BATCH; ++b) {
+          if (t0[b] >= V) continue;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int t = t0[b] + e;
+            const float l = e ? bf_hi(wd[b]) : bf_lo(wd[b]);
+            const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
+            if (key_upper(l, info.rcp, gtab[gt_offset(h) >> 2]) < thr) continue;
+            const float key = key_exact(l, info.T, h);
+            if (before(key, t, bv, bi)) {
+              bv = key;
+              bi = t;
+            }
           }
         }
       }
