@@ -74,8 +74,9 @@ enum {
 int32_t markov_max_rows(int32_t rank);
 
 /* Bytes of device workspace one loop of this shape needs: the noise bound
- * table (8448 bytes) and three per-row arrays of packed (key, id) maxima.
- * Independent of k. */
+ * tables (25856 bytes: 2176 per-bucket lines as (A, B) binary32 pairs, then
+ * 2112 binary32 constants) and three per-row arrays of packed (key, id)
+ * maxima. Independent of k. */
 size_t markov_workspace_bytes(const markov_shape_t* shape, int32_t k);
 
 /* Prepare a workspace once after allocating it (enqueued on `stream`): the
@@ -175,6 +176,18 @@ int markov_debug_gumbel(const float* logits, const uint32_t* ids, int64_t n, flo
 
 /* RN bf16 of n binary32 values with the kernel's conversion (test-only). */
 int markov_debug_bf16_round(const float* in, uint16_t* out, int64_t n, markov_stream_t stream);
+
+/* The noise bound tables, host side (test-only): for the first n of the
+ * 2050 hash buckets, three binary32 values each into out[3 n] (host
+ * memory): the bucket line's A and B (the kernel bounds the noise of a hash
+ * h of the bucket by fma(B, float(h), A)) and the constant bound C (the
+ * bucket's largest noise plus 1e-5). Returns the number of buckets written. */
+int32_t markov_debug_noise_table(float* out, int32_t n);
+
+/* A plain device copy of `bytes` (a multiple of 16; both pointers 16-byte
+ * aligned) from src to dst on `stream` (test-only): the reference kernel
+ * whose counter readings calibrate DRAM byte counts. */
+int markov_debug_copy(const void* src, void* dst, int64_t bytes, markov_stream_t stream);
 
 #ifdef __cplusplus
 }

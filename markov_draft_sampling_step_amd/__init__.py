@@ -230,13 +230,22 @@ def debug_bf16_round(x, out, stream=None):
            "markov_debug_bf16_round")
 
 
+# The workspace starts with the noise bound tables: 2176 (A, B) float32
+# pairs (the per-bucket lines), then 2112 float32 constants (each bucket's
+# largest noise plus 1e-5); the per-row slot arrays follow.
+TABLE_PAIRS_BYTES = 2176 * 8
+TABLES_BYTES = TABLE_PAIRS_BYTES + 2112 * 4
+
+
 def debug_noise_table():
-    """The noise bound table (host numpy float32 array of 2050 entries)."""
+    """The noise bound tables as a host numpy float32 array [2050, 3]: per
+    bucket the line's A and B (bound = fma(B, float(h), A)) and the constant
+    bound C."""
     import numpy as np
 
-    out = np.zeros(2050, dtype=np.float32)
-    n = lib().markov_debug_noise_table(out.ctypes.data_as(ctypes.c_void_p), out.size)
-    if n != out.size:
+    out = np.zeros((2050, 3), dtype=np.float32)
+    n = lib().markov_debug_noise_table(out.ctypes.data_as(ctypes.c_void_p), 2050)
+    if n != 2050:
         raise MarkovError(int(n) if n < 0 else -2, "markov_debug_noise_table")
     return out
 

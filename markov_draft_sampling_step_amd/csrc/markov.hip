@@ -36,6 +36,7 @@
 #include <string.h>
 
 #include <type_traits>
+#include <vector>
 
 #include "markov.h"
 
@@ -145,7 +146,7 @@ __device__ __forceinline__ uint32_t row_prefix_of(int64_t seed, int step, int64_
 
 // u = RN32((h + 1/2) 2^-32): (lo16 + 1/2) 2^-32 is exact, and one fma adds
 // hi16 * 2^-16 with the only rounding.
-__device__ __forceinline__ float uniform_of(uint32_t h) {
+__host__ __device__ __forceinline__ float uniform_of(uint32_t h) {
   float hi = (float)(h >> 16), lo = (float)(h & 0xffffu);
   return __builtin_fmaf(hi, 0x1p-16f, __builtin_fmaf(lo, 0x1p-32f, 0x1p-33f));
 }
@@ -154,7 +155,7 @@ __device__ __forceinline__ float uniform_of(uint32_t h) {
 // Exact key: RN32(RN32(l / T) - lb), lb = RN32(log(-L)), L = log(1 - u) in
 // the pages' stable form (a Horner series below u = 1/4, else a log of
 // max(1 - u, 2^-24)). Logs are taken in binary64 and rounded once.
-__device__ __forceinline__ float log1m_exact(float u) {
+__host__ __device__ __forceinline__ float log1m_exact(float u) {
   if (u < 0.25f) {
     float p = 0.125f;
     p = __builtin_fmaf(u, p, 1.0f / 7.0f);
@@ -170,10 +171,13 @@ __device__ __forceinline__ float log1m_exact(float u) {
   return (float)log((double)x);
 }
 
+__host__ __device__ __forceinline__ float noise_lb(uint32_t h) {
+  const float L = log1m_exact(uniform_of(h));
+  return (float)log((double)(-L));
+}
+
 __device__ __forceinline__ float key_exact(float l, float T, uint32_t h) {
-  float u = uniform_of(h);
-  float L = log1m_exact(u);
-  float lb = (float)log((double)(-L));
+  const float lb = noise_lb(h);
   float q = l / T;
   return q - lb;
 }
@@ -181,22 +185,42 @@ __device__ __forceinline__ float key_exact(float l, float T, uint32_t h) {
 // Noise bound table. Bucket b of h: b = 0 for h = 0, else
 // (bits(float(h)) >> 17) - 8127, i.e. the exponent and the top 6 mantissa
 // bits of the nearest binary32 to h (1 .. 2049; 2049 is h rounding to
-// 2^32). gtable[b] is at least the largest noise -lb of any h in the bucket
-// plus 3e-5 (the host builds it in binary64 at the bucket's smallest h; the
-// noise falls as h grows). The kernel's upper bound of an exact key is then
-//   hi = fma(l, RN(1/T), gtable[b]),  up = fma(|hi|, 2^-19, hi)
+// 2^32). gtable[b] = (A, B) is a line in float(h) on or above the noise -lb
+// of every h in the bucket: RN32(fma(B, float(h), A)) >= -lb(h). The host
+// builds it from the chord of the noise over the bucket and lifts it by the
+// largest shortfall found on a grid of the bucket, plus 1e-5 (the noise and
+// the line both fall as h grows, so a shortfall between two grid points is
+// at most the line at the next point below the noise at this one). The
+// kernel's upper bound of an exact key is then
+//   hi = fma(l, RN(1/T), fma(B, float(h), A)),  up = fma(|hi|, 2^-19, hi)
 // (2^-19 |hi| covers the roundings of l / T, of the key and of hi, and the
-// 3-bit id the kernel packs into up's low bits; 3e-5 covers the
-// definition's own binary32 roundings of L and lb).
+// 3-bit id the kernel packs into up's low bits). A second table holds a
+// constant bound per bucket, the largest noise on the bucket's grid plus
+// 1e-5 (the noise at its first h, as the noise falls with h): the plans with
+// two row groups use it, as the line's float(h) operand would cost them
+// registers they lack.
 constexpr int GT_BASE = 8127;
 constexpr int GT_N = 2050;
-constexpr int GT_PAD = 2112;              // stored entries: 528 chunks of 16 bytes
-constexpr uint32_t GT_BYTES = GT_PAD * 4;
+constexpr int GT_PAD = 2176;               // stored pairs: 17 chunks of 1 KiB
+constexpr uint32_t GT_BYTES = GT_PAD * 8;
+constexpr int GTC_PAD = 2112;              // stored constants: 8.25 chunks of 1 KiB
+constexpr uint32_t GTC_BYTES = GTC_PAD * 4;
+constexpr uint32_t TABLES_BYTES = GT_BYTES + GTC_BYTES;   // both, at the workspace's start
+constexpr int GT_GRID = 1024;              // grid intervals per bucket in the host's check
 
-// byte offset of h's table entry
-__device__ __forceinline__ uint32_t gt_offset(uint32_t h) {
-  const uint32_t fb = __float_as_uint((float)h);
-  return __builtin_elementwise_sub_sat((fb >> 15) & ~3u, (uint32_t)(GT_BASE * 4));
+__device__ __forceinline__ uint32_t gt_index(float fh) {
+  return __builtin_elementwise_sub_sat(__float_as_uint(fh) >> 17, (uint32_t)GT_BASE);
+}
+
+// the table's bound of the noise -lb(h): the line (LIN) or the constant
+template <bool LIN>
+__device__ __forceinline__ float noise_bound(const void* tab, uint32_t h) {
+  const float fh = (float)h;
+  if (LIN) {
+    const float2 ab = ((const float2*)tab)[gt_index(fh)];
+    return __builtin_fmaf(ab.y, fh, ab.x);
+  }
+  return ((const float*)tab)[gt_index(fh)];
 }
 
 __device__ __forceinline__ float key_upper(float l, float rcpT, float gh) {
@@ -387,7 +411,11 @@ __host__ __device__ __forceinline__ size_t lds_dynamic(int rp, int R) {
   return region0_bytes(rp, R) + (size_t)rp * 16 + (size_t)rp * 16 + 64 * 4;
 }
 
-__host__ __device__ __forceinline__ size_t lds_total(int rp, int R) { return GT_BYTES + lds_dynamic(rp, R); }
+// the noise table in LDS: the lines for one row group (up to MRB_MAX row
+// blocks), the constants for two
+__host__ __device__ __forceinline__ size_t lds_table(int rp) { return (rp >> 4) > MRB_MAX ? GTC_BYTES : GT_BYTES; }
+
+__host__ __device__ __forceinline__ size_t lds_total(int rp, int R) { return lds_table(rp) + lds_dynamic(rp, R); }
 
 // ---------------------------------------------------------------- the step
 //
@@ -403,8 +431,11 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   constexpr int D = MRB - 1 < 3 ? MRB - 1 : 3;           // row blocks contracted ahead
   constexpr int S = RG == 1 ? 2 : 1;                     // waves splitting one SIMD's slabs
   constexpr bool ROWREG = MRB <= 4;                      // row constants in registers
+  constexpr bool LIN = RG == 1;                          // the line bound (else the constant)
+  constexpr uint32_t TB = LIN ? GT_BYTES : GTC_BYTES;    // the table this plan copies to LDS
   extern __shared__ __align__(16) unsigned char lds[];
-  __shared__ __align__(16) float gtab[GT_PAD];
+  __shared__ __align__(16) float gtabf[TB / 4];          // LIN: (A, B) pairs; else constants
+  float2* const gtab = (float2*)gtabf;
   const int mode = a.mode;
   const bool bias_mode = mode == MODE_BIAS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -465,11 +496,12 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   // the noise bound table, straight into LDS: waited for with the first tile
   // (before the unit loop), in flight through the row set-up
   if (!bias_mode) {
-    for (int j = wave; j * 64 * 16 < (int)GT_BYTES; j += NWV) {
+    for (int j = wave; j * 64 * 16 < (int)TB; j += NWV) {
       const int p = j * 64 + lane;
-      if (p * 16 < (int)GT_BYTES)
-        __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.gtable + (size_t)p * 16),
-                                         (__attribute__((address_space(3))) void*)(gtab + (size_t)j * 256),
+      if (p * 16 < (int)TB)
+        __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.gtable + (LIN ? 0 : GT_BYTES) +
+                                                       (size_t)p * 16),
+                                         (__attribute__((address_space(3))) void*)(gtabf + (size_t)j * 256),
                                          16, 0, 0);
     }
   }
@@ -722,15 +754,19 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
           const float x1b = x1;
           bool spx = false;
           // all 8 table reads in flight before the first is used
-          uint32_t off[8];
+          float fh[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) off[e] = gt_offset(mm_finish(info.prefix, kw[e]));
-          float gh[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) gh[e] = gtab[off[e] >> 2];
+          for (int e = 0; e < 8; ++e) fh[e] = (float)mm_finish(info.prefix, kw[e]);
+          float2 ab[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float up = key_upper(l[e], info.rcp, gh[e]);
+            if (LIN) ab[e] = gtab[gt_index(fh[e])];
+            else ab[e].x = gtabf[gt_index(fh[e])];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float gh = LIN ? __builtin_fmaf(ab[e].y, fh[e], ab[e].x) : ab[e].x;
+            const float up = key_upper(l[e], info.rcp, gh);
             spx = spx || __builtin_amdgcn_class(up, 0x207);       // NaN or infinite
             const float pk = __uint_as_float((__float_as_uint(up) & ~7u) | (uint32_t)e);
             x2 = __builtin_amdgcn_fmed3f(x1, x2, pk);
@@ -900,8 +936,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
           const float l = e ? bf_hi(wd[b]) : bf_lo(wd[b]);
           if (screen) {
             const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
-            const float gh = gtab[gt_offset(h) >> 2];
-            if (!(key_upper(l, info.rcp, gh) < thr)) {
+            if (!(key_upper(l, info.rcp, noise_bound<LIN>(gtab, h)) < thr)) {
               if (nc == 0) {
                 ct0 = t;
                 cl0 = l;
@@ -945,7 +980,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
             const int t = t0[b] + e;
             const float l = e ? bf_hi(wd[b]) : bf_lo(wd[b]);
             const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
-            if (key_upper(l, info.rcp, gtab[gt_offset(h) >> 2]) < thr) continue;
+            if (key_upper(l, info.rcp, noise_bound<LIN>(gtab, h)) < thr) continue;
             const float key = key_exact(l, info.T, h);
             if (before(key, t, bv, bi)) {
               bv = key;
@@ -987,13 +1022,13 @@ __global__ __launch_bounds__(256) void markov_finish_kernel(unsigned long long* 
 // ---------------------------------------------------------------- test kernels
 
 __global__ void debug_gumbel_kernel(const float* logits, const uint32_t* ids, int64_t n, float T,
-                                    int64_t seed, int step, int64_t position, const float* gtable,
+                                    int64_t seed, int step, int64_t position, const float2* gtable,
                                     float* kx, float* ku) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   uint32_t h = mm_finish(row_prefix_of(seed, step, position), mm_token_word(ids[i]));
   float l = logits[i];
-  ku[i] = key_upper(l, 1.0f / T, gtable[gt_offset(h) / 4]);
+  ku[i] = key_upper(l, 1.0f / T, noise_bound<true>(gtable, h));
   kx[i] = !(T == 0.0f) ? key_exact(l, T, h) : l;
 }
 
@@ -1015,11 +1050,13 @@ __global__ __launch_bounds__(256) void markov_copy_kernel(const u32x4_t* __restr
 
 // ---------------------------------------------------------------- host side
 
-// The noise bound table (see gt_offset), built once in binary64: entry b
-// bounds the noise -log(-L(u)) of every h in bucket b from above by its
-// value at the bucket's smallest h (the noise falls as h, hence u, grows),
-// plus 3e-5, rounded up to binary32.
-float g_table[GT_PAD];
+// The noise bound table (see gt_index): for each bucket, the chord of the
+// noise -lb(h) between the bucket's first and last h, as a line in float(h),
+// then raised until it lies on or above the noise everywhere in the bucket,
+// checked on a grid of at most GT_GRID intervals in the kernel's own binary32
+// evaluation (every hash of a bucket narrower than that), and by 1e-5.
+float2 g_table[GT_PAD];
+float g_ctable[GTC_PAD];   // a constant bound per bucket
 bool g_table_ready = false;
 
 float up_to_float(double x) {
@@ -1028,26 +1065,66 @@ float up_to_float(double x) {
   return f;
 }
 
+// the smallest h whose bucket is b or above (b >= 1): below 2^24 every
+// integer is exact; above it, h reaches at least the midpoint between F's
+// predecessor and F (F's mantissa is even, so the midpoint rounds up to F)
+uint64_t bucket_first_h(int b) {
+  if (b >= GT_N) return (uint64_t)1 << 32;
+  if (b == 0) return 0;
+  const uint32_t fb = (uint32_t)(b + GT_BASE) << 17;
+  float F;
+  memcpy(&F, &fb, 4);
+  const double Fd = (double)F;
+  const double h = Fd <= 0x1p24 ? ceil(Fd) : floor(0.5 * ((double)nextafterf(F, 0.0f) + Fd));
+  return (uint64_t)h;
+}
+
+float line_at(float2 ab, uint32_t h) { return fmaf(ab.y, (float)h, ab.x); }
+
 void build_table() {
   if (g_table_ready) return;
+  std::vector<float> n((size_t)GT_GRID + 1);
+  std::vector<uint32_t> hs((size_t)GT_GRID + 1);
   for (int b = 0; b < GT_N; ++b) {
-    double hlo = 0.0;
-    if (b > 0) {
-      const uint32_t fb = (uint32_t)(b + GT_BASE) << 17;
-      float F;
-      memcpy(&F, &fb, 4);
-      // the smallest h whose nearest binary32 is F or above: below 2^24 every
-      // integer is exact, above it h reaches at least the midpoint between
-      // F's predecessor and F (taken rounded down)
-      const double Fd = (double)F;
-      hlo = Fd <= 0x1p24 ? ceil(Fd) : floor(0.5 * ((double)nextafterf(F, 0.0f) + Fd));
+    const uint64_t h0 = bucket_first_h(b), h1 = bucket_first_h(b + 1);
+    if (h1 <= h0) {   // no h falls in this bucket
+      g_table[b] = make_float2(0.0f, 0.0f);
+      g_ctable[b] = 0.0f;
+      continue;
     }
-    const float u = (float)((hlo + 0.5) * 0x1p-32);     // the page's uniform, RN32
-    const double L = u >= 1.0f ? log(0x1p-24) : log1p(-(double)u);
-    const double g = -log(-L);
-    g_table[b] = up_to_float(g + 3e-5);
+    const uint64_t span = h1 - 1 - h0;
+    const int M = span < (uint64_t)GT_GRID ? (int)span : GT_GRID;
+    for (int i = 0; i <= M; ++i) {
+      hs[i] = (uint32_t)(h0 + (M ? span * (uint64_t)i / (uint64_t)M : 0));
+      n[i] = -noise_lb(hs[i]);
+    }
+    double B = 0.0;
+    const double f0 = (double)(float)hs[0], f1 = (double)(float)hs[M];
+    if (M > 0 && f1 > f0) B = ((double)n[M] - (double)n[0]) / (f1 - f0);
+    if (B > 0.0) B = 0.0;   // the line must fall with h
+    float2 ab = make_float2(0.0f, (float)B);
+    if (ab.y > 0.0f) ab.y = 0.0f;
+    ab.x = up_to_float((double)n[0] - (double)ab.y * f0);
+    // shortfall: noise at a grid point above the line at the next one (a
+    // hash strictly between them has no more noise and no less line), or at
+    // the point itself where the next point is the next hash
+    for (int pass = 0; pass < 4; ++pass) {
+      double short_by = (double)n[M] - (double)line_at(ab, hs[M]);
+      for (int i = 0; i < M; ++i) {
+        const uint32_t hl = hs[i + 1] == hs[i] + 1 ? hs[i] : hs[i + 1];
+        const double d = (double)n[i] - (double)line_at(ab, hl);
+        if (d > short_by) short_by = d;
+      }
+      if (pass > 0 && short_by <= -1e-5) break;
+      ab.x = up_to_float((double)ab.x + (short_by > 0.0 ? short_by : 0.0) + 1e-5);
+    }
+    g_table[b] = ab;
+    double top = (double)n[0];
+    for (int i = 1; i <= M; ++i) top = (double)n[i] > top ? (double)n[i] : top;
+    g_ctable[b] = up_to_float(top + 1e-5);
   }
-  for (int b = GT_N; b < GT_PAD; ++b) g_table[b] = 0.0f;   // unused
+  for (int b = GT_N; b < GT_PAD; ++b) g_table[b] = make_float2(0.0f, 0.0f);   // unused
+  for (int b = GT_N; b < GTC_PAD; ++b) g_ctable[b] = 0.0f;
   g_table_ready = true;
 }
 
@@ -1165,7 +1242,7 @@ int launch_grid(StepFn fn, size_t lds, int nslabs, int S, int* grid) {
   return MARKOV_OK;
 }
 
-size_t ws_bytes(int rows) { return (size_t)GT_BYTES + (size_t)rows * 8 * 3; }
+size_t ws_bytes(int rows) { return (size_t)TABLES_BYTES + (size_t)rows * 8 * 3; }
 
 int launch_steps(int mode, const void* base, const void* w1, const void* w2, const int64_t* prev,
                  const int64_t* seeds, const int64_t* positions, int32_t k, int32_t s_begin,
@@ -1194,7 +1271,7 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   a.bias_out = (uint16_t*)bias_out;
   if (workspace) {
     a.gtable = (const float*)workspace;
-    a.slots = (unsigned long long*)((unsigned char*)workspace + GT_BYTES);
+    a.slots = (unsigned long long*)((unsigned char*)workspace + TABLES_BYTES);
   }
   a.rows = sh->rows;
   a.V = sh->vocab;
@@ -1255,11 +1332,12 @@ int markov_workspace_init(void* workspace, size_t bytes, markov_stream_t stream)
   if (!aligned16(workspace)) return MARKOV_ERR_ALIGN;
   if (bytes < ws_bytes(1)) return MARKOV_ERR_WORKSPACE;
   build_table();
-  if (hipMemcpyAsync(workspace, g_table, GT_BYTES, hipMemcpyHostToDevice, (hipStream_t)stream) !=
-      hipSuccess)
+  unsigned char* ws = (unsigned char*)workspace;
+  if (hipMemcpyAsync(ws, g_table, GT_BYTES, hipMemcpyHostToDevice, (hipStream_t)stream) != hipSuccess ||
+      hipMemcpyAsync(ws + GT_BYTES, g_ctable, GTC_BYTES, hipMemcpyHostToDevice, (hipStream_t)stream) !=
+          hipSuccess)
     return MARKOV_ERR_HIP;
-  if (hipMemsetAsync((unsigned char*)workspace + GT_BYTES, 0, bytes - GT_BYTES, (hipStream_t)stream) !=
-      hipSuccess)
+  if (hipMemsetAsync(ws + TABLES_BYTES, 0, bytes - TABLES_BYTES, (hipStream_t)stream) != hipSuccess)
     return MARKOV_ERR_HIP;
   return MARKOV_OK;
 }
@@ -1348,7 +1426,7 @@ int markov_debug_gumbel(const float* logits, const uint32_t* ids, int64_t n, flo
   const int tb = 256;
   const int64_t blocks = (n + tb - 1) / tb;
   debug_gumbel_kernel<<<dim3((unsigned)blocks), tb, 0, (hipStream_t)stream>>>(
-      logits, ids, n, temperature, seed, step, position, (const float*)workspace, key_exact_out,
+      logits, ids, n, temperature, seed, step, position, (const float2*)workspace, key_exact_out,
       key_upper_out);
   if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   return MARKOV_OK;
@@ -1358,7 +1436,11 @@ int32_t markov_debug_noise_table(float* out, int32_t n) {
   if (!out) return MARKOV_ERR_NULL;
   build_table();
   const int32_t c = n < GT_N ? n : GT_N;
-  for (int32_t i = 0; i < c; ++i) out[i] = g_table[i];
+  for (int32_t i = 0; i < c; ++i) {
+    out[3 * i] = g_table[i].x;
+    out[3 * i + 1] = g_table[i].y;
+    out[3 * i + 2] = g_ctable[i];
+  }
   return c;
 }
 

@@ -279,8 +279,10 @@ def test_workspace_reuse_is_deterministic(dev):
     assert np.array_equal(t1, t2) and np.array_equal(c1, c2)
     ws = d["workspace"].cpu().numpy()
     table = m.debug_noise_table()
-    assert np.array_equal(ws[: table.nbytes].view(np.float32), table), "noise table changed"
-    assert not ws[8448:].any(), "slots must be left zeroed"
+    pairs = ws[: 2050 * 8].view(np.float32).reshape(2050, 2)
+    consts = ws[m.TABLE_PAIRS_BYTES: m.TABLE_PAIRS_BYTES + 2050 * 4].view(np.float32)
+    assert np.array_equal(pairs, table[:, :2]) and np.array_equal(consts, table[:, 2]), "noise table changed"
+    assert not ws[m.TABLES_BYTES:].any(), "slots must be left zeroed"
 
 
 @pytest.mark.parametrize("args", [
@@ -304,7 +306,7 @@ def test_loop_equals_step_by_step_calls(dev, args):
     c2, t2 = workloads.fetch(d)
     assert np.array_equal(t1, t2)
     assert np.array_equal(c1, c2)
-    assert not d["workspace"].cpu().numpy()[8448:].any()
+    assert not d["workspace"].cpu().numpy()[m.TABLES_BYTES:].any()
     say(f"  {w.name}: loop == steps")
 
 
@@ -365,7 +367,7 @@ def test_graph_replay_matches_eager(dev):
         assert np.array_equal(c, c_ref), i
         workloads.run(w, d)          # eager work between replays
         torch.cuda.synchronize()
-    assert not d["workspace"].cpu().numpy()[8448:].any()       # slots left zeroed
+    assert not d["workspace"].cpu().numpy()[m.TABLES_BYTES:].any()       # slots left zeroed
 
 
 @pytest.mark.parametrize("mult,softcap", [(1.0, 30.0), (0.75, 30.0), (1.0, 0.5), (1.25, 0.0)])
