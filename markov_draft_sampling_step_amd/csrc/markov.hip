@@ -516,10 +516,15 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 
   // 1. the wave's first w2 tile: it depends on nothing above, and stays in
-  //    flight through the row set-up (a wave without units reads clamped rows)
+  //    flight through the row set-up (a wave without units reads clamped
+  //    rows). With one row group, only the first wave of each SIMD (the one
+  //    with more units) requests it here; the second requests its own after
+  //    the embedding gather, so that the gather waits behind half the bytes.
+  const bool tile_first = RG == 2 || sub == 0;   // uniform per wave
   bf16x8_t A0[NB][KB], A1[NB][KB];
-  load_w2_tile<KB>(a.w2, V, R, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE, m, g, kzero,
-                            A0[0], A1[0]);
+  if (tile_first)
+    load_w2_tile<KB>(a.w2, V, R, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[0],
+                     A1[0]);
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. rows: noisy rows first, so that 16-row blocks are of one kind
@@ -576,7 +581,6 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
 
   const float mult = a.mult, cap = a.cap, inv_cap = a.inv_cap;
   const bool has_cap = a.has_cap != 0;
-  const bool mult1 = mult == 1.0f;
   const float pinf = a.inf;
   float v1[MRB], v2[MRB];
   int idt[MRB];
@@ -609,8 +613,15 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       }
     }
   }
-  // the second tile in flight (two-tile waves), issued after the gather so
-  // that waiting for the gather does not wait for it
+  // the second tile in flight (two-tile waves), and the first of a wave that
+  // did not request it above, issued after the gather so that waiting for
+  // the gather does not wait for them (the compiler, which cannot tell that
+  // the two requests of the first tile exclude each other, waits for the
+  // gather before the later one)
+  __builtin_amdgcn_sched_barrier(0);
+  if (!tile_first)
+    load_w2_tile<KB>(a.w2, V, R, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[0],
+                     A1[0]);
   __builtin_amdgcn_sched_barrier(0);
   if (NB == 2)
     load_w2_tile<KB>(a.w2, V, R, (U > 1 ? slab0 + slab_step : 0) * SLAB + tw * TOK_PER_WAVE, m,
@@ -624,9 +635,14 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     idt[j] = NONE;
     sp[j] = false;
   }
-  // everything but the second tile: the embeddings (every wave's, hence
-  // the barrier), the first tile and base logits
-  wait_vm<NB == 2 ? 2 * KB : 0>();
+  // everything but the tiles requested after the gather: the embeddings
+  // (every wave's, hence the barrier), the table, base logits and a first
+  // tile requested before the gather (a count past the field's 63 waits for
+  // more, never for less)
+  constexpr int VM_FIRST = NB == 2 ? 2 * KB : 0;
+  constexpr int VM_AFTER = NB * 2 * KB < 63 ? NB * 2 * KB : 63;
+  if (tile_first) wait_vm<VM_FIRST>();
+  else wait_vm<VM_AFTER>();
   lds_barrier();
 
   // one 32-token unit (the wave's unit i, slab `sl`) with w2 tile buffer BUF
@@ -705,8 +721,8 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         float zmax = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          z[2 * q] = (mult1 ? bf_lo(cw[q]) : mult * bf_lo(cw[q])) * inv_cap;
-          z[2 * q + 1] = (mult1 ? bf_hi(cw[q]) : mult * bf_hi(cw[q])) * inv_cap;
+          z[2 * q] = (mult * bf_lo(cw[q])) * inv_cap;       // mult = 1: exact, no select
+          z[2 * q + 1] = (mult * bf_hi(cw[q])) * inv_cap;
           zmax = fmaxf(zmax, fmaxf(fabsf(z[2 * q]), fabsf(z[2 * q + 1])));
         }
         if (__any(!(zmax < 0.625f))) {
