@@ -73,17 +73,29 @@ enum {
  * rows are staged in LDS next to per-row data, within 160 KiB). */
 int32_t markov_max_rows(int32_t rank);
 
-/* Bytes of device workspace one loop of this shape needs: the noise bound
- * tables (25856 bytes: 2176 per-bucket lines as (A, B) binary32 pairs, then
- * 2112 binary32 constants) and three per-row arrays of packed (key, id)
- * maxima. Independent of k. */
+/* Bytes of device workspace one loop of this shape needs (independent of
+ * k), in this order:
+ *   - the noise bound tables, 25856 bytes: 2176 per-bucket lines as (A, B)
+ *     binary32 pairs, then 2112 binary32 constants;
+ *   - the output-transform table, 65792 bytes: a 256-byte stamp (a magic
+ *     word, then the bits of the mult and softcap it was built for), then
+ *     32768 bf16 entries, entry i holding the cached value of the bf16 sum
+ *     whose bits are i (the transform is odd, so negative sums take the
+ *     entry of their magnitude with the sign flipped);
+ *   - three per-row arrays of packed (key, id) maxima, 24 bytes per row. */
 size_t markov_workspace_bytes(const markov_shape_t* shape, int32_t k);
 
 /* Prepare a workspace once after allocating it (enqueued on `stream`): the
- * noise bound table is copied in and the rest zeroed. Every call of
- * markov_sample_sequential leaves it so again, so it is reused as is; it
- * must not be shared by two calls in flight at once. 16-byte aligned. */
-int markov_workspace_init(void* workspace, size_t bytes, markov_stream_t stream);
+ * noise bound tables are copied in, the transform table is built on the host
+ * for shape->mult and shape->softcap (only with a soft cap; shape may be
+ * NULL, then no transform table is stamped) and copied in, and the slot
+ * arrays are zeroed. Every call of markov_sample_sequential leaves it so
+ * again, so it is reused as is; it must not be shared by two calls in flight
+ * at once. 16-byte aligned. A call whose (mult, softcap) differ from the
+ * stamp still gives the same results within the stated tolerance: it
+ * evaluates the transform itself instead of looking it up. */
+int markov_workspace_init(void* workspace, size_t bytes, const markov_shape_t* shape,
+                          markov_stream_t stream);
 
 /* NULL when this shape and k are supported, else why not (a static string);
  * mirrors the pages' fallback gates (kimi_k3 `why_not`, deepseek_v41
@@ -183,6 +195,12 @@ int markov_debug_bf16_round(const float* in, uint16_t* out, int64_t n, markov_st
  * h of the bucket by fma(B, float(h), A)) and the constant bound C (the
  * bucket's largest noise plus 1e-5). Returns the number of buckets written. */
 int32_t markov_debug_noise_table(float* out, int32_t n);
+
+/* The output-transform table, host side (test-only): the first n (at most
+ * 32768) entries of the table markov_workspace_init stamps for this mult and
+ * softcap (softcap > 0), bf16 bit patterns into out[n] (host memory).
+ * Returns the number of entries written. */
+int32_t markov_debug_transform_table(float mult, float softcap, uint16_t* out, int32_t n);
 
 /* A plain device copy of `bytes` (a multiple of 16; both pointers 16-byte
  * aligned) from src to dst on `stream` (test-only): the reference kernel

@@ -41,7 +41,7 @@ _P = ctypes.c_void_p
 _SIGS = {
     "markov_max_rows": (ctypes.c_int32, [ctypes.c_int32]),
     "markov_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32]),
-    "markov_workspace_init": (ctypes.c_int, [_P, ctypes.c_size_t, _P]),
+    "markov_workspace_init": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.POINTER(Shape), _P]),
     "markov_why_not": (ctypes.c_char_p, [ctypes.POINTER(Shape), ctypes.c_int32]),
     "markov_sample_sequential": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
                                                 _P, _P, ctypes.POINTER(Shape), _P,
@@ -63,6 +63,8 @@ _SIGS = {
     "markov_debug_bf16_round": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
     "markov_debug_copy": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
     "markov_debug_noise_table": (ctypes.c_int32, [_P, ctypes.c_int32]),
+    "markov_debug_transform_table": (ctypes.c_int32, [ctypes.c_float, ctypes.c_float, _P,
+                                                      ctypes.c_int32]),
 }
 
 _lib = None
@@ -143,15 +145,19 @@ def _dev(t, dtype, name, shape=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def new_workspace(rows: int, vocab: int, rank: int, k: int, device="cuda", stream=None):
-    """Allocate and zero a workspace for this shape (a uint8 tensor)."""
+def new_workspace(rows: int, vocab: int, rank: int, k: int, device="cuda", stream=None,
+                  mult: float = 1.0, softcap: float = 0.0):
+    """Allocate and prepare a workspace for this shape (a uint8 tensor); the
+    output-transform table in it is built for (mult, softcap)."""
     import torch
 
+    sh = make_shape(rows, vocab, rank, mult, softcap)
     n = workspace_bytes(rows, vocab, rank, k)
     if n == 0:
         raise MarkovError(-2, "workspace_bytes")
     ws = torch.empty(n, dtype=torch.uint8, device=device)
-    _check(lib().markov_workspace_init(ctypes.c_void_p(ws.data_ptr()), n, _stream_ptr(stream)),
+    _check(lib().markov_workspace_init(ctypes.c_void_p(ws.data_ptr()), n, ctypes.byref(sh),
+                                       _stream_ptr(stream)),
            "markov_workspace_init")
     return ws
 
@@ -232,9 +238,26 @@ def debug_bf16_round(x, out, stream=None):
 
 # The workspace starts with the noise bound tables: 2176 (A, B) float32
 # pairs (the per-bucket lines), then 2112 float32 constants (each bucket's
-# largest noise plus 1e-5); the per-row slot arrays follow.
+# largest noise plus 1e-5); then the output-transform table (a 256-byte
+# stamp, 32768 bf16 entries); the per-row slot arrays follow.
 TABLE_PAIRS_BYTES = 2176 * 8
-TABLES_BYTES = TABLE_PAIRS_BYTES + 2112 * 4
+NOISE_TABLES_BYTES = TABLE_PAIRS_BYTES + 2112 * 4
+TRANSFORM_STAMP_BYTES = 256
+TRANSFORM_ENTRIES = 32768
+TABLES_BYTES = NOISE_TABLES_BYTES + TRANSFORM_STAMP_BYTES + 2 * TRANSFORM_ENTRIES
+
+
+def debug_transform_table(mult: float, softcap: float):
+    """The output-transform table the library builds for (mult, softcap) as a
+    host numpy uint16 array [32768] (bf16 bits; entry i for the sum of bits i)."""
+    import numpy as np
+
+    out = np.zeros(TRANSFORM_ENTRIES, dtype=np.uint16)
+    n = lib().markov_debug_transform_table(ctypes.c_float(mult), ctypes.c_float(softcap),
+                                           out.ctypes.data_as(ctypes.c_void_p), TRANSFORM_ENTRIES)
+    if n != TRANSFORM_ENTRIES:
+        raise MarkovError(int(n) if n < 0 else -2, "markov_debug_transform_table")
+    return out
 
 
 def debug_noise_table():

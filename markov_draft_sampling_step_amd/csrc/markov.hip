@@ -35,6 +35,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -71,8 +72,10 @@ struct StepArgs {
   int64_t* tokens;
   unsigned long long* slots;  // [3][rows] packed winners, step s uses s % 3
   const float* gtable;        // the noise bound table (in the workspace)
+  const uint32_t* ttable;     // the transform table's stamp, then its 32768 entries
   uint16_t* bias_out;
   int rows, V, R, k, step, nslabs, mode;
+  int tt_layout;              // LDS holds the transform table at address 0
   float mult, inv_cap, cap;
   int has_cap;
   float inf;                  // +infinity, opaque to the compiler (see the noise loop)
@@ -208,6 +211,20 @@ constexpr uint32_t GTC_BYTES = GTC_PAD * 4;
 constexpr uint32_t TABLES_BYTES = GT_BYTES + GTC_BYTES;   // both, at the workspace's start
 constexpr int GT_GRID = 1024;              // grid intervals per bucket in the host's check
 
+// Transform table. The output transform maps a bf16 x (the bf16 sum of base
+// and bias) to the cached bf16 c, and every step of it (the multiplier, the
+// scaling by RN(1/cap), tanh, the scaling by cap, the roundings) is odd, so
+// c(-x) = -c(x) bit for bit and the map is a table over the 32768 values of
+// |x|. The host fills it with correctly rounded arithmetic for one (mult,
+// cap) and stamps it with both; a kernel whose own (mult, cap) match the
+// stamp looks c up in LDS (two reads per word of two values, the sign put
+// back with one xor), else it evaluates the transform itself.
+constexpr uint32_t TT_MAGIC = 0x4d545431u;
+constexpr uint32_t TT_HEAD = 256;          // stamp: magic, bits(mult), bits(cap), then zeros
+constexpr uint32_t TT_BYTES = 65536;       // 32768 bf16 entries, index |x|
+constexpr uint32_t WS_TT = TABLES_BYTES;   // workspace offset of the stamp
+constexpr uint32_t WS_SLOTS = WS_TT + TT_HEAD + TT_BYTES;   // the slot arrays follow
+
 __device__ __forceinline__ uint32_t gt_index(float fh) {
   return __builtin_elementwise_sub_sat(__float_as_uint(fh) >> 17, (uint32_t)GT_BASE);
 }
@@ -307,6 +324,31 @@ __device__ __forceinline__ float tanh_fast(float z) {
   return az < 0.625f ? tanh_poly(z) : yl;
 }
 
+// c of both bf16 values of word x from the transform table at LDS address
+// 0: entry |x| sits at byte 2 |x|, which one SDWA shift forms from either
+// half of x (the sign bit falls out of the 16-bit result).
+__device__ __forceinline__ uint32_t tt_addr_lo(uint32_t x) {
+  uint32_t r;
+  asm("v_lshlrev_b16_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_0"
+      : "=v"(r) : "v"(x));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t tt_addr_hi(uint32_t x) {
+  uint32_t r;
+  asm("v_lshlrev_b16_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+      : "=v"(r) : "v"(x));
+  return r;
+}
+
+typedef __attribute__((address_space(3))) const uint16_t lds_u16_t;
+
+__device__ __forceinline__ uint32_t tt_map(uint32_t x) {
+  const uint32_t lo = *(lds_u16_t*)(size_t)tt_addr_lo(x);
+  const uint32_t hi = *(lds_u16_t*)(size_t)tt_addr_hi(x);
+  return (lo | (hi << 16)) ^ (x & 0x80008000u);
+}
+
 // ---------------------------------------------------------------- tiles
 
 // The w2 rows of one 32-token unit as MFMA A operands: lane (g, m) holds
@@ -368,18 +410,21 @@ struct RowInfo {
 
 // Merge rules of the per-row states. ORDER: the exact (key, id) under the
 // total order. TOP2: (v1, id) is the element with the largest upper bound
-// v1, v2 the largest upper bound among all other elements. sp: some element
+// v1, v2 the largest upper bound among all other elements, l the logit of
+// element id (so its exact key needs no read of the cache). sp: some element
 // had a non-finite estimate (noisy rows) or a NaN / -inf logit (T = 0 rows).
 struct RowState {
   float v1, v2;
   int id;
   int sp;
+  float l;
 };
 
 __device__ __forceinline__ void merge_order(RowState& a, const RowState& b) {
   if (before(b.v1, b.id, a.v1, a.id)) {
     a.v1 = b.v1;
     a.id = b.id;
+    a.l = b.l;
   }
   a.sp |= b.sp;
 }
@@ -392,18 +437,22 @@ __device__ __forceinline__ void merge_top2(RowState& a, const RowState& b) {
   if (bw) {
     a.v1 = b.v1;
     a.id = b.id;
+    a.l = b.l;
   }
   a.sp |= b.sp;
 }
 
-// LDS: the noise bound table is a static array (its address is a constant,
-// so the table reads need no base register); the rest is dynamic:
+// LDS, all of it dynamic (the kernel declares no static LDS, so the dynamic
+// array starts at address 0):
+//   [tt]            with the transform-table layout, its 32768 entries (64 KiB)
+//                   at address 0, else nothing
+//   table           the noise bound table (lines or constants)
 //   region0         embeddings [rp][R] bf16; after the slab loop the waves'
-//                   row states [4][NWV][rp] (v1, v2, id, sp)
+//                   row states [5][NWV][rp] (v1, v2, id, sp, l)
 //   info [rp] RowInfo, n_row [rp], n_src [rp], fb_row [rp], fb_thr [rp],
 //   misc [64] (per-wave row counts, fallback count)
 __host__ __device__ __forceinline__ size_t region0_bytes(int rp, int R) {
-  const size_t e = (size_t)rp * R * 2, st = (size_t)NWV * rp * 16;
+  const size_t e = (size_t)rp * R * 2, st = (size_t)NWV * rp * 20;
   return e > st ? e : st;
 }
 
@@ -416,6 +465,11 @@ __host__ __device__ __forceinline__ size_t lds_dynamic(int rp, int R) {
 __host__ __device__ __forceinline__ size_t lds_table(int rp) { return (rp >> 4) > MRB_MAX ? GTC_BYTES : GT_BYTES; }
 
 __host__ __device__ __forceinline__ size_t lds_total(int rp, int R) { return lds_table(rp) + lds_dynamic(rp, R); }
+
+// the transform-table layout: one row group (the lines), a soft cap, and room
+__host__ __device__ __forceinline__ bool tt_fits(int rp, int R) {
+  return (rp >> 4) <= MRB_MAX && TT_BYTES + lds_total(rp, R) <= LDS_MAX;
+}
 
 // ---------------------------------------------------------------- the step
 //
@@ -434,7 +488,12 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   constexpr bool LIN = RG == 1;                          // the line bound (else the constant)
   constexpr uint32_t TB = LIN ? GT_BYTES : GTC_BYTES;    // the table this plan copies to LDS
   extern __shared__ __align__(16) unsigned char lds[];
-  __shared__ __align__(16) float gtabf[TB / 4];          // LIN: (A, B) pairs; else constants
+  // the transform table sits at LDS address 0 only if the dynamic array
+  // starts there (no static LDS); its lookups form absolute addresses
+  const bool tt_lay = LIN && a.tt_layout != 0 &&
+                      (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds == 0u;
+  const uint32_t tt_off = tt_lay ? TT_BYTES : 0u;
+  float* const gtabf = (float*)(lds + tt_off);           // LIN: (A, B) pairs; else constants
   float2* const gtab = (float2*)gtabf;
   const int mode = a.mode;
   const bool bias_mode = mode == MODE_BIAS;
@@ -461,9 +520,9 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   const int U = (my_nrb > 0 && slab0 < lim) ? (lim - slab0 + slab_step - 1) / slab_step : 0;
 
 
-  uint16_t* emb = (uint16_t*)lds;
+  uint16_t* emb = (uint16_t*)(lds + tt_off + TB);
   const size_t r0 = region0_bytes(rp, R);
-  RowInfo* n_info = (RowInfo*)(lds + r0);
+  RowInfo* n_info = (RowInfo*)((unsigned char*)emb + r0);
   int* n_row = (int*)(n_info + rp);
   int* n_src = n_row + rp;
   int* fb_row = n_src + rp;
@@ -502,6 +561,15 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.gtable + (LIN ? 0 : GT_BYTES) +
                                                        (size_t)p * 16),
                                          (__attribute__((address_space(3))) void*)(gtabf + (size_t)j * 256),
+                                         16, 0, 0);
+    }
+    // the transform table likewise (the host asks for this layout only with
+    // a soft cap; whether the stamp matches is checked where it is used)
+    if (tt_lay) {
+      const unsigned char* src = (const unsigned char*)a.ttable + TT_HEAD;
+      for (int j = wave; j * 64 * 16 < (int)TT_BYTES; j += NWV)
+        __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)(j * 64 + lane) * 16),
+                                         (__attribute__((address_space(3))) void*)(lds + (size_t)j * 1024),
                                          16, 0, 0);
     }
   }
@@ -581,10 +649,14 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
 
   const float mult = a.mult, cap = a.cap, inv_cap = a.inv_cap;
   const bool has_cap = a.has_cap != 0;
+  // the transform table in LDS holds this launch's (mult, cap)
+  const bool tt = tt_lay && a.ttable[0] == TT_MAGIC && a.ttable[1] == __float_as_uint(mult) &&
+                  a.ttable[2] == __float_as_uint(cap);
   const float pinf = a.inf;
   float v1[MRB], v2[MRB];
   int idt[MRB];
   bool sp[MRB];
+  uint32_t lw[MRB];   // noisy rows: the word of cached logits holding the top element's
 
   unsigned long long* slots_cur = bias_mode ? nullptr : a.slots + (size_t)(s % 3) * rows;
   lds_barrier();
@@ -634,6 +706,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     v2[j] = -INFINITY;
     idt[j] = NONE;
     sp[j] = false;
+    lw[j] = 0u;
   }
   // everything but the tiles requested after the gather: the embeddings
   // (every wave's, hence the barrier), the table, base logits and a first
@@ -716,7 +789,10 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         cw[q] = pack_bf16(bf_lo(bwd[q]) + bf_lo(bw[q]), bf_hi(bwd[q]) + bf_hi(bw[q]));
-      if (has_cap) {
+      if (has_cap && tt) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cw[q] = tt_map(cw[q]);
+      } else if (has_cap) {
         float z[8];
         float zmax = 0.0f;
 #pragma unroll
@@ -788,7 +864,11 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
             x2 = __builtin_amdgcn_fmed3f(x1, x2, pk);
             x1 = __builtin_amdgcn_fmed3f(x1, pk, pinf);   // max, no canonicalising
           }
-          if (x1 != x1b) idt[j] = tg;
+          if (x1 != x1b) {
+            idt[j] = tg;
+            const uint32_t e1 = __float_as_uint(x1);
+            lw[j] = (e1 & 4u) ? ((e1 & 2u) ? cw[3] : cw[2]) : ((e1 & 2u) ? cw[1] : cw[0]);
+          }
           v1[j] = x1;
           v2[j] = x2;
           sp[j] = sp[j] || spx;
@@ -842,6 +922,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     if (EXACT) st.id = idt[j];
     else if (idt[j] == NONE) st.id = NONE;
     else st.id = idt[j] + (int)((noisy ? __float_as_uint(v1[j]) : __float_as_uint(v2[j])) & 7u);
+    st.l = (__float_as_uint(v1[j]) & 1u) ? bf_hi(lw[j]) : bf_lo(lw[j]);
     const bool top2 = noisy && !EXACT;
 #pragma unroll
     for (int sh = 16; sh <= 32; sh <<= 1) {
@@ -850,17 +931,21 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       o.v2 = __shfl_xor(st.v2, sh);
       o.id = __shfl_xor(st.id, sh);
       o.sp = __shfl_xor(st.sp, sh);
+      o.l = __shfl_xor(st.l, sh);
       if (top2) merge_top2(st, o);
       else merge_order(st, o);
     }
     fin[j] = st;
   }
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's cache stores, read back below
-  __syncthreads();
+  // every wave past its last contraction (the states go over the
+  // embeddings); the cache stores drain meanwhile (the barrier before the
+  // fallback scans, which read them back, waits for them)
+  lds_barrier();
   float* st_v1 = (float*)emb;
   float* st_v2 = st_v1 + NWV * rp;
   int* st_id = (int*)(st_v2 + NWV * rp);
   int* st_sp = st_id + NWV * rp;
+  float* st_l = (float*)(st_sp + NWV * rp);
 #pragma unroll
   for (int j = 0; j < MRB; ++j) {
     if (j >= my_nrb) break;
@@ -870,20 +955,22 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       st_v2[wave * rp + n] = fin[j].v2;
       st_id[wave * rp + n] = fin[j].id;
       st_sp[wave * rp + n] = fin[j].sp;
+      st_l[wave * rp + n] = fin[j].l;
     }
   }
   if (tid == 0) misc[16] = 0;
-  __syncthreads();
+  lds_barrier();
   for (int n = tid; n < rows; n += NTH) {
     const RowInfo info = n_info[n];
     const bool noisy = !(info.T == 0.0f);
     const bool top2 = noisy && !EXACT;
     const int w0 = RG == 1 ? 0 : 4 * ((n >> 4) & 1);
     const int w1n = RG == 1 ? NWV : w0 + 4;
-    RowState st = {st_v1[w0 * rp + n], st_v2[w0 * rp + n], st_id[w0 * rp + n], st_sp[w0 * rp + n]};
+    RowState st = {st_v1[w0 * rp + n], st_v2[w0 * rp + n], st_id[w0 * rp + n], st_sp[w0 * rp + n],
+                   st_l[w0 * rp + n]};
     for (int w = w0 + 1; w < w1n; ++w) {
       const int i = w * rp + n;
-      RowState o = {st_v1[i], st_v2[i], st_id[i], st_sp[i]};
+      RowState o = {st_v1[i], st_v2[i], st_id[i], st_sp[i], st_l[i]};
       if (top2) merge_top2(st, o);
       else merge_order(st, o);
     }
@@ -892,13 +979,18 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     bool fb = !EXACT && (st.sp != 0 || (mode == MODE_SAMPLE_FALLBACK && noisy));
     float thr = -INFINITY;
     if (!fb && top2 && st.id != NONE) {
-      const size_t e = (size_t)info.rk * V + st.id;
-      const uint32_t wd = load_cache_word(a.cache, e & ~(size_t)1);
-      const float l1 = (e & 1) ? bf_hi(wd) : bf_lo(wd);
-      key = key_exact(l1, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)st.id)));
+      key = key_exact(st.l, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)st.id)));
       if (!(key > st.v2)) {
-        fb = true;
-        thr = key;
+        // not certified: some other element's bound reaches the key. If a
+        // key already published for this row (by another workgroup) lies
+        // above that bound, no element here but the top one can win, and
+        // the top one is published below; else re-scan the row.
+        const unsigned long long cur =
+            __hip_atomic_load(slots_cur + rr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!((uint32_t)(cur >> 32) > (uint32_t)(pack_winner(st.v2, 0) >> 32))) {
+          fb = true;
+          thr = key;
+        }
       }
     }
     if (fb) {
@@ -1144,6 +1236,68 @@ void build_table() {
   g_table_ready = true;
 }
 
+// ---- the transform table, host side: c(x) for x = +0 .. the largest bf16
+// pattern below the sign bit, with the same operations the kernel's own
+// evaluation takes, each rounded once; tanh correctly rounded to binary32
+// (binary64 tanh, re-evaluated in x87 extended precision when the binary64
+// value lies within a few of its ulps of a binary32 rounding boundary).
+uint16_t bf16_rne_host(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);   // NaN stays NaN
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+float tanh_cr_host(float z) {
+  const double t = tanh((double)z);
+  float f = (float)t;
+  if (!(t == t)) return f;
+  const float g = (double)f < t ? nextafterf(f, INFINITY) : nextafterf(f, -INFINITY);
+  const double mid = 0.5 * ((double)f + (double)g);
+  if (fabs(t - mid) <= 16.0 * 0x1p-53 * fabs(t)) f = (float)tanhl((long double)z);
+  return f;
+}
+
+uint16_t transform_host(uint16_t xb, float mult, float cap) {
+  const uint32_t xu = (uint32_t)xb << 16;
+  float x;
+  memcpy(&x, &xu, 4);
+  const float inv_cap = 1.0f / cap;
+  const float y = mult * x;
+  const float z = y * inv_cap;
+  const float w = cap * tanh_cr_host(z);
+  return bf16_rne_host(w);
+}
+
+// Built tables, kept for the life of the process (an enqueued copy may still
+// read one after the call that asked for it has returned).
+struct TransformTable {
+  uint32_t mult_bits, cap_bits;
+  uint32_t data[(TT_HEAD + TT_BYTES) / 4];
+};
+std::mutex g_tt_mutex;
+std::vector<TransformTable*> g_tt;
+
+const TransformTable* transform_table(float mult, float cap) {
+  uint32_t mb, cb;
+  memcpy(&mb, &mult, 4);
+  memcpy(&cb, &cap, 4);
+  std::lock_guard<std::mutex> lock(g_tt_mutex);
+  for (const TransformTable* t : g_tt)
+    if (t->mult_bits == mb && t->cap_bits == cb) return t;
+  TransformTable* t = new TransformTable;
+  t->mult_bits = mb;
+  t->cap_bits = cb;
+  memset(t->data, 0, sizeof(t->data));
+  t->data[0] = TT_MAGIC;
+  t->data[1] = mb;
+  t->data[2] = cb;
+  uint16_t* e = (uint16_t*)((unsigned char*)t->data + TT_HEAD);
+  for (uint32_t i = 0; i < TT_BYTES / 2; ++i) e[i] = transform_host((uint16_t)i, mult, cap);
+  g_tt.push_back(t);
+  return t;
+}
+
 typedef void (*StepFn)(StepArgs);
 
 struct Plan {
@@ -1203,7 +1357,6 @@ StepFn pick_kernel(int R, Plan p, bool exact = false) {
 bool pow2_rank(int R) { return R >= 16 && R <= 512 && (R & (R - 1)) == 0; }
 
 size_t lds_bytes(int rows, int R) { return lds_total((rows + 15) & ~15, R); }
-size_t lds_dyn_bytes(int rows, int R) { return lds_dynamic((rows + 15) & ~15, R); }
 
 int32_t max_rows_of(int32_t R) {
   if (!pow2_rank(R)) return 0;
@@ -1258,7 +1411,7 @@ int launch_grid(StepFn fn, size_t lds, int nslabs, int S, int* grid) {
   return MARKOV_OK;
 }
 
-size_t ws_bytes(int rows) { return (size_t)TABLES_BYTES + (size_t)rows * 8 * 3; }
+size_t ws_bytes(int rows) { return (size_t)WS_SLOTS + (size_t)rows * 8 * 3; }
 
 int launch_steps(int mode, const void* base, const void* w1, const void* w2, const int64_t* prev,
                  const int64_t* seeds, const int64_t* positions, int32_t k, int32_t s_begin,
@@ -1268,7 +1421,9 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   const Plan plan = plan_of(sh->rows);
   StepFn fn = pick_kernel(sh->rank, plan, mode == MODE_SAMPLE_EXACT);
   if (!fn) return MARKOV_ERR_ROWS;
-  const size_t lds = lds_dyn_bytes(sh->rows, sh->rank);
+  const int rp = (sh->rows + 15) & ~15;
+  const bool tt_layout = mode != MODE_BIAS && sh->softcap > 0.0f && plan.rg == 1 && tt_fits(rp, sh->rank);
+  const size_t lds = (tt_layout ? TT_BYTES : 0) + lds_total(rp, sh->rank);
   const int nslabs = (sh->vocab + SLAB - 1) / SLAB;
   int grid = 0;
   int rc = launch_grid(fn, lds, nslabs, plan.rg == 1 ? 2 : 1, &grid);
@@ -1287,8 +1442,10 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   a.bias_out = (uint16_t*)bias_out;
   if (workspace) {
     a.gtable = (const float*)workspace;
-    a.slots = (unsigned long long*)((unsigned char*)workspace + TABLES_BYTES);
+    a.ttable = (const uint32_t*)((unsigned char*)workspace + WS_TT);
+    a.slots = (unsigned long long*)((unsigned char*)workspace + WS_SLOTS);
   }
+  a.tt_layout = tt_layout ? 1 : 0;
   a.rows = sh->rows;
   a.V = sh->vocab;
   a.R = sh->rank;
@@ -1343,18 +1500,25 @@ size_t markov_workspace_bytes(const markov_shape_t* shape, int32_t k) {
   return ws_bytes(shape->rows);
 }
 
-int markov_workspace_init(void* workspace, size_t bytes, markov_stream_t stream) {
+int markov_workspace_init(void* workspace, size_t bytes, const markov_shape_t* shape,
+                          markov_stream_t stream) {
   if (!workspace) return MARKOV_ERR_NULL;
   if (!aligned16(workspace)) return MARKOV_ERR_ALIGN;
   if (bytes < ws_bytes(1)) return MARKOV_ERR_WORKSPACE;
   build_table();
   unsigned char* ws = (unsigned char*)workspace;
-  if (hipMemcpyAsync(ws, g_table, GT_BYTES, hipMemcpyHostToDevice, (hipStream_t)stream) != hipSuccess ||
-      hipMemcpyAsync(ws + GT_BYTES, g_ctable, GTC_BYTES, hipMemcpyHostToDevice, (hipStream_t)stream) !=
-          hipSuccess)
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(ws, g_table, GT_BYTES, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipMemcpyAsync(ws + GT_BYTES, g_ctable, GTC_BYTES, hipMemcpyHostToDevice, st) != hipSuccess)
     return MARKOV_ERR_HIP;
-  if (hipMemsetAsync(ws + TABLES_BYTES, 0, bytes - TABLES_BYTES, (hipStream_t)stream) != hipSuccess)
+  if (shape && shape->softcap > 0.0f) {
+    const TransformTable* t = transform_table(shape->mult, shape->softcap);
+    if (hipMemcpyAsync(ws + WS_TT, t->data, TT_HEAD + TT_BYTES, hipMemcpyHostToDevice, st) != hipSuccess)
+      return MARKOV_ERR_HIP;
+  } else if (hipMemsetAsync(ws + WS_TT, 0, TT_HEAD, st) != hipSuccess) {   // no stamp
     return MARKOV_ERR_HIP;
+  }
+  if (hipMemsetAsync(ws + WS_SLOTS, 0, bytes - WS_SLOTS, st) != hipSuccess) return MARKOV_ERR_HIP;
   return MARKOV_OK;
 }
 
@@ -1457,6 +1621,15 @@ int32_t markov_debug_noise_table(float* out, int32_t n) {
     out[3 * i + 1] = g_table[i].y;
     out[3 * i + 2] = g_ctable[i];
   }
+  return c;
+}
+
+int32_t markov_debug_transform_table(float mult, float softcap, uint16_t* out, int32_t n) {
+  if (!out) return MARKOV_ERR_NULL;
+  if (!(softcap > 0.0f) || n < 0) return MARKOV_ERR_SHAPE;
+  const TransformTable* t = transform_table(mult, softcap);
+  const int32_t c = n < (int32_t)(TT_BYTES / 2) ? n : (int32_t)(TT_BYTES / 2);
+  memcpy(out, (const unsigned char*)t->data + TT_HEAD, (size_t)c * 2);
   return c;
 }
 

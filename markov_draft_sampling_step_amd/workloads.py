@@ -178,7 +178,7 @@ def to_device(w: Workload, device="cuda") -> dict:
         positions=plain(w.positions), temperature=plain(w.temperature),
         cache=torch.empty((w.rows, w.k, w.V), dtype=torch.bfloat16, device=device),
         tokens=torch.empty((w.rows, w.k), dtype=torch.int64, device=device),
-        workspace=new_workspace(w.rows, w.V, w.R, w.k, device=device),
+        workspace=new_workspace(w.rows, w.V, w.R, w.k, device=device, mult=w.mult, softcap=w.softcap),
     )
 
 

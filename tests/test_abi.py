@@ -60,8 +60,10 @@ def test_max_rows_and_workspace(lib):
         mr = m.max_rows(R)
         assert m.why_not(mr, 4096, R, 3) is None
         assert "LDS" in m.why_not(mr + 1, 4096, R, 3)
-    # the noise bound tables (25856 bytes) and three per-row slot arrays
-    assert m.TABLES_BYTES == 25856
+    # the noise bound tables (25856 bytes), the transform table (a 256-byte
+    # stamp, 32768 bf16 entries) and three per-row slot arrays
+    assert m.NOISE_TABLES_BYTES == 25856
+    assert m.TABLES_BYTES == 25856 + 256 + 65536
     assert m.workspace_bytes(64, 163840, 256, 5) == m.TABLES_BYTES + 64 * 8 * 3
     assert m.workspace_bytes(0, 163840, 256, 5) == 0
     assert m.workspace_bytes(4, 100, 256, 5) == 0        # vocab not a multiple of 8
@@ -86,7 +88,7 @@ def test_why_not(lib, rows, V, R, k, why):
         assert r is not None and why in r
 
 
-def _call(lib, shape, ptrs, k=3, ws_bytes=1 << 16):
+def _call(lib, shape, ptrs, k=3, ws_bytes=1 << 20):
     P = ctypes.c_void_p
     return lib.markov_sample_sequential(P(ptrs[0]), P(ptrs[1]), P(ptrs[2]), P(ptrs[3]),
                                         P(ptrs[4]), P(ptrs[5]), k, P(ptrs[6]), P(ptrs[7]),
@@ -119,4 +121,4 @@ def test_host_errors_before_any_device_work(lib):
                                    None) == -1
     bad = list(good)
     bad[9] += 8                                             # workspace must be 16-byte aligned
-    assert _call(lib, sh, bad, ws_bytes=1 << 16) == -4
+    assert _call(lib, sh, bad, ws_bytes=1 << 20) == -4
