@@ -82,7 +82,9 @@ int32_t markov_max_rows(int32_t rank);
  *     32768 bf16 entries, entry i holding the cached value of the bf16 sum
  *     whose bits are i (the transform is odd, so negative sums take the
  *     entry of their magnitude with the sign flipped);
- *   - three per-row arrays of packed (key, id) maxima, 24 bytes per row. */
+ *   - the winner slots: for each of three steps in turn, 8 per-row arrays of
+ *     packed (key, id) maxima (workgroups publish into 8 groups; a step's
+ *     winner is the largest over them), 192 bytes per row. */
 size_t markov_workspace_bytes(const markov_shape_t* shape, int32_t k);
 
 /* Prepare a workspace once after allocating it (enqueued on `stream`): the

@@ -53,6 +53,11 @@ constexpr int MRB_MAX = 8;             // row blocks one wave keeps in registers
 constexpr int FB_BATCH = 8;            // cache words in flight per lane in a fallback scan
 constexpr int WAIT_VM0 = 0x0F70;       // s_waitcnt vmcnt(0), the other counters free (gfx9 encoding)
 constexpr size_t LDS_MAX = 160 * 1024;
+// Winner slot groups: workgroup b publishes into group b % SG, and a step's
+// winner is the largest value over the groups. Device-scope atomics on one
+// cache line are served one after another, so SG groups cut the queue on
+// each line SG-fold; the reader pays SG loads per row.
+constexpr int SG = 8;
 
 enum Mode { MODE_SAMPLE = 0, MODE_SAMPLE_EXACT = 1, MODE_BIAS = 2, MODE_SAMPLE_FALLBACK = 3 };
 
@@ -70,7 +75,7 @@ struct StepArgs {
   const float* temperature;
   uint16_t* cache;
   int64_t* tokens;
-  unsigned long long* slots;  // [3][rows] packed winners, step s uses s % 3
+  unsigned long long* slots;  // [3][SG][rows] packed winners, step s uses s % 3
   const float* gtable;        // the noise bound table (in the workspace)
   const uint32_t* ttable;     // the transform table's stamp, then its 32768 entries
   uint16_t* bias_out;
@@ -126,9 +131,12 @@ __device__ __forceinline__ uint32_t times5_plus(uint32_t h, uint32_t c) {
   return r + c;
 }
 
-__device__ __forceinline__ uint32_t mm_finish(uint32_t prefix, uint32_t token_word) {
-  uint32_t h = prefix ^ token_word;
-  h = rotl32(h, 13);
+// The last block and the finaliser, from the row prefix and the token word
+// both already rotated left by 13 (rotation distributes over xor, so the
+// block's rotation moves onto the two operands: once per row, and once per
+// token for all rows).
+__device__ __forceinline__ uint32_t mm_finish_rot(uint32_t prefix_rot, uint32_t token_word_rot) {
+  uint32_t h = prefix_rot ^ token_word_rot;
   h = times5_plus(h, 0xe6546b64u);
   h ^= 16u;                       // message length in bytes
   h ^= h >> 16;
@@ -137,6 +145,10 @@ __device__ __forceinline__ uint32_t mm_finish(uint32_t prefix, uint32_t token_wo
   h *= 0xc2b2ae35u;
   h ^= h >> 16;
   return h;
+}
+
+__device__ __forceinline__ uint32_t mm_finish(uint32_t prefix, uint32_t token_word) {
+  return mm_finish_rot(rotl32(prefix, 13), rotl32(token_word, 13));
 }
 
 __device__ __forceinline__ uint32_t row_prefix_of(int64_t seed, int step, int64_t position) {
@@ -244,6 +256,13 @@ __device__ __forceinline__ float key_upper(float l, float rcpT, float gh) {
   const float hi = __builtin_fmaf(l, rcpT, gh);
   return __builtin_fmaf(fabsf(hi), 0x1p-19f, hi);
 }
+
+// The slot loop keeps, per row, the largest estimates fma(l, RN(1/T), bound)
+// with the element's index in the low 3 bits, without key_upper's margin;
+// the margin, monotone in the estimate, is added to the kept value once.
+// 2^-18 |v| is at least 32 of v's ulps: the 2^-19 of key_upper plus the
+// packed bits and an estimate a binade above v.
+__device__ __forceinline__ float slack_up(float v) { return __builtin_fmaf(fabsf(v), 0x1p-18f, v); }
 
 // The total order of every argmax here: a NaN beats every non-NaN, lower
 // id among NaNs; otherwise the larger value, and equal values (so -0 == +0)
@@ -535,16 +554,24 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   const bool valid = r < rows;
   float T = 0.0f;
   int64_t tok = 0, seed = 0, pos = 0;
+  unsigned long long slot_in[SG];
+#pragma unroll
+  for (int q = 0; q < SG; ++q) slot_in[q] = 0ull;
   if (valid) {
     if (!bias_mode) {
       T = a.temperature[r];
       seed = a.seeds[r];
       pos = a.positions[(int64_t)r * K + s];
     }
-    // the feeding token: prev at step 0, else the previous step's winner slot
-    // (one load from either address, decoded after the wait below)
-    const bool from_prev = bias_mode || s == 0;
-    tok = *(from_prev ? a.prev + r : (const int64_t*)(a.slots + (size_t)((s + 2) % 3) * rows + r));
+    // the feeding token: prev at step 0, else the previous step's winner
+    // slots (decoded after the wait below)
+    if (bias_mode || s == 0) {
+      tok = a.prev[r];
+    } else {
+      const unsigned long long* sp0 = a.slots + (size_t)((s + 2) % 3) * SG * rows + r;
+#pragma unroll
+      for (int q = 0; q < SG; ++q) slot_in[q] = sp0[(size_t)q * rows];
+    }
   }
   // the row data, waited for before the table copy is issued: a wait the
   // compiler sees, so that no later use of a row register waits for the copy;
@@ -552,6 +579,9 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   // so that all four loads are issued before the one wait
   __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   asm volatile("" : "+v"(T), "+v"(seed), "+v"(pos), "+v"(tok));
+  asm volatile("" : "+v"(slot_in[0]), "+v"(slot_in[1]), "+v"(slot_in[2]), "+v"(slot_in[3]),
+               "+v"(slot_in[4]), "+v"(slot_in[5]), "+v"(slot_in[6]), "+v"(slot_in[7]));
+  static_assert(SG == 8, "the asm above pins SG slot values");
   // the noise bound table, straight into LDS: waited for with the first tile
   // (before the unit loop), in flight through the row set-up
   if (!bias_mode) {
@@ -563,15 +593,6 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
                                          (__attribute__((address_space(3))) void*)(gtabf + (size_t)j * 256),
                                          16, 0, 0);
     }
-    // the transform table likewise (the host asks for this layout only with
-    // a soft cap; whether the stamp matches is checked where it is used)
-    if (tt_lay) {
-      const unsigned char* src = (const unsigned char*)a.ttable + TT_HEAD;
-      for (int j = wave; j * 64 * 16 < (int)TT_BYTES; j += NWV)
-        __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)(j * 64 + lane) * 16),
-                                         (__attribute__((address_space(3))) void*)(lds + (size_t)j * 1024),
-                                         16, 0, 0);
-    }
   }
   // everything the row set-up needs from the row data, before the tile loads
   // below
@@ -579,7 +600,12 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   const uint64_t bn = __ballot(noisy_r), bz = __ballot(valid && !noisy_r);
   const float rcp_r = 1.0f / T;
   const uint32_t prefix_r = (valid && !bias_mode) ? row_prefix_of(seed, s, pos) : 0u;
-  if (!(bias_mode || s == 0)) tok = slot_token((unsigned long long)tok);
+  if (!(bias_mode || s == 0)) {
+    unsigned long long w = slot_in[0];
+#pragma unroll
+    for (int q = 1; q < SG; ++q) w = slot_in[q] > w ? slot_in[q] : w;
+    tok = slot_token(w);
+  }
   const int tok32 = (int)tok;
   __builtin_amdgcn_sched_barrier(0);
 
@@ -624,7 +650,9 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       n_info[pos_n] = RowInfo{r * K + s, rcp_r, prefix_r, T};
       if (!bias_mode && blockIdx.x == 0) {
         if (s > 0) a.tokens[(int64_t)r * K + s - 1] = (int64_t)(uint32_t)tok32;   // previous step's
-        a.slots[(size_t)((s + 1) % 3) * rows + r] = 0ull;            // next step's slots start empty
+#pragma unroll
+        for (int q = 0; q < SG; ++q)                                  // next step's slots start empty
+          a.slots[((size_t)((s + 1) % 3) * SG + q) * rows + r] = 0ull;
       }
     } else if (r < rp) {
       n_row[r] = 0;
@@ -658,7 +686,8 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   bool sp[MRB];
   uint32_t lw[MRB];   // noisy rows: the word of cached logits holding the top element's
 
-  unsigned long long* slots_cur = bias_mode ? nullptr : a.slots + (size_t)(s % 3) * rows;
+  unsigned long long* slots_step = bias_mode ? nullptr : a.slots + (size_t)(s % 3) * SG * rows;
+  unsigned long long* slots_cur = bias_mode ? nullptr : slots_step + (size_t)(blockIdx.x % SG) * rows;
   lds_barrier();
   if (ROWREG) {
 #pragma unroll
@@ -684,6 +713,17 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
                                          16, 0, 0);
       }
     }
+  }
+  // the transform table likewise (the host asks for this layout only with a
+  // soft cap; whether the stamp matches is checked where it is used): after
+  // the first tiles and the gather, so that it does not hold them up, and
+  // waited for with them (its lines come from L2)
+  if (tt_lay) {
+    const unsigned char* src = (const unsigned char*)a.ttable + TT_HEAD;
+    for (int j = wave; j * 64 * 16 < (int)TT_BYTES; j += NWV)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)(j * 64 + lane) * 16),
+                                       (__attribute__((address_space(3))) void*)(lds + (size_t)j * 1024),
+                                       16, 0, 0);
   }
   // the second tile in flight (two-tile waves), and the first of a wave that
   // did not request it above, issued after the gather so that waiting for
@@ -733,7 +773,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       uint32_t kc = (uint32_t)tg * MM_C1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        kw[e] = rotl32(kc, 15) * MM_C2;
+        kw[e] = rotl32(rotl32(kc, 15) * MM_C2, 13);   // the token word, rotated for mm_finish_rot
         kc += MM_C1;
       }
     }
@@ -829,7 +869,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             float key = l[e];
-            if (noisy) key = key_exact(l[e], info.T, mm_finish(info.prefix, kw[e]));
+            if (noisy) key = key_exact(l[e], info.T, mm_finish_rot(rotl32(info.prefix, 13), kw[e]));
             if (before(key, tg + e, v1[j], idt[j])) {
               v1[j] = key;
               idt[j] = tg + e;
@@ -847,8 +887,9 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
           bool spx = false;
           // all 8 table reads in flight before the first is used
           float fh[8];
+          const uint32_t pr = rotl32(info.prefix, 13);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) fh[e] = (float)mm_finish(info.prefix, kw[e]);
+          for (int e = 0; e < 8; ++e) fh[e] = (float)mm_finish_rot(pr, kw[e]);
           float2 ab[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -858,9 +899,12 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float gh = LIN ? __builtin_fmaf(ab[e].y, fh[e], ab[e].x) : ab[e].x;
-            const float up = key_upper(l[e], info.rcp, gh);
-            spx = spx || __builtin_amdgcn_class(up, 0x207);       // NaN or infinite
-            const float pk = __uint_as_float((__float_as_uint(up) & ~7u) | (uint32_t)e);
+            // the estimate fma(l, RN(1/T), bound); its margin for the
+            // roundings and the packed index is added once per row (see
+            // slack_up), as it grows with the estimate
+            const float hi = __builtin_fmaf(l[e], info.rcp, gh);
+            spx = spx || __builtin_amdgcn_class(hi, 0x207);       // NaN or infinite
+            const float pk = __uint_as_float((__float_as_uint(hi) & ~7u) | (uint32_t)e);
             x2 = __builtin_amdgcn_fmed3f(x1, x2, pk);
             x1 = __builtin_amdgcn_fmed3f(x1, pk, pinf);   // max, no canonicalising
           }
@@ -980,14 +1024,19 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     float thr = -INFINITY;
     if (!fb && top2 && st.id != NONE) {
       key = key_exact(st.l, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)st.id)));
-      if (!(key > st.v2)) {
+      const float v2u = slack_up(st.v2);
+      if (!(key > v2u)) {
         // not certified: some other element's bound reaches the key. If a
         // key already published for this row (by another workgroup) lies
         // above that bound, no element here but the top one can win, and
         // the top one is published below; else re-scan the row.
-        const unsigned long long cur =
-            __hip_atomic_load(slots_cur + rr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!((uint32_t)(cur >> 32) > (uint32_t)(pack_winner(st.v2, 0) >> 32))) {
+        unsigned long long cur = 0ull;
+        for (int q = 0; q < SG; ++q) {
+          const unsigned long long c =
+              __hip_atomic_load(slots_step + (size_t)q * rows + rr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          cur = c > cur ? c : cur;
+        }
+        if (!((uint32_t)(cur >> 32) > (uint32_t)(pack_winner(v2u, 0) >> 32))) {
           fb = true;
           thr = key;
         }
@@ -1002,13 +1051,19 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
                              __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // 6. fallback rows, one per wave at a time: the wave re-reads the row's
   //    cached logits over the workgroup's slabs and takes the exact key of
   //    every element whose bound reaches the threshold (all of them for a
-  //    row with a non-finite estimate).
+  //    row with a non-finite estimate). Only then does the workgroup wait
+  //    for its cache stores (they are read back); otherwise they drain as
+  //    the kernel ends.
   const int nfb = misc[16];
+  if (nfb > 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
   const int wg_slabs = (int)blockIdx.x < nslabs ? (nslabs - (int)blockIdx.x + G - 1) / G : 0;
   for (int f = wave; f < nfb; f += NWV) {
     const int n = fb_row[f];
@@ -1114,16 +1169,17 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
 
 }
 
-// After the last step: its winners become tokens[:, k-1], and all three
-// slot buffers are left zeroed for the next call.
+// After the last step: its winners (the largest over the slot groups)
+// become tokens[:, k-1], and all slot buffers are left zeroed for the next
+// call.
 __global__ __launch_bounds__(256) void markov_finish_kernel(unsigned long long* slots, int64_t* tokens,
                                                             int rows, int k) {
   for (int r = threadIdx.x; r < rows; r += 256) {
-    const unsigned long long w = slots[(size_t)((k - 1) % 3) * rows + r];
+    const unsigned long long* last = slots + (size_t)((k - 1) % 3) * SG * rows + r;
+    unsigned long long w = 0ull;
+    for (int q = 0; q < SG; ++q) w = last[(size_t)q * rows] > w ? last[(size_t)q * rows] : w;
     tokens[(int64_t)r * k + k - 1] = slot_token(w);
-    slots[r] = 0ull;
-    slots[(size_t)rows + r] = 0ull;
-    slots[(size_t)2 * rows + r] = 0ull;
+    for (int q = 0; q < 3 * SG; ++q) slots[(size_t)q * rows + r] = 0ull;
   }
 }
 
@@ -1411,7 +1467,7 @@ int launch_grid(StepFn fn, size_t lds, int nslabs, int S, int* grid) {
   return MARKOV_OK;
 }
 
-size_t ws_bytes(int rows) { return (size_t)WS_SLOTS + (size_t)rows * 8 * 3; }
+size_t ws_bytes(int rows) { return (size_t)WS_SLOTS + (size_t)rows * 8 * 3 * SG; }
 
 int launch_steps(int mode, const void* base, const void* w1, const void* w2, const int64_t* prev,
                  const int64_t* seeds, const int64_t* positions, int32_t k, int32_t s_begin,
