@@ -505,6 +505,9 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   constexpr int S = RG == 1 ? 2 : 1;                     // waves splitting one SIMD's slabs
   constexpr bool ROWREG = MRB <= 4;                      // row constants in registers
   constexpr bool LIN = RG == 1;                          // the line bound (else the constant)
+  // lanes carry their top element's cached logit (one word per row block;
+  // the two-row-group plans have no registers to spare and read it back)
+  constexpr bool CARRY = RG == 1;
   constexpr uint32_t TB = LIN ? GT_BYTES : GTC_BYTES;    // the table this plan copies to LDS
   extern __shared__ __align__(16) unsigned char lds[];
   // the transform table sits at LDS address 0 only if the dynamic array
@@ -684,7 +687,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   float v1[MRB], v2[MRB];
   int idt[MRB];
   bool sp[MRB];
-  uint32_t lw[MRB];   // noisy rows: the word of cached logits holding the top element's
+  uint32_t lw[CARRY ? MRB : 1];   // noisy rows: the word of cached logits holding the top element's
 
   unsigned long long* slots_step = bias_mode ? nullptr : a.slots + (size_t)(s % 3) * SG * rows;
   unsigned long long* slots_cur = bias_mode ? nullptr : slots_step + (size_t)(blockIdx.x % SG) * rows;
@@ -746,7 +749,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     v2[j] = -INFINITY;
     idt[j] = NONE;
     sp[j] = false;
-    lw[j] = 0u;
+    if (CARRY) lw[CARRY ? j : 0] = 0u;
   }
   // everything but the tiles requested after the gather: the embeddings
   // (every wave's, hence the barrier), the table, base logits and a first
@@ -910,8 +913,10 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
           }
           if (x1 != x1b) {
             idt[j] = tg;
-            const uint32_t e1 = __float_as_uint(x1);
-            lw[j] = (e1 & 4u) ? ((e1 & 2u) ? cw[3] : cw[2]) : ((e1 & 2u) ? cw[1] : cw[0]);
+            if (CARRY) {
+              const uint32_t e1 = __float_as_uint(x1);
+              lw[CARRY ? j : 0] = (e1 & 4u) ? ((e1 & 2u) ? cw[3] : cw[2]) : ((e1 & 2u) ? cw[1] : cw[0]);
+            }
           }
           v1[j] = x1;
           v2[j] = x2;
@@ -966,7 +971,8 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     if (EXACT) st.id = idt[j];
     else if (idt[j] == NONE) st.id = NONE;
     else st.id = idt[j] + (int)((noisy ? __float_as_uint(v1[j]) : __float_as_uint(v2[j])) & 7u);
-    st.l = (__float_as_uint(v1[j]) & 1u) ? bf_hi(lw[j]) : bf_lo(lw[j]);
+    st.l = 0.0f;
+    if (CARRY) st.l = (__float_as_uint(v1[j]) & 1u) ? bf_hi(lw[CARRY ? j : 0]) : bf_lo(lw[CARRY ? j : 0]);
     const bool top2 = noisy && !EXACT;
 #pragma unroll
     for (int sh = 16; sh <= 32; sh <<= 1) {
@@ -982,9 +988,15 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     fin[j] = st;
   }
   // every wave past its last contraction (the states go over the
-  // embeddings); the cache stores drain meanwhile (the barrier before the
-  // fallback scans, which read them back, waits for them)
-  lds_barrier();
+  // embeddings); with carried logits the cache stores drain meanwhile (the
+  // barrier before the fallback scans, which read them back, waits for
+  // them), else they are read back below and waited for here
+  if (CARRY) {
+    lds_barrier();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
   float* st_v1 = (float*)emb;
   float* st_v2 = st_v1 + NWV * rp;
   int* st_id = (int*)(st_v2 + NWV * rp);
@@ -1008,22 +1020,33 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     const RowInfo info = n_info[n];
     const bool noisy = !(info.T == 0.0f);
     const bool top2 = noisy && !EXACT;
+    // the row's wave states, all loads issued before the first merge
+    constexpr int NS = RG == 1 ? NWV : 4;
     const int w0 = RG == 1 ? 0 : 4 * ((n >> 4) & 1);
-    const int w1n = RG == 1 ? NWV : w0 + 4;
-    RowState st = {st_v1[w0 * rp + n], st_v2[w0 * rp + n], st_id[w0 * rp + n], st_sp[w0 * rp + n],
-                   st_l[w0 * rp + n]};
-    for (int w = w0 + 1; w < w1n; ++w) {
-      const int i = w * rp + n;
-      RowState o = {st_v1[i], st_v2[i], st_id[i], st_sp[i], st_l[i]};
-      if (top2) merge_top2(st, o);
-      else merge_order(st, o);
+    RowState o[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+      const int i = (w0 + q) * rp + n;
+      o[q] = RowState{st_v1[i], st_v2[i], st_id[i], st_sp[i], st_l[i]};
+    }
+    RowState st = o[0];
+#pragma unroll
+    for (int q = 1; q < NS; ++q) {
+      if (top2) merge_top2(st, o[q]);
+      else merge_order(st, o[q]);
     }
     const int rr = n_row[n];
     float key = st.v1;
     bool fb = !EXACT && (st.sp != 0 || (mode == MODE_SAMPLE_FALLBACK && noisy));
     float thr = -INFINITY;
     if (!fb && top2 && st.id != NONE) {
-      key = key_exact(st.l, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)st.id)));
+      float l1 = st.l;
+      if (!CARRY) {
+        const size_t e = (size_t)info.rk * V + st.id;
+        const uint32_t wd = load_cache_word(a.cache, e & ~(size_t)1);
+        l1 = (e & 1) ? bf_hi(wd) : bf_lo(wd);
+      }
+      key = key_exact(l1, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)st.id)));
       const float v2u = slack_up(st.v2);
       if (!(key > v2u)) {
         // not certified: some other element's bound reaches the key. If a
