@@ -191,6 +191,11 @@ __host__ __device__ __forceinline__ float noise_lb(uint32_t h) {
   return (float)log((double)(-L));
 }
 
+// key_exact(l, T, h) is NaN exactly for these (its noise term is finite)
+__device__ __forceinline__ bool key_is_nan(float l, float T) {
+  return __builtin_isnan(l) || __builtin_isnan(T) || (__builtin_isinf(l) && __builtin_isinf(T));
+}
+
 __device__ __forceinline__ float key_exact(float l, float T, uint32_t h) {
   const float lb = noise_lb(h);
   float q = l / T;
@@ -1096,6 +1101,11 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     const int rr = n_row[n];
     float bv = -INFINITY;
     int bi = NONE;
+    // once some element of the row has a NaN key (a NaN logit or
+    // temperature, or an infinite logit over an infinite temperature; the
+    // noise term is always finite), only the lowest such id can win, and no
+    // other key is needed
+    bool nan_mode = false;
     // the lane's words, FB_BATCH loads in flight at a time
     const int nq = wg_slabs * (SLAB / 2);
     for (int q0 = 0; q0 < nq; q0 += 64 * FB_BATCH) {
@@ -1113,6 +1123,15 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       float cl0 = 0.0f, cl1 = 0.0f;
       uint32_t ch0 = 0u, ch1 = 0u;
       const bool screen = noisy && !(thr == -INFINITY);
+      if (noisy && !screen) {
+        bool any_nan = false;
+#pragma unroll
+        for (int b = 0; b < FB_BATCH; ++b) {
+          if (t0[b] >= V) continue;
+          any_nan = any_nan || key_is_nan(bf_lo(wd[b]), info.T) || key_is_nan(bf_hi(wd[b]), info.T);
+        }
+        nan_mode = nan_mode || __any(any_nan);
+      }
 #pragma unroll
       for (int b = 0; b < FB_BATCH; ++b) {
         if (t0[b] >= V) continue;
@@ -1135,7 +1154,11 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
               ++nc;
             }
           } else {
-            const float key = noisy ? key_exact(l, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)t))) : l;
+            float key = l;
+            if (noisy && nan_mode)
+              key = key_is_nan(l, info.T) ? __builtin_nanf("") : -INFINITY;
+            else if (noisy)
+              key = key_exact(l, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)t)));
             if (before(key, t, bv, bi)) {
               bv = key;
               bi = t;
