@@ -2,7 +2,7 @@
 """Throughput of the Markov draft-sampling loop on one MI355X.
 
 One bench "step" is one k-step loop (markov_sample_sequential: one step
-kernel per draft step plus one small finishing kernel) over the workload's
+kernel launch per draft step; the last one also writes the last tokens) over the workload's
 synthetic inputs, which are resident in HBM before timing starts. `value` is
 draft steps per second (k per loop) of the headline mode, plain launches
 (eager); the same loop captured once as a HIP graph and replayed is reported
@@ -155,7 +155,7 @@ def main():
     d = workloads.to_device(w, dev)
     call = m.prepare(w, d)
     step_calls = [m.prepare(w, d, step=s) for s in range(w.k)]
-    launches = w.k + 1                       # k step kernels and the finishing kernel
+    launches = w.k                           # one step kernel per draft step
 
     for _ in range(max(1, args.warmup)):
         call()
@@ -178,7 +178,7 @@ def main():
     value = w.k / (head_wall * 1e-6)
 
     # the step kernel alone: events around each step-kernel launch of eager
-    # loops (the last step's launch also carries the finishing kernel, so it
+    # loops (the last step's launch also turns the winners into tokens, so it
     # is left out of the average)
     n2 = max(1, min(args.steps, 50))
     timed = [s for s in range(w.k) if s < w.k - 1] or [0]

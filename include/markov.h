@@ -82,6 +82,8 @@ int32_t markov_max_rows(int32_t rank);
  *     32768 bf16 entries, entry i holding the cached value of the bf16 sum
  *     whose bits are i (the transform is odd, so negative sums take the
  *     entry of their magnitude with the sign flipped);
+ *   - a 256-byte block holding the last step's completion count (zero
+ *     between calls);
  *   - the winner slots: for each of three steps in turn, 8 per-row arrays of
  *     packed (key, id) maxima (workgroups publish into 8 groups; a step's
  *     winner is the largest over them), 192 bytes per row. */
@@ -133,9 +135,9 @@ int markov_sample_sequential(const void* base_logits, const void* w1, const void
 /*
  * Step `step` (0 <= step < k) of the same loop alone: one kernel launch that
  * feeds on prev (step 0) or on the previous step's winners (kept in the
- * workspace), writes cache[:, step, :] and tokens[:, step-1]; for the last
- * step (step = k-1) a second, small launch also writes tokens[:, k-1] and
- * re-zeroes the workspace. Arguments and errors as markov_sample_sequential;
+ * workspace), writes cache[:, step, :] and tokens[:, step-1]; the launch of
+ * the last step (step = k-1) also writes tokens[:, k-1] and re-zeroes the
+ * workspace's slots. Arguments and errors as markov_sample_sequential;
  * calling it for step = 0..k-1 in order is that loop.
  */
 int markov_sample_step(const void* base_logits, const void* w1, const void* w2,

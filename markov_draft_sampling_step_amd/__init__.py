@@ -239,7 +239,9 @@ def debug_bf16_round(x, out, stream=None):
 # The workspace starts with the noise bound tables: 2176 (A, B) float32
 # pairs (the per-bucket lines), then 2112 float32 constants (each bucket's
 # largest noise plus 1e-5); then the output-transform table (a 256-byte
-# stamp, 32768 bf16 entries); the per-row slot arrays follow.
+# stamp, 32768 bf16 entries); then a 256-byte block with the last step's
+# completion count and the per-row slot arrays, both zero between calls
+# (TABLES_BYTES is where that zero part starts).
 TABLE_PAIRS_BYTES = 2176 * 8
 NOISE_TABLES_BYTES = TABLE_PAIRS_BYTES + 2112 * 4
 TRANSFORM_STAMP_BYTES = 256

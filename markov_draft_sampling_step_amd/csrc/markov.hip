@@ -76,6 +76,7 @@ struct StepArgs {
   uint16_t* cache;
   int64_t* tokens;
   unsigned long long* slots;  // [3][SG][rows] packed winners, step s uses s % 3
+  unsigned int* ticket;       // workgroups of the last step done so far (zero between calls)
   const float* gtable;        // the noise bound table (in the workspace)
   const uint32_t* ttable;     // the transform table's stamp, then its 32768 entries
   uint16_t* bias_out;
@@ -240,7 +241,8 @@ constexpr uint32_t TT_MAGIC = 0x4d545431u;
 constexpr uint32_t TT_HEAD = 256;          // stamp: magic, bits(mult), bits(cap), then zeros
 constexpr uint32_t TT_BYTES = 65536;       // 32768 bf16 entries, index |x|
 constexpr uint32_t WS_TT = TABLES_BYTES;   // workspace offset of the stamp
-constexpr uint32_t WS_SLOTS = WS_TT + TT_HEAD + TT_BYTES;   // the slot arrays follow
+constexpr uint32_t WS_TICKET = WS_TT + TT_HEAD + TT_BYTES;  // the last step's completion count
+constexpr uint32_t WS_SLOTS = WS_TICKET + 256;              // the slot arrays follow
 
 __device__ __forceinline__ uint32_t gt_index(float fh) {
   return __builtin_elementwise_sub_sat(__float_as_uint(fh) >> 17, (uint32_t)GT_BASE);
@@ -474,7 +476,7 @@ __device__ __forceinline__ void merge_top2(RowState& a, const RowState& b) {
 //   region0         embeddings [rp][R] bf16; after the slab loop the waves'
 //                   row states [5][NWV][rp] (v1, v2, id, sp, l)
 //   info [rp] RowInfo, n_row [rp], n_src [rp], fb_row [rp], fb_thr [rp],
-//   misc [64] (per-wave row counts, fallback count)
+//   misc [64] (per-wave row counts, fallback count, last-workgroup flag)
 __host__ __device__ __forceinline__ size_t region0_bytes(int rp, int R) {
   const size_t e = (size_t)rp * R * 2, st = (size_t)NWV * rp * 20;
   return e > st ? e : st;
@@ -1213,19 +1215,38 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
                              __HIP_MEMORY_SCOPE_AGENT);
   }
 
-}
-
-// After the last step: its winners (the largest over the slot groups)
-// become tokens[:, k-1], and all slot buffers are left zeroed for the next
-// call.
-__global__ __launch_bounds__(256) void markov_finish_kernel(unsigned long long* slots, int64_t* tokens,
-                                                            int rows, int k) {
-  for (int r = threadIdx.x; r < rows; r += 256) {
-    const unsigned long long* last = slots + (size_t)((k - 1) % 3) * SG * rows + r;
-    unsigned long long w = 0ull;
-    for (int q = 0; q < SG; ++q) w = last[(size_t)q * rows] > w ? last[(size_t)q * rows] : w;
-    tokens[(int64_t)r * k + k - 1] = slot_token(w);
-    for (int q = 0; q < 3 * SG; ++q) slots[(size_t)q * rows + r] = 0ull;
+  // 7. the last step: the workgroup that finishes last turns the winners into
+  //    tokens[:, k-1] and leaves every slot and the ticket zeroed for the next
+  //    call. The slots and the ticket are only ever read or written by
+  //    device-scope atomics, which are performed at one point for the whole
+  //    device; each workgroup takes its ticket only after its own slot
+  //    atomics have completed (vmcnt(0)), so the one that takes the last
+  //    ticket reads final values. Nothing waits on another workgroup.
+  if (s == K - 1) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      misc[17] = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                         (unsigned)G - 1u
+                     ? 1
+                     : 0;
+    __syncthreads();
+    if (misc[17]) {
+      unsigned long long* fin_slots = a.slots + (size_t)(s % 3) * SG * rows;
+      for (int r2 = tid; r2 < rows; r2 += NTH) {
+        unsigned long long w = 0ull;
+#pragma unroll
+        for (int q = 0; q < SG; ++q) {
+          const unsigned long long c = __hip_atomic_exchange(fin_slots + (size_t)q * rows + r2, 0ull,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          w = c > w ? c : w;
+        }
+        a.tokens[(int64_t)r2 * K + K - 1] = slot_token(w);
+      }
+      for (int i = tid; i < 3 * SG * rows; i += NTH)
+        if (i / (SG * rows) != s % 3) a.slots[i] = 0ull;
+      if (tid == 0) __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -1546,6 +1567,7 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
     a.gtable = (const float*)workspace;
     a.ttable = (const uint32_t*)((unsigned char*)workspace + WS_TT);
     a.slots = (unsigned long long*)((unsigned char*)workspace + WS_SLOTS);
+    a.ticket = (unsigned int*)((unsigned char*)workspace + WS_TICKET);
   }
   a.tt_layout = tt_layout ? 1 : 0;
   a.rows = sh->rows;
@@ -1562,11 +1584,6 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   for (int s = s_begin; s < s_end; ++s) {
     a.step = s;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(NTH), lds, (hipStream_t)stream, a);
-    if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
-  }
-  if (mode != MODE_BIAS && s_end == k) {
-    hipLaunchKernelGGL(markov_finish_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, a.slots,
-                       tokens, sh->rows, k);
     if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   }
   return MARKOV_OK;
@@ -1620,7 +1637,7 @@ int markov_workspace_init(void* workspace, size_t bytes, const markov_shape_t* s
   } else if (hipMemsetAsync(ws + WS_TT, 0, TT_HEAD, st) != hipSuccess) {   // no stamp
     return MARKOV_ERR_HIP;
   }
-  if (hipMemsetAsync(ws + WS_SLOTS, 0, bytes - WS_SLOTS, st) != hipSuccess) return MARKOV_ERR_HIP;
+  if (hipMemsetAsync(ws + WS_TICKET, 0, bytes - WS_TICKET, st) != hipSuccess) return MARKOV_ERR_HIP;
   return MARKOV_OK;
 }
 

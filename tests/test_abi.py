@@ -61,10 +61,11 @@ def test_max_rows_and_workspace(lib):
         assert m.why_not(mr, 4096, R, 3) is None
         assert "LDS" in m.why_not(mr + 1, 4096, R, 3)
     # the noise bound tables (25856 bytes), the transform table (a 256-byte
-    # stamp, 32768 bf16 entries) and three per-row slot arrays
+    # stamp, 32768 bf16 entries), the ticket block (256 bytes) and three
+    # steps' eight per-row slot arrays
     assert m.NOISE_TABLES_BYTES == 25856
     assert m.TABLES_BYTES == 25856 + 256 + 65536
-    assert m.workspace_bytes(64, 163840, 256, 5) == m.TABLES_BYTES + 64 * 8 * 3 * 8
+    assert m.workspace_bytes(64, 163840, 256, 5) == m.TABLES_BYTES + 256 + 64 * 8 * 3 * 8
     assert m.workspace_bytes(0, 163840, 256, 5) == 0
     assert m.workspace_bytes(4, 100, 256, 5) == 0        # vocab not a multiple of 8
 
@@ -104,7 +105,7 @@ def test_host_errors_before_any_device_work(lib):
     assert _call(lib, sh, good, k=0) == -2
     assert _call(lib, m.make_shape(2, 4096, 40), good) == -3
     assert _call(lib, m.make_shape(300, 4096, 256), good) == -5
-    assert _call(lib, sh, good, ws_bytes=m.TABLES_BYTES + 2 * 24 * 8 - 1) == -6
+    assert _call(lib, sh, good, ws_bytes=m.TABLES_BYTES + 256 + 2 * 24 * 8 - 1) == -6
     for i in range(10):
         bad = list(good)
         bad[i] = 0
