@@ -3,6 +3,11 @@
   python -m markov_draft_sampling_step_amd.rocprof_summary stats DIR
       per-kernel calls / average / min / max duration from *_kernel_stats.csv
 
+  python -m markov_draft_sampling_step_amd.rocprof_summary counters DIR --elements N
+      per-dispatch counter means of one --pmc run and clock-free ratios
+      (VALU lane-instructions per element, VALU share of wave time, LDS
+      bank-conflict stalls per LDS quad-cycle)
+
   python -m markov_draft_sampling_step_amd.rocprof_summary traffic \\
       --fetch DIR --write DIR --copy-bytes N [--kernel markov_step_kernel]
       DRAM bytes per dispatch of the kernel from two --pmc runs (FETCH_SIZE,
@@ -81,9 +86,48 @@ def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, kernel: str) -> str
     ])
 
 
+def counters(d: str, kernel: str, elements: int) -> str:
+    """Per-dispatch means of every counter of one --pmc run for the kernel,
+    and three ratios that need no clock: VALU lane-instructions per (row,
+    token) element (SQ_INSTS_VALU counts wave64 instructions), the share of
+    wave time spent issuing VALU work (SQ_ACTIVE_INST_VALU over
+    SQ_WAVE_CYCLES, both quad-cycles summed over waves), and LDS cycles
+    stalled by bank conflicts per LDS-active quad-cycle."""
+    path = _one(os.path.join(d, "**", "*counter_collection.csv"))
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if kernel in r["Kernel_Name"]:
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id") or ""
+            per.setdefault(r["Counter_Name"], {}).setdefault(key, 0.0)
+            per[r["Counter_Name"]][key] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{path}: no rows for a kernel named *{kernel}*")
+    mean = {c: statistics.mean(v.values()) for c, v in per.items()}
+    n = len(next(iter(per.values())))
+    out = [f"{kernel}: {n} dispatches; per-dispatch means (summed over the device):"]
+    out += [f"  {c:28s} {mean[c]:16.1f}" for c in sorted(mean)]
+    if "SQ_INSTS_VALU" in mean and elements > 0:
+        out.append(f"VALU lane-instructions per element = {mean['SQ_INSTS_VALU'] * 64 / elements:.2f} "
+                   f"({elements} elements per dispatch)")
+    if "SQ_INSTS_MFMA" in mean and "SQ_WAVES" in mean:
+        out.append(f"MFMA instructions per wave = {mean['SQ_INSTS_MFMA'] / mean['SQ_WAVES']:.1f}")
+    if "SQ_ACTIVE_INST_VALU" in mean and "SQ_WAVE_CYCLES" in mean:
+        out.append(f"VALU-issuing share of wave time = "
+                   f"{mean['SQ_ACTIVE_INST_VALU'] / mean['SQ_WAVE_CYCLES']:.3f}")
+    if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_ACTIVE_INST_LDS" in mean:
+        out.append(f"LDS bank-conflict cycles per LDS-active quad-cycle = "
+                   f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_ACTIVE_INST_LDS']:.3f}")
+    out.append(f"kernel_source_sha256 = {hashlib.sha256(open(KERNEL_SOURCE, 'rb').read()).hexdigest()}")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--kernel", default="markov_step_kernel")
+    c.add_argument("--elements", type=int, default=0, help="(row, token) elements per dispatch")
     a = sub.add_parser("stats")
     a.add_argument("dir")
     b = sub.add_parser("traffic")
@@ -94,6 +138,8 @@ def main():
     args = ap.parse_args()
     if args.cmd == "stats":
         print(stats(args.dir))
+    elif args.cmd == "counters":
+        print(counters(args.dir, args.kernel, args.elements))
     else:
         print(traffic(args.fetch, args.write, args.copy_bytes, args.kernel))
 
