@@ -21,9 +21,14 @@
 //     bounds of its row; the workgroup takes one exact key (binary64 logs,
 //     IEEE division) per row, for the element with the largest bound, and
 //     only re-scans a row when another bound reaches that key;
+//   * with a soft cap, the output transform is looked up in a host-built
+//     table of all 32768 bf16 magnitudes (the transform is odd), copied to
+//     LDS address 0;
 //   * per-row winners go out as one packed (order-preserving key, ~id)
-//     64-bit atomicMax per row per workgroup; the next step's kernel decodes
-//     them (no fences: the kernel boundary orders the steps).
+//     64-bit atomicMax per row per workgroup, into one of 8 slot groups; the
+//     next step's kernel decodes the largest (no fences: the kernel boundary
+//     orders the steps), and in the last step the workgroup that takes the
+//     last device-scope ticket writes the last tokens. One launch per step.
 //
 // The definition followed is stated in include/markov.h, with the pages it
 // comes from (vLLM Markov-drafter API pages: kimi_k3 `_gumbel_key` and the
