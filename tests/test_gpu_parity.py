@@ -285,6 +285,31 @@ def test_workspace_reuse_is_deterministic(dev):
     assert not ws[m.TABLES_BYTES:].any(), "slots must be left zeroed"
 
 
+def test_workspace_shared_across_loops_of_different_k(dev):
+    """One workspace serves loops of k = 3, 1 and 2 in turn (its slots and the
+    last step's ticket are left zeroed by every loop): each loop gives the
+    bits it gives on a fresh workspace of its own."""
+    shared = None
+    for k, seed in ((3, 41), (1, 42), (2, 43), (3, 44)):
+        w = custom(V=2056, R=64, rows=33, k=k, seed=seed, temps=(1.0, 0.0, 0.7), softcap=30.0)
+        d = workloads.to_device(w, dev)
+        workloads.run(w, d)
+        torch.cuda.synchronize()
+        c_ref, t_ref = workloads.fetch(d)
+        if shared is None:
+            shared = m.new_workspace(w.rows, w.V, w.R, w.k, device=dev, mult=w.mult, softcap=w.softcap)
+        d["workspace"] = shared
+        d["cache"].zero_()
+        d["tokens"].fill_(-1)
+        workloads.run(w, d)
+        torch.cuda.synchronize()
+        c, t = workloads.fetch(d)
+        assert np.array_equal(t, t_ref), k
+        assert np.array_equal(c, c_ref), k
+        assert not shared.cpu().numpy()[m.TABLES_BYTES:].any(), k
+    say("  shared workspace: k = 3, 1, 2, 3 match fresh workspaces")
+
+
 @pytest.mark.parametrize("args", [
     dict(V=4104, R=128, rows=70, k=3, seed=31, temps=(1.0, 0.0, 0.6)),
     dict(V=1000, R=32, rows=19, k=4, seed=32, temps=(0.0, 1.0)),
