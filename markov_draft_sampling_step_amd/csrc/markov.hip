@@ -973,7 +973,8 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   RowState fin[MRB];
 #pragma unroll
   for (int j = 0; j < MRB; ++j) {
-    if (j >= my_nrb) break;
+    fin[j] = RowState{-INFINITY, -INFINITY, NONE, 0, 0.0f};
+    if (j >= my_nrb) continue;   // uniform: the shuffles below run for the whole wave
     const int n = 16 * (wr + RG * j) + m;
     const bool noisy = !((ROWREG ? ri[ROWREG ? j : 0].T : n_info[n].T) == 0.0f);
     RowState st;
@@ -1764,8 +1765,9 @@ int markov_debug_copy(const void* src, void* dst, int64_t bytes, markov_stream_t
   if (bytes == 0) return MARKOV_OK;
   const int64_t n16 = bytes / 16;
   int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
   const int64_t want = (n16 + 255) / 256;
   const int64_t blocks = want < (int64_t)cus * 8 ? want : (int64_t)cus * 8;
   markov_copy_kernel<<<dim3((unsigned)blocks), 256, 0, (hipStream_t)stream>>>(
