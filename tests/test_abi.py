@@ -123,3 +123,15 @@ def test_host_errors_before_any_device_work(lib):
     bad = list(good)
     bad[9] += 8                                             # workspace must be 16-byte aligned
     assert _call(lib, sh, bad, ws_bytes=1 << 20) == -4
+
+
+def test_workspace_init_host_errors(lib):
+    """markov_workspace_init rejects a NULL, misaligned or too small workspace
+    before any device call (a NULL shape is allowed: no transform stamp)."""
+    P = ctypes.c_void_p
+    sh = m.make_shape(2, 4096, 32, 1.0, 30.0)
+    need = m.workspace_bytes(2, 4096, 32, 3)
+    assert lib.markov_workspace_init(None, need, ctypes.byref(sh), None) == -1
+    assert lib.markov_workspace_init(P(0x10008), need, ctypes.byref(sh), None) == -4
+    assert lib.markov_workspace_init(P(0x10000), 64, ctypes.byref(sh), None) == -6
+    assert lib.markov_workspace_init(P(0x10000), 64, None, None) == -6
