@@ -92,8 +92,8 @@ size_t markov_workspace_bytes(const markov_shape_t* shape, int32_t k);
 /* Prepare a workspace once after allocating it (enqueued on `stream`): the
  * noise bound tables are copied in, the transform table is built on the host
  * for shape->mult and shape->softcap (only with a soft cap; shape may be
- * NULL, then no transform table is stamped) and copied in, and the slot
- * arrays are zeroed. Every call of markov_sample_sequential leaves it so
+ * NULL, then no transform table is stamped) and copied in, and the ticket
+ * and the slot arrays are zeroed. Every call of markov_sample_sequential leaves it so
  * again, so it is reused as is; it must not be shared by two calls in flight
  * at once. 16-byte aligned. A call whose (mult, softcap) differ from the
  * stamp still gives the same results within the stated tolerance: it
