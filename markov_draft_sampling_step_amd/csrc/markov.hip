@@ -1294,7 +1294,7 @@ __global__ __launch_bounds__(256) void markov_copy_kernel(const u32x4_t* __restr
 // evaluation (every hash of a bucket narrower than that), and by 1e-5.
 float2 g_table[GT_PAD];
 float g_ctable[GTC_PAD];   // a constant bound per bucket
-bool g_table_ready = false;
+std::once_flag g_table_once;   // the tables are built once per process, by whichever thread comes first
 
 float up_to_float(double x) {
   float f = (float)x;
@@ -1318,8 +1318,7 @@ uint64_t bucket_first_h(int b) {
 
 float line_at(float2 ab, uint32_t h) { return fmaf(ab.y, (float)h, ab.x); }
 
-void build_table() {
-  if (g_table_ready) return;
+void build_table_once() {
   std::vector<float> n((size_t)GT_GRID + 1);
   std::vector<uint32_t> hs((size_t)GT_GRID + 1);
   for (int b = 0; b < GT_N; ++b) {
@@ -1362,8 +1361,9 @@ void build_table() {
   }
   for (int b = GT_N; b < GT_PAD; ++b) g_table[b] = make_float2(0.0f, 0.0f);   // unused
   for (int b = GT_N; b < GTC_PAD; ++b) g_ctable[b] = 0.0f;
-  g_table_ready = true;
 }
+
+void build_table() { std::call_once(g_table_once, build_table_once); }
 
 // ---- the transform table, host side: c(x) for x = +0 .. the largest bf16
 // pattern below the sign bit, with the same operations the kernel's own
@@ -1513,6 +1513,7 @@ struct LaunchCache {
 };
 LaunchCache g_cache[64];
 int g_cache_n = 0;
+std::mutex g_cache_mutex;   // host threads may launch concurrently
 
 // Workgroups to launch: one per CU (the kernel is sized for one resident
 // 8-wave workgroup), never more than there are slab pairs (one slab for each
@@ -1521,6 +1522,7 @@ int launch_grid(StepFn fn, size_t lds, int nslabs, int S, int* grid) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MARKOV_ERR_HIP;
   int cus = 0;
+  std::lock_guard<std::mutex> lock(g_cache_mutex);
   for (int i = 0; i < g_cache_n; ++i)
     if (g_cache[i].fn == fn && g_cache[i].device == dev && g_cache[i].lds == lds) cus = g_cache[i].cus;
   if (cus == 0) {
