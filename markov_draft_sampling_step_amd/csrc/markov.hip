@@ -746,7 +746,10 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   // the two requests of the first tile exclude each other, waits for the
   // gather before the later one)
   __builtin_amdgcn_sched_barrier(0);
-  if (!tile_first)
+  // (one-tile waves that did not request their first tile above do so after
+  // the prologue's barrier: kept out of the burst the barrier waits on, it
+  // streams while the SIMD's first wave computes)
+  if (!tile_first && NB == 2)
     load_w2_tile<KB>(a.w2, V, R, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[0],
                      A1[0]);
   __builtin_amdgcn_sched_barrier(0);
@@ -768,10 +771,12 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   // tile requested before the gather (a count past the field's 63 waits for
   // more, never for less)
   constexpr int VM_FIRST = NB == 2 ? 2 * KB : 0;
-  constexpr int VM_AFTER = NB * 2 * KB < 63 ? NB * 2 * KB : 63;
+  constexpr int VM_AFTER = NB == 2 ? (NB * 2 * KB < 63 ? NB * 2 * KB : 63) : 0;
   if (tile_first) wait_vm<VM_FIRST>();
   else wait_vm<VM_AFTER>();
   lds_barrier();
+  if (!tile_first && NB == 1 && U > 0)
+    load_w2_tile<KB>(a.w2, V, R, slab0 * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[0], A1[0]);
 
   // one 32-token unit (the wave's unit i, slab `sl`) with w2 tile buffer BUF
   auto unit = [&](auto bufc, int i, int sl) {
