@@ -259,6 +259,16 @@ def test_ragged_and_edge_shapes(dev, args):
     run_and_check(w, dev)
 
 
+@pytest.mark.parametrize("R", [32, 256, 512])
+def test_max_rows(dev, R):
+    """The most rows each rank class takes (the LDS budget's limit): 512 at
+    R = 32 (one thread per row in the prologue), 272 at R = 256 and 144 at
+    R = 512 (the embeddings fill LDS; 16-block and 512-rank plans)."""
+    rows = m.max_rows(R)
+    assert m.why_not(rows, 2056, R, 2) is None
+    run_and_check(custom(V=2056, R=R, rows=rows, k=2, seed=50 + R, temps=(1.0, 0.0, 0.7)), dev)
+
+
 def test_exact_and_pruned_agree_small(dev):
     w = custom(V=2056, R=64, rows=33, k=4, seed=11, temps=(0.0, 1.0, 0.3))
     cg1, tg1, _ = run_and_check(w, dev)
