@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft steps/s + µs per k-step loop, V=163840 R=256; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "markov_draft_sampling_step_amd", "csrc", "markov.hip")
+KERNEL_SOURCE = os.path.join(ROOT, "markov_draft_sampling_step_amd", "csrc", "step_kernel.h")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "markov_step_kernel_{cfg}_traffic.txt")
 
 

@@ -1,5 +1,9 @@
 """Build ``libmarkov.so`` in-tree for gfx950 with hipcc.
 
+The step kernels of each rank class are compiled in a translation unit of
+their own (``csrc/step_kb*.hip``), in parallel, next to the host side
+(``csrc/markov.hip``); the objects are linked into one shared library.
+
 Flags: -ffp-contract=off so every rounding in the kernels is where the source
 writes it; packed-FP32 instructions are switched off for the device code
 (the host pass warns that it does not know the feature: harmless).
@@ -7,34 +11,56 @@ writes it; packed-FP32 instructions are switched off for the device code
 
 from __future__ import annotations
 
+import glob
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCE = os.path.join(HERE, "csrc", "markov.hip")
+CSRC = os.path.join(HERE, "csrc")
+OBJDIR = os.path.join(HERE, "_build")
 OUTPUT = os.path.join(HERE, "libmarkov.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-
-def command(output: str = OUTPUT):
-    return [
-        HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-        "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", os.path.join(ROOT, "include"), "-o", output, SOURCE,
-    ]
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = OUTPUT + ".tmp"
-    cmd = command(tmp)
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def compile_command(src: str, obj: str):
+    return [HIPCC, *FLAGS, "-c", "-o", obj, src]
+
+
+def link_command(objs, output: str = OUTPUT):
+    return [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", output, *objs]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed")
+        raise RuntimeError(f"hipcc failed: {' '.join(cmd)}")
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda so: _run(compile_command(*so), verbose), zip(srcs, objs)))
+    tmp = OUTPUT + ".tmp"
+    _run(link_command(objs, tmp), verbose)
     os.replace(tmp, OUTPUT)
     return OUTPUT
 

@@ -1,1265 +1,12 @@
-// MI355X (gfx950, CDNA4) DSpark sequential Markov draft-sampling step.
+// MI355X (gfx950) DSpark sequential Markov draft-sampling step: host side.
 //
-// One kernel launch per draft step; one 8-wave workgroup per CU. The
-// vocabulary is cut into 128-token slabs (four 32-token units, one per
-// SIMD); a workgroup owns the slabs blockIdx.x + G i, and the two waves on
-// each SIMD take every other one of them, so every SIMD gets the same share
-// of the vocabulary. Each wave handles all request rows of its units:
-//   * the rows' Markov embeddings w1[prev] sit in LDS (16-byte chunks,
-//     XOR-swizzled by row so the MFMA operand reads hit distinct banks);
-//   * each wave streams its unit's w2 rows from HBM once per step, straight
-//     into v_mfma_f32_16x16x32_bf16 A operands (16-byte loads, issued before
-//     anything else at kernel start and again as soon as a unit's last
-//     contraction has issued); tokens sit on the MFMA's M side in an order
-//     that leaves each lane with 8 consecutive tokens of one row, so the
-//     base read and the cache write are 16-byte vectors with no transpose;
-//   * the epilogue (bf16 bias, bf16 add, multiplier / soft cap, cache store)
-//     and the Gumbel noise run in registers. The noise is bounded, not
-//     computed: MurmurHash3 gives h, and a 2050-entry table in LDS, indexed
-//     by the exponent and top 6 mantissa bits of float(h), holds an upper
-//     bound of the noise over each bucket of h. A lane keeps the largest two
-//     bounds of its row; the workgroup takes one exact key (binary64 logs,
-//     IEEE division) per row, for the element with the largest bound, and
-//     only re-scans a row when another bound reaches that key;
-//   * with a soft cap, the output transform is looked up in a host-built
-//     table of all 32768 bf16 magnitudes (the transform is odd), copied to
-//     LDS address 0;
-//   * per-row winners go out as one packed (order-preserving key, ~id)
-//     64-bit atomicMax per row per workgroup, into one of 8 slot groups; the
-//     next step's kernel decodes the largest (no fences: the kernel boundary
-//     orders the steps), and in the last step the workgroup that takes the
-//     last device-scope ticket writes the last tokens. One launch per step.
-//
-// The definition followed is stated in include/markov.h, with the pages it
-// comes from (vLLM Markov-drafter API pages: kimi_k3 `_gumbel_key` and the
-// module's exactness paragraph; muse_spark cutedsl `_logit`, `_gumbel`,
-// `_murmur_prefix`, `_combine`, `_w1_row`, `markov_step`).
+// The step kernel itself is in step_kernel.h (compiled per rank class in
+// step_kb*.hip); this file holds the host-built tables, the launch code, the
+// test-only kernels and the C ABI of include/markov.h.
 
-#include <hip/hip_runtime.h>
-#include <math.h>
-#include <stdint.h>
-#include <string.h>
-
-#include <mutex>
-#include <type_traits>
-#include <vector>
-
-#include "markov.h"
+#include "step_kernel.h"
 
 namespace {
-
-constexpr int NWV = 8;                 // waves per workgroup (two per SIMD)
-constexpr int NTH = 64 * NWV;          // threads per workgroup
-constexpr int TOK_PER_WAVE = 32;       // two 16-token MFMA M tiles
-constexpr int SLAB = 4 * TOK_PER_WAVE; // one unit per SIMD
-constexpr int NONE = 0x7fffffff;       // id of "no element yet"
-constexpr int ROWS_CAP = NTH;          // the prologue gives every row one thread
-constexpr int MRB_MAX = 8;             // row blocks one wave keeps in registers
-constexpr int FB_BATCH = 8;            // cache words in flight per lane in a fallback scan
-constexpr int WAIT_VM0 = 0x0F70;       // s_waitcnt vmcnt(0), the other counters free (gfx9 encoding)
-constexpr size_t LDS_MAX = 160 * 1024;
-// Winner slot groups: workgroup b publishes into group b % SG, and a step's
-// winner is the largest value over the groups. Device-scope atomics on one
-// cache line are served one after another, so SG groups cut the queue on
-// each line SG-fold; the reader pays SG loads per row.
-constexpr int SG = 8;
-
-enum Mode { MODE_SAMPLE = 0, MODE_SAMPLE_EXACT = 1, MODE_BIAS = 2, MODE_SAMPLE_FALLBACK = 3 };
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-struct StepArgs {
-  const uint16_t* base;
-  const uint16_t* w1;
-  const uint16_t* w2;
-  const int64_t* prev;
-  const int64_t* seeds;
-  const int64_t* positions;
-  const float* temperature;
-  uint16_t* cache;
-  int64_t* tokens;
-  unsigned long long* slots;  // [3][SG][rows] packed winners, step s uses s % 3
-  unsigned int* ticket;       // workgroups of the last step done so far (zero between calls)
-  const float* gtable;        // the noise bound table (in the workspace)
-  const uint32_t* ttable;     // the transform table's stamp, then its 32768 entries
-  uint16_t* bias_out;
-  int rows, V, R, k, step, nslabs, mode;
-  int tt_layout;              // LDS holds the transform table at address 0
-  float mult, inv_cap, cap;
-  int has_cap;
-  float inf;                  // +infinity, opaque to the compiler (see the noise loop)
-};
-
-// ---------------------------------------------------------------- numbers
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Two binary32 -> one word of two bf16 (round to nearest even; one
-// hardware v_cvt_pk_bf16_f32), `a` in the low half.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
-}
-
-// ---------------------------------------------------------------- noise hash
-// MurmurHash3_x86_32 over the 16-byte message (lo32 S, hi32 S, lo32 P, id),
-// seed 0, S = seed ^ (step << 32), P = position - 1 + 2^30. The three
-// per-row words are folded once per row (`row_prefix`); the id word's
-// scramble depends on the token only and is shared by all rows.
-constexpr uint32_t MM_C1 = 0xcc9e2d51u, MM_C2 = 0x1b873593u;
-
-__device__ __forceinline__ uint32_t rotl32(uint32_t x, int r) { return (x << r) | (x >> (32 - r)); }
-
-__device__ __forceinline__ uint32_t mm_block(uint32_t h, uint32_t k) {
-  k *= MM_C1;
-  k = rotl32(k, 15);
-  k *= MM_C2;
-  h ^= k;
-  h = rotl32(h, 13);
-  return h * 5u + 0xe6546b64u;
-}
-
-__device__ __forceinline__ uint32_t mm_token_word(uint32_t id) {
-  uint32_t k = id * MM_C1;
-  k = rotl32(k, 15);
-  return k * MM_C2;
-}
-
-// h * 5 + c as a shift-add and an add (two full-rate ops; left to itself
-// the compiler picks a 64-bit multiply-add)
-__device__ __forceinline__ uint32_t times5_plus(uint32_t h, uint32_t c) {
-  uint32_t r;
-  asm("v_lshl_add_u32 %0, %1, 2, %1" : "=v"(r) : "v"(h));
-  return r + c;
-}
-
-// The last block and the finaliser, from the row prefix and the token word
-// both already rotated left by 13 (rotation distributes over xor, so the
-// block's rotation moves onto the two operands: once per row, and once per
-// token for all rows).
-__device__ __forceinline__ uint32_t mm_finish_rot(uint32_t prefix_rot, uint32_t token_word_rot) {
-  uint32_t h = prefix_rot ^ token_word_rot;
-  h = times5_plus(h, 0xe6546b64u);
-  h ^= 16u;                       // message length in bytes
-  h ^= h >> 16;
-  h *= 0x85ebca6bu;
-  h ^= h >> 13;
-  h *= 0xc2b2ae35u;
-  h ^= h >> 16;
-  return h;
-}
-
-__device__ __forceinline__ uint32_t mm_finish(uint32_t prefix, uint32_t token_word) {
-  return mm_finish_rot(rotl32(prefix, 13), rotl32(token_word, 13));
-}
-
-__device__ __forceinline__ uint32_t row_prefix_of(int64_t seed, int step, int64_t position) {
-  uint64_t S = (uint64_t)seed ^ ((uint64_t)(uint32_t)step << 32);
-  int64_t P = position - 1 + ((int64_t)1 << 30);
-  uint32_t h = mm_block(0u, (uint32_t)S);
-  h = mm_block(h, (uint32_t)(S >> 32));
-  return mm_block(h, (uint32_t)(uint64_t)P);
-}
-
-// u = RN32((h + 1/2) 2^-32): (lo16 + 1/2) 2^-32 is exact, and one fma adds
-// hi16 * 2^-16 with the only rounding.
-__host__ __device__ __forceinline__ float uniform_of(uint32_t h) {
-  float hi = (float)(h >> 16), lo = (float)(h & 0xffffu);
-  return __builtin_fmaf(hi, 0x1p-16f, __builtin_fmaf(lo, 0x1p-32f, 0x1p-33f));
-}
-
-// ---------------------------------------------------------------- keys
-// Exact key: RN32(RN32(l / T) - lb), lb = RN32(log(-L)), L = log(1 - u) in
-// the pages' stable form (a Horner series below u = 1/4, else a log of
-// max(1 - u, 2^-24)). Logs are taken in binary64 and rounded once.
-__host__ __device__ __forceinline__ float log1m_exact(float u) {
-  if (u < 0.25f) {
-    float p = 0.125f;
-    p = __builtin_fmaf(u, p, 1.0f / 7.0f);
-    p = __builtin_fmaf(u, p, 1.0f / 6.0f);
-    p = __builtin_fmaf(u, p, 1.0f / 5.0f);
-    p = __builtin_fmaf(u, p, 0.25f);
-    p = __builtin_fmaf(u, p, 1.0f / 3.0f);
-    p = __builtin_fmaf(u, p, 0.5f);
-    p = __builtin_fmaf(u, p, 1.0f);
-    return p * (-u);
-  }
-  float x = fmaxf(1.0f - u, 0x1p-24f);
-  return (float)log((double)x);
-}
-
-__host__ __device__ __forceinline__ float noise_lb(uint32_t h) {
-  const float L = log1m_exact(uniform_of(h));
-  return (float)log((double)(-L));
-}
-
-// key_exact(l, T, h) is NaN exactly for these (its noise term is finite)
-__device__ __forceinline__ bool key_is_nan(float l, float T) {
-  return __builtin_isnan(l) || __builtin_isnan(T) || (__builtin_isinf(l) && __builtin_isinf(T));
-}
-
-__device__ __forceinline__ float key_exact(float l, float T, uint32_t h) {
-  const float lb = noise_lb(h);
-  float q = l / T;
-  return q - lb;
-}
-
-// Noise bound table. Bucket b of h: b = 0 for h = 0, else
-// (bits(float(h)) >> 17) - 8127, i.e. the exponent and the top 6 mantissa
-// bits of the nearest binary32 to h (1 .. 2049; 2049 is h rounding to
-// 2^32). gtable[b] = (A, B) is a line in float(h) on or above the noise -lb
-// of every h in the bucket: RN32(fma(B, float(h), A)) >= -lb(h). The host
-// builds it from the chord of the noise over the bucket and lifts it by the
-// largest shortfall found on a grid of the bucket, plus 1e-5 (the noise and
-// the line both fall as h grows, so a shortfall between two grid points is
-// at most the line at the next point below the noise at this one). The
-// kernel's upper bound of an exact key is then
-//   hi = fma(l, RN(1/T), fma(B, float(h), A)),  up = fma(|hi|, 2^-19, hi)
-// (2^-19 |hi| covers the roundings of l / T, of the key and of hi, and the
-// 3-bit id the kernel packs into up's low bits). A second table holds a
-// constant bound per bucket, the largest noise on the bucket's grid plus
-// 1e-5 (the noise at its first h, as the noise falls with h): the plans with
-// two row groups use it, as the line's float(h) operand would cost them
-// registers they lack.
-constexpr int GT_BASE = 8127;
-constexpr int GT_N = 2050;
-constexpr int GT_PAD = 2176;               // stored pairs: 17 chunks of 1 KiB
-constexpr uint32_t GT_BYTES = GT_PAD * 8;
-constexpr int GTC_PAD = 2112;              // stored constants: 8.25 chunks of 1 KiB
-constexpr uint32_t GTC_BYTES = GTC_PAD * 4;
-constexpr uint32_t TABLES_BYTES = GT_BYTES + GTC_BYTES;   // both, at the workspace's start
-constexpr int GT_GRID = 1024;              // grid intervals per bucket in the host's check
-
-// Transform table. The output transform maps a bf16 x (the bf16 sum of base
-// and bias) to the cached bf16 c, and every step of it (the multiplier, the
-// scaling by RN(1/cap), tanh, the scaling by cap, the roundings) is odd, so
-// c(-x) = -c(x) bit for bit and the map is a table over the 32768 values of
-// |x|. The host fills it with correctly rounded arithmetic for one (mult,
-// cap) and stamps it with both; a kernel whose own (mult, cap) match the
-// stamp looks c up in LDS (two reads per word of two values, the sign put
-// back with one xor), else it evaluates the transform itself.
-constexpr uint32_t TT_MAGIC = 0x4d545431u;
-constexpr uint32_t TT_HEAD = 256;          // stamp: magic, bits(mult), bits(cap), then zeros
-constexpr uint32_t TT_BYTES = 65536;       // 32768 bf16 entries, index |x|
-constexpr uint32_t WS_TT = TABLES_BYTES;   // workspace offset of the stamp
-constexpr uint32_t WS_TICKET = WS_TT + TT_HEAD + TT_BYTES;  // the last step's completion count
-constexpr uint32_t WS_SLOTS = WS_TICKET + 256;              // the slot arrays follow
-
-__device__ __forceinline__ uint32_t gt_index(float fh) {
-  return __builtin_elementwise_sub_sat(__float_as_uint(fh) >> 17, (uint32_t)GT_BASE);
-}
-
-// the table's bound of the noise -lb(h): the line (LIN) or the constant
-template <bool LIN>
-__device__ __forceinline__ float noise_bound(const void* tab, uint32_t h) {
-  const float fh = (float)h;
-  if (LIN) {
-    const float2 ab = ((const float2*)tab)[gt_index(fh)];
-    return __builtin_fmaf(ab.y, fh, ab.x);
-  }
-  return ((const float*)tab)[gt_index(fh)];
-}
-
-__device__ __forceinline__ float key_upper(float l, float rcpT, float gh) {
-  const float hi = __builtin_fmaf(l, rcpT, gh);
-  return __builtin_fmaf(fabsf(hi), 0x1p-19f, hi);
-}
-
-// The slot loop keeps, per row, the largest estimates fma(l, RN(1/T), bound)
-// with the element's index in the low 3 bits, without key_upper's margin;
-// the margin, monotone in the estimate, is added to the kept value once.
-// 2^-18 |v| is at least 32 of v's ulps: the 2^-19 of key_upper plus the
-// packed bits and an estimate a binade above v.
-__device__ __forceinline__ float slack_up(float v) { return __builtin_fmaf(fabsf(v), 0x1p-18f, v); }
-
-// The total order of every argmax here: a NaN beats every non-NaN, lower
-// id among NaNs; otherwise the larger value, and equal values (so -0 == +0)
-// go to the lower id.
-__device__ __forceinline__ bool before(float v1, int i1, float v2, int i2) {
-  bool n1 = __builtin_isnan(v1), n2 = __builtin_isnan(v2);
-  return (v1 > v2) || (v1 == v2 && i1 < i2) || (n1 && (!n2 || i1 < i2));
-}
-
-// Order-preserving 64-bit image of (key, id) under that order: the high word
-// maps every NaN to the top and -0 to +0; the low word is ~id, so the lower
-// id of equal keys is the larger word. Zero is below every real element.
-__device__ __forceinline__ unsigned long long pack_winner(float v, int id) {
-  uint32_t o;
-  if (__builtin_isnan(v)) {
-    o = 0xffffffffu;
-  } else {
-    uint32_t b = __float_as_uint(v);
-    if (b == 0x80000000u) b = 0u;
-    o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  }
-  return ((unsigned long long)o << 32) | (unsigned long long)(uint32_t)(~(uint32_t)id);
-}
-
-// The winner slot of a row decodes to its token id.
-__device__ __forceinline__ int64_t slot_token(unsigned long long w) {
-  return (int64_t)(uint32_t)(~(uint32_t)w);
-}
-
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-// Workgroup barrier for LDS data only: this wave's LDS operations are
-// complete, then all waves meet. (__syncthreads also waits for every
-// outstanding global load, which would hold the prologue up on the w2 tiles
-// already in flight.) The asm keeps the compiler from moving memory
-// operations across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Wait until at most N vector memory operations of this wave are
-// outstanding (they complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// A cache word written by another wave of this workgroup (agent-coherent load).
-__device__ __forceinline__ uint32_t load_cache_word(const uint16_t* cache, size_t elem_even) {
-  return __hip_atomic_load((const uint32_t*)(cache + elem_even), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// ---------------------------------------------------------------- output transform
-// tanh for the soft cap: an odd minimax polynomial z + z^3 P(z^2) below
-// |z| = 0.625 (fitted here for binary32 Horner evaluation, within 0.7 ulp),
-// else 1 - 2 / (e^{2|z|} + 1) with the hardware exp2 and reciprocal (about
-// 2 ulp). The cache rounds the result to bf16.
-__device__ __forceinline__ float tanh_poly(float z) {
-  const float t = z * z;
-  float p = 0x1.18dc88p-9f;
-  p = __builtin_fmaf(p, t, -0x1.0bf272p-7f);
-  p = __builtin_fmaf(p, t, 0x1.638a82p-6f);
-  p = __builtin_fmaf(p, t, -0x1.b9ee7p-5f);
-  p = __builtin_fmaf(p, t, 0x1.111066p-3f);
-  p = __builtin_fmaf(p, t, -0x1.555554p-2f);
-  return __builtin_fmaf(t * z, p, z);
-}
-
-__device__ __forceinline__ float tanh_fast(float z) {
-  const float az = fabsf(z);
-  const float e = __builtin_amdgcn_exp2f(az * 2.88539008177792681f);
-  const float r = __builtin_amdgcn_rcpf(e + 1.0f);
-  const float yl = __builtin_copysignf(__builtin_fmaf(-2.0f, r, 1.0f), z);
-  return az < 0.625f ? tanh_poly(z) : yl;
-}
-
-// c of both bf16 values of word x from the transform table at LDS address
-// 0: entry |x| sits at byte 2 |x|, which one SDWA shift forms from either
-// half of x (the sign bit falls out of the 16-bit result).
-__device__ __forceinline__ uint32_t tt_addr_lo(uint32_t x) {
-  uint32_t r;
-  asm("v_lshlrev_b16_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_0"
-      : "=v"(r) : "v"(x));
-  return r;
-}
-
-__device__ __forceinline__ uint32_t tt_addr_hi(uint32_t x) {
-  uint32_t r;
-  asm("v_lshlrev_b16_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
-      : "=v"(r) : "v"(x));
-  return r;
-}
-
-typedef __attribute__((address_space(3))) const uint16_t lds_u16_t;
-
-__device__ __forceinline__ uint32_t tt_map(uint32_t x) {
-  const uint32_t lo = *(lds_u16_t*)(size_t)tt_addr_lo(x);
-  const uint32_t hi = *(lds_u16_t*)(size_t)tt_addr_hi(x);
-  return (lo | (hi << 16)) ^ (x & 0x80008000u);
-}
-
-// ---------------------------------------------------------------- tiles
-
-// The w2 rows of one 32-token unit as MFMA A operands: lane (g, m) holds
-// k-chunks 4i + g of tokens t0 = tok0 + 8 (m >> 2) + (m & 3) (A0) and t0 + 4
-// (A1); tokens past the vocabulary read its last row (never stored).
-// Ordinary (not nontemporal) loads: the table is read again by the next
-// step, and unmarked lines of it stay in the memory-side cache between steps
-// (measured: a nontemporal tile stream made the step about 5% slower).
-template <int KB>
-__device__ __forceinline__ void load_w2_tile(const uint16_t* w2, int V, int R, int tok0, int m, int g,
-                                             bool kzero, bf16x8_t* A0, bf16x8_t* A1) {
-  const int t0 = tok0 + 8 * (m >> 2) + (m & 3);
-  const int ta = t0 < V ? t0 : V - 1, tb = t0 + 4 < V ? t0 + 4 : V - 1;
-  const uint16_t* pa = w2 + (size_t)ta * R;
-  const uint16_t* pb = w2 + (size_t)tb * R;
-#pragma unroll
-  for (int i = 0; i < KB; ++i) {
-    if (kzero) {
-      A0[i] = (bf16x8_t){};
-      A1[i] = (bf16x8_t){};
-    } else {
-      const int ch = 4 * i + g;
-      A0[i] = *(const bf16x8_t*)(pa + ch * 8);
-      A1[i] = *(const bf16x8_t*)(pb + ch * 8);
-    }
-  }
-}
-
-// The bias of one 16-row block for the wave's 32 tokens: lane (g, m) gets
-// row n = 16 rb + m, tokens tg .. tg+3 in c0 and tg+4 .. tg+7 in c1.
-template <int KB>
-__device__ __forceinline__ void block_bias(const bf16x8_t* A0, const bf16x8_t* A1, const uint16_t* emb,
-                                           int n, int R, int g, int swz, bool kzero, f32x4_t& c0,
-                                           f32x4_t& c1) {
-  c0 = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  c1 = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < KB; ++i) {
-    bf16x8_t B;
-    if (kzero) {
-      B = (bf16x8_t){};
-    } else {
-      const int ch = 4 * i + g;
-      B = *(const bf16x8_t*)(emb + (size_t)n * R + ((ch ^ (n & swz)) * 8));
-    }
-    c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[i], B, c0, 0, 0, 0);
-    c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[i], B, c1, 0, 0, 0);
-  }
-}
-
-// Per LDS row n, one 16-byte record: rk = row * k + step (the row's slice of
-// base / cache starts at rk * V), 1/T, the hash prefix and T.
-struct RowInfo {
-  int rk;
-  float rcp;
-  uint32_t prefix;
-  float T;
-};
-
-// Merge rules of the per-row states. ORDER: the exact (key, id) under the
-// total order. TOP2: (v1, id) is the element with the largest upper bound
-// v1, v2 the largest upper bound among all other elements, l the logit of
-// element id (so its exact key needs no read of the cache). sp: some element
-// had a non-finite estimate (noisy rows) or a NaN / -inf logit (T = 0 rows).
-struct RowState {
-  float v1, v2;
-  int id;
-  int sp;
-  float l;
-};
-
-__device__ __forceinline__ void merge_order(RowState& a, const RowState& b) {
-  if (before(b.v1, b.id, a.v1, a.id)) {
-    a.v1 = b.v1;
-    a.id = b.id;
-    a.l = b.l;
-  }
-  a.sp |= b.sp;
-}
-
-__device__ __forceinline__ void merge_top2(RowState& a, const RowState& b) {
-  const bool bw = (b.v1 > a.v1) || (b.v1 == a.v1 && b.id < a.id);
-  const float lose = bw ? a.v1 : b.v1;
-  const float win2 = bw ? b.v2 : a.v2;
-  a.v2 = fmaxf(lose, win2);
-  if (bw) {
-    a.v1 = b.v1;
-    a.id = b.id;
-    a.l = b.l;
-  }
-  a.sp |= b.sp;
-}
-
-// LDS, all of it dynamic (the kernel declares no static LDS, so the dynamic
-// array starts at address 0):
-//   [tt]            with the transform-table layout, its 32768 entries (64 KiB)
-//                   at address 0, else nothing
-//   table           the noise bound table (lines or constants)
-//   region0         embeddings [rp][R] bf16; after the slab loop the waves'
-//                   row states [5][NWV][rp] (v1, v2, id, sp, l)
-//   info [rp] RowInfo, n_row [rp], n_src [rp], fb_row [rp], fb_thr [rp],
-//   misc [64] (per-wave row counts, fallback count, last-workgroup flag)
-__host__ __device__ __forceinline__ size_t region0_bytes(int rp, int R) {
-  const size_t e = (size_t)rp * R * 2, st = (size_t)NWV * rp * 20;
-  return e > st ? e : st;
-}
-
-__host__ __device__ __forceinline__ size_t lds_dynamic(int rp, int R) {
-  return region0_bytes(rp, R) + (size_t)rp * 16 + (size_t)rp * 16 + 64 * 4;
-}
-
-// the noise table in LDS: the lines for one row group (up to MRB_MAX row
-// blocks), the constants for two
-__host__ __device__ __forceinline__ size_t lds_table(int rp) { return (rp >> 4) > MRB_MAX ? GTC_BYTES : GT_BYTES; }
-
-__host__ __device__ __forceinline__ size_t lds_total(int rp, int R) { return lds_table(rp) + lds_dynamic(rp, R); }
-
-// the transform-table layout: one row group (the lines), a soft cap, and room
-__host__ __device__ __forceinline__ bool tt_fits(int rp, int R) {
-  return (rp >> 4) <= MRB_MAX && TT_BYTES + lds_total(rp, R) <= LDS_MAX;
-}
-
-// ---------------------------------------------------------------- the step
-//
-// KB = R / 32 (1 for R = 16 with half the chunks zero), RG row groups (1,
-// or 2 for more than 8 row blocks: then the two waves of a SIMD split the
-// rows, both take every slab of the workgroup and read its w2 tiles through
-// L2), MRB = row blocks per wave (a power of two, the wave's real count may
-// be lower), EXACT = the test-only variant that takes the exact key of
-// every element. One launch runs step a.step.
-template <int KB, int RG, int MRB, bool EXACT>
-__global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
-  constexpr int NB = MRB == 1 ? 2 : 1;                   // w2 tiles in flight per wave
-  constexpr int D = MRB - 1 < 3 ? MRB - 1 : 3;           // row blocks contracted ahead
-  constexpr int S = RG == 1 ? 2 : 1;                     // waves splitting one SIMD's slabs
-  constexpr bool ROWREG = MRB <= 4;                      // row constants in registers
-  constexpr bool LIN = RG == 1;                          // the line bound (else the constant)
-  // lanes carry their top element's cached logit (one word per row block;
-  // the two-row-group plans have no registers to spare and read it back)
-  constexpr bool CARRY = RG == 1;
-  constexpr uint32_t TB = LIN ? GT_BYTES : GTC_BYTES;    // the table this plan copies to LDS
-  extern __shared__ __align__(16) unsigned char lds[];
-  // the transform table sits at LDS address 0 only if the dynamic array
-  // starts there (no static LDS); its lookups form absolute addresses
-  const bool tt_lay = LIN && a.tt_layout != 0 &&
-                      (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds == 0u;
-  const uint32_t tt_off = tt_lay ? TT_BYTES : 0u;
-  float* const gtabf = (float*)(lds + tt_off);           // LIN: (A, B) pairs; else constants
-  float2* const gtab = (float2*)gtabf;
-  const int mode = a.mode;
-  const bool bias_mode = mode == MODE_BIAS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tw = wave & 3;
-  const int sub = RG == 1 ? wave >> 2 : 0;
-  const int wr = RG == 1 ? 0 : wave >> 2;
-  const int g = lane >> 4, m = lane & 15;
-  const int R = KB >= 2 ? 32 * KB : a.R;
-  const int rows = a.rows, rp = (rows + 15) & ~15, V = a.V, K = a.k;
-  const int s = a.step;
-  const int nslabs = a.nslabs, G = gridDim.x;
-  const int cpr = R >> 3;
-  const int swz = (cpr < 16 ? cpr : 16) - 1;
-  const int nrb = rp >> 4;
-  const int my_nrb = nrb > wr ? (nrb - wr + RG - 1) / RG : 0;
-  const int slab_step = G * S;
-  const int slab0 = blockIdx.x + G * sub;
-  const bool kzero = (KB == 1) && (R == 16) && (g >= 2);
-  // this wave's units per step: slabs slab0 + i slab_step whose 32 tokens
-  // start inside the vocabulary
-  int lim = (V - tw * TOK_PER_WAVE + SLAB - 1) / SLAB;
-  lim = lim < nslabs ? lim : nslabs;
-  const int U = (my_nrb > 0 && slab0 < lim) ? (lim - slab0 + slab_step - 1) / slab_step : 0;
-
-
-  uint16_t* emb = (uint16_t*)(lds + tt_off + TB);
-  const size_t r0 = region0_bytes(rp, R);
-  RowInfo* n_info = (RowInfo*)((unsigned char*)emb + r0);
-  int* n_row = (int*)(n_info + rp);
-  int* n_src = n_row + rp;
-  int* fb_row = n_src + rp;
-  float* fb_thr = (float*)(fb_row + rp);
-  int* misc = (int*)(fb_thr + rp);
-
-  // 0. this thread's request row: everything the first step needs, in one
-  //    round trip
-  const int r = tid;
-  const bool valid = r < rows;
-  float T = 0.0f;
-  int64_t tok = 0, seed = 0, pos = 0;
-  unsigned long long slot_in[SG];
-#pragma unroll
-  for (int q = 0; q < SG; ++q) slot_in[q] = 0ull;
-  if (valid) {
-    if (!bias_mode) {
-      T = a.temperature[r];
-      seed = a.seeds[r];
-      pos = a.positions[(int64_t)r * K + s];
-    }
-    // the feeding token: prev at step 0, else the previous step's winner
-    // slots (decoded after the wait below)
-    if (bias_mode || s == 0) {
-      tok = a.prev[r];
-    } else {
-      const unsigned long long* sp0 = a.slots + (size_t)((s + 2) % 3) * SG * rows + r;
-#pragma unroll
-      for (int q = 0; q < SG; ++q) slot_in[q] = sp0[(size_t)q * rows];
-    }
-  }
-  // the row data, waited for before the table copy is issued: a wait the
-  // compiler sees, so that no later use of a row register waits for the copy;
-  // the empty asm keeps every use of the four values (the row hash) below it,
-  // so that all four loads are issued before the one wait
-  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-  asm volatile("" : "+v"(T), "+v"(seed), "+v"(pos), "+v"(tok));
-  asm volatile("" : "+v"(slot_in[0]), "+v"(slot_in[1]), "+v"(slot_in[2]), "+v"(slot_in[3]),
-               "+v"(slot_in[4]), "+v"(slot_in[5]), "+v"(slot_in[6]), "+v"(slot_in[7]));
-  static_assert(SG == 8, "the asm above pins SG slot values");
-  // the noise bound table, straight into LDS: waited for with the first tile
-  // (before the unit loop), in flight through the row set-up
-  if (!bias_mode) {
-    for (int j = wave; j * 64 * 16 < (int)TB; j += NWV) {
-      const int p = j * 64 + lane;
-      if (p * 16 < (int)TB)
-        __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.gtable + (LIN ? 0 : GT_BYTES) +
-                                                       (size_t)p * 16),
-                                         (__attribute__((address_space(3))) void*)(gtabf + (size_t)j * 256),
-                                         16, 0, 0);
-    }
-  }
-  // everything the row set-up needs from the row data, before the tile loads
-  // below
-  const bool noisy_r = valid && !bias_mode && !(T == 0.0f);
-  const uint64_t bn = __ballot(noisy_r), bz = __ballot(valid && !noisy_r);
-  const float rcp_r = 1.0f / T;
-  const uint32_t prefix_r = (valid && !bias_mode) ? row_prefix_of(seed, s, pos) : 0u;
-  if (!(bias_mode || s == 0)) {
-    unsigned long long w = slot_in[0];
-#pragma unroll
-    for (int q = 1; q < SG; ++q) w = slot_in[q] > w ? slot_in[q] : w;
-    tok = slot_token(w);
-  }
-  const int tok32 = (int)tok;
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 1. the wave's first w2 tile: it depends on nothing above, and stays in
-  //    flight through the row set-up (a wave without units reads clamped
-  //    rows). With one row group, only the first wave of each SIMD (the one
-  //    with more units) requests it here; the second requests its own after
-  //    the embedding gather, so that the gather waits behind half the bytes.
-  const bool tile_first = RG == 2 || sub == 0;   // uniform per wave
-  bf16x8_t A0[NB][KB], A1[NB][KB];
-  if (tile_first)
-    load_w2_tile<KB>(a.w2, V, R, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[0],
-                     A1[0]);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 2. rows: noisy rows first, so that 16-row blocks are of one kind
-  if (lane == 0) {
-    misc[wave] = __builtin_popcountll(bn);
-    misc[8 + wave] = __builtin_popcountll(bz);
-  }
-  if (tid == 0) misc[16] = 0;
-  lds_barrier();
-  {
-    int pre_n = 0, pre_z = 0, tot_n = 0;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      const int cn = misc[w], cz = misc[8 + w];
-      tot_n += cn;
-      if (w < wave) {
-        pre_n += cn;
-        pre_z += cz;
-      }
-    }
-    if (valid) {
-      const int pos_n = bias_mode ? r
-                      : noisy_r ? pre_n + (int)lanes_below(bn)
-                                : tot_n + pre_z + (int)lanes_below(bz);
-      n_row[pos_n] = r;
-      // the feeding token (any int64 at step 0, clamped as unsigned)
-      const uint64_t ut = (uint64_t)tok, last = (uint64_t)(V - 1);
-      n_src[pos_n] = (int)(ut < last ? ut : last);
-      n_info[pos_n] = RowInfo{r * K + s, rcp_r, prefix_r, T};
-      if (!bias_mode && blockIdx.x == 0) {
-        if (s > 0) a.tokens[(int64_t)r * K + s - 1] = (int64_t)(uint32_t)tok32;   // previous step's
-#pragma unroll
-        for (int q = 0; q < SG; ++q)                                  // next step's slots start empty
-          a.slots[((size_t)((s + 1) % 3) * SG + q) * rows + r] = 0ull;
-      }
-    } else if (r < rp) {
-      n_row[r] = 0;
-      n_src[r] = 0;
-      n_info[r] = RowInfo{0, 0.0f, 0u, 0.0f};
-    }
-  }
-
-  u32x4_t bq[MRB];
-  RowInfo ri[ROWREG ? MRB : 1];
-  auto rk_of = [&](int j) -> int {
-    return ROWREG ? ri[ROWREG ? j : 0].rk : n_info[16 * (wr + RG * j) + m].rk;
-  };
-  // base logits of block j of the unit in slab sl, for this lane's 8 tokens
-  auto fetch_base = [&](int j, int sl, u32x4_t& dst) {
-    const int n = 16 * (wr + RG * j) + m;
-    const int tgt = sl * SLAB + tw * TOK_PER_WAVE + 8 * g;
-    dst = (u32x4_t){0u, 0u, 0u, 0u};
-    if (j < my_nrb && n < rows && tgt < V)
-      dst = *(const u32x4_t*)(a.base + (size_t)rk_of(j) * V + tgt);
-  };
-
-  const float mult = a.mult, cap = a.cap, inv_cap = a.inv_cap;
-  const bool has_cap = a.has_cap != 0;
-  // the transform table in LDS holds this launch's (mult, cap)
-  const bool tt = tt_lay && a.ttable[0] == TT_MAGIC && a.ttable[1] == __float_as_uint(mult) &&
-                  a.ttable[2] == __float_as_uint(cap);
-  const float pinf = a.inf;
-  float v1[MRB], v2[MRB];
-  int idt[MRB];
-  bool sp[MRB];
-  uint32_t lw[CARRY ? MRB : 1];   // noisy rows: the word of cached logits holding the top element's
-
-  unsigned long long* slots_step = bias_mode ? nullptr : a.slots + (size_t)(s % 3) * SG * rows;
-  unsigned long long* slots_cur = bias_mode ? nullptr : slots_step + (size_t)(blockIdx.x % SG) * rows;
-  lds_barrier();
-  if (ROWREG) {
-#pragma unroll
-    for (int j = 0; j < (ROWREG ? MRB : 1); ++j) ri[j] = n_info[j < my_nrb ? 16 * (wr + RG * j) + m : 0];
-  }
-  // base logits of the first unit
-  if (!bias_mode && U > 0) {
-#pragma unroll
-    for (int j = 0; j < MRB; ++j) fetch_base(j, slab0, bq[j]);
-  }
-
-  // 4. the embeddings, straight into LDS (16-byte chunks, swizzled);
-  //    padding rows read row 0 and are never used
-  {
-    const int total = rp * cpr;
-    for (int j = wave; j * 64 < total; j += NWV) {
-      const int p = j * 64 + lane;
-      if (p < total) {
-        const int n = p / cpr, cs = p - n * cpr;
-        const uint16_t* src = a.w1 + (size_t)n_src[n] * R + ((cs ^ (n & swz)) * 8);
-        __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (__attribute__((address_space(3))) void*)(emb + (size_t)j * 512),
-                                         16, 0, 0);
-      }
-    }
-  }
-  // the transform table likewise (the host asks for this layout only with a
-  // soft cap; whether the stamp matches is checked where it is used): after
-  // the first tiles and the gather, so that it does not hold them up, and
-  // waited for with them (its lines come from L2)
-  if (tt_lay) {
-    const unsigned char* src = (const unsigned char*)a.ttable + TT_HEAD;
-    for (int j = wave; j * 64 * 16 < (int)TT_BYTES; j += NWV)
-      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)(j * 64 + lane) * 16),
-                                       (__attribute__((address_space(3))) void*)(lds + (size_t)j * 1024),
-                                       16, 0, 0);
-  }
-  // the second tile in flight (two-tile waves), and the first of a wave that
-  // did not request it above, issued after the gather so that waiting for
-  // the gather does not wait for them (the compiler, which cannot tell that
-  // the two requests of the first tile exclude each other, waits for the
-  // gather before the later one)
-  __builtin_amdgcn_sched_barrier(0);
-  // (one-tile waves that did not request their first tile above do so after
-  // the prologue's barrier: kept out of the burst the barrier waits on, it
-  // streams while the SIMD's first wave computes)
-  if (!tile_first && NB == 2)
-    load_w2_tile<KB>(a.w2, V, R, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[0],
-                     A1[0]);
-  __builtin_amdgcn_sched_barrier(0);
-  if (NB == 2)
-    load_w2_tile<KB>(a.w2, V, R, (U > 1 ? slab0 + slab_step : 0) * SLAB + tw * TOK_PER_WAVE, m,
-                              g, kzero, A0[NB - 1], A1[NB - 1]);
-  __builtin_amdgcn_sched_barrier(0);
-
-#pragma unroll
-  for (int j = 0; j < MRB; ++j) {
-    v1[j] = -INFINITY;
-    v2[j] = -INFINITY;
-    idt[j] = NONE;
-    sp[j] = false;
-    if (CARRY) lw[CARRY ? j : 0] = 0u;
-  }
-  // everything but the tiles requested after the gather: the embeddings
-  // (every wave's, hence the barrier), the table, base logits and a first
-  // tile requested before the gather (a count past the field's 63 waits for
-  // more, never for less)
-  constexpr int VM_FIRST = NB == 2 ? 2 * KB : 0;
-  constexpr int VM_AFTER = NB == 2 ? (NB * 2 * KB < 63 ? NB * 2 * KB : 63) : 0;
-  if (tile_first) wait_vm<VM_FIRST>();
-  else wait_vm<VM_AFTER>();
-  lds_barrier();
-  if (!tile_first && NB == 1 && U > 0)
-    load_w2_tile<KB>(a.w2, V, R, slab0 * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[0], A1[0]);
-
-  // one 32-token unit (the wave's unit i, slab `sl`) with w2 tile buffer BUF
-  auto unit = [&](auto bufc, int i, int sl) {
-    constexpr int BUF = decltype(bufc)::value;
-    const int tok0 = sl * SLAB + tw * TOK_PER_WAVE;
-    const int tg = tok0 + 8 * g;               // this lane's 8 tokens: tg .. tg+7
-    const bool tok_ok = tg < V;
-    const bool ntile = i + NB < U;             // the unit whose tile goes into this buffer next
-    const int nsl = sl + NB * slab_step;
-    const bool pnext = i + 1 < U;              // the next unit (base logit prefetch)
-    const int psl = sl + slab_step;
-    uint32_t kw[8];
-    if (!bias_mode) {
-      uint32_t kc = (uint32_t)tg * MM_C1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kw[e] = rotl32(rotl32(kc, 15) * MM_C2, 13);   // the token word, rotated for mm_finish_rot
-        kc += MM_C1;
-      }
-    }
-    f32x4_t cb0[MRB], cb1[MRB];
-#pragma unroll
-    for (int j = 0; j < D; ++j)
-      if (j < my_nrb)
-        block_bias<KB>(A0[BUF], A1[BUF], emb, 16 * (wr + RG * j) + m, R, g, swz, kzero, cb0[j], cb1[j]);
-    if (D > 0 && my_nrb <= D && ntile)
-      load_w2_tile<KB>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF], A1[BUF]);
-#pragma unroll
-    for (int j = 0; j < MRB; ++j) {
-      const int n = 16 * (wr + RG * j) + m;
-      // the contraction of block j + D (of block j itself when D == 0);
-      // once the unit's last one has issued, this buffer's next tile
-      if (D == 0) {
-        if (j < my_nrb) {
-          block_bias<KB>(A0[BUF], A1[BUF], emb, n, R, g, swz, kzero, cb0[j], cb1[j]);
-          if (j == my_nrb - 1 && ntile)
-            load_w2_tile<KB>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF],
-                                      A1[BUF]);
-        }
-      } else if (j + D < MRB && j + D < my_nrb) {
-        block_bias<KB>(A0[BUF], A1[BUF], emb, n + 16 * RG * D, R, g, swz, kzero, cb0[j + D], cb1[j + D]);
-        if (j + D == my_nrb - 1 && ntile)
-          load_w2_tile<KB>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF],
-                                    A1[BUF]);
-      }
-      const u32x4_t bv = bq[j];
-      // block j of the next unit (a whole unit ahead: earlier requests
-      // would queue behind the next tile, vector memory completing in
-      // issue order)
-      if (!bias_mode && pnext) fetch_base(j, psl, bq[j]);
-      if (j >= my_nrb) continue;
-
-      const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[n];
-      const bool active = n < rows && tok_ok;
-      const bool noisy = !(info.T == 0.0f);
-      const f32x4_t c0 = cb0[j], c1 = cb1[j];
-      uint32_t bw[4];
-      bw[0] = pack_bf16(c0[0], c0[1]);
-      bw[1] = pack_bf16(c0[2], c0[3]);
-      bw[2] = pack_bf16(c1[0], c1[1]);
-      bw[3] = pack_bf16(c1[2], c1[3]);
-      if (bias_mode) {
-        if (active)
-          *(uint4*)(a.bias_out + (size_t)n_row[n] * V + tg) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-        continue;
-      }
-      // logits: bf16 add (one binary32 add, rounded), multiplier, soft cap
-      const uint32_t bwd[4] = {bv.x, bv.y, bv.z, bv.w};
-      uint32_t cw[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        cw[q] = pack_bf16(bf_lo(bwd[q]) + bf_lo(bw[q]), bf_hi(bwd[q]) + bf_hi(bw[q]));
-      if (has_cap && tt) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cw[q] = tt_map(cw[q]);
-      } else if (has_cap) {
-        float z[8];
-        float zmax = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          z[2 * q] = (mult * bf_lo(cw[q])) * inv_cap;       // mult = 1: exact, no select
-          z[2 * q + 1] = (mult * bf_hi(cw[q])) * inv_cap;
-          zmax = fmaxf(zmax, fmaxf(fabsf(z[2 * q]), fabsf(z[2 * q + 1])));
-        }
-        if (__any(!(zmax < 0.625f))) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            cw[q] = pack_bf16(cap * tanh_fast(z[2 * q]), cap * tanh_fast(z[2 * q + 1]));
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            cw[q] = pack_bf16(cap * tanh_poly(z[2 * q]), cap * tanh_poly(z[2 * q + 1]));
-        }
-      } else if (mult != 1.0f) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cw[q] = pack_bf16(mult * bf_lo(cw[q]), mult * bf_hi(cw[q]));
-      }
-      float l[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        l[2 * q] = bf_lo(cw[q]);
-        l[2 * q + 1] = bf_hi(cw[q]);
-      }
-      if (active)
-        __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]},
-                                    (u32x4_t*)(a.cache + (size_t)info.rk * V + tg));
-
-      if (EXACT) {
-        if (active) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float key = l[e];
-            if (noisy) key = key_exact(l[e], info.T, mm_finish_rot(rotl32(info.prefix, 13), kw[e]));
-            if (before(key, tg + e, v1[j], idt[j])) {
-              v1[j] = key;
-              idt[j] = tg + e;
-            }
-          }
-        }
-        continue;
-      }
-      // noisy rows: the two largest upper bounds, the element's index in
-      // the tile packed into the bound's low 3 bits
-      if (__any(active && noisy)) {
-        if (active && noisy) {
-          float x1 = v1[j], x2 = v2[j];
-          const float x1b = x1;
-          bool spx = false;
-          // all 8 table reads in flight before the first is used
-          float fh[8];
-          const uint32_t pr = rotl32(info.prefix, 13);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) fh[e] = (float)mm_finish_rot(pr, kw[e]);
-          float2 ab[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (LIN) ab[e] = gtab[gt_index(fh[e])];
-            else ab[e].x = gtabf[gt_index(fh[e])];
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float gh = LIN ? __builtin_fmaf(ab[e].y, fh[e], ab[e].x) : ab[e].x;
-            // the estimate fma(l, RN(1/T), bound); its margin for the
-            // roundings and the packed index is added once per row (see
-            // slack_up), as it grows with the estimate
-            const float hi = __builtin_fmaf(l[e], info.rcp, gh);
-            spx = spx || __builtin_amdgcn_class(hi, 0x207);       // NaN or infinite
-            const float pk = __uint_as_float((__float_as_uint(hi) & ~7u) | (uint32_t)e);
-            x2 = __builtin_amdgcn_fmed3f(x1, x2, pk);
-            x1 = __builtin_amdgcn_fmed3f(x1, pk, pinf);   // max, no canonicalising
-          }
-          if (x1 != x1b) {
-            idt[j] = tg;
-            if (CARRY) {
-              const uint32_t e1 = __float_as_uint(x1);
-              lw[CARRY ? j : 0] = (e1 & 4u) ? ((e1 & 2u) ? cw[3] : cw[2]) : ((e1 & 2u) ? cw[1] : cw[0]);
-            }
-          }
-          v1[j] = x1;
-          v2[j] = x2;
-          sp[j] = sp[j] || spx;
-        }
-      }
-      // temperature-0 rows: the exact largest logit, the earliest on ties
-      // (elements arrive in rising id); v2 holds its index in the tile
-      if (__any(active && !noisy)) {
-        if (active && !noisy) {
-          float x1 = v1[j];
-          const float x1b = x1;
-          uint32_t e1 = __float_as_uint(v2[j]);
-          bool spx = false;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            spx = spx || __builtin_amdgcn_class(l[e], 0x007);   // NaN or -inf
-            const bool gt = l[e] > x1;
-            x1 = gt ? l[e] : x1;
-            e1 = gt ? (uint32_t)e : e1;
-          }
-          if (x1 != x1b) idt[j] = tg;
-          v1[j] = x1;
-          v2[j] = __uint_as_float(e1);
-          sp[j] = sp[j] || spx;
-        }
-      }
-    }
-  };
-
-  // the wave's units (a two-tile wave alternates its buffers)
-  for (int i = 0; i < U; i += NB) {
-    unit(std::integral_constant<int, 0>{}, i, slab0 + i * slab_step);
-    if (NB == 2 && i + 1 < U) unit(std::integral_constant<int, NB - 1>{}, i + 1, slab0 + (i + 1) * slab_step);
-  }
-  if (bias_mode) return;
-
-  // 5. each row's state: this lane's, merged over the row's 4 lanes, stored
-  //    per wave (over the embeddings, once every wave is past its last
-  //    contraction), merged over the waves; then per row either the packed
-  //    atomicMax of its certified winner or the fallback list.
-  RowState fin[MRB];
-#pragma unroll
-  for (int j = 0; j < MRB; ++j) {
-    fin[j] = RowState{-INFINITY, -INFINITY, NONE, 0, 0.0f};
-    if (j >= my_nrb) continue;   // uniform: the shuffles below run for the whole wave
-    const int n = 16 * (wr + RG * j) + m;
-    const bool noisy = !((ROWREG ? ri[ROWREG ? j : 0].T : n_info[n].T) == 0.0f);
-    RowState st;
-    st.v1 = v1[j];
-    st.v2 = v2[j];
-    st.sp = sp[j] ? 1 : 0;
-    if (EXACT) st.id = idt[j];
-    else if (idt[j] == NONE) st.id = NONE;
-    else st.id = idt[j] + (int)((noisy ? __float_as_uint(v1[j]) : __float_as_uint(v2[j])) & 7u);
-    st.l = 0.0f;
-    if (CARRY) st.l = (__float_as_uint(v1[j]) & 1u) ? bf_hi(lw[CARRY ? j : 0]) : bf_lo(lw[CARRY ? j : 0]);
-    const bool top2 = noisy && !EXACT;
-#pragma unroll
-    for (int sh = 16; sh <= 32; sh <<= 1) {
-      RowState o;
-      o.v1 = __shfl_xor(st.v1, sh);
-      o.v2 = __shfl_xor(st.v2, sh);
-      o.id = __shfl_xor(st.id, sh);
-      o.sp = __shfl_xor(st.sp, sh);
-      o.l = __shfl_xor(st.l, sh);
-      if (top2) merge_top2(st, o);
-      else merge_order(st, o);
-    }
-    fin[j] = st;
-  }
-  // every wave past its last contraction (the states go over the
-  // embeddings); with carried logits the cache stores drain meanwhile (the
-  // barrier before the fallback scans, which read them back, waits for
-  // them), else they are read back below and waited for here
-  if (CARRY) {
-    lds_barrier();
-  } else {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  float* st_v1 = (float*)emb;
-  float* st_v2 = st_v1 + NWV * rp;
-  int* st_id = (int*)(st_v2 + NWV * rp);
-  int* st_sp = st_id + NWV * rp;
-  float* st_l = (float*)(st_sp + NWV * rp);
-#pragma unroll
-  for (int j = 0; j < MRB; ++j) {
-    if (j >= my_nrb) break;
-    const int n = 16 * (wr + RG * j) + m;
-    if (g == 0) {
-      st_v1[wave * rp + n] = fin[j].v1;
-      st_v2[wave * rp + n] = fin[j].v2;
-      st_id[wave * rp + n] = fin[j].id;
-      st_sp[wave * rp + n] = fin[j].sp;
-      st_l[wave * rp + n] = fin[j].l;
-    }
-  }
-  if (tid == 0) misc[16] = 0;
-  lds_barrier();
-  for (int n = tid; n < rows; n += NTH) {
-    const RowInfo info = n_info[n];
-    const bool noisy = !(info.T == 0.0f);
-    const bool top2 = noisy && !EXACT;
-    // the row's wave states, all loads issued before the first merge
-    constexpr int NS = RG == 1 ? NWV : 4;
-    const int w0 = RG == 1 ? 0 : 4 * ((n >> 4) & 1);
-    RowState o[NS];
-#pragma unroll
-    for (int q = 0; q < NS; ++q) {
-      const int i = (w0 + q) * rp + n;
-      o[q] = RowState{st_v1[i], st_v2[i], st_id[i], st_sp[i], st_l[i]};
-    }
-    RowState st = o[0];
-#pragma unroll
-    for (int q = 1; q < NS; ++q) {
-      if (top2) merge_top2(st, o[q]);
-      else merge_order(st, o[q]);
-    }
-    const int rr = n_row[n];
-    float key = st.v1;
-    bool fb = !EXACT && (st.sp != 0 || (mode == MODE_SAMPLE_FALLBACK && noisy));
-    float thr = -INFINITY;
-    if (!fb && top2 && st.id != NONE) {
-      float l1 = st.l;
-      if (!CARRY) {
-        const size_t e = (size_t)info.rk * V + st.id;
-        const uint32_t wd = load_cache_word(a.cache, e & ~(size_t)1);
-        l1 = (e & 1) ? bf_hi(wd) : bf_lo(wd);
-      }
-      key = key_exact(l1, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)st.id)));
-      const float v2u = slack_up(st.v2);
-      if (!(key > v2u)) {
-        // not certified: some other element's bound reaches the key. If a
-        // key already published for this row (by another workgroup) lies
-        // above that bound, no element here but the top one can win, and
-        // the top one is published below; else re-scan the row.
-        unsigned long long cur = 0ull;
-        for (int q = 0; q < SG; ++q) {
-          const unsigned long long c =
-              __hip_atomic_load(slots_step + (size_t)q * rows + rr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          cur = c > cur ? c : cur;
-        }
-        if (!((uint32_t)(cur >> 32) > (uint32_t)(pack_winner(v2u, 0) >> 32))) {
-          fb = true;
-          thr = key;
-        }
-      }
-    }
-    if (fb) {
-      const int i = atomicAdd(&misc[16], 1);
-      fb_row[i] = n;
-      fb_thr[i] = thr;
-    } else if (st.id != NONE) {
-      __hip_atomic_fetch_max(slots_cur + rr, pack_winner(key, st.id), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  lds_barrier();
-
-  // 6. fallback rows, one per wave at a time: the wave re-reads the row's
-  //    cached logits over the workgroup's slabs and takes the exact key of
-  //    every element whose bound reaches the threshold (all of them for a
-  //    row with a non-finite estimate). Only then does the workgroup wait
-  //    for its cache stores (they are read back); otherwise they drain as
-  //    the kernel ends.
-  const int nfb = misc[16];
-  if (nfb > 0) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  const int wg_slabs = (int)blockIdx.x < nslabs ? (nslabs - (int)blockIdx.x + G - 1) / G : 0;
-  for (int f = wave; f < nfb; f += NWV) {
-    const int n = fb_row[f];
-    const float thr = fb_thr[f];
-    const RowInfo info = n_info[n];
-    const bool noisy = !(info.T == 0.0f);
-    const int rr = n_row[n];
-    float bv = -INFINITY;
-    int bi = NONE;
-    // once some element of the row has a NaN key (a NaN logit or
-    // temperature, or an infinite logit over an infinite temperature; the
-    // noise term is always finite), only the lowest such id can win, and no
-    // other key is needed
-    bool nan_mode = false;
-    // the lane's words, FB_BATCH loads in flight at a time
-    const int nq = wg_slabs * (SLAB / 2);
-    for (int q0 = 0; q0 < nq; q0 += 64 * FB_BATCH) {
-      uint32_t wd[FB_BATCH];
-      int t0[FB_BATCH];
-#pragma unroll
-      for (int b = 0; b < FB_BATCH; ++b) {
-        const int q = q0 + 64 * b + lane;
-        t0[b] = q < nq ? ((int)blockIdx.x + (q / (SLAB / 2)) * G) * SLAB + 2 * (q % (SLAB / 2)) : V;
-        wd[b] = t0[b] < V ? load_cache_word(a.cache, (size_t)info.rk * V + t0[b]) : 0u;
-      }
-      // with a threshold: the elements whose bound reaches it, the first two
-      // of the lane's kept aside and their exact keys taken together below
-      int nc = 0, ct0 = 0, ct1 = 0;
-      float cl0 = 0.0f, cl1 = 0.0f;
-      uint32_t ch0 = 0u, ch1 = 0u;
-      const bool screen = noisy && !(thr == -INFINITY);
-      if (noisy && !screen) {
-        bool any_nan = false;
-#pragma unroll
-        for (int b = 0; b < FB_BATCH; ++b) {
-          if (t0[b] >= V) continue;
-          any_nan = any_nan || key_is_nan(bf_lo(wd[b]), info.T) || key_is_nan(bf_hi(wd[b]), info.T);
-        }
-        nan_mode = nan_mode || __any(any_nan);
-      }
-#pragma unroll
-      for (int b = 0; b < FB_BATCH; ++b) {
-        if (t0[b] >= V) continue;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int t = t0[b] + e;
-          const float l = e ? bf_hi(wd[b]) : bf_lo(wd[b]);
-          if (screen) {
-            const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
-            if (!(key_upper(l, info.rcp, noise_bound<LIN>(gtab, h)) < thr)) {
-              if (nc == 0) {
-                ct0 = t;
-                cl0 = l;
-                ch0 = h;
-              } else if (nc == 1) {
-                ct1 = t;
-                cl1 = l;
-                ch1 = h;
-              }
-              ++nc;
-            }
-          } else {
-            float key = l;
-            if (noisy && nan_mode)
-              key = key_is_nan(l, info.T) ? __builtin_nanf("") : -INFINITY;
-            else if (noisy)
-              key = key_exact(l, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)t)));
-            if (before(key, t, bv, bi)) {
-              bv = key;
-              bi = t;
-            }
-          }
-        }
-      }
-      if (nc > 0) {
-        const float key = key_exact(cl0, info.T, ch0);
-        if (before(key, ct0, bv, bi)) {
-          bv = key;
-          bi = ct0;
-        }
-      }
-      if (nc > 1) {
-        const float key = key_exact(cl1, info.T, ch1);
-        if (before(key, ct1, bv, bi)) {
-          bv = key;
-          bi = ct1;
-        }
-      }
-      if (nc > 2) {   // rare: every candidate of the batch, again
-#pragma unroll
-        for (int b = 0; b < FB_BATCH; ++b) {
-          if (t0[b] >= V) continue;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int t = t0[b] + e;
-            const float l = e ? bf_hi(wd[b]) : bf_lo(wd[b]);
-            const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
-            if (key_upper(l, info.rcp, noise_bound<LIN>(gtab, h)) < thr) continue;
-            const float key = key_exact(l, info.T, h);
-            if (before(key, t, bv, bi)) {
-              bv = key;
-              bi = t;
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      const float ov = __shfl_xor(bv, sh);
-      const int oi = __shfl_xor(bi, sh);
-      if (before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (lane == 0 && bi != NONE)
-      __hip_atomic_fetch_max(slots_cur + rr, pack_winner(bv, bi), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  // 7. the last step: the workgroup that finishes last turns the winners into
-  //    tokens[:, k-1] and leaves every slot and the ticket zeroed for the next
-  //    call. The slots and the ticket are only ever read or written by
-  //    device-scope atomics, which are performed at one point for the whole
-  //    device; each workgroup takes its ticket only after its own slot
-  //    atomics have completed (vmcnt(0)), so the one that takes the last
-  //    ticket reads final values. Nothing waits on another workgroup.
-  if (s == K - 1) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0)
-      misc[17] = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                         (unsigned)G - 1u
-                     ? 1
-                     : 0;
-    __syncthreads();
-    if (misc[17]) {
-      unsigned long long* fin_slots = a.slots + (size_t)(s % 3) * SG * rows;
-      for (int r2 = tid; r2 < rows; r2 += NTH) {
-        unsigned long long w = 0ull;
-#pragma unroll
-        for (int q = 0; q < SG; ++q) {
-          const unsigned long long c = __hip_atomic_exchange(fin_slots + (size_t)q * rows + r2, 0ull,
-                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          w = c > w ? c : w;
-        }
-        a.tokens[(int64_t)r2 * K + K - 1] = slot_token(w);
-      }
-      for (int i = tid; i < 3 * SG * rows; i += NTH)
-        if (i / (SG * rows) != s % 3) a.slots[i] = 0ull;
-      if (tid == 0) __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
 
 // ---------------------------------------------------------------- test kernels
 
@@ -1432,8 +179,6 @@ const TransformTable* transform_table(float mult, float cap) {
   return t;
 }
 
-typedef void (*StepFn)(StepArgs);
-
 struct Plan {
   int rg, mrb;
 };
@@ -1450,42 +195,17 @@ Plan plan_of(int rows) {
   return Plan{rg, mrb};
 }
 
-template <int KB, bool EX>
-StepFn pick_plan(Plan p) {
-  if (p.rg == 1) {
-    switch (p.mrb) {
-      case 1: return markov_step_kernel<KB, 1, 1, EX>;
-      case 2: return markov_step_kernel<KB, 1, 2, EX>;
-      case 4: return markov_step_kernel<KB, 1, 4, EX>;
-      case 8: return markov_step_kernel<KB, 1, 8, EX>;
-    }
-  } else if (p.rg == 2) {
-    switch (p.mrb) {
-      case 8: return markov_step_kernel<KB, 2, 8, EX>;
-      case 16:
-        if constexpr (KB <= 8) return markov_step_kernel<KB, 2, 16, EX>;
-        break;
-    }
-  }
-  return nullptr;
-}
-
-template <bool EX>
-StepFn pick_rank(int R, Plan p) {
-  switch (R) {
-    case 16:
-    case 32: return pick_plan<1, EX>(p);
-    case 64: return pick_plan<2, EX>(p);
-    case 128: return pick_plan<4, EX>(p);
-    case 256: return pick_plan<8, EX>(p);
-    case 512: return pick_plan<16, EX>(p);
-  }
-  return nullptr;
-}
-
 // exact: the test-only exact-everywhere variant
 StepFn pick_kernel(int R, Plan p, bool exact = false) {
-  return exact ? pick_rank<true>(R, p) : pick_rank<false>(R, p);
+  switch (R) {
+    case 16:
+    case 32: return markov_impl::step_kernel_kb1(p.rg, p.mrb, exact);
+    case 64: return markov_impl::step_kernel_kb2(p.rg, p.mrb, exact);
+    case 128: return markov_impl::step_kernel_kb4(p.rg, p.mrb, exact);
+    case 256: return markov_impl::step_kernel_kb8(p.rg, p.mrb, exact);
+    case 512: return markov_impl::step_kernel_kb16(p.rg, p.mrb, exact);
+  }
+  return nullptr;
 }
 
 bool pow2_rank(int R) { return R >= 16 && R <= 512 && (R & (R - 1)) == 0; }

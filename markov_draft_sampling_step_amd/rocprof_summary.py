@@ -30,7 +30,7 @@ import os
 import statistics
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(HERE, "csrc", "markov.hip")
+KERNEL_SOURCE = os.path.join(HERE, "csrc", "step_kernel.h")
 
 
 def _one(pattern: str) -> str:
