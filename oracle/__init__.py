@@ -65,7 +65,9 @@ _SIGS = {
     "oracle_sample_sequential": (None, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                                         _F32, _F32, _P, _P, _I32]),
     "oracle_decided": (ctypes.c_int, [_I32, _P, _P, _F32, _I64, _I32, _I64, _I32, _P]),
+    "oracle_near_tie": (ctypes.c_int, [_I32, _P, _P, _F32, _I64, _I32, _I64, _I32, _I64]),
     "oracle_log_hard_cases": (_I64, [_F32, _F32, _F64, _P, _I64]),
+    "oracle_noise_many": (None, [_U32, _I64, _P, _I32]),
 }
 
 
@@ -223,6 +225,24 @@ def decided(cache_o_row: np.ndarray, cache_g_row: np.ndarray, T: float, seed: in
     ok = lib().oracle_decided(len(co), _ptr(co), _ptr(cg), float(T), int(seed), int(step_index),
                               int(position), 1 if literal else 0, ctypes.byref(w))
     return bool(ok), int(w.value)
+
+
+def near_tie(cache_o_row: np.ndarray, cache_g_row: np.ndarray, T: float, seed: int,
+             step_index: int, position: int, cand: int, literal: bool = False) -> bool:
+    """Whether token `cand` is in the near-tie set of the row-step (see
+    ``oracle_near_tie``)."""
+    co = np.ascontiguousarray(cache_o_row, dtype=np.uint16)
+    cg = np.ascontiguousarray(cache_g_row, dtype=np.uint16)
+    return bool(lib().oracle_near_tie(len(co), _ptr(co), _ptr(cg), float(T), int(seed),
+                                      int(step_index), int(position), 1 if literal else 0,
+                                      int(cand)))
+
+
+def noise_many(h0: int, n: int, threads: int = 1) -> np.ndarray:
+    """-lb(h) for h = h0 .. h0+n-1, float32 [n]."""
+    out = np.empty(int(n), dtype=np.float32)
+    lib().oracle_noise_many(int(h0) & 0xFFFFFFFF, int(n), _ptr(out), int(threads))
+    return out
 
 
 def log_hard_cases(lo: float, hi: float, ulps: float = 1.0, cap: int = 4096):

@@ -209,3 +209,29 @@ def step(base_row, w1, w2, prev: int, seed: int, position: int, step_index: int,
         keys.append(key(c, T, noise_hash(seed, step_index, position, v)))
     token = sorted(range(V), key=lambda v: order_key(keys[v], v))[0]
     return cache, keys, token
+
+
+# -- spacing of the formats, from the definition ----------------------------------
+
+def _binade(a: Fraction) -> int:
+    """e with 2^e <= a < 2^(e+1), for a > 0."""
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    return e
+
+
+def ulp32(x: float) -> float:
+    """Gap between the binary32 values around |x| in its binade: 2^(e-23)
+    for 2^e <= |x| < 2^(e+1), e clamped at the smallest normal exponent -126
+    (so 2^-149 across the subnormals and at zero)."""
+    a = Fraction(abs(x))
+    e = -126 if a == 0 else max(_binade(a), -126)
+    return float(Fraction(2) ** (e - 23))
+
+
+def ulp_bf16(x: float) -> float:
+    """The same for bf16 (8 significand bits): 2^(e-7), 2^-133 at the bottom."""
+    a = Fraction(abs(x))
+    e = -126 if a == 0 else max(_binade(a), -126)
+    return float(Fraction(2) ** (e - 7))

@@ -84,11 +84,15 @@ EXPORT uint16_t oracle_bf16_round(float x) {
   return (lo & 1u) ? hi : lo;
 }
 
-/* Unit in the last place of a binary32 magnitude (the gap above |x|). */
+/* Unit in the last place of a binary32 magnitude: the spacing of the
+ * binary32 values in |x|'s binade (the gap above |x|; at the largest finite
+ * value, which has no finite successor, the gap below it, the same binade). */
 EXPORT double oracle_ulp32(float x) {
   float a = fabsf(x);
   if (isnan(a) || isinf(a)) return INFINITY;
-  return (double)nextafterf(a, INFINITY) - (double)a;
+  float n = nextafterf(a, INFINITY);
+  if (isinf(n)) return (double)a - (double)nextafterf(a, 0.0f);
+  return (double)n - (double)a;
 }
 
 /* Unit in the last place of a bf16 magnitude. */
@@ -442,11 +446,12 @@ EXPORT void oracle_sample_sequential(int32_t rows, int32_t V, int32_t R, int32_t
  * Any v where exactly one of the two caches is NaN makes the step undecided.
  * Returns 1 (decided) or 0; *winner gets the oracle's token.
  */
-EXPORT int oracle_decided(int32_t V, const uint16_t* cache_o, const uint16_t* cache_g, float T,
-                          int64_t seed, int32_t step, int64_t position, int32_t literal,
-                          int64_t* winner) {
-  float* K = (float*)malloc(sizeof(float) * (size_t)V);
-  double* d = (double*)malloc(sizeof(double) * (size_t)V);
+/* The keys K(v) and perturbation bands d(v) of one row-step (see
+ * oracle_decided); returns 0 where exactly one of the two caches is NaN at
+ * some v, else 1. */
+static int keys_and_bands(int32_t V, const uint16_t* cache_o, const uint16_t* cache_g, float T,
+                          int64_t seed, int32_t step, int64_t position, int32_t literal, float* K,
+                          double* d) {
   int ok = 1;
   int noisy = oracle_noisy(T);
   for (int32_t v = 0; v < V; ++v) {
@@ -469,6 +474,15 @@ EXPORT int oracle_decided(int32_t V, const uint16_t* cache_o, const uint16_t* ca
       d[v] = dc;
     }
   }
+  return ok;
+}
+
+EXPORT int oracle_decided(int32_t V, const uint16_t* cache_o, const uint16_t* cache_g, float T,
+                          int64_t seed, int32_t step, int64_t position, int32_t literal,
+                          int64_t* winner) {
+  float* K = (float*)malloc(sizeof(float) * (size_t)V);
+  double* d = (double*)malloc(sizeof(double) * (size_t)V);
+  int ok = keys_and_bands(V, cache_o, cache_g, T, seed, step, position, literal, K, d);
   int64_t w = oracle_argmax(K, V);
   *winner = w;
   if (ok && isnan(K[w])) {
@@ -494,6 +508,33 @@ EXPORT int oracle_decided(int32_t V, const uint16_t* cache_o, const uint16_t* ca
   free(K);
   free(d);
   return ok;
+}
+
+/*
+ * Whether token `cand` lies in the near-tie set of an undecided row-step:
+ * it is the oracle's winner w, or its key is NaN while some key may be, or
+ * the bands of the two overlap, K(w) - K(cand) <= d(w) + d(cand), with the
+ * same K and d as oracle_decided. A device token outside this set is wrong
+ * whatever the row's margin. cand outside [0, V) is never in the set.
+ */
+EXPORT int oracle_near_tie(int32_t V, const uint16_t* cache_o, const uint16_t* cache_g, float T,
+                           int64_t seed, int32_t step, int64_t position, int32_t literal,
+                           int64_t cand) {
+  if (cand < 0 || cand >= V) return 0;
+  float* K = (float*)malloc(sizeof(float) * (size_t)V);
+  double* d = (double*)malloc(sizeof(double) * (size_t)V);
+  int one_side_nan = !keys_and_bands(V, cache_o, cache_g, T, seed, step, position, literal, K, d);
+  int64_t w = oracle_argmax(K, V);
+  int in;
+  if (cand == w)
+    in = 1;
+  else if (isnan(K[w]) || isnan(K[cand]))
+    in = one_side_nan || isnan(T);   /* a NaN on one side only can move the winner anywhere */
+  else
+    in = ((double)K[w] - (double)K[cand]) <= d[w] + d[cand];
+  free(K);
+  free(d);
+  return in;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -526,4 +567,17 @@ EXPORT int64_t oracle_log_hard_cases(float lo, float hi, double ulps, float* out
     if (b == 0xffffffffu) break;
   }
   return n;
+}
+
+/*
+ * The Gumbel noise -lb(h) = log(-log1m(u(h))) negated, for the n hashes
+ * h0, h0+1, ... (wrapping at 2^32), into out[n]: the key of a zero logit at
+ * temperature 1. For checks that sweep every hash.
+ */
+EXPORT void oracle_noise_many(uint32_t h0, int64_t n, float* out, int32_t threads) {
+#ifdef _OPENMP
+  int nt = threads > 0 ? threads : 1;
+#pragma omp parallel for num_threads(nt) schedule(static)
+#endif
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_gumbel_key(0.0f, 1.0f, (uint32_t)(h0 + (uint64_t)i), NULL, NULL);
 }

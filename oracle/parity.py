@@ -9,7 +9,8 @@ The bar (the tolerance the definition admits, see ``oracle_decided``):
   * cache: each element equal up to one bf16 ulp (or both NaN);
   * tokens: equal on every decided row-step (realized reading); undecided
     row-steps are counted, and the device token must lie in the near-tie set
-    (its oracle key within the perturbation band of the best key).
+    (``oracle_near_tie``: its key within the two perturbation bands of the
+    winner's, the bands ``oracle_decided`` uses).
 """
 
 from __future__ import annotations
@@ -87,16 +88,22 @@ def check_loop(w, cache_g: np.ndarray, tokens_g: np.ndarray, rows=None, steps=No
             else:
                 rep["undecided"] += 1
                 rep["undecided_cases"].append((r, s, gt, win))
-                keys = out["keys"][i]
-                kb, kg = float(keys[win]), float(keys[gt]) if 0 <= gt < w.V else float("nan")
-                band = 4.0 * (abs(kb) + 1.0) * 2.0 ** -20 + (2.0 ** -6 / max(abs(T), 1e-30) if T else 1.0)
-                if not (np.isnan(kb) or (kb - kg) <= band):
-                    rep["near_tie_violations"].append((r, s, gt, win, kb, kg))
+                # the device token must lie in the near-tie set: its oracle
+                # key within the two perturbation bands of the winner's
+                if not oracle.near_tie(co[i], cg[i], T, int(w.seeds[r]), s,
+                                       int(w.positions[r, s]), gt, literal=False):
+                    keys = out["keys"][i]
+                    kg = float(keys[gt]) if 0 <= gt < w.V else float("nan")
+                    rep["near_tie_violations"].append((r, s, gt, win, float(keys[win]), kg))
     return rep
 
 
-def assert_parity(rep: dict, max_undecided_frac: float = 0.02):
+def assert_parity(rep: dict):
+    """The bar: no cache element beyond one bf16 ulp, no token mismatch on a
+    decided row-step, and every undecided row-step's token inside its
+    near-tie set (``oracle_near_tie``: the same bands that decide the
+    row-step). Undecided row-steps are allowed -- the definition itself
+    leaves their token open -- and are counted in the report."""
     assert rep["cache_beyond"] == 0, f"cache beyond one bf16 ulp: {rep['cache_beyond']}"
     assert not rep["token_mismatch"], f"token mismatches on decided row-steps: {rep['token_mismatch'][:10]}"
-    assert not rep["near_tie_violations"], f"undecided tokens outside the tie band: {rep['near_tie_violations'][:5]}"
-    assert rep["undecided"] <= max(1, max_undecided_frac * rep["row_steps"]), rep["undecided_cases"][:10]
+    assert not rep["near_tie_violations"], f"undecided tokens outside the near-tie set: {rep['near_tie_violations'][:5]}"

@@ -58,7 +58,7 @@ def test_noise_hash_two_implementations_agree(oracle_lib):
     from oracle import brute
 
     rng = np.random.default_rng(123)
-    for _ in range(4000):
+    for _ in range(100000):
         seed = int(rng.integers(-(2 ** 63), 2 ** 63 - 1))
         step = int(rng.integers(0, 16))
         pos = int(rng.integers(-5, 2 ** 40))
@@ -402,7 +402,8 @@ def test_oracle_matches_brute_force_on_tiny_inputs(oracle_lib):
     for V in (1, 2, 3, 7, 64, 257):
         for R in (16, 32):
             cases.append((V, R, 1 if V > 64 else 3, 2 if V > 64 else 3))
-    for i, (V, R, rows, k) in enumerate(cases):
+    for i, (V, R, rows, _) in enumerate(cases):
+        k = 1 + i % 4                                  # every k in 1..4
         softcap = 30.0 if i % 3 == 1 else 0.0
         w1, w2, base, prev, seeds, pos, temp, mult, cap = _tiny_case(
             rng, V, R, rows, k, (0.0, 1.0, 0.7, 2.0), softcap, inject=(i % 2 == 0))
@@ -519,3 +520,199 @@ def test_decided_rules(oracle_lib):
     far[5] = 0x4300                                # 128.0 alone on top
     ok, w = oracle_lib.decided(far, far, 1.0, 1, 0, 5, literal=True)
     assert ok and w == 5
+
+
+# -- the tolerance band: where decided turns undecided -------------------------------
+
+def test_ulp_helpers_match_the_formats_spacing(oracle_lib):
+    """oracle_ulp32 / oracle_ulp_bf16 against the spacing of each binade
+    taken from the formats' definitions (brute.ulp32 / ulp_bf16)."""
+    from oracle import brute
+
+    rng = np.random.default_rng(23)
+    xs = [0.0, -0.0, 2.0 ** -149, 2.0 ** -140, 2.0 ** -127, 2.0 ** -126, 2.0 ** -125,
+          1.0, -1.0, 1.5, float(np.nextafter(np.float32(2.0), np.float32(0))), 2.0, 3.0,
+          1.9999, 1.00001, 64.0, 1e-3, 3.3895313892515355e38, 3.4028234663852886e38]
+    xs += [float(x) for x in (rng.standard_normal(2000) * 10.0 ** rng.integers(-30, 30, 2000))
+           .astype(np.float32)]
+    for x in xs:
+        x = float(np.float32(x))
+        assert oracle_lib.lib().oracle_ulp32(x) == brute.ulp32(x), x
+        assert oracle_lib.lib().oracle_ulp_bf16(x) == brute.ulp_bf16(x), x
+
+
+BF = {}
+
+
+def _bf(x: float) -> int:
+    """bf16 bits of a value that is a bf16."""
+    from oracle.brute import bf_bits
+
+    return bf_bits(float(x))
+
+
+def _row(V, entries, fill=-100.0):
+    row = np.full(V, _bf(fill), dtype=np.uint16)
+    for t, x in entries.items():
+        row[t] = _bf(x)
+    return row
+
+
+def _bf_neighbour(x: float, up: bool) -> float:
+    """The bf16 value nearest to x > 0 on the side asked: at or above x (up),
+    at or below it (not up)."""
+    from oracle.brute import bf_bits, bf_value, rnbf
+
+    r = rnbf(Fraction(x))
+    if up and r < x:
+        r = bf_value(bf_bits(r) + 1)
+    if not up and r > x:
+        r = bf_value(bf_bits(r) - 1)
+    return r
+
+
+def test_decided_band_at_temperature_zero(oracle_lib):
+    """T = 0: keys are the cached logits and a token's band is its cache
+    difference alone. A winner 2^-6 ahead stays decided while the two
+    differences sum to less than 2^-6 and turns undecided exactly when they
+    reach it (the rule asks for a gap strictly greater than the bands)."""
+    V = 16
+    co = _row(V, {3: 2.0, 9: 2.0 - 2 ** -6})
+    cases = [
+        ({}, True),                                        # no difference
+        ({9: 2.0 - 2 ** -7}, True),                        # 2^-7 < 2^-6
+        ({9: 2.0}, False),                                 # 2^-6 == gap
+        ({3: 2.0 + 2 ** -6}, False),                       # at the winner
+        ({3: 2.0 + 2 ** -6, 9: 2.0 - 2 ** -6}, False),
+        ({12: -99.5}, True),                               # far tokens do not matter
+    ]
+    for change, want in cases:
+        cg = co.copy()
+        for t, x in change.items():
+            cg[t] = _bf(x)
+        ok, w = oracle_lib.decided(co, cg, 0.0, 1, 0, 5, literal=False)
+        assert w == 3 and ok == want, change
+        if not ok:
+            assert oracle_lib.near_tie(co, cg, 0.0, 1, 0, 5, 9)
+        assert not oracle_lib.near_tie(co, cg, 0.0, 1, 0, 5, 12)
+
+
+def _noise(T, seed, step, pos, t):
+    from oracle import brute
+
+    return brute.key(0.0, 1.0, brute.noise_hash(seed, step, pos, t))   # -lb(t)
+
+
+@pytest.mark.parametrize("T", [0.7, 1.0, 2.0])
+@pytest.mark.parametrize("moved", ["runner_up", "winner"])
+def test_decided_band_scales_with_temperature(oracle_lib, T, moved):
+    """Noisy rows: a cache difference dc at a token moves its key by up to
+    dc / |T|. The row is built so that the moved token's oracle cache value
+    is 0 (then any bf16 is a possible device value, so dc is fine-grained)
+    and the winner leads the runner-up by a gap G of a few thousandths.
+    A device value with dc / |T| at least G (1 + 2^-6) must leave the row
+    undecided, one with dc / |T| at most G (1 - 2^-6) decided (the key's own
+    rounding band is far below G 2^-6). Keys and G come from the brute-force
+    statement (mpmath logs). At T = 0.7 and 2 a band without the 1/|T| factor
+    fails one of the two."""
+    from oracle import brute
+
+    V, seed, step, pos = 16, 424242, 1, 99
+    lb = {t: -_noise(T, seed, step, pos, t) for t in range(V)}
+    w, v = 4, 11
+    zero, other = (v, w) if moved == "runner_up" else (w, v)
+    # the moved token's logit is 0; the other's puts the winner ~0.01 ahead
+    target = 0.01 if moved == "runner_up" else -0.01
+    # K(other) = RN(l/T) - lb(other) ~ K(zero) + target, K(zero) = -lb(zero)
+    l_other = brute.rnbf(Fraction(T) * (Fraction(lb[other]) - Fraction(lb[zero]) + Fraction(target)))
+    co = _row(V, {zero: 0.0, other: l_other})
+    K = {t: brute.key(brute.bf_value(int(co[t])), T, brute.noise_hash(seed, step, pos, t))
+         for t in (w, v)}
+    G = K[w] - K[v]
+    assert 0.002 < G < 0.05, G
+    ok, win = oracle_lib.decided(co, co, T, seed, step, pos)
+    assert ok and win == w
+    inside = _bf_neighbour(T * G * (1 + 2 ** -6), up=True)
+    outside = _bf_neighbour(T * G * (1 - 2 ** -6), up=False)
+    assert inside / T >= G * (1 + 2 ** -6) and outside / T <= G * (1 - 2 ** -6)
+    for dc, want in ((inside, False), (outside, True), (-inside, False), (-outside, True)):
+        cg = co.copy()
+        cg[zero] = _bf(dc)
+        ok, win = oracle_lib.decided(co, cg, T, seed, step, pos)
+        assert win == w and ok == want, (dc, G)
+        assert oracle_lib.near_tie(co, cg, T, seed, step, pos, v) == (not want)
+
+
+def test_decided_band_covers_the_keys_own_rounding(oracle_lib):
+    """With equal caches (dc = 0) a noisy row is still undecided when the
+    runner-up's key is within a few binary32 ulps of the winner's (either
+    log may be off by an ulp), and decided once the gap is 10^-4. A search
+    over pairs of ids finds two whose noises nearly cancel."""
+    from oracle import brute
+
+    T, seed, step, pos = 1.0, 77, 0, 1000
+    V = 2048
+    noise = np.array([oracle_lib.gumbel_key(0.0, 1.0, oracle_lib.noise_hash(seed, step, pos, t))
+                      for t in range(V)], dtype=np.float64)
+    order = np.argsort(noise)
+    gaps = np.diff(noise[order])
+    found = 0
+    for j in np.argsort(gaps)[:200]:
+        a, b = int(order[j]), int(order[j + 1])          # noise[a] <= noise[b]
+        # v keeps logit 0 (K = noise[b] is the larger); w's logit lifts it to
+        # just above: the smallest bf16 l with RN(l) - lb(w) >= K(v)
+        v, w = b, a
+        need = Fraction(noise[b]) - Fraction(noise[a])
+        l_w = brute.rnbf(need)
+        while brute.rn32(Fraction(l_w) + Fraction(noise[a])) < noise[b]:
+            l_w = float(np.float32(l_w) + np.float32(brute.ulp_bf16(l_w)))
+            l_w = brute.rnbf(Fraction(l_w))
+        co = _row(V, {v: 0.0, w: l_w})
+        Kw = brute.key(l_w, T, brute.noise_hash(seed, step, pos, w))
+        Kv = brute.key(0.0, T, brute.noise_hash(seed, step, pos, v))
+        G = Kw - Kv
+        if not (0 <= G <= 4 * brute.ulp32(Kw)) or (G == 0 and w > v):
+            continue
+        ok, win = oracle_lib.decided(co, co, T, seed, step, pos)
+        assert win == w and not ok, (w, v, G)
+        assert oracle_lib.near_tie(co, co, T, seed, step, pos, v)
+        # the same pair with the winner 10^-4 further ahead is decided
+        l_far = brute.rnbf(Fraction(l_w) + Fraction(1, 10000))
+        co2 = _row(V, {v: 0.0, w: l_far})
+        ok, win = oracle_lib.decided(co2, co2, T, seed, step, pos)
+        assert win == w and ok
+        assert not oracle_lib.near_tie(co2, co2, T, seed, step, pos, v)
+        found += 1
+        if found >= 3:
+            break
+    assert found >= 1
+
+
+def test_decided_band_literal_reading(oracle_lib):
+    """The literal reading gives every token a band of one bf16 ulp of its
+    own cached value. At T = 0: a winner at 4.0 (ulp 2^-5) ahead of 3.9375
+    (ulp 2^-6) by 2^-4 is decided; ahead of 3.984375 by 2^-6 it is not. On
+    noisy rows the literal bands contain the realized ones, so every row
+    the literal reading decides, the realized reading (equal caches) decides
+    too, and with the same winner."""
+    V = 8
+    co = _row(V, {2: 4.0, 6: 4.0 - 2 ** -4})
+    ok, w = oracle_lib.decided(co, co, 0.0, 3, 0, 9, literal=True)
+    assert w == 2 and ok
+    co = _row(V, {2: 4.0, 6: 4.0 - 2 ** -6})
+    ok, w = oracle_lib.decided(co, co, 0.0, 3, 0, 9, literal=True)
+    assert w == 2 and not ok
+    rng = np.random.default_rng(31)
+    from markov_draft_sampling_step_amd.workloads import to_bf16_bits
+
+    n_lit = 0
+    for trial in range(200):
+        row = to_bf16_bits(rng.standard_normal(64).astype(np.float32) * 3)
+        T = float(rng.choice([0.7, 1.0, 2.0]))
+        ok_l, w_l = oracle_lib.decided(row, row, T, trial, 0, 5, literal=True)
+        ok_r, w_r = oracle_lib.decided(row, row, T, trial, 0, 5, literal=False)
+        assert w_l == w_r
+        if ok_l:
+            assert ok_r
+            n_lit += 1
+    assert 0 < n_lit < 200
