@@ -29,6 +29,8 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -79,10 +81,24 @@ def measured_traffic(cfg: str):
     return int(m.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s: float):
-    """The oracle (plain C, untuned) on a bounded sample: whole k-step loops
-    over every row of the workload, repeated until the wall-time budget is
-    spent, on the host's cores (its OpenMP loop runs over rows)."""
+    """The oracle (plain C, untuned) on a bounded sample of the workload.
+
+    Leg 1: whole k-step loops over every row, repeated until the wall-time
+    budget is spent, on the host threads a GPU machine gives one GPU (16; its
+    OpenMP loop runs over rows). Leg 2: one thread, one draft step over the
+    first rows (a slice of about a second), extrapolated to draft steps/s of
+    the whole workload (rows are independent and cost the same)."""
     import oracle
 
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -98,10 +114,26 @@ def cpu_baseline(w, budget_s: float):
         dt = time.perf_counter() - t0
         if dt >= budget_s or loops >= 1000:
             break
+    # single thread: one step over n1 rows, n1 grown until it takes ~1 s
+    n1, t1 = 1, 0.0
+    while True:
+        rows = np.arange(min(n1, w.rows))
+        t = time.perf_counter()
+        oracle.step(np.ascontiguousarray(w.base[rows, 0]), w.w1, w.w2, w.prev[rows],
+                    w.seeds[rows], w.positions[rows, 0], 0, w.temperature[rows], w.mult,
+                    w.softcap, threads=1)
+        t1 = time.perf_counter() - t
+        if t1 >= 1.0 or n1 >= w.rows:
+            break
+        n1 = min(w.rows, n1 * 2)
+    single = (len(rows) / w.rows) / t1          # whole-workload draft steps/s, one thread
     return {"value": round(loops * w.k / dt, 4), "unit": "draft steps/s", "cores": used,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
             "sample": f"{loops} whole {w.k}-step loop(s) of the {w.name} workload (all {w.rows} "
-                      f"rows, V={w.V}), {used} OpenMP thread(s) over rows, {dt:.2f} s wall"}
+                      f"rows, V={w.V}), {used} OpenMP thread(s) over rows, {dt:.2f} s wall",
+            "single_thread": {"value": round(single, 5), "unit": "draft steps/s",
+                              "sample": f"one draft step of {len(rows)} of {w.rows} rows on one "
+                                        f"thread in {t1:.2f} s, extrapolated to all rows"}}
 
 
 def percentile(xs, q):
@@ -178,24 +210,21 @@ def main():
     value = w.k / (head_wall * 1e-6)
 
     # the step kernel alone: events around each step-kernel launch of eager
-    # loops (the last step's launch also turns the winners into tokens, so it
-    # is left out of the average)
+    # loops, every step index (the last one also turns the winners into
+    # tokens); the average over all k launches is the roofline's duration
     n2 = max(1, min(args.steps, 50))
-    timed = [s for s in range(w.k) if s < w.k - 1] or [0]
-    evs = []
+    evs = [[] for _ in range(w.k)]
     torch.cuda.synchronize()
     for _ in range(n2):
         for s in range(w.k):
-            if s in timed:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                step_calls[s]()
-                b.record(stream)
-                evs.append((a, b))
-            else:
-                step_calls[s]()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step_calls[s]()
+            b.record(stream)
+            evs[s].append((a, b))
     torch.cuda.synchronize()
-    kern_us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+    per_step = [sum(a.elapsed_time(b) for a, b in e) / len(e) * 1e3 for e in evs]
+    kern_us = sum(per_step) / len(per_step)
     bytes_step = w.bytes_per_step()
     achieved = bytes_step / (kern_us * 1e-6) / 1e9
 
@@ -238,6 +267,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.config), "kernel_us": round(kern_us, 3),
+                     "kernel_us_per_step_index": [round(x, 3) for x in per_step],
                      "bytes_per_launch": bytes_step, "kernel": "markov_step_kernel"},
     }
     if not args.no_cpu_baseline:

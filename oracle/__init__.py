@@ -65,6 +65,8 @@ _SIGS = {
     "oracle_sample_sequential": (None, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                                         _F32, _F32, _P, _P, _I32]),
     "oracle_decided": (ctypes.c_int, [_I32, _P, _P, _F32, _I64, _I32, _I64, _I32, _P]),
+    "oracle_cache_admissible": (ctypes.c_int, [ctypes.c_uint16, _P, _P, _I32, _F32, _F32,
+                                                ctypes.c_uint16]),
     "oracle_near_tie": (ctypes.c_int, [_I32, _P, _P, _F32, _I64, _I32, _I64, _I32, _I64]),
     "oracle_log_hard_cases": (_I64, [_F32, _F32, _F64, _P, _I64]),
     "oracle_noise_many": (None, [_U32, _I64, _P, _I32]),
@@ -143,6 +145,16 @@ def bias(e: np.ndarray, w: np.ndarray) -> tuple[int, float, float]:
 
 def cache_value(base: int, bias_bits: int, mult: float, softcap: float) -> int:
     return int(lib().oracle_cache_value(int(base), int(bias_bits), float(mult), float(softcap)))
+
+
+def cache_admissible(base: int, e: np.ndarray, w: np.ndarray, mult: float, softcap: float,
+                     c_dev: int) -> bool:
+    """Whether c_dev is a cached value the definition admits for this element
+    (see ``oracle_cache_admissible``)."""
+    e = np.ascontiguousarray(e, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    return bool(lib().oracle_cache_admissible(int(base), _ptr(e), _ptr(w), len(e), float(mult),
+                                              float(softcap), int(c_dev)))
 
 
 def before(v1: float, i1: int, v2: float, i2: int) -> bool:

@@ -304,6 +304,46 @@ EXPORT uint16_t oracle_cache_value(uint16_t base, uint16_t bias, float mult, flo
   return oracle_bf16_round(w);
 }
 
+/* The bf16 value next to b toward +infinity (up) or -infinity (down). */
+static uint16_t bf16_step(uint16_t b, int up) {
+  float v = oracle_bf16_to_f32(b);
+  if (v == 0.0f) return up ? (uint16_t)0x0001u : (uint16_t)0x8001u;
+  int away = (v > 0.0f) == (up != 0);       /* moving away from zero */
+  return (uint16_t)(away ? b + 1u : b - 1u);
+}
+
+/*
+ * Whether a device's cached value c_dev of one element is one the
+ * definition admits. The pages leave only the bias's summation order open
+ * ([KIMI] exactness paragraph, [DSV41] module docstring: the last bf16 bit of
+ * the bias may differ), so the admissible biases b' span from the lower to
+ * the upper of: the oracle's bias one bf16 step down / up, and the bf16
+ * roundings of the ends of [S - gamma_R sum|p|, S + gamma_R sum|p|] (S the
+ * exact sum; any order of R binary32 additions stays that close, gamma_R =
+ * R u / (1 - R u), u = 2^-24), one step further out for the rounding of the
+ * ends. The cached value is monotone in the bias (bf16 add, a multiplier, a
+ * rising tanh, roundings), so the admissible cache values are those between
+ * the cache values at the two extreme biases. Where base and bias nearly
+ * cancel, a one-ulp bias difference moves the cache by many of its own
+ * ulps: this is the rule such elements are held to.
+ */
+EXPORT int oracle_cache_admissible(uint16_t base, const uint16_t* e, const uint16_t* w, int32_t R,
+                                   float mult, float softcap, uint16_t c_dev) {
+  double s64 = 0.0, sabs = 0.0;
+  uint16_t b_o = oracle_bias(e, w, R, &s64, &sabs);
+  const double u = ldexp(1.0, -24), gamma = R * u / (1.0 - R * u);
+  uint16_t lo = bf16_step(oracle_bf16_round((float)(s64 - gamma * sabs)), 0);
+  uint16_t hi = bf16_step(oracle_bf16_round((float)(s64 + gamma * sabs)), 1);
+  uint16_t dn = bf16_step(b_o, 0), up = bf16_step(b_o, 1);
+  if (oracle_bf16_to_f32(dn) < oracle_bf16_to_f32(lo)) lo = dn;
+  if (oracle_bf16_to_f32(up) > oracle_bf16_to_f32(hi)) hi = up;
+  const float c1 = oracle_bf16_to_f32(oracle_cache_value(base, lo, mult, softcap));
+  const float c2 = oracle_bf16_to_f32(oracle_cache_value(base, hi, mult, softcap));
+  const float cd = oracle_bf16_to_f32(c_dev);
+  if (isnan(c1) || isnan(c2) || isnan(cd)) return isnan(c1) && isnan(c2) && isnan(cd);
+  return (c1 <= cd && cd <= c2) || (c2 <= cd && cd <= c1);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Argmax under the total order                                              */
 /* ------------------------------------------------------------------------ */

@@ -6,7 +6,9 @@ the oracle, teacher-forced: step s of row r is fed the device's own token of
 step s-1, so every step is compared from the same state.
 
 The bar (the tolerance the definition admits, see ``oracle_decided``):
-  * cache: each element equal up to one bf16 ulp (or both NaN);
+  * cache: each element equal up to one bf16 ulp (or both NaN), or, where
+    base and bias nearly cancel, the cached value of an admissible bias
+    (``oracle_cache_admissible``; counted as ``cache_cancel``);
   * tokens: equal on every decided row-step (realized reading); undecided
     row-steps are counted, and the device token must lie in the near-tie set
     (``oracle_near_tie``: its key within the two perturbation bands of the
@@ -31,8 +33,9 @@ def ulp_bf16(x: np.ndarray) -> np.ndarray:
     return np.maximum(np.ldexp(1.0, e - 8), 2.0 ** -133)
 
 
-def compare_cache(cg: np.ndarray, co: np.ndarray):
-    """(elements beyond one bf16 ulp, elements that differ at all)."""
+def compare_cache(cg: np.ndarray, co: np.ndarray, where: bool = False):
+    """(elements beyond one bf16 ulp, elements that differ at all), and with
+    `where` the indices of the elements beyond."""
     g = bf16_to_f32(cg).astype(np.float64)
     o = bf16_to_f32(co).astype(np.float64)
     gn, on = np.isnan(g), np.isnan(o)
@@ -43,7 +46,19 @@ def compare_cache(cg: np.ndarray, co: np.ndarray):
     tol = ulp_bf16(np.maximum(np.abs(np.nan_to_num(g)), np.abs(np.nan_to_num(o))))
     beyond = one_nan | (~same & ~(diff <= tol))
     differ = ~same
+    if where:
+        return int(beyond.sum()), int(differ.sum()), np.argwhere(beyond)
     return int(beyond.sum()), int(differ.sum())
+
+
+def _row_verdict(args):
+    """Realized and (optionally) literal decisions of one row-step, and
+    whether an undecided device token lies in its near-tie set."""
+    co, cg, T, seed, s, pos, gt, literal = args
+    ok, win = oracle.decided(co, cg, T, seed, s, pos, literal=False)
+    ok_l = oracle.decided(co, co, T, seed, s, pos, literal=True)[0] if literal else False
+    near = True if ok else oracle.near_tie(co, cg, T, seed, s, pos, gt, literal=False)
+    return ok, win, ok_l, near
 
 
 def check_loop(w, cache_g: np.ndarray, tokens_g: np.ndarray, rows=None, steps=None,
@@ -51,14 +66,19 @@ def check_loop(w, cache_g: np.ndarray, tokens_g: np.ndarray, rows=None, steps=No
     """Teacher-forced comparison of a device loop with the oracle.
 
     w: a Workload; cache_g uint16 [rows, k, V]; tokens_g int64 [rows, k].
-    rows / steps: subsets to check (default all).
+    rows / steps: subsets to check (default all). The oracle's step runs on
+    `threads` OpenMP threads, the per-row decisions on as many host threads.
     """
+    from concurrent.futures import ThreadPoolExecutor
+
     rows = list(range(w.rows)) if rows is None else list(rows)
     steps = list(range(w.k)) if steps is None else list(steps)
     rows_a = np.array(rows, dtype=np.int64)
-    rep = dict(row_steps=0, cache_beyond=0, cache_differ=0, cache_elems=0, decided=0,
+    rep = dict(row_steps=0, cache_beyond=0, cache_cancel=0, cache_bad=[], cache_differ=0,
+               cache_elems=0, decided=0,
                undecided=0, decided_literal=0, token_mismatch=[], undecided_cases=[],
                near_tie_violations=[])
+    pool = ThreadPoolExecutor(max(1, threads))
     for s in steps:
         feed = w.prev[rows_a] if s == 0 else tokens_g[rows_a, s - 1]
         out = oracle.step(np.ascontiguousarray(w.base[rows_a, s]), w.w1, w.w2, feed,
@@ -66,20 +86,26 @@ def check_loop(w, cache_g: np.ndarray, tokens_g: np.ndarray, rows=None, steps=No
                           w.mult, w.softcap, want_keys=True, threads=threads)
         co = out["cache"]
         cg = np.ascontiguousarray(cache_g[rows_a, s])
-        beyond, differ = compare_cache(cg, co)
+        beyond, differ, idx = compare_cache(cg, co, where=True)
+        # beyond one ulp: admissible only as the cache value of an admissible
+        # bias (base and bias nearly cancelling; see oracle_cache_admissible)
+        for i, v in idx:
+            e = w.w1[oracle.w1_row(int(feed[i]), w.V)]
+            if oracle.cache_admissible(int(w.base[rows_a[i], s, v]), e, w.w2[v], w.mult,
+                                       w.softcap, int(cg[i, v])):
+                rep["cache_cancel"] += 1
+                beyond -= 1
+            else:
+                rep["cache_bad"].append((int(rows_a[i]), s, int(v), int(cg[i, v]), int(co[i, v])))
         rep["cache_beyond"] += beyond
         rep["cache_differ"] += differ
         rep["cache_elems"] += co.size
-        for i, r in enumerate(rows):
-            rep["row_steps"] += 1
-            T = float(w.temperature[r])
-            ok, win = oracle.decided(co[i], cg[i], T, int(w.seeds[r]), s,
-                                     int(w.positions[r, s]), literal=False)
+        jobs = [(co[i], cg[i], float(w.temperature[r]), int(w.seeds[r]), s,
+                 int(w.positions[r, s]), int(tokens_g[r, s]), literal) for i, r in enumerate(rows)]
+        for (i, r), (ok, win, ok_l, near) in zip(enumerate(rows), pool.map(_row_verdict, jobs)):
             assert win == int(out["tokens"][i])
-            if literal:
-                ok_l, _ = oracle.decided(co[i], co[i], T, int(w.seeds[r]), s,
-                                         int(w.positions[r, s]), literal=True)
-                rep["decided_literal"] += int(ok_l)
+            rep["row_steps"] += 1
+            rep["decided_literal"] += int(ok_l)
             gt = int(tokens_g[r, s])
             if ok:
                 rep["decided"] += 1
@@ -88,13 +114,11 @@ def check_loop(w, cache_g: np.ndarray, tokens_g: np.ndarray, rows=None, steps=No
             else:
                 rep["undecided"] += 1
                 rep["undecided_cases"].append((r, s, gt, win))
-                # the device token must lie in the near-tie set: its oracle
-                # key within the two perturbation bands of the winner's
-                if not oracle.near_tie(co[i], cg[i], T, int(w.seeds[r]), s,
-                                       int(w.positions[r, s]), gt, literal=False):
+                if not near:
                     keys = out["keys"][i]
                     kg = float(keys[gt]) if 0 <= gt < w.V else float("nan")
                     rep["near_tie_violations"].append((r, s, gt, win, float(keys[win]), kg))
+    pool.shutdown()
     return rep
 
 
@@ -104,6 +128,6 @@ def assert_parity(rep: dict):
     near-tie set (``oracle_near_tie``: the same bands that decide the
     row-step). Undecided row-steps are allowed -- the definition itself
     leaves their token open -- and are counted in the report."""
-    assert rep["cache_beyond"] == 0, f"cache beyond one bf16 ulp: {rep['cache_beyond']}"
+    assert rep["cache_beyond"] == 0, f"cache beyond one bf16 ulp, not admissible: {rep['cache_bad'][:10]}"
     assert not rep["token_mismatch"], f"token mismatches on decided row-steps: {rep['token_mismatch'][:10]}"
     assert not rep["near_tie_violations"], f"undecided tokens outside the near-tie set: {rep['near_tie_violations'][:5]}"

@@ -21,7 +21,7 @@ import markov_draft_sampling_step_amd as m  # noqa: E402
 from markov_draft_sampling_step_amd import workloads  # noqa: E402
 from oracle import parity  # noqa: E402
 
-THREADS = min(16, os.cpu_count() or 4)
+THREADS = min(16, os.cpu_count() or 4)   # the GPU machine's CPU share
 
 
 def say(*a):
@@ -37,7 +37,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run_and_check(w, dev, rows=None, exact=False, max_undecided_frac=0.02, fallback=False):
+def run_and_check(w, dev, rows=None, exact=False, fallback=False):
     say(f"case {w.name} V={w.V} R={w.R} rows={w.rows} k={w.k} exact={exact} fallback={fallback}")
     d = workloads.to_device(w, dev)
     workloads.run(w, d, exact=exact, fallback=fallback)
@@ -46,7 +46,10 @@ def run_and_check(w, dev, rows=None, exact=False, max_undecided_frac=0.02, fallb
     rep = parity.check_loop(w, cg, tg, rows=rows, threads=THREADS)
     say(f"  row-steps {rep['row_steps']} decided {rep['decided']} (literal {rep['decided_literal']}) "
         f"undecided {rep['undecided']} cache differing {rep['cache_differ']}/{rep['cache_elems']}")
-    parity.assert_parity(rep, max_undecided_frac)
+    say(f"COUNTS {w.name} row_steps={rep['row_steps']} decided={rep['decided']} "
+        f"decided_literal={rep['decided_literal']} undecided={rep['undecided']} "
+        f"cache_differ={rep['cache_differ']} cache_elems={rep['cache_elems']}")
+    parity.assert_parity(rep)
     return cg, tg, rep
 
 
@@ -253,6 +256,12 @@ def test_tiny(dev):
     dict(V=1032, R=512, rows=5, k=2, seed=5, temps=(1.5, -0.0, 0.5), mult=0.5),
     dict(V=4104, R=128, rows=70, k=2, seed=6, temps=(1.0, float("nan"), 0.0)),
     dict(V=1016, R=256, rows=256, k=2, seed=7, temps=(0.0, 1.0)),
+    # two row groups with a soft cap (the kernel's own tanh, constant noise bounds)
+    dict(V=2056, R=256, rows=160, k=3, seed=8, temps=(1.0, 0.0, 0.7), softcap=30.0),
+    dict(V=1544, R=128, rows=200, k=2, seed=9, temps=(0.6, 1.3), softcap=20.0, mult=0.9),
+    # negative and infinite temperatures (a negative T divides; an infinite
+    # one leaves the noise alone, and an infinite logit over it a NaN key)
+    dict(V=1032, R=64, rows=24, k=3, seed=10, temps=(-0.8, float("inf"), 1.0, -float("inf"), 0.0)),
 ])
 def test_ragged_and_edge_shapes(dev, args):
     w = custom(**args)
@@ -350,11 +359,12 @@ def test_full_config(dev, name):
     run_and_check(workloads.make(name), dev)
 
 
-def test_full_stress_sampled_rows(dev):
+def test_full_stress(dev):
+    """Every row and step of the stress workload against the oracle, and the
+    injected rows' tokens: the first of two NaN logits at any temperature,
+    the first of two tied maxima at T = 0."""
     w = workloads.make("stress")
-    rng = np.random.default_rng(0)
-    rows = sorted(set(w.tie_rows) | set(w.nan_rows) | set(int(r) for r in rng.choice(w.rows, 36, replace=False)))
-    cg, tg, rep = run_and_check(w, dev, rows=rows)
+    cg, tg, rep = run_and_check(w, dev)
     for r in w.nan_rows:
         for (s, t1, t2) in w.injected[r]:
             assert tg[r, s] == t1, (r, s)

@@ -716,3 +716,77 @@ def test_decided_band_literal_reading(oracle_lib):
             assert ok_r
             n_lit += 1
     assert 0 < n_lit < 200
+
+
+def test_cache_admissible_where_base_and_bias_cancel(oracle_lib):
+    """A device cache value is admissible when it is the cache value of an
+    admissible bias. Built so the base nearly cancels the bias: the cache
+    values at the oracle's bias and at its two bf16 neighbours (computed by
+    the brute-force statement, exact rationals) are admissible although
+    they are many cache ulps apart; one at five bias ulps is not."""
+    from oracle import brute
+    from markov_draft_sampling_step_amd.workloads import to_bf16_bits
+
+    rng = np.random.default_rng(41)
+    checked = 0
+    for trial in range(40):
+        R = 32
+        e = to_bf16_bits(rng.standard_normal(R).astype(np.float32) * 0.2)
+        w = to_bf16_bits(rng.standard_normal(R).astype(np.float32) * 0.2)
+        b_bits, s64, sabs = oracle_lib.bias(e, w)
+        b = brute.bf_value(b_bits)
+        if b == 0 or abs(b) < 1e-3:
+            continue
+        ub = brute.ulp_bf16(b)
+        gamma = R * 2.0 ** -24 / (1 - R * 2.0 ** -24)
+        assert gamma * sabs < ub / 4                      # no widening by the order bound here
+        base = brute.bf_bits(brute.rnbf(Fraction(-b) + Fraction(ub) / 3))
+        nb = lambda k: brute.bf_bits(brute.rnbf(Fraction(b) + k * Fraction(ub)))
+        vals = {k: brute.cache_value(base, nb(k), 1.0, 0.0) for k in (-1, 0, 1, 5, -5)}
+        for k in (-1, 0, 1):
+            assert oracle_lib.cache_admissible(base, e, w, 1.0, 0.0, brute.bf_bits(vals[k])), (trial, k)
+        for k in (5, -5):
+            assert not oracle_lib.cache_admissible(base, e, w, 1.0, 0.0, brute.bf_bits(vals[k])), (trial, k)
+        # the small sum makes one bias ulp many cache ulps
+        assert abs(vals[1] - vals[0]) > 2 * brute.ulp_bf16(max(abs(vals[1]), abs(vals[0])))
+        checked += 1
+    assert checked >= 20
+
+
+def test_cache_admissible_inside_the_summation_order_bound(oracle_lib):
+    """A bias that cancels inside its own sum: products +-x in pairs (sum 0,
+    sum |p| = 22). Any summation order stays within gamma_32 sum|p| of 0,
+    about 4e-5, so with a zero base a device cache of 1e-5 is admissible and
+    one of 1e-3 is not."""
+    from oracle import brute
+    from markov_draft_sampling_step_amd.workloads import to_bf16_bits
+
+    R = 32
+    x = to_bf16_bits(np.float32([0.5, 0.75, 0.625, 0.875] * 4))
+    e = np.full(R, brute.bf_bits(1.0), dtype=np.uint16)
+    w = np.concatenate([x, x ^ np.uint16(0x8000)])
+    b_bits, s64, sabs = oracle_lib.bias(e, w)
+    assert s64 == 0.0 and sabs == 22.0
+    zero = brute.bf_bits(0.0)
+    assert oracle_lib.cache_admissible(zero, e, w, 1.0, 0.0, brute.bf_bits(brute.rnbf(Fraction(1, 100000))))
+    assert oracle_lib.cache_admissible(zero, e, w, 1.0, 0.0, brute.bf_bits(brute.rnbf(-Fraction(1, 100000))))
+    assert not oracle_lib.cache_admissible(zero, e, w, 1.0, 0.0, brute.bf_bits(brute.rnbf(Fraction(1, 1000))))
+
+
+def test_cache_is_monotone_in_the_bias(oracle_lib):
+    """The rule above rests on the cached value rising with the bias (falling
+    for a negative multiplier): checked with the brute-force statement over
+    runs of consecutive bf16 biases, with and without a soft cap."""
+    from oracle import brute
+
+    rng = np.random.default_rng(43)
+    for trial in range(60):
+        base = int(rng.integers(0, 0x7F00)) | (int(rng.integers(0, 2)) << 15)
+        b0 = int(rng.integers(0x3800, 0x3D80)) | (int(rng.integers(0, 2)) << 15)
+        mult, cap = [(1.0, 0.0), (0.75, 30.0), (-1.25, 0.0), (1.0, 2.0)][trial % 4]
+        bs = sorted((brute.bf_value((b0 + d) & 0xFFFF) for d in range(-6, 7)))
+        cs = [brute.cache_value(base, brute.bf_bits(b), mult, cap) for b in bs]
+        if mult > 0:
+            assert all(c1 <= c2 for c1, c2 in zip(cs, cs[1:])), (trial, cs)
+        else:
+            assert all(c1 >= c2 for c1, c2 in zip(cs, cs[1:])), (trial, cs)
