@@ -146,6 +146,34 @@ int markov_sample_step(const void* base_logits, const void* w1, const void* w2,
                        int64_t* tokens, markov_stream_t stream, const markov_shape_t* shape,
                        void* workspace, size_t workspace_bytes);
 
+/*
+ * markov_sample_sequential for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same loop and results, with the library's own workspace
+ * instead of a caller's. Each GPU the library runs on holds one such
+ * workspace, a file-scope device array of 190208 bytes, until the process
+ * ends; it takes at most markov_noalloc_max_rows() rows (512), and a larger
+ * shape fails with MARKOV_ERR_WORKSPACE. The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine). The first call on a
+ * device copies the noise bound tables into its workspace, and a call whose
+ * (mult, softcap) differ from the last soft-capped call's copies that
+ * transform table in (host-to-device copies on `stream`; the table is built
+ * on the host once per (mult, softcap) and kept): make one such call outside
+ * any graph capture first. Every call enqueues a small fill kernel that
+ * clears the workspace's ticket and slots, then the k step launches. All
+ * calls on one GPU share its workspace: calls that overlap in time on one
+ * GPU (two streams, two host threads) race and must be serialised by the
+ * caller. Other arguments and errors as markov_sample_sequential.
+ */
+int markov_sample_sequential_noalloc(const void* base_logits, const void* w1, const void* w2,
+                                     const int64_t* prev, const int64_t* seeds,
+                                     const int64_t* positions, int32_t k,
+                                     const float* temperature, void* cache, int64_t* tokens,
+                                     markov_stream_t stream, const markov_shape_t* shape);
+
+/* The most rows markov_sample_sequential_noalloc takes. */
+int32_t markov_noalloc_max_rows(void);
+
 /* A readable name of a status code (static string). */
 const char* markov_status_string(int status);
 

@@ -55,6 +55,9 @@ _SIGS = {
     "markov_sample_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                           _P, _P, _P, _P, ctypes.POINTER(Shape), _P,
                                           ctypes.c_size_t]),
+    "markov_sample_sequential_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                                        _P, _P, _P, _P, ctypes.POINTER(Shape)]),
+    "markov_noalloc_max_rows": (ctypes.c_int32, []),
     "markov_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "markov_debug_bias": (ctypes.c_int, [_P, _P, _P, _P, ctypes.POINTER(Shape), _P]),
     "markov_debug_gumbel": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_float,
@@ -199,6 +202,33 @@ def sample_sequential(base_logits, w1, w2, prev, seeds, positions, temperature, 
     fn = (lib().markov_debug_sample_exact if exact else
           lib().markov_debug_sample_fallback if fallback else lib().markov_sample_sequential)
     _check(fn(*args), "markov_sample_sequential")
+
+
+def sample_sequential_noalloc(base_logits, w1, w2, prev, seeds, positions, temperature, cache,
+                              tokens, mult: float = 1.0, softcap: float = 0.0, stream=None):
+    """markov_sample_sequential_noalloc: the loop with the library's own
+    per-device workspace (no workspace argument, nothing allocated)."""
+    import torch
+
+    rows, k, V = base_logits.shape
+    R = w1.shape[1]
+    sh = make_shape(rows, V, R, mult, softcap)
+    _check(lib().markov_sample_sequential_noalloc(
+        _dev(base_logits, torch.bfloat16, "base_logits"),
+        _dev(w1, torch.bfloat16, "w1", (V, R)),
+        _dev(w2, torch.bfloat16, "w2", (V, R)),
+        _dev(prev, torch.int64, "prev", (rows,)),
+        _dev(seeds, torch.int64, "seeds", (rows,)),
+        _dev(positions, torch.int64, "positions", (rows, k)),
+        ctypes.c_int32(k),
+        _dev(temperature, torch.float32, "temperature", (rows,)),
+        _dev(cache, torch.bfloat16, "cache", (rows, k, V)),
+        _dev(tokens, torch.int64, "tokens", (rows, k)),
+        _stream_ptr(stream), ctypes.byref(sh)), "markov_sample_sequential_noalloc")
+
+
+def noalloc_max_rows() -> int:
+    return int(lib().markov_noalloc_max_rows())
 
 
 def debug_bias(w1, w2, tok, bias, stream=None):

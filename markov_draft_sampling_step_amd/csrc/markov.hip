@@ -341,6 +341,77 @@ int sample_common(int mode, const void* base_logits, const void* w1, const void*
                       temperature, cache, tokens, nullptr, stream, shape, workspace);
 }
 
+// ---------------------------------------------------------------- no-alloc variant
+//
+// For callers that cannot allocate device memory: the workspace is this
+// library's own file-scope array, one per GPU the library runs on (held until
+// the process ends), sized for the most rows any rank takes. Host code never
+// passes the array's name to a kernel or a copy: it takes the array's device
+// address from hipGetSymbolAddress once per device and uses that.
+constexpr int32_t NOALLOC_MAX_ROWS = ROWS_CAP;
+constexpr size_t NOALLOC_BYTES = (size_t)WS_SLOTS + (size_t)NOALLOC_MAX_ROWS * 8 * 3 * SG;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_BYTES];
+
+__global__ __launch_bounds__(256) void zero_kernel(u32x4_t* p, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = (u32x4_t){0u, 0u, 0u, 0u};
+}
+
+struct ScratchState {
+  void* ptr = nullptr;          // the device address of `scratch` on this device
+  bool tables = false;          // noise bound tables copied in
+  bool stamped = false;         // a transform table is in, for (mult_bits, cap_bits)
+  uint32_t mult_bits = 0, cap_bits = 0;
+};
+constexpr int NOALLOC_DEVICES = 64;
+ScratchState g_scratch[NOALLOC_DEVICES];
+std::mutex g_scratch_mutex;
+
+// The scratch of the current device, prepared for a call of this shape: set
+// up once per device (its address, the noise bound tables), the transform
+// table copied in when the call's (mult, softcap) differ from the one in it,
+// and the ticket and the slots of `rows` rows cleared by a fill kernel.
+int scratch_for(const markov_shape_t* sh, hipStream_t st, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MARKOV_ERR_HIP;
+  if (dev < 0 || dev >= NOALLOC_DEVICES) return MARKOV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  ScratchState& S = g_scratch[dev];
+  if (!S.ptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MARKOV_ERR_HIP;
+    S.ptr = p;
+  }
+  unsigned char* ws = (unsigned char*)S.ptr;
+  if (!S.tables) {
+    build_table();
+    if (hipMemcpyAsync(ws, g_table, GT_BYTES, hipMemcpyHostToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(ws + GT_BYTES, g_ctable, GTC_BYTES, hipMemcpyHostToDevice, st) != hipSuccess)
+      return MARKOV_ERR_HIP;
+    S.tables = true;
+  }
+  if (sh->softcap > 0.0f) {
+    uint32_t mb, cb;
+    memcpy(&mb, &sh->mult, 4);
+    memcpy(&cb, &sh->softcap, 4);
+    if (!S.stamped || S.mult_bits != mb || S.cap_bits != cb) {
+      const TransformTable* t = transform_table(sh->mult, sh->softcap);
+      if (hipMemcpyAsync(ws + WS_TT, t->data, TT_HEAD + TT_BYTES, hipMemcpyHostToDevice, st) !=
+          hipSuccess)
+        return MARKOV_ERR_HIP;
+      S.stamped = true;
+      S.mult_bits = mb;
+      S.cap_bits = cb;
+    }
+  }
+  const int64_t n16 = (int64_t)(ws_bytes(sh->rows) - WS_TICKET) / 16;
+  zero_kernel<<<dim3((unsigned)((n16 + 255) / 256)), 256, 0, st>>>((u32x4_t*)(ws + WS_TICKET), n16);
+  if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
+  *out = S.ptr;
+  return MARKOV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -393,6 +464,29 @@ int markov_sample_sequential(const void* base_logits, const void* w1, const void
   return sample_common(MODE_SAMPLE, base_logits, w1, w2, prev, seeds, positions, k, 0, k,
                        temperature, cache, tokens, stream, shape, workspace, workspace_bytes);
 }
+
+int markov_sample_sequential_noalloc(const void* base_logits, const void* w1, const void* w2,
+                                     const int64_t* prev, const int64_t* seeds,
+                                     const int64_t* positions, int32_t k,
+                                     const float* temperature, void* cache, int64_t* tokens,
+                                     markov_stream_t stream, const markov_shape_t* shape) {
+  int rc = check_shape(shape, k);
+  if (rc) return rc;
+  if (shape->rows > NOALLOC_MAX_ROWS || ws_bytes(shape->rows) > NOALLOC_BYTES)
+    return MARKOV_ERR_WORKSPACE;
+  if (!base_logits || !w1 || !w2 || !prev || !seeds || !positions || !temperature || !cache ||
+      !tokens)
+    return MARKOV_ERR_NULL;
+  if (!aligned16(base_logits) || !aligned16(w1) || !aligned16(w2) || !aligned16(cache))
+    return MARKOV_ERR_ALIGN;
+  void* ws = nullptr;
+  rc = scratch_for(shape, (hipStream_t)stream, &ws);
+  if (rc) return rc;
+  return sample_common(MODE_SAMPLE, base_logits, w1, w2, prev, seeds, positions, k, 0, k,
+                       temperature, cache, tokens, stream, shape, ws, NOALLOC_BYTES);
+}
+
+int32_t markov_noalloc_max_rows(void) { return NOALLOC_MAX_ROWS; }
 
 int markov_sample_step(const void* base_logits, const void* w1, const void* w2,
                        const int64_t* prev, const int64_t* seeds, const int64_t* positions,
