@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "draft steps/s + µs per k-step loop, V=163840 R=256; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "markov_draft_sampling_step_amd", "csrc", "step_kernel.h")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "markov_step_kernel_{cfg}_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "markov_step_kernel_{cfg}{path}_traffic.txt")
 
 
 def parse():
@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="large",
                     choices=["tiny", "single", "small", "large", "stress"])
+    ap.add_argument("--path", default="sample", choices=["sample", "greedy", "greedy-chain"],
+                    help="sample: markov_sample_sequential (the headline); greedy: "
+                         "markov_greedy_sequential writing the cache; greedy-chain: the same "
+                         "without the cache write")
     ap.add_argument("--graph", action="store_true",
                     help="headline from replays of the loop captured as a HIP graph")
     ap.add_argument("--eager", action="store_true",
@@ -67,10 +71,10 @@ def source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(cfg: str):
+def measured_traffic(cfg: str, kpath: str = "sample"):
     """DRAM bytes per step-kernel launch from the committed counter summary,
     or None when there is none or the kernel source changed since."""
-    path = TRAFFIC_SUMMARY.format(cfg=cfg)
+    path = TRAFFIC_SUMMARY.format(cfg=cfg, path="" if kpath == "sample" else "_" + kpath.replace("-", "_"))
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -185,8 +189,16 @@ def main():
 
     w = workloads.make(args.config)
     d = workloads.to_device(w, dev)
-    call = m.prepare(w, d)
-    step_calls = [m.prepare(w, d, step=s) for s in range(w.k)]
+    bytes_step = w.bytes_per_step()
+    if args.path == "sample":
+        call = m.prepare(w, d)
+        step_calls = [m.prepare(w, d, step=s) for s in range(w.k)]
+    else:
+        chain = args.path == "greedy-chain"
+        call = m.prepare_greedy(w, d, cache=not chain)
+        step_calls = [m.prepare_greedy(w, d, cache=not chain, step=s) for s in range(w.k)]
+        if chain:
+            bytes_step -= 2 * w.rows * w.V       # no cache slice written
     launches = w.k                           # one step kernel per draft step
 
     for _ in range(max(1, args.warmup)):
@@ -225,7 +237,6 @@ def main():
     torch.cuda.synchronize()
     per_step = [sum(a.elapsed_time(b) for a, b in e) / len(e) * 1e3 for e in evs]
     kern_us = sum(per_step) / len(per_step)
-    bytes_step = w.bytes_per_step()
     achieved = bytes_step / (kern_us * 1e-6) / 1e9
 
     cold = None
@@ -256,7 +267,7 @@ def main():
         "config": {"workload": f"{w.name}: V={w.V} R={w.R} rows={w.rows} k={w.k}"
                                f"{' softcap=%g' % w.softcap if w.softcap > 0 else ''}",
                    "V": w.V, "R": w.R, "rows": w.rows, "k": w.k,
-                   "launches_per_loop": launches,
+                   "launches_per_loop": launches, "path": args.path,
                    "mode": "graph" if (graph and args.graph) else "eager"},
         "us_per_loop": round(head_wall, 2),
         "us_per_loop_p10_p50_p90": [round(percentile(head_ev, q), 2) for q in (0.1, 0.5, 0.9)],
@@ -266,11 +277,11 @@ def main():
         "draft_tokens_per_s": round(w.rows * value, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.config), "kernel_us": round(kern_us, 3),
+                     "traffic": measured_traffic(args.config, args.path), "kernel_us": round(kern_us, 3),
                      "kernel_us_per_step_index": [round(x, 3) for x in per_step],
                      "bytes_per_launch": bytes_step, "kernel": "markov_step_kernel"},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.path == "sample":
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

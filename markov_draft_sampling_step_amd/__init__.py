@@ -58,6 +58,11 @@ _SIGS = {
     "markov_sample_sequential_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                         _P, _P, _P, _P, ctypes.POINTER(Shape)]),
     "markov_noalloc_max_rows": (ctypes.c_int32, []),
+    "markov_greedy_sequential": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
+                                                ctypes.POINTER(Shape), _P, ctypes.c_size_t]),
+    "markov_greedy_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                          _P, _P, ctypes.POINTER(Shape), _P, ctypes.c_size_t]),
+    "markov_greedy_finalize": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P]),
     "markov_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "markov_debug_bias": (ctypes.c_int, [_P, _P, _P, _P, ctypes.POINTER(Shape), _P]),
     "markov_debug_gumbel": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_float,
@@ -227,6 +232,48 @@ def sample_sequential_noalloc(base_logits, w1, w2, prev, seeds, positions, tempe
         _stream_ptr(stream), ctypes.byref(sh)), "markov_sample_sequential_noalloc")
 
 
+def _opt(t, dtype, name, shape=None):
+    return ctypes.c_void_p(None) if t is None else _dev(t, dtype, name, shape)
+
+
+def greedy_sequential(base_logits, w1, w2, prev, tokens, workspace, cache=None, winners=None,
+                      mult: float = 1.0, softcap: float = 0.0, stream=None,
+                      step: int | None = None):
+    """markov_greedy_sequential: every row at temperature 0. base_logits bf16
+    [rows, k, V]; cache bf16 [rows, k, V] or None (not written); tokens int64
+    [rows, k]; winners int64 [rows, k] (the packed u64 winners, as int64
+    bits) or None; ``step`` runs that one step alone (markov_greedy_step)."""
+    import torch
+
+    rows, k, V = base_logits.shape
+    R = w1.shape[1]
+    sh = make_shape(rows, V, R, mult, softcap)
+    head = (_dev(base_logits, torch.bfloat16, "base_logits"), _dev(w1, torch.bfloat16, "w1", (V, R)),
+            _dev(w2, torch.bfloat16, "w2", (V, R)), _dev(prev, torch.int64, "prev", (rows,)),
+            ctypes.c_int32(k))
+    tail = (_opt(cache, torch.bfloat16, "cache", (rows, k, V)),
+            _dev(tokens, torch.int64, "tokens", (rows, k)),
+            _opt(winners, torch.int64, "winners", (rows, k)),
+            _stream_ptr(stream), ctypes.byref(sh), _dev(workspace, torch.uint8, "workspace"),
+            ctypes.c_size_t(workspace.numel()))
+    if step is not None:
+        _check(lib().markov_greedy_step(*head, ctypes.c_int32(step), *tail), "markov_greedy_step")
+    else:
+        _check(lib().markov_greedy_sequential(*head, *tail), "markov_greedy_sequential")
+
+
+def greedy_finalize(winners, tokens, stream=None):
+    """markov_greedy_finalize: token ids of packed winners (int64 tensors of
+    the same number of elements)."""
+    import torch
+
+    if winners.numel() != tokens.numel():
+        raise ValueError("greedy_finalize: winners and tokens differ in size")
+    _check(lib().markov_greedy_finalize(_dev(winners, torch.int64, "winners"), winners.numel(),
+                                        _dev(tokens, torch.int64, "tokens"), _stream_ptr(stream)),
+           "markov_greedy_finalize")
+
+
 def noalloc_max_rows() -> int:
     return int(lib().markov_noalloc_max_rows())
 
@@ -329,6 +376,37 @@ class PreparedCall:
 
     def __call__(self):
         _check(self._fn(*self._args), self._what)
+
+
+def prepare_greedy(w, d, cache: bool = True, winners=None, stream=None,
+                   step: int | None = None) -> PreparedCall:
+    """Marshal a greedy loop (or one step) of workload `w` on device tensors
+    `d` once; ``cache`` False leaves the cache unwritten."""
+    import torch
+
+    rows, k, V, R = w.rows, w.k, w.V, w.R
+    sh = make_shape(rows, V, R, w.mult, w.softcap)
+    args = [
+        _dev(d["base"], torch.bfloat16, "base_logits", (rows, k, V)),
+        _dev(d["w1"], torch.bfloat16, "w1", (V, R)),
+        _dev(d["w2"], torch.bfloat16, "w2", (V, R)),
+        _dev(d["prev"], torch.int64, "prev", (rows,)),
+        ctypes.c_int32(k),
+        _dev(d["cache"], torch.bfloat16, "cache", (rows, k, V)) if cache else ctypes.c_void_p(None),
+        _dev(d["tokens"], torch.int64, "tokens", (rows, k)),
+        _opt(winners, torch.int64, "winners", (rows, k)),
+        _stream_ptr(stream),
+        ctypes.byref(sh),
+        _dev(d["workspace"], torch.uint8, "workspace"),
+        ctypes.c_size_t(d["workspace"].numel()),
+    ]
+    if step is not None:
+        args.insert(5, ctypes.c_int32(step))
+        call = PreparedCall(lib().markov_greedy_step, args, 9, "markov_greedy_step")
+    else:
+        call = PreparedCall(lib().markov_greedy_sequential, args, 8, "markov_greedy_sequential")
+    call._keep = sh
+    return call
 
 
 def prepare(w, d, step: int | None = None, exact: bool = False, stream=None,

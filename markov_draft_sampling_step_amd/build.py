@@ -1,8 +1,10 @@
 """Build ``libmarkov.so`` in-tree for gfx950 with hipcc.
 
-The step kernels of each rank class are compiled in a translation unit of
-their own (``csrc/step_kb*.hip``), in parallel, next to the host side
-(``csrc/markov.hip``); the objects are linked into one shared library.
+The step kernels of each (rank class, variant) pair listed in
+``MARKOV_STEP_INSTANCES`` (``csrc/step_kernel.h``) are compiled from
+``csrc/step_inst.hip`` as a translation unit of their own, in parallel, next
+to the host side (``csrc/markov.hip``); the objects are linked into one shared
+library.
 
 Flags: -ffp-contract=off so every rounding in the kernels is where the source
 writes it; packed-FP32 instructions are switched off for the device code
@@ -11,8 +13,8 @@ writes it; packed-FP32 instructions are switched off for the device code
 
 from __future__ import annotations
 
-import glob
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -31,12 +33,26 @@ FLAGS = [
 ]
 
 
-def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def instances():
+    """The (rank class, variant) pairs the header lists."""
+    text = open(os.path.join(CSRC, "step_kernel.h")).read()
+    body = text[text.index("#define MARKOV_STEP_INSTANCES(X)"):]
+    body = body[: body.index("\n\n")]
+    return [(int(a), int(b)) for a, b in re.findall(r"X\((\d+),\s*(\d+)\)", body)]
 
 
-def compile_command(src: str, obj: str):
-    return [HIPCC, *FLAGS, "-c", "-o", obj, src]
+def units():
+    """(source, object, extra flags) of every translation unit."""
+    out = [(os.path.join(CSRC, "markov.hip"), os.path.join(OBJDIR, "markov.o"), [])]
+    for kb, var in instances():
+        out.append((os.path.join(CSRC, "step_inst.hip"),
+                    os.path.join(OBJDIR, f"step_kb{kb}_v{var}.o"),
+                    [f"-DSTEP_KB={kb}", f"-DSTEP_VAR={var}"]))
+    return out
+
+
+def compile_command(src: str, obj: str, extra=()):
+    return [HIPCC, *FLAGS, *extra, "-c", "-o", obj, src]
 
 
 def link_command(objs, output: str = OUTPUT):
@@ -54,11 +70,11 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
-    srcs = sources()
-    objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    us = units()
+    objs = [o for _, o, _ in us]
+    jobs = jobs or max(1, min(len(us), os.cpu_count() or 1, 16))
     with ThreadPoolExecutor(jobs) as ex:
-        list(ex.map(lambda so: _run(compile_command(*so), verbose), zip(srcs, objs)))
+        list(ex.map(lambda u: _run(compile_command(*u), verbose), us))
     tmp = OUTPUT + ".tmp"
     _run(link_command(objs, tmp), verbose)
     os.replace(tmp, OUTPUT)

@@ -195,16 +195,13 @@ Plan plan_of(int rows) {
   return Plan{rg, mrb};
 }
 
-// exact: the test-only exact-everywhere variant
-StepFn pick_kernel(int R, Plan p, bool exact = false) {
-  switch (R) {
-    case 16:
-    case 32: return markov_impl::step_kernel_kb1(p.rg, p.mrb, exact);
-    case 64: return markov_impl::step_kernel_kb2(p.rg, p.mrb, exact);
-    case 128: return markov_impl::step_kernel_kb4(p.rg, p.mrb, exact);
-    case 256: return markov_impl::step_kernel_kb8(p.rg, p.mrb, exact);
-    case 512: return markov_impl::step_kernel_kb16(p.rg, p.mrb, exact);
-  }
+// The step kernel of a rank, plan and variant (V_SAMPLE, V_EXACT, V_GREEDY).
+StepFn pick_kernel(int R, Plan p, int var = V_SAMPLE) {
+  const int kb = R == 16 ? 1 : R / 32;
+#define MARKOV_PICK(KB, VAR) \
+  if (kb == KB && var == VAR) return markov_impl::step_kernel_kb##KB##_v##VAR(p.rg, p.mrb);
+  MARKOV_STEP_INSTANCES(MARKOV_PICK)
+#undef MARKOV_PICK
   return nullptr;
 }
 
@@ -269,33 +266,46 @@ int launch_grid(StepFn fn, size_t lds, int nslabs, int S, int* grid) {
 
 size_t ws_bytes(int rows) { return (size_t)WS_SLOTS + (size_t)rows * 8 * 3 * SG; }
 
-int launch_steps(int mode, const void* base, const void* w1, const void* w2, const int64_t* prev,
-                 const int64_t* seeds, const int64_t* positions, int32_t k, int32_t s_begin,
-                 int32_t s_end, const float* temperature, void* cache, int64_t* tokens,
-                 void* bias_out, markov_stream_t stream, const markov_shape_t* sh,
-                 void* workspace) {
+// One call's arguments: the mode (runtime) and variant (compile time) of the
+// kernel, the caller's buffers and the steps to launch.
+struct Call {
+  int mode = MODE_SAMPLE, var = V_SAMPLE;
+  const void *base = nullptr, *w1 = nullptr, *w2 = nullptr;
+  const int64_t *prev = nullptr, *seeds = nullptr, *positions = nullptr;
+  const float* temperature = nullptr;
+  void* cache = nullptr;
+  int64_t* tokens = nullptr;
+  unsigned long long* winners = nullptr;
+  void* bias_out = nullptr;
+  int32_t k = 1, s_begin = 0, s_end = 1;
+};
+
+int launch_steps(const Call& c, markov_stream_t stream, const markov_shape_t* sh, void* workspace) {
   const Plan plan = plan_of(sh->rows);
-  StepFn fn = pick_kernel(sh->rank, plan, mode == MODE_SAMPLE_EXACT);
+  StepFn fn = pick_kernel(sh->rank, plan, c.var);
   if (!fn) return MARKOV_ERR_ROWS;
+  const bool greedy = (c.var & V_GREEDY) != 0;
   const int rp = (sh->rows + 15) & ~15;
-  const bool tt_layout = mode != MODE_BIAS && sh->softcap > 0.0f && plan.rg == 1 && tt_fits(rp, sh->rank);
-  const size_t lds = (tt_layout ? TT_BYTES : 0) + lds_total(rp, sh->rank);
+  const bool tt_layout = c.mode != MODE_BIAS && sh->softcap > 0.0f && plan.rg == 1 &&
+                         tt_fits(rp, sh->rank, greedy);
+  const size_t lds = (tt_layout ? TT_BYTES : 0) + lds_total(rp, sh->rank, greedy);
   const int nslabs = (sh->vocab + SLAB - 1) / SLAB;
   int grid = 0;
   int rc = launch_grid(fn, lds, nslabs, plan.rg == 1 ? 2 : 1, &grid);
   if (rc) return rc;
   StepArgs a;
   memset(&a, 0, sizeof(a));
-  a.base = (const uint16_t*)base;
-  a.w1 = (const uint16_t*)w1;
-  a.w2 = (const uint16_t*)w2;
-  a.prev = prev;
-  a.seeds = seeds;
-  a.positions = positions;
-  a.temperature = temperature;
-  a.cache = (uint16_t*)cache;
-  a.tokens = tokens;
-  a.bias_out = (uint16_t*)bias_out;
+  a.base = (const uint16_t*)c.base;
+  a.w1 = (const uint16_t*)c.w1;
+  a.w2 = (const uint16_t*)c.w2;
+  a.prev = c.prev;
+  a.seeds = c.seeds;
+  a.positions = c.positions;
+  a.temperature = c.temperature;
+  a.cache = (uint16_t*)c.cache;
+  a.tokens = c.tokens;
+  a.winners = c.winners;
+  a.bias_out = (uint16_t*)c.bias_out;
   if (workspace) {
     a.gtable = (const float*)workspace;
     a.ttable = (const uint32_t*)((unsigned char*)workspace + WS_TT);
@@ -306,15 +316,15 @@ int launch_steps(int mode, const void* base, const void* w1, const void* w2, con
   a.rows = sh->rows;
   a.V = sh->vocab;
   a.R = sh->rank;
-  a.k = k;
+  a.k = c.k;
   a.nslabs = nslabs;
-  a.mode = mode;
+  a.mode = c.mode;
   a.mult = sh->mult;
   a.has_cap = sh->softcap > 0.0f;
   a.cap = sh->softcap;
   a.inv_cap = a.has_cap ? 1.0f / sh->softcap : 0.0f;
   a.inf = INFINITY;
-  for (int s = s_begin; s < s_end; ++s) {
+  for (int s = c.s_begin; s < c.s_end; ++s) {
     a.step = s;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(NTH), lds, (hipStream_t)stream, a);
     if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
@@ -337,8 +347,57 @@ int sample_common(int mode, const void* base_logits, const void* w1, const void*
       !aligned16(workspace))
     return MARKOV_ERR_ALIGN;
   if (workspace_bytes < ws_bytes(shape->rows)) return MARKOV_ERR_WORKSPACE;
-  return launch_steps(mode, base_logits, w1, w2, prev, seeds, positions, k, s_begin, s_end,
-                      temperature, cache, tokens, nullptr, stream, shape, workspace);
+  Call c;
+  c.mode = mode;
+  c.var = mode == MODE_SAMPLE_EXACT ? V_EXACT : V_SAMPLE;
+  c.base = base_logits;
+  c.w1 = w1;
+  c.w2 = w2;
+  c.prev = prev;
+  c.seeds = seeds;
+  c.positions = positions;
+  c.temperature = temperature;
+  c.cache = cache;
+  c.tokens = tokens;
+  c.k = k;
+  c.s_begin = s_begin;
+  c.s_end = s_end;
+  return launch_steps(c, stream, shape, workspace);
+}
+
+int greedy_common(const void* base_logits, const void* w1, const void* w2, const int64_t* prev,
+                  int32_t k, int32_t s_begin, int32_t s_end, void* cache, int64_t* tokens,
+                  unsigned long long* winners, markov_stream_t stream,
+                  const markov_shape_t* shape, void* workspace, size_t workspace_bytes) {
+  int rc = check_shape(shape, k);
+  if (rc) return rc;
+  if (s_begin < 0 || s_end > k || s_begin >= s_end) return MARKOV_ERR_SHAPE;
+  if (!base_logits || !w1 || !w2 || !prev || !tokens || !workspace) return MARKOV_ERR_NULL;
+  if (!aligned16(base_logits) || !aligned16(w1) || !aligned16(w2) || !aligned16(workspace) ||
+      (cache && !aligned16(cache)))
+    return MARKOV_ERR_ALIGN;
+  if (workspace_bytes < ws_bytes(shape->rows)) return MARKOV_ERR_WORKSPACE;
+  Call c;
+  c.mode = MODE_GREEDY;
+  c.var = V_GREEDY;
+  c.base = base_logits;
+  c.w1 = w1;
+  c.w2 = w2;
+  c.prev = prev;
+  c.cache = cache;
+  c.tokens = tokens;
+  c.winners = winners;
+  c.k = k;
+  c.s_begin = s_begin;
+  c.s_end = s_end;
+  return launch_steps(c, stream, shape, workspace);
+}
+
+// The packed winners' token ids (the low word holds ~id).
+__global__ __launch_bounds__(256) void finalize_kernel(const unsigned long long* winners, int64_t n,
+                                                       int64_t* tokens) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) tokens[i] = slot_token(winners[i]);
 }
 
 // ---------------------------------------------------------------- no-alloc variant
@@ -488,6 +547,34 @@ int markov_sample_sequential_noalloc(const void* base_logits, const void* w1, co
 
 int32_t markov_noalloc_max_rows(void) { return NOALLOC_MAX_ROWS; }
 
+int markov_greedy_sequential(const void* base_logits, const void* w1, const void* w2,
+                             const int64_t* prev, int32_t k, void* cache, int64_t* tokens,
+                             uint64_t* winners, markov_stream_t stream,
+                             const markov_shape_t* shape, void* workspace,
+                             size_t workspace_bytes) {
+  return greedy_common(base_logits, w1, w2, prev, k, 0, k, cache, tokens,
+                       (unsigned long long*)winners, stream, shape, workspace, workspace_bytes);
+}
+
+int markov_greedy_step(const void* base_logits, const void* w1, const void* w2,
+                       const int64_t* prev, int32_t k, int32_t step, void* cache, int64_t* tokens,
+                       uint64_t* winners, markov_stream_t stream, const markov_shape_t* shape,
+                       void* workspace, size_t workspace_bytes) {
+  return greedy_common(base_logits, w1, w2, prev, k, step, step + 1, cache, tokens,
+                       (unsigned long long*)winners, stream, shape, workspace, workspace_bytes);
+}
+
+int markov_greedy_finalize(const uint64_t* winners, int64_t n, int64_t* tokens,
+                           markov_stream_t stream) {
+  if (n < 0) return MARKOV_ERR_SHAPE;
+  if (n == 0) return MARKOV_OK;
+  if (!winners || !tokens) return MARKOV_ERR_NULL;
+  finalize_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, (hipStream_t)stream>>>(
+      (const unsigned long long*)winners, n, tokens);
+  if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
+  return MARKOV_OK;
+}
+
 int markov_sample_step(const void* base_logits, const void* w1, const void* w2,
                        const int64_t* prev, const int64_t* seeds, const int64_t* positions,
                        int32_t k, int32_t step, const float* temperature, void* cache,
@@ -539,8 +626,13 @@ int markov_debug_bias(const void* w1, const void* w2, const int64_t* tok, void* 
   if (rc) return rc;
   if (!w1 || !w2 || !tok || !bias) return MARKOV_ERR_NULL;
   if (!aligned16(w1) || !aligned16(w2) || !aligned16(bias)) return MARKOV_ERR_ALIGN;
-  return launch_steps(MODE_BIAS, nullptr, w1, w2, tok, nullptr, nullptr, 1, 0, 1, nullptr,
-                      nullptr, nullptr, bias, stream, shape, nullptr);
+  Call c;
+  c.mode = MODE_BIAS;
+  c.w1 = w1;
+  c.w2 = w2;
+  c.prev = tok;
+  c.bias_out = bias;
+  return launch_steps(c, stream, shape, nullptr);
 }
 
 int markov_debug_gumbel(const float* logits, const uint32_t* ids, int64_t n, float temperature,

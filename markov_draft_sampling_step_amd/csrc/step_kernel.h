@@ -65,6 +65,7 @@ struct StepArgs {
   const float* gtable;        // the noise bound table (in the workspace)
   const uint32_t* ttable;     // the transform table's stamp, then its 32768 entries
   uint16_t* bias_out;
+  unsigned long long* winners;  // greedy: [rows, k] packed winners (NULL: not written)
   int rows, V, R, k, step, nslabs, mode;
   int tt_layout;              // LDS holds the transform table at address 0
   float mult, inv_cap, cap;
@@ -93,7 +94,14 @@ constexpr size_t LDS_MAX = 160 * 1024;
 // each line SG-fold; the reader pays SG loads per row.
 constexpr int SG = 8;
 
-enum Mode { MODE_SAMPLE = 0, MODE_SAMPLE_EXACT = 1, MODE_BIAS = 2, MODE_SAMPLE_FALLBACK = 3 };
+enum Mode { MODE_SAMPLE = 0, MODE_SAMPLE_EXACT = 1, MODE_BIAS = 2, MODE_SAMPLE_FALLBACK = 3, MODE_GREEDY = 4 };
+
+// Compile-time variants of the step kernel (bits):
+//   V_EXACT   the test-only variant that takes the exact key of every element;
+//   V_GREEDY  every row at temperature 0: no noise table, no hashing, an
+//             exact in-register argmax under the total order (NaN and -inf
+//             included, so no re-scan and the cache write may be skipped).
+constexpr int V_SAMPLE = 0, V_EXACT = 1, V_GREEDY = 2;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -503,13 +511,17 @@ __host__ __device__ __forceinline__ size_t lds_dynamic(int rp, int R) {
 
 // the noise table in LDS: the lines for one row group (up to MRB_MAX row
 // blocks), the constants for two
-__host__ __device__ __forceinline__ size_t lds_table(int rp) { return (rp >> 4) > MRB_MAX ? GTC_BYTES : GT_BYTES; }
+__host__ __device__ __forceinline__ size_t lds_table(int rp, bool greedy = false) {
+  return greedy ? 0 : (rp >> 4) > MRB_MAX ? GTC_BYTES : GT_BYTES;
+}
 
-__host__ __device__ __forceinline__ size_t lds_total(int rp, int R) { return lds_table(rp) + lds_dynamic(rp, R); }
+__host__ __device__ __forceinline__ size_t lds_total(int rp, int R, bool greedy = false) {
+  return lds_table(rp, greedy) + lds_dynamic(rp, R);
+}
 
 // the transform-table layout: one row group (the lines), a soft cap, and room
-__host__ __device__ __forceinline__ bool tt_fits(int rp, int R) {
-  return (rp >> 4) <= MRB_MAX && TT_BYTES + lds_total(rp, R) <= LDS_MAX;
+__host__ __device__ __forceinline__ bool tt_fits(int rp, int R, bool greedy = false) {
+  return (rp >> 4) <= MRB_MAX && TT_BYTES + lds_total(rp, R, greedy) <= LDS_MAX;
 }
 
 // ---------------------------------------------------------------- the step
@@ -518,10 +530,12 @@ __host__ __device__ __forceinline__ bool tt_fits(int rp, int R) {
 // or 2 for more than 8 row blocks: then the two waves of a SIMD split the
 // rows, both take every slab of the workgroup and read its w2 tiles through
 // L2), MRB = row blocks per wave (a power of two, the wave's real count may
-// be lower), EXACT = the test-only variant that takes the exact key of
-// every element. One launch runs step a.step.
-template <int KB, int RG, int MRB, bool EXACT>
+// be lower), VAR = the variant bits (V_EXACT, V_GREEDY). One launch runs
+// step a.step.
+template <int KB, int RG, int MRB, int VAR>
 __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
+  constexpr bool EXACT = (VAR & V_EXACT) != 0;
+  constexpr bool GREEDY = (VAR & V_GREEDY) != 0;
   constexpr int NB = MRB == 1 ? 2 : 1;                   // w2 tiles in flight per wave
   constexpr int D = MRB - 1 < 3 ? MRB - 1 : 3;           // row blocks contracted ahead
   constexpr int S = RG == 1 ? 2 : 1;                     // waves splitting one SIMD's slabs
@@ -530,7 +544,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   // lanes carry their top element's cached logit (one word per row block;
   // the two-row-group plans have no registers to spare and read it back)
   constexpr bool CARRY = RG == 1;
-  constexpr uint32_t TB = LIN ? GT_BYTES : GTC_BYTES;    // the table this plan copies to LDS
+  constexpr uint32_t TB = GREEDY ? 0u : LIN ? GT_BYTES : GTC_BYTES;   // the table this plan copies to LDS
   extern __shared__ __align__(16) unsigned char lds[];
   // the transform table sits at LDS address 0 only if the dynamic array
   // starts there (no static LDS); its lookups form absolute addresses
@@ -583,7 +597,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
 #pragma unroll
   for (int q = 0; q < SG; ++q) slot_in[q] = 0ull;
   if (valid) {
-    if (!bias_mode) {
+    if (!bias_mode && !GREEDY) {
       T = a.temperature[r];
       seed = a.seeds[r];
       pos = a.positions[(int64_t)r * K + s];
@@ -609,7 +623,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   static_assert(SG == 8, "the asm above pins SG slot values");
   // the noise bound table, straight into LDS: waited for with the first tile
   // (before the unit loop), in flight through the row set-up
-  if (!bias_mode) {
+  if (!bias_mode && !GREEDY) {
     for (int j = wave; j * 64 * 16 < (int)TB; j += NWV) {
       const int p = j * 64 + lane;
       if (p * 16 < (int)TB)
@@ -624,12 +638,13 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   const bool noisy_r = valid && !bias_mode && !(T == 0.0f);
   const uint64_t bn = __ballot(noisy_r), bz = __ballot(valid && !noisy_r);
   const float rcp_r = 1.0f / T;
-  const uint32_t prefix_r = (valid && !bias_mode) ? row_prefix_of(seed, s, pos) : 0u;
+  const uint32_t prefix_r = (valid && !bias_mode && !GREEDY) ? row_prefix_of(seed, s, pos) : 0u;
+  unsigned long long win_in = 0ull;   // the previous step's packed winner of this row
   if (!(bias_mode || s == 0)) {
-    unsigned long long w = slot_in[0];
+    win_in = slot_in[0];
 #pragma unroll
-    for (int q = 1; q < SG; ++q) w = slot_in[q] > w ? slot_in[q] : w;
-    tok = slot_token(w);
+    for (int q = 1; q < SG; ++q) win_in = slot_in[q] > win_in ? slot_in[q] : win_in;
+    tok = slot_token(win_in);
   }
   const int tok32 = (int)tok;
   __builtin_amdgcn_sched_barrier(0);
@@ -674,7 +689,10 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       n_src[pos_n] = (int)(ut < last ? ut : last);
       n_info[pos_n] = RowInfo{r * K + s, rcp_r, prefix_r, T};
       if (!bias_mode && blockIdx.x == 0) {
-        if (s > 0) a.tokens[(int64_t)r * K + s - 1] = (int64_t)(uint32_t)tok32;   // previous step's
+        if (s > 0) {                                                 // previous step's
+          a.tokens[(int64_t)r * K + s - 1] = (int64_t)(uint32_t)tok32;
+          if (a.winners) a.winners[(int64_t)r * K + s - 1] = win_in;
+        }
 #pragma unroll
         for (int q = 0; q < SG; ++q)                                  // next step's slots start empty
           a.slots[((size_t)((s + 1) % 3) * SG + q) * rows + r] = 0ull;
@@ -799,7 +817,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     const bool pnext = i + 1 < U;              // the next unit (base logit prefetch)
     const int psl = sl + slab_step;
     uint32_t kw[8];
-    if (!bias_mode) {
+    if (!bias_mode && !GREEDY) {
       uint32_t kc = (uint32_t)tg * MM_C1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -890,9 +908,33 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         l[2 * q] = bf_lo(cw[q]);
         l[2 * q + 1] = bf_hi(cw[q]);
       }
-      if (active)
+      if (active && (!GREEDY || a.cache != nullptr))
         __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]},
                                     (u32x4_t*)(a.cache + (size_t)info.rk * V + tg));
+      if (GREEDY) {
+        // the row's largest logit under the total order, exactly: elements
+        // arrive in rising id, so an element wins over the kept one iff the
+        // kept one is not NaN and the element is NaN or larger (a NaN is
+        // kept from its first occurrence; ties keep the earlier id); the
+        // first element of a row is taken whatever it is (so -inf too)
+        if (active) {
+          float x1 = v1[j];
+          uint32_t e1 = __float_as_uint(v2[j]);
+          bool have = idt[j] != NONE, upd = false;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool take = !have || (!__builtin_isnan(x1) && (__builtin_isnan(l[e]) || l[e] > x1));
+            x1 = take ? l[e] : x1;
+            e1 = take ? (uint32_t)e : e1;
+            upd = upd || take;
+            have = true;
+          }
+          if (upd) idt[j] = tg;
+          v1[j] = x1;
+          v2[j] = __uint_as_float(e1);
+        }
+        continue;
+      }
 
       if (EXACT) {
         if (active) {
@@ -1019,7 +1061,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   // embeddings); with carried logits the cache stores drain meanwhile (the
   // barrier before the fallback scans, which read them back, waits for
   // them), else they are read back below and waited for here
-  if (CARRY) {
+  if (CARRY || GREEDY) {
     lds_barrier();
   } else {
     __builtin_amdgcn_s_waitcnt(0);
@@ -1263,6 +1305,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
           w = c > w ? c : w;
         }
         a.tokens[(int64_t)r2 * K + K - 1] = slot_token(w);
+        if (a.winners) a.winners[(int64_t)r2 * K + K - 1] = w;
       }
       for (int i = tid; i < 3 * SG * rows; i += NTH)
         if (i / (SG * rows) != s % 3) a.slots[i] = 0ull;
@@ -1273,20 +1316,20 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
 
 // One kernel of the step for a rank class KB and a plan (row groups, row
 // blocks per wave); nullptr for a plan the rank class does not build.
-template <int KB, bool EX>
+template <int KB, int VAR>
 StepFn pick_plan(int rg, int mrb) {
   if (rg == 1) {
     switch (mrb) {
-      case 1: return markov_step_kernel<KB, 1, 1, EX>;
-      case 2: return markov_step_kernel<KB, 1, 2, EX>;
-      case 4: return markov_step_kernel<KB, 1, 4, EX>;
-      case 8: return markov_step_kernel<KB, 1, 8, EX>;
+      case 1: return markov_step_kernel<KB, 1, 1, VAR>;
+      case 2: return markov_step_kernel<KB, 1, 2, VAR>;
+      case 4: return markov_step_kernel<KB, 1, 4, VAR>;
+      case 8: return markov_step_kernel<KB, 1, 8, VAR>;
     }
   } else if (rg == 2) {
     switch (mrb) {
-      case 8: return markov_step_kernel<KB, 2, 8, EX>;
+      case 8: return markov_step_kernel<KB, 2, 8, VAR>;
       case 16:
-        if constexpr (KB <= 8) return markov_step_kernel<KB, 2, 16, EX>;
+        if constexpr (KB <= 8) return markov_step_kernel<KB, 2, 16, VAR>;
         break;
     }
   }
@@ -1295,12 +1338,15 @@ StepFn pick_plan(int rg, int mrb) {
 
 }  // namespace
 
-// The step kernels of each rank class are compiled in a translation unit of
-// their own (step_kb<KB>.hip); each returns its kernel for a plan.
+// The step kernels of each (rank class, variant) are compiled in a translation
+// unit of their own (step_inst.hip built once per pair); each returns its
+// kernel for a plan. X(KB, VAR) lists the pairs built.
+#define MARKOV_STEP_INSTANCES(X) \
+  X(1, 0) X(1, 1) X(1, 2) X(2, 0) X(2, 1) X(2, 2) X(4, 0) X(4, 1) X(4, 2) \
+  X(8, 0) X(8, 1) X(8, 2) X(16, 0) X(16, 1) X(16, 2)
+
 namespace markov_impl {
-StepFn step_kernel_kb1(int rg, int mrb, bool exact);
-StepFn step_kernel_kb2(int rg, int mrb, bool exact);
-StepFn step_kernel_kb4(int rg, int mrb, bool exact);
-StepFn step_kernel_kb8(int rg, int mrb, bool exact);
-StepFn step_kernel_kb16(int rg, int mrb, bool exact);
+#define MARKOV_DECLARE_PICKER(KB, VAR) StepFn step_kernel_kb##KB##_v##VAR(int rg, int mrb);
+MARKOV_STEP_INSTANCES(MARKOV_DECLARE_PICKER)
+#undef MARKOV_DECLARE_PICKER
 }  // namespace markov_impl

@@ -59,6 +59,7 @@ _SIGS = {
     "oracle_cache_value": (ctypes.c_uint16, [ctypes.c_uint16, ctypes.c_uint16, _F32, _F32]),
     "oracle_before": (ctypes.c_int, [_F32, _I64, _F32, _I64]),
     "oracle_argmax": (_I64, [_P, _I64]),
+    "oracle_pack_winner": (ctypes.c_uint64, [_F32, _I64]),
     "oracle_w1_row": (_I64, [_I64, _I32]),
     "oracle_step": (None, [_I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _I64, _I32, _P,
                            _F32, _F32, _P, _I64, _P, _I64, _P, _I64, _P, _I32]),
@@ -159,6 +160,10 @@ def cache_admissible(base: int, e: np.ndarray, w: np.ndarray, mult: float, softc
 
 def before(v1: float, i1: int, v2: float, i2: int) -> bool:
     return bool(lib().oracle_before(float(v1), int(i1), float(v2), int(i2)))
+
+
+def pack_winner(v: float, i: int) -> int:
+    return int(lib().oracle_pack_winner(float(v), int(i)))
 
 
 def argmax(keys: np.ndarray) -> int:

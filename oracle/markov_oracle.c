@@ -365,6 +365,26 @@ EXPORT int oracle_before(float v1, int64_t i1, float v2, int64_t i2) {
   return i1 < i2;
 }
 
+/*
+ * The packed 64-bit image of a winner (v, id) in the greedy slot format
+ * (TensorRT Edge-LLM "DSpark kernels" page, `dsparkMarkovGreedyFusedStep`:
+ * an orderable float key, ties to the lowest vocabulary index): unsigned
+ * comparison of two images agrees with oracle_before. High word: every NaN
+ * maps to 0xffffffff; otherwise -0 counts as +0, a non-negative value maps to
+ * its bits with the top bit set, a negative one to its bits inverted (larger
+ * magnitude, smaller image). Low word: the complement of the 32-bit id.
+ */
+EXPORT uint64_t oracle_pack_winner(float v, int64_t id) {
+  uint32_t hi;
+  if (isnan(v)) {
+    hi = 0xffffffffu;
+  } else {
+    uint32_t b = f32_to_bits(v == 0.0f ? 0.0f : v);
+    hi = (b >> 31) ? ~b : (b | 0x80000000u);
+  }
+  return ((uint64_t)hi << 32) | (uint64_t)(uint32_t)~(uint32_t)id;
+}
+
 /* Argmax of keys[0..n) under that order, scanning ids upward. */
 EXPORT int64_t oracle_argmax(const float* keys, int64_t n) {
   int64_t best = 0;
@@ -479,6 +499,9 @@ EXPORT void oracle_sample_sequential(int32_t rows, int32_t V, int32_t R, int32_t
  * `literal` != 0 takes dc(v) = one bf16 ulp of the oracle's cache value at
  * every v; otherwise dc(v) = |cache_g(v) - cache_o(v)| (the realized
  * difference; 0 where the two agree).
+ * Equal cache values (infinities included) differ by 0; an infinite key has
+ * no rounding band (its quotient is infinite, the noise finite), and at
+ * an infinite cached value the literal band is 0.
  * Decided: for every v != w, K(w) - K(v) > d(w) + d(v), or K(w) == K(v) with
  * d(w) = d(v) = 0 and w < v. A NaN winner is decided when its NaN comes from
  * the cache on both sides and no lower id has a NaN cache value on either
@@ -500,15 +523,18 @@ static int keys_and_bands(int32_t V, const uint16_t* cache_o, const uint16_t* ca
     if (isnan(lo) != isnan(lg)) ok = 0;
     double dc;
     if (literal)
-      dc = oracle_ulp_bf16(lo);
+      dc = isinf(lo) ? 0.0 : oracle_ulp_bf16(lo);   /* infinities are exact */
     else
-      dc = (isnan(lo) && isnan(lg)) ? 0.0 : fabs((double)lg - (double)lo);
+      dc = ((isnan(lo) && isnan(lg)) || lo == lg) ? 0.0 : fabs((double)lg - (double)lo);
     float lb = 0.0f, L = 0.0f;
     uint32_t h = noisy ? oracle_noise_hash(seed, step, position, (uint32_t)v) : 0u;
     K[v] = oracle_gumbel_key(lo, T, h, &lb, &L);
     if (noisy) {
-      double eps = 2.0 * oracle_ulp32(K[v]) + 2.0 * oracle_ulp32(lb) +
-                   2.0 * fabs(oracle_ulp32(L) / (double)L);
+      /* an infinite key is exact: the quotient is infinite and the finite
+       * noise cannot move it */
+      double eps = isinf(K[v]) ? 0.0
+                               : 2.0 * oracle_ulp32(K[v]) + 2.0 * oracle_ulp32(lb) +
+                                     2.0 * fabs(oracle_ulp32(L) / (double)L);
       d[v] = dc / fabs((double)T) + eps;
     } else {
       d[v] = dc;

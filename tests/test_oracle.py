@@ -790,3 +790,49 @@ def test_cache_is_monotone_in_the_bias(oracle_lib):
             assert all(c1 <= c2 for c1, c2 in zip(cs, cs[1:])), (trial, cs)
         else:
             assert all(c1 >= c2 for c1, c2 in zip(cs, cs[1:])), (trial, cs)
+
+
+def test_packed_winner_orders_as_the_total_order(oracle_lib):
+    """The greedy slot format: unsigned comparison of two packed images gives
+    the total order (oracle_before), on random pairs rich in ties, signed
+    zeros, infinities and NaNs of any payload; the low word returns the id."""
+    rng = np.random.default_rng(47)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 1.0, -1.0, 2.0 ** -149, -(2.0 ** -149),
+                        3.4028234663852886e38], dtype=np.float32)
+    nans = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF], dtype=np.uint32).view(np.float32)
+    for trial in range(20000):
+        v = []
+        for _ in range(2):
+            c = rng.integers(0, 4)
+            v.append(float(special[rng.integers(0, len(special))]) if c == 0 else
+                     float(nans[rng.integers(0, len(nans))]) if c == 1 else
+                     float(np.float32(rng.integers(-3, 4))) if c == 2 else
+                     float(np.float32(rng.standard_normal() * 10.0 ** rng.integers(-5, 5))))
+        i1, i2 = (int(x) for x in rng.integers(0, 200000, size=2))
+        p1, p2 = oracle_lib.pack_winner(v[0], i1), oracle_lib.pack_winner(v[1], i2)
+        if (i1, np.float32(v[0]).view(np.uint32)) == (i2, np.float32(v[1]).view(np.uint32)):
+            continue
+        assert (p1 > p2) == oracle_lib.before(v[0], i1, v[1], i2) or (i1 == i2 and p1 == p2), \
+            (v, i1, i2)
+        assert (~p1) & 0xFFFFFFFF == i1
+
+
+def test_decided_with_infinite_logits(oracle_lib):
+    """Masked logits: a row whose other tokens are -inf is decided (at T = 0
+    and at a noisy T), a tie of two +inf logits at T = 0 goes to the lower id
+    and is decided, and a row that is -inf everywhere is decided for token 0
+    (all keys equal, the lowest id)."""
+    V = 32
+    NEG, POS = -float("inf"), float("inf")
+    for T in (0.0, 1.0, 0.7):
+        co = _row(V, {5: 1.5}, fill=NEG)
+        for lit in (False, True):
+            ok, w = oracle_lib.decided(co, co, T, 9, 0, 3, literal=lit)
+            assert ok and w == 5, (T, lit)
+    co = _row(V, {7: POS, 12: POS})
+    ok, w = oracle_lib.decided(co, co, 0.0, 9, 0, 3)
+    assert ok and w == 7
+    co = np.full(V, _bf(NEG), dtype=np.uint16)
+    ok, w = oracle_lib.decided(co, co, 0.0, 9, 0, 3)
+    assert ok and w == 0
+    assert oracle_lib.near_tie(co, co, 0.0, 9, 0, 3, 0)
