@@ -59,6 +59,17 @@ _SIGS = {
     "oracle_cache_value": (ctypes.c_uint16, [ctypes.c_uint16, ctypes.c_uint16, _F32, _F32]),
     "oracle_before": (ctypes.c_int, [_F32, _I64, _F32, _I64]),
     "oracle_argmax": (_I64, [_P, _I64]),
+    "oracle_e4m3_decode": (_F32, [ctypes.c_uint8]),
+    "oracle_e4m3_encode": (ctypes.c_uint8, [_F32]),
+    "oracle_fp16_to_f32": (_F32, [ctypes.c_uint16]),
+    "oracle_fp16_round": (ctypes.c_uint16, [_F64]),
+    "oracle_quantize_row_fp8": (ctypes.c_uint16, [_P, _I32, _P]),
+    "oracle_quantize_w2_fp8": (None, [_I32, _I32, _P, _P, _P]),
+    "oracle_bias_fp8": (ctypes.c_uint16, [_P, _P, ctypes.c_uint16, _I32, _P, _P]),
+    "oracle_cache_admissible_fp8": (ctypes.c_int, [ctypes.c_uint16, _P, _P, ctypes.c_uint16, _I32,
+                                                    _F32, _F32, ctypes.c_uint16]),
+    "oracle_step_fp8": (None, [_I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _I64, _I32, _P,
+                               _F32, _F32, _P, _I64, _P, _I64, _P, _I64, _P, _I32]),
     "oracle_pack_winner": (ctypes.c_uint64, [_F32, _I64]),
     "oracle_w1_row": (_I64, [_I64, _I32]),
     "oracle_step": (None, [_I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _I64, _I32, _P,
@@ -166,6 +177,49 @@ def pack_winner(v: float, i: int) -> int:
     return int(lib().oracle_pack_winner(float(v), int(i)))
 
 
+def e4m3_decode(c: int) -> float:
+    return lib().oracle_e4m3_decode(int(c))
+
+
+def e4m3_encode(x: float) -> int:
+    return int(lib().oracle_e4m3_encode(float(x)))
+
+
+def fp16_to_f32(h: int) -> float:
+    return lib().oracle_fp16_to_f32(int(h))
+
+
+def fp16_round(x: float) -> int:
+    return int(lib().oracle_fp16_round(float(x)))
+
+
+def quantize_w2_fp8(w2: np.ndarray):
+    """(codes uint8 [V, R], scales uint16 [V] FP16 bits) of a bf16 w2."""
+    w2 = np.ascontiguousarray(w2, dtype=np.uint16)
+    V, R = w2.shape
+    q = np.empty((V, R), dtype=np.uint8)
+    sc = np.empty(V, dtype=np.uint16)
+    lib().oracle_quantize_w2_fp8(V, R, _ptr(w2), _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def bias_fp8(e: np.ndarray, q: np.ndarray, scale_bits: int) -> tuple[int, float, float]:
+    e = np.ascontiguousarray(e, dtype=np.uint16)
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s64, sabs = ctypes.c_double(), ctypes.c_double()
+    b = lib().oracle_bias_fp8(_ptr(e), _ptr(q), int(scale_bits), len(e), ctypes.byref(s64),
+                              ctypes.byref(sabs))
+    return int(b), s64.value, sabs.value
+
+
+def cache_admissible_fp8(base: int, e: np.ndarray, q: np.ndarray, scale_bits: int, mult: float,
+                         softcap: float, c_dev: int) -> bool:
+    e = np.ascontiguousarray(e, dtype=np.uint16)
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    return bool(lib().oracle_cache_admissible_fp8(int(base), _ptr(e), _ptr(q), int(scale_bits),
+                                                  len(e), float(mult), float(softcap), int(c_dev)))
+
+
 def argmax(keys: np.ndarray) -> int:
     keys = np.ascontiguousarray(keys, dtype=np.float32)
     return int(lib().oracle_argmax(_ptr(keys), len(keys)))
@@ -180,17 +234,25 @@ def w1_row(token: int, V: int) -> int:
 def step(base_step: np.ndarray, w1: np.ndarray, w2: np.ndarray, prev: np.ndarray,
          seeds: np.ndarray, positions_step: np.ndarray, step_index: int,
          temperature: np.ndarray, mult: float = 1.0, softcap: float = 0.0,
-         want_keys: bool = False, want_bias: bool = False, threads: int = 1):
+         want_keys: bool = False, want_bias: bool = False, threads: int = 1,
+         w2q: np.ndarray | None = None, w2s: np.ndarray | None = None):
     """One teacher-forced draft step for every row.
 
     base_step: bf16 bits [rows, V] of this step; positions_step: [rows].
+    With w2q / w2s (E4M3 codes [V, R], FP16 scale bits [V]) the bias comes
+    from them instead of w2 (w2 is then ignored and may be None).
     Returns dict(cache [rows,V] u16, tokens [rows] i64, keys?, bias?).
     """
     rows, V = base_step.shape
     R = w1.shape[1]
     base_step = np.ascontiguousarray(base_step, dtype=np.uint16)
     w1 = np.ascontiguousarray(w1, dtype=np.uint16)
-    w2 = np.ascontiguousarray(w2, dtype=np.uint16)
+    fp8 = w2q is not None
+    if fp8:
+        w2q = np.ascontiguousarray(w2q, dtype=np.uint8)
+        w2s = np.ascontiguousarray(w2s, dtype=np.uint16)
+    else:
+        w2 = np.ascontiguousarray(w2, dtype=np.uint16)
     prev = np.ascontiguousarray(prev, dtype=np.int64)
     seeds = np.ascontiguousarray(seeds, dtype=np.int64)
     pos = np.ascontiguousarray(positions_step, dtype=np.int64)
@@ -199,10 +261,16 @@ def step(base_step: np.ndarray, w1: np.ndarray, w2: np.ndarray, prev: np.ndarray
     tokens = np.empty(rows, dtype=np.int64)
     keys = np.empty((rows, V), dtype=np.float32) if want_keys else None
     bias_out = np.empty((rows, V), dtype=np.uint16) if want_bias else None
-    lib().oracle_step(rows, V, R, _ptr(base_step), V, _ptr(w1), _ptr(w2), _ptr(prev),
-                      _ptr(seeds), _ptr(pos), 1, int(step_index), _ptr(temp), float(mult),
-                      float(softcap), _ptr(cache), V, _ptr(keys), V, _ptr(bias_out), V,
-                      _ptr(tokens), int(threads))
+    if fp8:
+        lib().oracle_step_fp8(rows, V, R, _ptr(base_step), V, _ptr(w1), _ptr(w2q), _ptr(w2s),
+                              _ptr(prev), _ptr(seeds), _ptr(pos), 1, int(step_index), _ptr(temp),
+                              float(mult), float(softcap), _ptr(cache), V, _ptr(keys), V,
+                              _ptr(bias_out), V, _ptr(tokens), int(threads))
+    else:
+        lib().oracle_step(rows, V, R, _ptr(base_step), V, _ptr(w1), _ptr(w2), _ptr(prev),
+                          _ptr(seeds), _ptr(pos), 1, int(step_index), _ptr(temp), float(mult),
+                          float(softcap), _ptr(cache), V, _ptr(keys), V, _ptr(bias_out), V,
+                          _ptr(tokens), int(threads))
     out = {"cache": cache, "tokens": tokens}
     if want_keys:
         out["keys"] = keys

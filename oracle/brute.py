@@ -235,3 +235,76 @@ def ulp_bf16(x: float) -> float:
     a = Fraction(abs(x))
     e = -126 if a == 0 else max(_binade(a), -126)
     return float(Fraction(2) ** (e - 7))
+
+
+# -- FP8 (E4M3) w2 with an FP16 row scale ----------------------------------------
+# TensorRT Edge-LLM "DSpark kernels" page: `dsparkQuantizeMarkovW2Fp8`,
+# `dsparkMarkovGreedyFusedStepFp8`. Closed forms of the formats, exact
+# rationals, a bisection over the sorted code values.
+
+def e4m3_value(c: int):
+    """Exact value of an E4M3 code (Fraction), or None for NaN."""
+    s, e, m = c >> 7, (c >> 3) & 15, c & 7
+    if e == 15 and m == 7:
+        return None
+    v = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return -v if s else v
+
+
+_E4M3_POS = [(e4m3_value(c), c) for c in range(0x7F)]        # rising values, codes 0 .. 0x7E
+
+
+def e4m3_encode(x: float) -> int:
+    if math.isnan(x):
+        return 0xFF if math.copysign(1.0, x) < 0 else 0x7F
+    sign = 0x80 if math.copysign(1.0, x) < 0 else 0
+    a = Fraction(abs(x)) if not math.isinf(x) else Fraction(10 ** 6)
+    if a >= 448:
+        return sign | 0x7E
+    import bisect
+
+    vals = [v for v, _ in _E4M3_POS]
+    i = bisect.bisect_left(vals, a)
+    if i < len(vals) and vals[i] == a:
+        return sign | _E4M3_POS[i][1]
+    lo, hi = _E4M3_POS[i - 1], _E4M3_POS[i]
+    dl, dh = a - lo[0], hi[0] - a
+    pick = lo if dl < dh else hi if dh < dl else (lo if lo[1] % 2 == 0 else hi)
+    return sign | pick[1]
+
+
+def fp16_rn(q) -> float:
+    """Nearest binary16 value (11 significand bits, exponents -14 .. 15)."""
+    return rn(Fraction(q), 11, -14, 15)
+
+
+def quantize_row(w_bits):
+    """(codes, scale value) of a bf16 row."""
+    amax = max(abs(Fraction(bf_value(int(b)))) for b in w_bits)
+    scale = fp16_rn(amax / 448)
+    if scale == 0:
+        return [0] * len(w_bits), 0.0
+    return [e4m3_encode(rn32(Fraction(bf_value(int(b))) / Fraction(scale))) for b in w_bits], scale
+
+
+def bias_fp8(e_bits, codes, scale: float) -> float:
+    acc = 0.0
+    for eb, c in zip(e_bits, codes):
+        acc = rn32(Fraction(acc) + Fraction(bf_value(int(eb))) * e4m3_value(int(c)))
+    return rnbf(rn32(Fraction(scale) * Fraction(acc)))
+
+
+def step_fp8(base_row, w1, codes, scales, prev: int, seed: int, position: int, step_index: int,
+             T: float, mult: float = 1.0, softcap: float = 0.0):
+    """One row, one step with an E4M3 w2 (codes [V][R], scale values [V])."""
+    V = len(base_row)
+    row = min(prev & 0xFFFFFFFFFFFFFFFF, V - 1)
+    e = [int(x) for x in w1[row]]
+    cache, keys = [], []
+    for v in range(V):
+        b = bias_fp8(e, [int(c) for c in codes[v]], float(scales[v]))
+        c = cache_value(int(base_row[v]), bf_bits(b), mult, softcap)
+        cache.append(bf_bits(c))
+        keys.append(key(c, T, noise_hash(seed, step_index, position, v)))
+    token = sorted(range(V), key=lambda v: order_key(keys[v], v))[0]
+    return cache, keys, token

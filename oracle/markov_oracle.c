@@ -345,6 +345,146 @@ EXPORT int oracle_cache_admissible(uint16_t base, const uint16_t* e, const uint1
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP8 (E4M3) w2 with a per-row FP16 scale                                   */
+/* ------------------------------------------------------------------------ */
+/*
+ * [EDGE] TensorRT Edge-LLM "DSpark kernels" page: `dsparkQuantizeMarkovW2Fp8`
+ * (w2 [V, R] to E4M3 bytes of w / rowScale, one FP16 scale per row,
+ * rowScale = rowAbsMax / 448 so each row spans the E4M3 range; R % 16 == 0)
+ * and `dsparkMarkovGreedyFusedStepFp8` (the step with that w2). Readings:
+ *   - the source w2 is the bf16 w2 of the other pages;
+ *   - rowScale = the FP16 value nearest rowAbsMax / 448 (ties to even);
+ *   - code = E4M3 of the binary32 quotient w / float(rowScale), nearest, ties
+ *     to even, saturating at +-448 (E4M3 has no infinities); a zero scale (a
+ *     zero row, or a scale below FP16's range) gives zero codes;
+ *   - the bias is bf16(RN32(float(rowScale) * sum_j e_j q_j)) with q_j the
+ *     code's value: the dot as for bf16 w2 (every E4M3 value is a bf16, so
+ *     the products are exact in binary32), then the scale, then one bf16
+ *     rounding.
+ */
+
+/* The value of an E4M3 code: sign, 4 exponent bits (bias 7), 3 mantissa
+ * bits; exponent 0 holds the subnormals m 2^-9; S.1111.111 is NaN. */
+EXPORT float oracle_e4m3_decode(uint8_t c) {
+  int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return (float)(sgn ? -v : v);
+}
+
+/* E4M3 nearest to x, ties to the even code, saturating at +-448; NaN gives
+ * the NaN code of x's sign. Found by search over the 127 non-negative finite
+ * codes (their values rise with the code). */
+EXPORT uint8_t oracle_e4m3_encode(float x) {
+  uint8_t sgn = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return (uint8_t)(sgn | 0x7F);
+  double a = fabs((double)x);
+  if (a >= 448.0) return (uint8_t)(sgn | 0x7E);
+  uint8_t best = 0;
+  for (int c = 1; c <= 0x7E; ++c) {
+    double dc = fabs((double)oracle_e4m3_decode((uint8_t)c) - a);
+    double db = fabs((double)oracle_e4m3_decode(best) - a);
+    if (dc < db || (dc == db && (c & 1) == 0)) best = (uint8_t)c;
+  }
+  return (uint8_t)(sgn | best);
+}
+
+/* IEEE binary16: the value of a pattern, and the pattern nearest to x (ties
+ * to even, overflow to infinity, NaN kept). */
+EXPORT float oracle_fp16_to_f32(uint16_t h) {
+  int sgn = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 31) v = m ? NAN : INFINITY;
+  else if (e == 0) v = ldexp((double)m, -24);
+  else v = ldexp(1.0 + m / 1024.0, e - 15);
+  return (float)(sgn ? -v : v);
+}
+
+EXPORT uint16_t oracle_fp16_round(double x) {
+  uint16_t sgn = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return (uint16_t)(sgn | 0x7E00);
+  double a = fabs(x);
+  /* the two neighbours among the non-negative patterns 0 .. 0x7C00 (inf) */
+  uint16_t lo = 0, hi = 0x7C00;
+  while (hi - lo > 1) {                  /* values rise with the pattern */
+    uint16_t mid = (uint16_t)((lo + hi) / 2);
+    if ((double)oracle_fp16_to_f32(mid) <= a) lo = mid; else hi = mid;
+  }
+  double vl = (double)oracle_fp16_to_f32(lo);
+  if (vl == a) return (uint16_t)(sgn | lo);
+  /* one ulp past the largest finite (65504) counts as 65536 for the tie */
+  double vh = hi == 0x7C00 ? 65536.0 : (double)oracle_fp16_to_f32(hi);
+  if (a >= vh) return (uint16_t)(sgn | hi);
+  double dl = a - vl, dh = vh - a;
+  uint16_t r = dl < dh ? lo : dh < dl ? hi : ((lo & 1) ? hi : lo);
+  return (uint16_t)(sgn | r);
+}
+
+/* One w2 row to E4M3 codes q[R] and its FP16 scale (the bits). */
+EXPORT uint16_t oracle_quantize_row_fp8(const uint16_t* w, int32_t R, uint8_t* q) {
+  float amax = 0.0f;
+  for (int32_t j = 0; j < R; ++j) {
+    float a = fabsf(oracle_bf16_to_f32(w[j]));
+    if (a > amax) amax = a;               /* a NaN weight is skipped */
+  }
+  uint16_t sbits = oracle_fp16_round((double)amax / 448.0);
+  float scale = oracle_fp16_to_f32(sbits);
+  for (int32_t j = 0; j < R; ++j)
+    q[j] = scale == 0.0f ? (uint8_t)0 : oracle_e4m3_encode(oracle_bf16_to_f32(w[j]) / scale);
+  return sbits;
+}
+
+EXPORT void oracle_quantize_w2_fp8(int32_t V, int32_t R, const uint16_t* w2, uint8_t* q,
+                                   uint16_t* scales) {
+  for (int32_t v = 0; v < V; ++v)
+    scales[v] = oracle_quantize_row_fp8(w2 + (size_t)v * R, R, q + (size_t)v * R);
+}
+
+/* The bias against an E4M3 w2 row: the binary32 dot of e and the codes'
+ * values in index order, times the scale in binary32, rounded to bf16.
+ * s64 / sabs (optional) get the unscaled dot in binary64 and its sum of
+ * |products|. */
+EXPORT uint16_t oracle_bias_fp8(const uint16_t* e, const uint8_t* q, uint16_t scale_bits, int32_t R,
+                                double* s64, double* sabs) {
+  float acc = 0.0f;
+  double d = 0.0, a = 0.0;
+  for (int32_t j = 0; j < R; ++j) {
+    float p = oracle_bf16_to_f32(e[j]) * oracle_e4m3_decode(q[j]);
+    acc = acc + p;
+    d += (double)p;
+    a += fabs((double)p);
+  }
+  if (s64) *s64 = d;
+  if (sabs) *sabs = a;
+  float scaled = oracle_fp16_to_f32(scale_bits) * acc;
+  return oracle_bf16_round(scaled);
+}
+
+/* oracle_cache_admissible for an E4M3 w2 row: the admissible unscaled dots
+ * are those within gamma_R sum|p| of the exact one (any summation order),
+ * then scaled and rounded as the definition does; the oracle's bias one
+ * bf16 step either way also counts. */
+EXPORT int oracle_cache_admissible_fp8(uint16_t base, const uint16_t* e, const uint8_t* q,
+                                       uint16_t scale_bits, int32_t R, float mult, float softcap,
+                                       uint16_t c_dev) {
+  double s64 = 0.0, sabs = 0.0;
+  uint16_t b_o = oracle_bias_fp8(e, q, scale_bits, R, &s64, &sabs);
+  const double u = ldexp(1.0, -24), gamma = R * u / (1.0 - R * u);
+  const float sc = oracle_fp16_to_f32(scale_bits);
+  float x1 = sc * (float)(s64 - gamma * sabs), x2 = sc * (float)(s64 + gamma * sabs);
+  if (x1 > x2) { float t = x1; x1 = x2; x2 = t; }
+  uint16_t lo = bf16_step(oracle_bf16_round(x1), 0), hi = bf16_step(oracle_bf16_round(x2), 1);
+  uint16_t dn = bf16_step(b_o, 0), up = bf16_step(b_o, 1);
+  if (oracle_bf16_to_f32(dn) < oracle_bf16_to_f32(lo)) lo = dn;
+  if (oracle_bf16_to_f32(up) > oracle_bf16_to_f32(hi)) hi = up;
+  const float c1 = oracle_bf16_to_f32(oracle_cache_value(base, lo, mult, softcap));
+  const float c2 = oracle_bf16_to_f32(oracle_cache_value(base, hi, mult, softcap));
+  const float cd = oracle_bf16_to_f32(c_dev);
+  if (isnan(c1) || isnan(c2) || isnan(cd)) return isnan(c1) && isnan(c2) && isnan(cd);
+  return (c1 <= cd && cd <= c2) || (c2 <= cd && cd <= c1);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Argmax under the total order                                              */
 /* ------------------------------------------------------------------------ */
 
@@ -403,6 +543,44 @@ EXPORT int64_t oracle_w1_row(int64_t token, int32_t V) {
   return (int64_t)(t < last ? t : last);
 }
 
+/* One step for every row with either a bf16 w2 (w2 != NULL) or an E4M3 w2
+ * (q, scales); otherwise as oracle_step below. */
+static void step_any(int32_t rows, int32_t V, int32_t R, const uint16_t* base, int64_t base_rs,
+                     const uint16_t* w1, const uint16_t* w2, const uint8_t* q,
+                     const uint16_t* scales, const int64_t* prev, const int64_t* seeds,
+                     const int64_t* positions, int64_t pos_rs, int32_t step,
+                     const float* temperature, float mult, float softcap, uint16_t* cache,
+                     int64_t cache_rs, float* keys, int64_t keys_rs, uint16_t* bias,
+                     int64_t bias_rs, int64_t* tokens, int32_t threads) {
+#ifdef _OPENMP
+  int nt = threads > 0 ? threads : 1;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+#endif
+  for (int32_t r = 0; r < rows; ++r) {
+    const uint16_t* e = w1 + (size_t)oracle_w1_row(prev[r], V) * (size_t)R;
+    float T = temperature[r];
+    int64_t position = positions[(int64_t)r * pos_rs];
+    int64_t best = -1;
+    float best_key = 0.0f;
+    for (int32_t v = 0; v < V; ++v) {
+      uint16_t b = w2 ? oracle_bias(e, w2 + (size_t)v * (size_t)R, R, NULL, NULL)
+                      : oracle_bias_fp8(e, q + (size_t)v * (size_t)R, scales[v], R, NULL, NULL);
+      uint16_t c = oracle_cache_value(base[(int64_t)r * base_rs + v], b, mult, softcap);
+      cache[(int64_t)r * cache_rs + v] = c;
+      if (bias) bias[(int64_t)r * bias_rs + v] = b;
+      float l = oracle_bf16_to_f32(c);
+      uint32_t h = oracle_noisy(T) ? oracle_noise_hash(seeds[r], step, position, (uint32_t)v) : 0u;
+      float key = oracle_gumbel_key(l, T, h, NULL, NULL);
+      if (keys) keys[(int64_t)r * keys_rs + v] = key;
+      if (best < 0 || oracle_before(key, v, best_key, best)) {
+        best = v;
+        best_key = key;
+      }
+    }
+    tokens[r] = best;
+  }
+}
+
 /*
  * One draft step for every row, teacher-forced from `prev` (the token that
  * feeds this step). Follows one iteration of the eager loop ([KIMI] and
@@ -425,32 +603,23 @@ EXPORT void oracle_step(int32_t rows, int32_t V, int32_t R, const uint16_t* base
                         int32_t step, const float* temperature, float mult, float softcap,
                         uint16_t* cache, int64_t cache_rs, float* keys, int64_t keys_rs,
                         uint16_t* bias, int64_t bias_rs, int64_t* tokens, int32_t threads) {
-#ifdef _OPENMP
-  int nt = threads > 0 ? threads : 1;
-#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
-#endif
-  for (int32_t r = 0; r < rows; ++r) {
-    const uint16_t* e = w1 + (size_t)oracle_w1_row(prev[r], V) * (size_t)R;
-    float T = temperature[r];
-    int64_t position = positions[(int64_t)r * pos_rs];
-    int64_t best = -1;
-    float best_key = 0.0f;
-    for (int32_t v = 0; v < V; ++v) {
-      uint16_t b = oracle_bias(e, w2 + (size_t)v * (size_t)R, R, NULL, NULL);
-      uint16_t c = oracle_cache_value(base[(int64_t)r * base_rs + v], b, mult, softcap);
-      cache[(int64_t)r * cache_rs + v] = c;
-      if (bias) bias[(int64_t)r * bias_rs + v] = b;
-      float l = oracle_bf16_to_f32(c);
-      uint32_t h = oracle_noisy(T) ? oracle_noise_hash(seeds[r], step, position, (uint32_t)v) : 0u;
-      float key = oracle_gumbel_key(l, T, h, NULL, NULL);
-      if (keys) keys[(int64_t)r * keys_rs + v] = key;
-      if (best < 0 || oracle_before(key, v, best_key, best)) {
-        best = v;
-        best_key = key;
-      }
-    }
-    tokens[r] = best;
-  }
+  step_any(rows, V, R, base, base_rs, w1, w2, NULL, NULL, prev, seeds, positions, pos_rs, step,
+           temperature, mult, softcap, cache, cache_rs, keys, keys_rs, bias, bias_rs, tokens,
+           threads);
+}
+
+/* oracle_step with the E4M3 w2 (q [V, R] codes, scales [V] FP16 bits) in
+ * place of w2 ([EDGE] `dsparkMarkovGreedyFusedStepFp8`). */
+EXPORT void oracle_step_fp8(int32_t rows, int32_t V, int32_t R, const uint16_t* base,
+                            int64_t base_rs, const uint16_t* w1, const uint8_t* q,
+                            const uint16_t* scales, const int64_t* prev, const int64_t* seeds,
+                            const int64_t* positions, int64_t pos_rs, int32_t step,
+                            const float* temperature, float mult, float softcap, uint16_t* cache,
+                            int64_t cache_rs, float* keys, int64_t keys_rs, uint16_t* bias,
+                            int64_t bias_rs, int64_t* tokens, int32_t threads) {
+  step_any(rows, V, R, base, base_rs, w1, NULL, q, scales, prev, seeds, positions, pos_rs, step,
+           temperature, mult, softcap, cache, cache_rs, keys, keys_rs, bias, bias_rs, tokens,
+           threads);
 }
 
 /*

@@ -79,11 +79,12 @@ def check_loop(w, cache_g: np.ndarray, tokens_g: np.ndarray, rows=None, steps=No
                undecided=0, decided_literal=0, token_mismatch=[], undecided_cases=[],
                near_tie_violations=[])
     pool = ThreadPoolExecutor(max(1, threads))
+    w2q, w2s = getattr(w, "w2q", None), getattr(w, "w2s", None)   # an E4M3 w2, if the run used one
     for s in steps:
         feed = w.prev[rows_a] if s == 0 else tokens_g[rows_a, s - 1]
         out = oracle.step(np.ascontiguousarray(w.base[rows_a, s]), w.w1, w.w2, feed,
                           w.seeds[rows_a], w.positions[rows_a, s], s, w.temperature[rows_a],
-                          w.mult, w.softcap, want_keys=True, threads=threads)
+                          w.mult, w.softcap, want_keys=True, threads=threads, w2q=w2q, w2s=w2s)
         co = out["cache"]
         cg = np.ascontiguousarray(cache_g[rows_a, s])
         beyond, differ, idx = compare_cache(cg, co, where=True)
@@ -91,8 +92,11 @@ def check_loop(w, cache_g: np.ndarray, tokens_g: np.ndarray, rows=None, steps=No
         # bias (base and bias nearly cancelling; see oracle_cache_admissible)
         for i, v in idx:
             e = w.w1[oracle.w1_row(int(feed[i]), w.V)]
-            if oracle.cache_admissible(int(w.base[rows_a[i], s, v]), e, w.w2[v], w.mult,
-                                       w.softcap, int(cg[i, v])):
+            b = int(w.base[rows_a[i], s, v])
+            ok = (oracle.cache_admissible_fp8(b, e, w2q[v], int(w2s[v]), w.mult, w.softcap,
+                                              int(cg[i, v])) if w2q is not None else
+                  oracle.cache_admissible(b, e, w.w2[v], w.mult, w.softcap, int(cg[i, v])))
+            if ok:
                 rep["cache_cancel"] += 1
                 beyond -= 1
             else:
