@@ -47,10 +47,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="large",
                     choices=["tiny", "single", "small", "large", "stress"])
-    ap.add_argument("--path", default="sample", choices=["sample", "greedy", "greedy-chain"],
+    ap.add_argument("--path", default="sample",
+                    choices=["sample", "greedy", "greedy-chain", "fp8", "fp8-greedy"],
                     help="sample: markov_sample_sequential (the headline); greedy: "
                          "markov_greedy_sequential writing the cache; greedy-chain: the same "
-                         "without the cache write")
+                         "without the cache write; fp8 / fp8-greedy: the same two with the E4M3 "
+                         "w2 (quantized once, untimed)")
     ap.add_argument("--graph", action="store_true",
                     help="headline from replays of the loop captured as a HIP graph")
     ap.add_argument("--eager", action="store_true",
@@ -193,6 +195,16 @@ def main():
     if args.path == "sample":
         call = m.prepare(w, d)
         step_calls = [m.prepare(w, d, step=s) for s in range(w.k)]
+    elif args.path.startswith("fp8"):
+        q = torch.empty((w.V, w.R), dtype=torch.uint8, device=dev)
+        sc = torch.empty(w.V, dtype=torch.int16, device=dev)
+        m.quantize_w2_fp8(d["w2"], q, sc)
+        torch.cuda.synchronize()
+        d["w2q"], d["w2s"] = q, sc
+        greedy = args.path == "fp8-greedy"
+        call = m.prepare_fp8(w, d, greedy=greedy)
+        step_calls = [m.prepare_fp8(w, d, greedy=greedy, step=s) for s in range(w.k)]
+        bytes_step -= w.V * w.R - 2 * w.V       # 1-byte codes and a 2-byte scale per row
     else:
         chain = args.path == "greedy-chain"
         call = m.prepare_greedy(w, d, cache=not chain)

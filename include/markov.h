@@ -217,6 +217,59 @@ int markov_greedy_step(const void* base_logits, const void* w1, const void* w2,
 int markov_greedy_finalize(const uint64_t* winners, int64_t n, int64_t* tokens,
                            markov_stream_t stream);
 
+/* ---- E4M3 w2 (TensorRT Edge-LLM "DSpark kernels" page:
+ * `dsparkQuantizeMarkovW2Fp8`, `dsparkMarkovGreedyFusedStepFp8`) ---------- */
+
+/*
+ * Quantize a bf16 w2 [V, R] to E4M3 codes with one FP16 scale per row: the
+ * scale is RN16(rowAbsMax / 448), so each row spans the E4M3 range; code j is
+ * the E4M3 nearest to the binary32 quotient w[j] / scale (ties to even,
+ * saturating at +-448); a zero scale gives zero codes.
+ *   w2         device bf16 [vocab, rank] (read)
+ *   w2q        device uint8 [vocab, rank] (write), 16-byte aligned for the steps below
+ *   w2_scales  device uint16 [vocab] FP16 bit patterns (write), 16-byte aligned likewise
+ * One kernel on `stream` (a wave per row). Errors: NULL pointers, vocab < 1,
+ * rank not a power of two in [16, 512].
+ */
+int markov_quantize_w2_fp8(const void* w2, uint8_t* w2q, uint16_t* w2_scales, int32_t vocab,
+                           int32_t rank, markov_stream_t stream);
+
+/*
+ * markov_sample_sequential with the E4M3 w2 in place of the bf16 one: the
+ * bias is bf16(RN32(scale[v] * sum_j emb[j] * value(w2q[v][j]))), the dot in
+ * fp32 (the codes decode exactly to bf16 for the same MFMA contraction), the
+ * scale applied once, then one rounding to bf16. Everything else as
+ * markov_sample_sequential; w2q and w2_scales as markov_quantize_w2_fp8
+ * writes them (16-byte aligned).
+ */
+int markov_sample_sequential_fp8(const void* base_logits, const void* w1, const uint8_t* w2q,
+                                 const uint16_t* w2_scales, const int64_t* prev,
+                                 const int64_t* seeds, const int64_t* positions, int32_t k,
+                                 const float* temperature, void* cache, int64_t* tokens,
+                                 markov_stream_t stream, const markov_shape_t* shape,
+                                 void* workspace, size_t workspace_bytes);
+
+/* markov_greedy_sequential with the E4M3 w2 (the page's
+ * `dsparkMarkovGreedyFusedStepFp8`); arguments as the two above. */
+int markov_greedy_sequential_fp8(const void* base_logits, const void* w1, const uint8_t* w2q,
+                                 const uint16_t* w2_scales, const int64_t* prev, int32_t k,
+                                 void* cache, int64_t* tokens, uint64_t* winners,
+                                 markov_stream_t stream, const markov_shape_t* shape,
+                                 void* workspace, size_t workspace_bytes);
+
+/* One step of either E4M3 loop alone (as markov_sample_step and
+ * markov_greedy_step are to their loops). */
+int markov_sample_step_fp8(const void* base_logits, const void* w1, const uint8_t* w2q,
+                           const uint16_t* w2_scales, const int64_t* prev, const int64_t* seeds,
+                           const int64_t* positions, int32_t k, int32_t step,
+                           const float* temperature, void* cache, int64_t* tokens,
+                           markov_stream_t stream, const markov_shape_t* shape, void* workspace,
+                           size_t workspace_bytes);
+int markov_greedy_step_fp8(const void* base_logits, const void* w1, const uint8_t* w2q,
+                           const uint16_t* w2_scales, const int64_t* prev, int32_t k, int32_t step,
+                           void* cache, int64_t* tokens, uint64_t* winners, markov_stream_t stream,
+                           const markov_shape_t* shape, void* workspace, size_t workspace_bytes);
+
 /* A readable name of a status code (static string). */
 const char* markov_status_string(int status);
 
@@ -276,6 +329,19 @@ int32_t markov_debug_noise_table(float* out, int32_t n);
  * softcap (softcap > 0), bf16 bit patterns into out[n] (host memory).
  * Returns the number of entries written. */
 int32_t markov_debug_transform_table(float mult, float softcap, uint16_t* out, int32_t n);
+
+/* The E4M3 code of each of n binary32 values with the quantizer's own
+ * rounding (test-only; device arrays). */
+int markov_debug_e4m3_encode(const float* x, uint8_t* out, int64_t n, markov_stream_t stream);
+
+/* The bf16 values of n E4M3 codes (n a multiple of 8; codes 8-byte aligned,
+ * out 16-byte aligned) through the step kernel's own decode (test-only). */
+int markov_debug_e4m3_decode(const uint8_t* codes, void* out, int64_t n, markov_stream_t stream);
+
+/* markov_debug_bias with the E4M3 w2 (test-only). */
+int markov_debug_bias_fp8(const void* w1, const uint8_t* w2q, const uint16_t* w2_scales,
+                          const int64_t* tok, void* bias, const markov_shape_t* shape,
+                          markov_stream_t stream);
 
 /* A plain device copy of `bytes` (a multiple of 16; both pointers 16-byte
  * aligned) from src to dst on `stream` (test-only): the reference kernel

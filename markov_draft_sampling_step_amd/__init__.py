@@ -63,6 +63,22 @@ _SIGS = {
     "markov_greedy_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                           _P, _P, ctypes.POINTER(Shape), _P, ctypes.c_size_t]),
     "markov_greedy_finalize": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P]),
+    "markov_quantize_w2_fp8": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P]),
+    "markov_sample_sequential_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                                    _P, _P, _P, _P, ctypes.POINTER(Shape), _P,
+                                                    ctypes.c_size_t]),
+    "markov_greedy_sequential_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
+                                                    _P, _P, ctypes.POINTER(Shape), _P,
+                                                    ctypes.c_size_t]),
+    "markov_debug_e4m3_encode": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
+    "markov_debug_e4m3_decode": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
+    "markov_debug_bias_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(Shape), _P]),
+    "markov_sample_step_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                              ctypes.c_int32, _P, _P, _P, _P,
+                                              ctypes.POINTER(Shape), _P, ctypes.c_size_t]),
+    "markov_greedy_step_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                              _P, _P, _P, _P, ctypes.POINTER(Shape), _P,
+                                              ctypes.c_size_t]),
     "markov_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "markov_debug_bias": (ctypes.c_int, [_P, _P, _P, _P, ctypes.POINTER(Shape), _P]),
     "markov_debug_gumbel": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_float,
@@ -274,6 +290,87 @@ def greedy_finalize(winners, tokens, stream=None):
            "markov_greedy_finalize")
 
 
+def quantize_w2_fp8(w2, w2q, w2_scales, stream=None):
+    """markov_quantize_w2_fp8: w2 bf16 [V, R] -> w2q uint8 [V, R], w2_scales
+    int16 [V] (FP16 bit patterns)."""
+    import torch
+
+    V, R = w2.shape
+    _check(lib().markov_quantize_w2_fp8(_dev(w2, torch.bfloat16, "w2"),
+                                        _dev(w2q, torch.uint8, "w2q", (V, R)),
+                                        _dev(w2_scales, torch.int16, "w2_scales", (V,)), V, R,
+                                        _stream_ptr(stream)), "markov_quantize_w2_fp8")
+
+
+def sample_sequential_fp8(base_logits, w1, w2q, w2_scales, prev, seeds, positions, temperature,
+                          cache, tokens, workspace, mult: float = 1.0, softcap: float = 0.0,
+                          stream=None):
+    """markov_sample_sequential_fp8 (arguments as sample_sequential, with the
+    E4M3 w2 of ``quantize_w2_fp8`` for w2)."""
+    import torch
+
+    rows, k, V = base_logits.shape
+    R = w1.shape[1]
+    sh = make_shape(rows, V, R, mult, softcap)
+    _check(lib().markov_sample_sequential_fp8(
+        _dev(base_logits, torch.bfloat16, "base_logits"), _dev(w1, torch.bfloat16, "w1", (V, R)),
+        _dev(w2q, torch.uint8, "w2q", (V, R)), _dev(w2_scales, torch.int16, "w2_scales", (V,)),
+        _dev(prev, torch.int64, "prev", (rows,)), _dev(seeds, torch.int64, "seeds", (rows,)),
+        _dev(positions, torch.int64, "positions", (rows, k)), ctypes.c_int32(k),
+        _dev(temperature, torch.float32, "temperature", (rows,)),
+        _dev(cache, torch.bfloat16, "cache", (rows, k, V)),
+        _dev(tokens, torch.int64, "tokens", (rows, k)), _stream_ptr(stream), ctypes.byref(sh),
+        _dev(workspace, torch.uint8, "workspace"), ctypes.c_size_t(workspace.numel())),
+        "markov_sample_sequential_fp8")
+
+
+def greedy_sequential_fp8(base_logits, w1, w2q, w2_scales, prev, tokens, workspace, cache=None,
+                          winners=None, mult: float = 1.0, softcap: float = 0.0, stream=None):
+    """markov_greedy_sequential_fp8 (as greedy_sequential, E4M3 w2)."""
+    import torch
+
+    rows, k, V = base_logits.shape
+    R = w1.shape[1]
+    sh = make_shape(rows, V, R, mult, softcap)
+    _check(lib().markov_greedy_sequential_fp8(
+        _dev(base_logits, torch.bfloat16, "base_logits"), _dev(w1, torch.bfloat16, "w1", (V, R)),
+        _dev(w2q, torch.uint8, "w2q", (V, R)), _dev(w2_scales, torch.int16, "w2_scales", (V,)),
+        _dev(prev, torch.int64, "prev", (rows,)), ctypes.c_int32(k),
+        _opt(cache, torch.bfloat16, "cache", (rows, k, V)),
+        _dev(tokens, torch.int64, "tokens", (rows, k)),
+        _opt(winners, torch.int64, "winners", (rows, k)), _stream_ptr(stream), ctypes.byref(sh),
+        _dev(workspace, torch.uint8, "workspace"), ctypes.c_size_t(workspace.numel())),
+        "markov_greedy_sequential_fp8")
+
+
+def debug_e4m3_encode(x, out, stream=None):
+    import torch
+
+    _check(lib().markov_debug_e4m3_encode(_dev(x, torch.float32, "x"), _dev(out, torch.uint8, "out"),
+                                          x.numel(), _stream_ptr(stream)), "markov_debug_e4m3_encode")
+
+
+def debug_e4m3_decode(codes, out, stream=None):
+    import torch
+
+    _check(lib().markov_debug_e4m3_decode(_dev(codes, torch.uint8, "codes"),
+                                          _dev(out, torch.int16, "out"), codes.numel(),
+                                          _stream_ptr(stream)), "markov_debug_e4m3_decode")
+
+
+def debug_bias_fp8(w1, w2q, w2_scales, tok, bias, stream=None):
+    import torch
+
+    V, R = w1.shape
+    rows = tok.shape[0]
+    sh = make_shape(rows, V, R)
+    _check(lib().markov_debug_bias_fp8(_dev(w1, torch.bfloat16, "w1"), _dev(w2q, torch.uint8, "w2q"),
+                                       _dev(w2_scales, torch.int16, "w2_scales"),
+                                       _dev(tok, torch.int64, "tok"),
+                                       _dev(bias, torch.bfloat16, "bias", (rows, V)),
+                                       ctypes.byref(sh), _stream_ptr(stream)), "markov_debug_bias_fp8")
+
+
 def noalloc_max_rows() -> int:
     return int(lib().markov_noalloc_max_rows())
 
@@ -405,6 +502,41 @@ def prepare_greedy(w, d, cache: bool = True, winners=None, stream=None,
         call = PreparedCall(lib().markov_greedy_step, args, 9, "markov_greedy_step")
     else:
         call = PreparedCall(lib().markov_greedy_sequential, args, 8, "markov_greedy_sequential")
+    call._keep = sh
+    return call
+
+
+def prepare_fp8(w, d, greedy: bool = False, stream=None, step: int | None = None) -> PreparedCall:
+    """Marshal an E4M3-w2 loop (or one step) of workload `w` on device tensors
+    `d` (with d["w2q"], d["w2s"] from quantize_w2_fp8) once."""
+    import torch
+
+    rows, k, V, R = w.rows, w.k, w.V, w.R
+    sh = make_shape(rows, V, R, w.mult, w.softcap)
+    head = [
+        _dev(d["base"], torch.bfloat16, "base_logits", (rows, k, V)),
+        _dev(d["w1"], torch.bfloat16, "w1", (V, R)),
+        _dev(d["w2q"], torch.uint8, "w2q", (V, R)),
+        _dev(d["w2s"], torch.int16, "w2_scales", (V,)),
+        _dev(d["prev"], torch.int64, "prev", (rows,)),
+    ]
+    tail = [_stream_ptr(stream), ctypes.byref(sh), _dev(d["workspace"], torch.uint8, "workspace"),
+            ctypes.c_size_t(d["workspace"].numel())]
+    st = [ctypes.c_int32(step)] if step is not None else []
+    if greedy:
+        args = head + [ctypes.c_int32(k)] + st + [
+            _dev(d["cache"], torch.bfloat16, "cache", (rows, k, V)),
+            _dev(d["tokens"], torch.int64, "tokens", (rows, k)), ctypes.c_void_p(None)] + tail
+        fn = lib().markov_greedy_step_fp8 if step is not None else lib().markov_greedy_sequential_fp8
+    else:
+        args = head + [_dev(d["seeds"], torch.int64, "seeds", (rows,)),
+                       _dev(d["positions"], torch.int64, "positions", (rows, k)),
+                       ctypes.c_int32(k)] + st + [
+            _dev(d["temperature"], torch.float32, "temperature", (rows,)),
+            _dev(d["cache"], torch.bfloat16, "cache", (rows, k, V)),
+            _dev(d["tokens"], torch.int64, "tokens", (rows, k))] + tail
+        fn = lib().markov_sample_step_fp8 if step is not None else lib().markov_sample_sequential_fp8
+    call = PreparedCall(fn, args, len(args) - 4, "fp8 loop")
     call._keep = sh
     return call
 

@@ -276,6 +276,8 @@ struct Call {
   void* cache = nullptr;
   int64_t* tokens = nullptr;
   unsigned long long* winners = nullptr;
+  const uint8_t* w2q = nullptr;               // E4M3 w2 (with var & V_W8)
+  const uint16_t* w2s = nullptr;
   void* bias_out = nullptr;
   int32_t k = 1, s_begin = 0, s_end = 1;
 };
@@ -305,6 +307,8 @@ int launch_steps(const Call& c, markov_stream_t stream, const markov_shape_t* sh
   a.cache = (uint16_t*)c.cache;
   a.tokens = c.tokens;
   a.winners = c.winners;
+  a.w2q = c.w2q;
+  a.w2s = c.w2s;
   a.bias_out = (uint16_t*)c.bias_out;
   if (workspace) {
     a.gtable = (const float*)workspace;
@@ -336,20 +340,24 @@ int sample_common(int mode, const void* base_logits, const void* w1, const void*
                   const int64_t* prev, const int64_t* seeds, const int64_t* positions, int32_t k,
                   int32_t s_begin, int32_t s_end, const float* temperature, void* cache,
                   int64_t* tokens, markov_stream_t stream, const markov_shape_t* shape,
-                  void* workspace, size_t workspace_bytes) {
+                  void* workspace, size_t workspace_bytes, const uint8_t* w2q = nullptr,
+                  const uint16_t* w2s = nullptr) {
   int rc = check_shape(shape, k);
   if (rc) return rc;
   if (s_begin < 0 || s_end > k || s_begin >= s_end) return MARKOV_ERR_SHAPE;
-  if (!base_logits || !w1 || !w2 || !prev || !seeds || !positions || !temperature || !cache ||
-      !tokens || !workspace)
+  const bool w8 = w2q != nullptr || w2s != nullptr;
+  if (!base_logits || !w1 || (!w8 && !w2) || (w8 && (!w2q || !w2s)) || !prev || !seeds ||
+      !positions || !temperature || !cache || !tokens || !workspace)
     return MARKOV_ERR_NULL;
-  if (!aligned16(base_logits) || !aligned16(w1) || !aligned16(w2) || !aligned16(cache) ||
-      !aligned16(workspace))
+  if (!aligned16(base_logits) || !aligned16(w1) || (!w8 && !aligned16(w2)) || !aligned16(cache) ||
+      !aligned16(workspace) || (w8 && (!aligned16(w2q) || !aligned16(w2s))))
     return MARKOV_ERR_ALIGN;
   if (workspace_bytes < ws_bytes(shape->rows)) return MARKOV_ERR_WORKSPACE;
   Call c;
   c.mode = mode;
-  c.var = mode == MODE_SAMPLE_EXACT ? V_EXACT : V_SAMPLE;
+  c.var = (mode == MODE_SAMPLE_EXACT ? V_EXACT : V_SAMPLE) | (w8 ? V_W8 : 0);
+  c.w2q = w2q;
+  c.w2s = w2s;
   c.base = base_logits;
   c.w1 = w1;
   c.w2 = w2;
@@ -368,18 +376,25 @@ int sample_common(int mode, const void* base_logits, const void* w1, const void*
 int greedy_common(const void* base_logits, const void* w1, const void* w2, const int64_t* prev,
                   int32_t k, int32_t s_begin, int32_t s_end, void* cache, int64_t* tokens,
                   unsigned long long* winners, markov_stream_t stream,
-                  const markov_shape_t* shape, void* workspace, size_t workspace_bytes) {
+                  const markov_shape_t* shape, void* workspace, size_t workspace_bytes,
+                  const uint8_t* w2q = nullptr, const uint16_t* w2s = nullptr) {
   int rc = check_shape(shape, k);
   if (rc) return rc;
   if (s_begin < 0 || s_end > k || s_begin >= s_end) return MARKOV_ERR_SHAPE;
-  if (!base_logits || !w1 || !w2 || !prev || !tokens || !workspace) return MARKOV_ERR_NULL;
-  if (!aligned16(base_logits) || !aligned16(w1) || !aligned16(w2) || !aligned16(workspace) ||
-      (cache && !aligned16(cache)))
+  const bool w8 = w2q != nullptr || w2s != nullptr;
+  if (!base_logits || !w1 || (!w8 && !w2) || (w8 && (!w2q || !w2s)) || !prev || !tokens ||
+      !workspace)
+    return MARKOV_ERR_NULL;
+  if (!aligned16(base_logits) || !aligned16(w1) || (!w8 && !aligned16(w2)) ||
+      !aligned16(workspace) || (cache && !aligned16(cache)) ||
+      (w8 && (!aligned16(w2q) || !aligned16(w2s))))
     return MARKOV_ERR_ALIGN;
   if (workspace_bytes < ws_bytes(shape->rows)) return MARKOV_ERR_WORKSPACE;
   Call c;
   c.mode = MODE_GREEDY;
-  c.var = V_GREEDY;
+  c.var = V_GREEDY | (w8 ? V_W8 : 0);
+  c.w2q = w2q;
+  c.w2s = w2s;
   c.base = base_logits;
   c.w1 = w1;
   c.w2 = w2;
@@ -391,6 +406,52 @@ int greedy_common(const void* base_logits, const void* w1, const void* w2, const
   c.s_begin = s_begin;
   c.s_end = s_end;
   return launch_steps(c, stream, shape, workspace);
+}
+
+// ---- E4M3 w2 (the Edge-LLM page's `dsparkQuantizeMarkovW2Fp8`)
+
+// E4M3 code of x: nearest, ties to even, saturating at +-448, NaN to the NaN
+// code of its sign. Integer rounding on x's bits: at or above 2^-6 the top 3
+// fraction bits are kept (a carry moves into the exponent), the exponent
+// rebiased from 127 to 7; below, the subnormal m 2^-9 with m = RN(|x| 2^9)
+// (m = 8 is the smallest normal, code 8).
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t u = __float_as_uint(x), sgn = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sgn | 0x7fu;
+  if (a >= 0x43e00000u) return sgn | 0x7eu;                     // |x| >= 448
+  if (a < 0x3c800000u) return sgn | (uint32_t)rintf(__uint_as_float(a) * 512.0f);   // < 2^-6
+  return sgn | (((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3));
+}
+
+// One w2 row per wave: the row's largest magnitude, its FP16 scale
+// RN16(max / 448), and every element's code of w / scale (zero codes when the
+// scale is 0).
+__global__ __launch_bounds__(256) void quantize_w2_fp8_kernel(const uint16_t* w2, uint8_t* q,
+                                                              uint16_t* scales, int V, int R) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= V) return;
+  const uint16_t* w = w2 + (size_t)row * R;
+  float amax = 0.0f;
+  for (int j = lane; j < R; j += 64) amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)w[j] << 16)));
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
+  const _Float16 sh16 = (_Float16)(amax / 448.0f);
+  const float scale = (float)sh16;
+  for (int j = lane; j < R; j += 64)
+    q[(size_t)row * R + j] =
+        scale == 0.0f ? (uint8_t)0 : (uint8_t)e4m3_encode(__uint_as_float((uint32_t)w[j] << 16) / scale);
+  if (lane == 0) scales[row] = __builtin_bit_cast(uint16_t, sh16);
+}
+
+__global__ void debug_e4m3_encode_kernel(const float* x, uint8_t* out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)e4m3_encode(x[i]);
+}
+
+// 8 codes per thread through the step kernel's own decode (decode8).
+__global__ void debug_e4m3_decode_kernel(const uint2* codes, bf16x8_t* out, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n8) out[i] = decode8(codes[i].x, codes[i].y);
 }
 
 // The packed winners' token ids (the low word holds ~id).
@@ -562,6 +623,102 @@ int markov_greedy_step(const void* base_logits, const void* w1, const void* w2,
                        void* workspace, size_t workspace_bytes) {
   return greedy_common(base_logits, w1, w2, prev, k, step, step + 1, cache, tokens,
                        (unsigned long long*)winners, stream, shape, workspace, workspace_bytes);
+}
+
+int markov_quantize_w2_fp8(const void* w2, uint8_t* w2q, uint16_t* w2_scales, int32_t vocab,
+                           int32_t rank, markov_stream_t stream) {
+  if (vocab < 1 || !pow2_rank(rank)) return vocab < 1 ? MARKOV_ERR_SHAPE : MARKOV_ERR_RANK;
+  if (!w2 || !w2q || !w2_scales) return MARKOV_ERR_NULL;
+  const unsigned blocks = (unsigned)((vocab + 3) / 4);
+  quantize_w2_fp8_kernel<<<dim3(blocks), 256, 0, (hipStream_t)stream>>>(
+      (const uint16_t*)w2, w2q, w2_scales, vocab, rank);
+  if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
+  return MARKOV_OK;
+}
+
+int markov_sample_sequential_fp8(const void* base_logits, const void* w1, const uint8_t* w2q,
+                                 const uint16_t* w2_scales, const int64_t* prev,
+                                 const int64_t* seeds, const int64_t* positions, int32_t k,
+                                 const float* temperature, void* cache, int64_t* tokens,
+                                 markov_stream_t stream, const markov_shape_t* shape,
+                                 void* workspace, size_t workspace_bytes) {
+  if (!w2q || !w2_scales) return MARKOV_ERR_NULL;
+  return sample_common(MODE_SAMPLE, base_logits, w1, nullptr, prev, seeds, positions, k, 0, k,
+                       temperature, cache, tokens, stream, shape, workspace, workspace_bytes, w2q,
+                       w2_scales);
+}
+
+int markov_greedy_sequential_fp8(const void* base_logits, const void* w1, const uint8_t* w2q,
+                                 const uint16_t* w2_scales, const int64_t* prev, int32_t k,
+                                 void* cache, int64_t* tokens, uint64_t* winners,
+                                 markov_stream_t stream, const markov_shape_t* shape,
+                                 void* workspace, size_t workspace_bytes) {
+  if (!w2q || !w2_scales) return MARKOV_ERR_NULL;
+  return greedy_common(base_logits, w1, nullptr, prev, k, 0, k, cache, tokens,
+                       (unsigned long long*)winners, stream, shape, workspace, workspace_bytes,
+                       w2q, w2_scales);
+}
+
+int markov_sample_step_fp8(const void* base_logits, const void* w1, const uint8_t* w2q,
+                           const uint16_t* w2_scales, const int64_t* prev, const int64_t* seeds,
+                           const int64_t* positions, int32_t k, int32_t step,
+                           const float* temperature, void* cache, int64_t* tokens,
+                           markov_stream_t stream, const markov_shape_t* shape, void* workspace,
+                           size_t workspace_bytes) {
+  if (!w2q || !w2_scales) return MARKOV_ERR_NULL;
+  return sample_common(MODE_SAMPLE, base_logits, w1, nullptr, prev, seeds, positions, k, step,
+                       step + 1, temperature, cache, tokens, stream, shape, workspace,
+                       workspace_bytes, w2q, w2_scales);
+}
+
+int markov_greedy_step_fp8(const void* base_logits, const void* w1, const uint8_t* w2q,
+                           const uint16_t* w2_scales, const int64_t* prev, int32_t k, int32_t step,
+                           void* cache, int64_t* tokens, uint64_t* winners, markov_stream_t stream,
+                           const markov_shape_t* shape, void* workspace, size_t workspace_bytes) {
+  if (!w2q || !w2_scales) return MARKOV_ERR_NULL;
+  return greedy_common(base_logits, w1, nullptr, prev, k, step, step + 1, cache, tokens,
+                       (unsigned long long*)winners, stream, shape, workspace, workspace_bytes,
+                       w2q, w2_scales);
+}
+
+int markov_debug_e4m3_encode(const float* x, uint8_t* out, int64_t n, markov_stream_t stream) {
+  if (n < 0) return MARKOV_ERR_SHAPE;
+  if (n == 0) return MARKOV_OK;
+  if (!x || !out) return MARKOV_ERR_NULL;
+  debug_e4m3_encode_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, (hipStream_t)stream>>>(x, out, n);
+  if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
+  return MARKOV_OK;
+}
+
+int markov_debug_e4m3_decode(const uint8_t* codes, void* out, int64_t n, markov_stream_t stream) {
+  if (n < 0 || (n & 7)) return MARKOV_ERR_SHAPE;
+  if (n == 0) return MARKOV_OK;
+  if (!codes || !out) return MARKOV_ERR_NULL;
+  if (((uintptr_t)codes & 7u) || !aligned16(out)) return MARKOV_ERR_ALIGN;
+  const int64_t n8 = n / 8;
+  debug_e4m3_decode_kernel<<<dim3((unsigned)((n8 + 255) / 256)), 256, 0, (hipStream_t)stream>>>(
+      (const uint2*)codes, (bf16x8_t*)out, n8);
+  if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
+  return MARKOV_OK;
+}
+
+int markov_debug_bias_fp8(const void* w1, const uint8_t* w2q, const uint16_t* w2_scales,
+                          const int64_t* tok, void* bias, const markov_shape_t* shape,
+                          markov_stream_t stream) {
+  int rc = check_shape(shape, 1);
+  if (rc) return rc;
+  if (!w1 || !w2q || !w2_scales || !tok || !bias) return MARKOV_ERR_NULL;
+  if (!aligned16(w1) || !aligned16(w2q) || !aligned16(w2_scales) || !aligned16(bias))
+    return MARKOV_ERR_ALIGN;
+  Call c;
+  c.mode = MODE_BIAS;
+  c.var = V_W8;
+  c.w1 = w1;
+  c.w2q = w2q;
+  c.w2s = w2_scales;
+  c.prev = tok;
+  c.bias_out = bias;
+  return launch_steps(c, stream, shape, nullptr);
 }
 
 int markov_greedy_finalize(const uint64_t* winners, int64_t n, int64_t* tokens,

@@ -66,6 +66,8 @@ struct StepArgs {
   const uint32_t* ttable;     // the transform table's stamp, then its 32768 entries
   uint16_t* bias_out;
   unsigned long long* winners;  // greedy: [rows, k] packed winners (NULL: not written)
+  const uint8_t* w2q;           // E4M3 w2 [V, R] codes (the V_W8 variant)
+  const uint16_t* w2s;          // its FP16 row scales [V]
   int rows, V, R, k, step, nslabs, mode;
   int tt_layout;              // LDS holds the transform table at address 0
   float mult, inv_cap, cap;
@@ -101,7 +103,12 @@ enum Mode { MODE_SAMPLE = 0, MODE_SAMPLE_EXACT = 1, MODE_BIAS = 2, MODE_SAMPLE_F
 //   V_GREEDY  every row at temperature 0: no noise table, no hashing, an
 //             exact in-register argmax under the total order (NaN and -inf
 //             included, so no re-scan and the cache write may be skipped).
-constexpr int V_SAMPLE = 0, V_EXACT = 1, V_GREEDY = 2;
+//   V_W8      w2 as E4M3 codes with an FP16 scale per row (the Edge-LLM
+//             page's `dsparkMarkovGreedyFusedStepFp8` layout): the codes are
+//             decoded to bf16 (exact: every E4M3 value is a bf16) for the
+//             same MFMA contraction, and the fp32 sum is scaled before it is
+//             rounded to bf16.
+constexpr int V_SAMPLE = 0, V_EXACT = 1, V_GREEDY = 2, V_W8 = 4;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -426,9 +433,92 @@ __device__ __forceinline__ void load_w2_tile(const uint16_t* w2, int V, int R, i
   }
 }
 
+// The k-chunk (8 consecutive elements) that lane group g feeds to MFMA i. With
+// bf16 w2, chunk 4i + g (one 16-byte load per chunk). With E4M3 w2 a 16-byte
+// load holds two chunks, so lane group g takes chunks 8 (i / 2) + 2g and the
+// next for MFMAs i = 2p, 2p + 1 (the sum over k is the same in any order, and
+// the embedding operand reads the same chunks).
+template <int KB, bool W8>
+__device__ __forceinline__ int chunk_of(int i, int g) {
+  return (W8 && KB >= 2) ? 8 * (i >> 1) + 2 * g + (i & 1) : 4 * i + g;
+}
+
+// The E4M3 codes of one 32-token unit, raw (decoded by decode_w2q_tile once
+// they are needed): lane (g, m) loads, for tokens t0 and t0 + 4 as in
+// load_w2_tile, 16 bytes (two chunks) per pair of MFMAs, or with KB = 1 the 8
+// bytes of chunk g; and the FP16 scales of the 8 tokens tok0 + 8g .. +7 whose
+// bias it finishes (one 16-byte load; none past the vocabulary).
+template <int KB>
+__device__ __forceinline__ void load_w2q_tile(const uint8_t* q, const uint16_t* sc, int V, int R,
+                                              int tok0, int m, int g, bool kzero, u32x4_t* Qa,
+                                              u32x4_t* Qb, u32x4_t& S) {
+  constexpr int KP = KB >= 2 ? KB / 2 : 1;
+  const int t0 = tok0 + 8 * (m >> 2) + (m & 3);
+  const int ta = t0 < V ? t0 : V - 1, tb = t0 + 4 < V ? t0 + 4 : V - 1;
+  const uint8_t* pa = q + (size_t)ta * R;
+  const uint8_t* pb = q + (size_t)tb * R;
+  if (KB == 1) {
+    if (kzero) {
+      Qa[0] = (u32x4_t){0u, 0u, 0u, 0u};
+      Qb[0] = (u32x4_t){0u, 0u, 0u, 0u};
+    } else {
+      const uint2 x = *(const uint2*)(pa + g * 8), y = *(const uint2*)(pb + g * 8);
+      Qa[0] = (u32x4_t){x.x, x.y, 0u, 0u};
+      Qb[0] = (u32x4_t){y.x, y.y, 0u, 0u};
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {
+      Qa[p] = *(const u32x4_t*)(pa + 64 * p + 16 * g);
+      Qb[p] = *(const u32x4_t*)(pb + 64 * p + 16 * g);
+    }
+  }
+  const int tg = tok0 + 8 * g;
+  S = (u32x4_t){0u, 0u, 0u, 0u};
+  if (tg < V) S = *(const u32x4_t*)(sc + tg);
+}
+
+// 8 E4M3 codes (bytes of lo, then of hi) to 8 bf16, in order: two codes per
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1.
+__device__ __forceinline__ bf16x8_t decode8(uint32_t lo, uint32_t hi) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return (bf16x8_t){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// The binary16 halves of a word as binary32 (exact). Each half goes through a
+// scalar _Float16: a bit cast of a whole word to a two-element _Float16
+// vector, taken from an element of a wider vector, was compiled here into
+// conversions of the first element only.
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+template <int KB>
+__device__ __forceinline__ void decode_w2q_tile(const u32x4_t* Qa, const u32x4_t* Qb, bf16x8_t* A0,
+                                                bf16x8_t* A1) {
+  if (KB == 1) {
+    A0[0] = decode8(Qa[0].x, Qa[0].y);
+    A1[0] = decode8(Qb[0].x, Qb[0].y);
+  } else {
+#pragma unroll
+    for (int p = 0; p < KB / 2; ++p) {
+      A0[2 * p] = decode8(Qa[p].x, Qa[p].y);
+      A0[2 * p + 1] = decode8(Qa[p].z, Qa[p].w);
+      A1[2 * p] = decode8(Qb[p].x, Qb[p].y);
+      A1[2 * p + 1] = decode8(Qb[p].z, Qb[p].w);
+    }
+  }
+}
+
 // The bias of one 16-row block for the wave's 32 tokens: lane (g, m) gets
 // row n = 16 rb + m, tokens tg .. tg+3 in c0 and tg+4 .. tg+7 in c1.
-template <int KB>
+template <int KB, bool W8 = false>
 __device__ __forceinline__ void block_bias(const bf16x8_t* A0, const bf16x8_t* A1, const uint16_t* emb,
                                            int n, int R, int g, int swz, bool kzero, f32x4_t& c0,
                                            f32x4_t& c1) {
@@ -440,7 +530,7 @@ __device__ __forceinline__ void block_bias(const bf16x8_t* A0, const bf16x8_t* A
     if (kzero) {
       B = (bf16x8_t){};
     } else {
-      const int ch = 4 * i + g;
+      const int ch = chunk_of<KB, W8>(i, g);
       B = *(const bf16x8_t*)(emb + (size_t)n * R + ((ch ^ (n & swz)) * 8));
     }
     c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[i], B, c0, 0, 0, 0);
@@ -536,6 +626,7 @@ template <int KB, int RG, int MRB, int VAR>
 __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   constexpr bool EXACT = (VAR & V_EXACT) != 0;
   constexpr bool GREEDY = (VAR & V_GREEDY) != 0;
+  constexpr bool W8 = (VAR & V_W8) != 0;
   constexpr int NB = MRB == 1 ? 2 : 1;                   // w2 tiles in flight per wave
   constexpr int D = MRB - 1 < 3 ? MRB - 1 : 3;           // row blocks contracted ahead
   constexpr int S = RG == 1 ? 2 : 1;                     // waves splitting one SIMD's slabs
@@ -655,10 +746,20 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   //    with more units) requests it here; the second requests its own after
   //    the embedding gather, so that the gather waits behind half the bytes.
   const bool tile_first = RG == 2 || sub == 0;   // uniform per wave
-  bf16x8_t A0[NB][KB], A1[NB][KB];
-  if (tile_first)
-    load_w2_tile<KB>(a.w2, V, R, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[0],
-                     A1[0]);
+  // bf16 w2: NB tiles of MFMA operands in flight. E4M3 w2: NB raw tiles in
+  // flight (codes and scales) and one decoded tile of operands.
+  constexpr int NA = W8 ? 1 : NB;
+  constexpr int KP = W8 ? (KB >= 2 ? KB / 2 : 1) : 1;
+  bf16x8_t A0[NA][KB], A1[NA][KB];
+  u32x4_t Qa[W8 ? NB : 1][KP], Qb[W8 ? NB : 1][KP], QS[W8 ? NB : 1];
+  // the tile of the unit at token tok0 into buffer b
+  auto tile = [&](int b, int tok0) {
+    if constexpr (W8)
+      load_w2q_tile<KB>(a.w2q, a.w2s, V, R, tok0, m, g, kzero, Qa[b], Qb[b], QS[b]);
+    else
+      load_w2_tile<KB>(a.w2, V, R, tok0, m, g, kzero, A0[b], A1[b]);
+  };
+  if (tile_first) tile(0, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE);
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. rows: noisy rows first, so that 16-row blocks are of one kind
@@ -777,13 +878,9 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   // (one-tile waves that did not request their first tile above do so after
   // the prologue's barrier: kept out of the burst the barrier waits on, it
   // streams while the SIMD's first wave computes)
-  if (!tile_first && NB == 2)
-    load_w2_tile<KB>(a.w2, V, R, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[0],
-                     A1[0]);
+  if (!tile_first && NB == 2) tile(0, (U > 0 ? slab0 : 0) * SLAB + tw * TOK_PER_WAVE);
   __builtin_amdgcn_sched_barrier(0);
-  if (NB == 2)
-    load_w2_tile<KB>(a.w2, V, R, (U > 1 ? slab0 + slab_step : 0) * SLAB + tw * TOK_PER_WAVE, m,
-                              g, kzero, A0[NB - 1], A1[NB - 1]);
+  if (NB == 2) tile(NB - 1, (U > 1 ? slab0 + slab_step : 0) * SLAB + tw * TOK_PER_WAVE);
   __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
@@ -803,8 +900,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   if (tile_first) wait_vm<VM_FIRST>();
   else wait_vm<VM_AFTER>();
   lds_barrier();
-  if (!tile_first && NB == 1 && U > 0)
-    load_w2_tile<KB>(a.w2, V, R, slab0 * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[0], A1[0]);
+  if (!tile_first && NB == 1 && U > 0) tile(0, slab0 * SLAB + tw * TOK_PER_WAVE);
 
   // one 32-token unit (the wave's unit i, slab `sl`) with w2 tile buffer BUF
   auto unit = [&](auto bufc, int i, int sl) {
@@ -825,13 +921,24 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         kc += MM_C1;
       }
     }
+    // E4M3 w2: this unit's codes to operands, its tokens' scales to binary32;
+    // with two raw buffers the buffer's next tile goes out at once
+    constexpr int AB = W8 ? 0 : BUF;           // the operand buffer of this unit
+    f32x4_t sc0 = (f32x4_t){1.f, 1.f, 1.f, 1.f}, sc1 = sc0;
+    if constexpr (W8) {
+      decode_w2q_tile<KB>(Qa[BUF], Qb[BUF], A0[0], A1[0]);
+      const u32x4_t S = QS[BUF];
+      sc0 = (f32x4_t){f16_lo(S.x), f16_hi(S.x), f16_lo(S.y), f16_hi(S.y)};
+      sc1 = (f32x4_t){f16_lo(S.z), f16_hi(S.z), f16_lo(S.w), f16_hi(S.w)};
+      if (NB == 2 && ntile) tile(BUF, nsl * SLAB + tw * TOK_PER_WAVE);
+    }
+    constexpr bool LATE = !(W8 && NB == 2);    // the next tile after the unit's last contraction
     f32x4_t cb0[MRB], cb1[MRB];
 #pragma unroll
     for (int j = 0; j < D; ++j)
       if (j < my_nrb)
-        block_bias<KB>(A0[BUF], A1[BUF], emb, 16 * (wr + RG * j) + m, R, g, swz, kzero, cb0[j], cb1[j]);
-    if (D > 0 && my_nrb <= D && ntile)
-      load_w2_tile<KB>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF], A1[BUF]);
+        block_bias<KB, W8>(A0[AB], A1[AB], emb, 16 * (wr + RG * j) + m, R, g, swz, kzero, cb0[j], cb1[j]);
+    if (LATE && D > 0 && my_nrb <= D && ntile) tile(BUF, nsl * SLAB + tw * TOK_PER_WAVE);
 #pragma unroll
     for (int j = 0; j < MRB; ++j) {
       const int n = 16 * (wr + RG * j) + m;
@@ -839,16 +946,12 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       // once the unit's last one has issued, this buffer's next tile
       if (D == 0) {
         if (j < my_nrb) {
-          block_bias<KB>(A0[BUF], A1[BUF], emb, n, R, g, swz, kzero, cb0[j], cb1[j]);
-          if (j == my_nrb - 1 && ntile)
-            load_w2_tile<KB>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF],
-                                      A1[BUF]);
+          block_bias<KB, W8>(A0[AB], A1[AB], emb, n, R, g, swz, kzero, cb0[j], cb1[j]);
+          if (LATE && j == my_nrb - 1 && ntile) tile(BUF, nsl * SLAB + tw * TOK_PER_WAVE);
         }
       } else if (j + D < MRB && j + D < my_nrb) {
-        block_bias<KB>(A0[BUF], A1[BUF], emb, n + 16 * RG * D, R, g, swz, kzero, cb0[j + D], cb1[j + D]);
-        if (j + D == my_nrb - 1 && ntile)
-          load_w2_tile<KB>(a.w2, V, R, nsl * SLAB + tw * TOK_PER_WAVE, m, g, kzero, A0[BUF],
-                                    A1[BUF]);
+        block_bias<KB, W8>(A0[AB], A1[AB], emb, n + 16 * RG * D, R, g, swz, kzero, cb0[j + D], cb1[j + D]);
+        if (LATE && j + D == my_nrb - 1 && ntile) tile(BUF, nsl * SLAB + tw * TOK_PER_WAVE);
       }
       const u32x4_t bv = bq[j];
       // block j of the next unit (a whole unit ahead: earlier requests
@@ -860,7 +963,11 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[n];
       const bool active = n < rows && tok_ok;
       const bool noisy = !(info.T == 0.0f);
-      const f32x4_t c0 = cb0[j], c1 = cb1[j];
+      f32x4_t c0 = cb0[j], c1 = cb1[j];
+      if constexpr (W8) {                      // the row scale, one binary32 product
+        c0 = c0 * sc0;
+        c1 = c1 * sc1;
+      }
       uint32_t bw[4];
       bw[0] = pack_bf16(c0[0], c0[1]);
       bw[1] = pack_bf16(c0[2], c0[3]);
@@ -1342,8 +1449,9 @@ StepFn pick_plan(int rg, int mrb) {
 // unit of their own (step_inst.hip built once per pair); each returns its
 // kernel for a plan. X(KB, VAR) lists the pairs built.
 #define MARKOV_STEP_INSTANCES(X) \
-  X(1, 0) X(1, 1) X(1, 2) X(2, 0) X(2, 1) X(2, 2) X(4, 0) X(4, 1) X(4, 2) \
-  X(8, 0) X(8, 1) X(8, 2) X(16, 0) X(16, 1) X(16, 2)
+  X(1, 0) X(1, 1) X(1, 2) X(1, 4) X(1, 6) X(2, 0) X(2, 1) X(2, 2) X(2, 4) X(2, 6) \
+  X(4, 0) X(4, 1) X(4, 2) X(4, 4) X(4, 6) X(8, 0) X(8, 1) X(8, 2) X(8, 4) X(8, 6) \
+  X(16, 0) X(16, 1) X(16, 2) X(16, 4) X(16, 6)
 
 namespace markov_impl {
 #define MARKOV_DECLARE_PICKER(KB, VAR) StepFn step_kernel_kb##KB##_v##VAR(int rg, int mrb);
