@@ -48,11 +48,15 @@ def parse():
     ap.add_argument("--config", default="large",
                     choices=["tiny", "single", "small", "large", "stress"])
     ap.add_argument("--path", default="sample",
-                    choices=["sample", "greedy", "greedy-chain", "fp8", "fp8-greedy"],
+                    choices=["sample", "greedy", "greedy-chain", "fp8", "fp8-greedy", "shard"],
                     help="sample: markov_sample_sequential (the headline); greedy: "
                          "markov_greedy_sequential writing the cache; greedy-chain: the same "
                          "without the cache write; fp8 / fp8-greedy: the same two with the E4M3 "
-                         "w2 (quantized once, untimed)")
+                         "w2 (quantized once, untimed); shard: one GPU's share of a vocabulary-"
+                         "parallel loop (markov_shard_step on slab 0 of --shards, then "
+                         "markov_pick over the shards' packets, per step)")
+    ap.add_argument("--shards", type=int, default=8,
+                    help="vocabulary slabs of --path shard (one GPU's share is timed)")
     ap.add_argument("--graph", action="store_true",
                     help="headline from replays of the loop captured as a HIP graph")
     ap.add_argument("--eager", action="store_true",
@@ -205,6 +209,36 @@ def main():
         call = m.prepare_fp8(w, d, greedy=greedy)
         step_calls = [m.prepare_fp8(w, d, greedy=greedy, step=s) for s in range(w.k)]
         bytes_step -= w.V * w.R - 2 * w.V       # 1-byte codes and a 2-byte scale per row
+    elif args.path == "shard":
+        G = args.shards
+        Vs = w.V // G
+        base0 = d["base"][:, :, :Vs].contiguous()
+        w20 = d["w2"][:Vs].contiguous()
+        cache0 = torch.empty((w.rows, w.k, Vs), dtype=torch.bfloat16, device=dev)
+        ws0 = m.new_workspace(w.rows, Vs, w.R, w.k, device=dev, mult=w.mult, softcap=w.softcap)
+        packets = torch.zeros((G, w.rows), dtype=torch.int64, device=dev)
+        flat = d["tokens"].view(-1)
+
+        def shard_call(s):
+            def f():
+                feed, stride = (d["prev"], 1) if s == 0 else (flat[s - 1:], w.k)
+                m.shard_step(base0, d["w1"], w20, feed, d["seeds"], d["positions"],
+                             d["temperature"], cache0, packets[0], ws0, step=s, vocab_offset=0,
+                             feed_stride=stride, mult=w.mult, softcap=w.softcap)
+            return f
+
+        def pick_call(s):
+            return lambda: m.pick(packets, flat[s:], stride=w.k)
+
+        step_calls = [shard_call(s) for s in range(w.k)]
+        picks = [pick_call(s) for s in range(w.k)]
+
+        def call():
+            for s in range(w.k):
+                step_calls[s]()
+                picks[s]()
+        call.on = None
+        bytes_step = 2 * Vs * w.R + 4 * w.rows * Vs + 2 * w.rows * w.R
     else:
         chain = args.path == "greedy-chain"
         call = m.prepare_greedy(w, d, cache=not chain)
@@ -218,7 +252,7 @@ def main():
     torch.cuda.synchronize()
 
     graph = None
-    if not args.eager:
+    if not args.eager and args.path != "shard":
         side = torch.cuda.Stream()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=side):
@@ -279,7 +313,10 @@ def main():
         "config": {"workload": f"{w.name}: V={w.V} R={w.R} rows={w.rows} k={w.k}"
                                f"{' softcap=%g' % w.softcap if w.softcap > 0 else ''}",
                    "V": w.V, "R": w.R, "rows": w.rows, "k": w.k,
-                   "launches_per_loop": launches, "path": args.path,
+                   "launches_per_loop": launches * (2 if args.path == "shard" else 1),
+                   "path": args.path,
+                   **({"shards": args.shards, "slab_vocab": w.V // args.shards}
+                      if args.path == "shard" else {}),
                    "mode": "graph" if (graph and args.graph) else "eager"},
         "us_per_loop": round(head_wall, 2),
         "us_per_loop_p10_p50_p90": [round(percentile(head_ev, q), 2) for q in (0.1, 0.5, 0.9)],

@@ -270,6 +270,52 @@ int markov_greedy_step_fp8(const void* base_logits, const void* w1, const uint8_
                            void* cache, int64_t* tokens, uint64_t* winners, markov_stream_t stream,
                            const markov_shape_t* shape, void* workspace, size_t workspace_bytes);
 
+/* ---- one GPU's share of a vocabulary-parallel step (vLLM muse_spark
+ * cutedsl draft Markov page: module docstring on tensor-parallel drafting,
+ * the last block's packet, `_PickKernel` / `markov_pick`) -------------------- */
+
+/*
+ * One draft step on the vocabulary slab [vocab_offset, vocab_offset + V) of
+ * a vocabulary of vocab_total tokens, where V = shape->vocab (a multiple of
+ * 8): the same arithmetic as markov_sample_sequential's step `step`, with
+ * every token id global (the noise hash and the packed winner use
+ * vocab_offset + local id), so that the shards' winners combine into the
+ * full-vocabulary token.
+ *   base_logits, cache  device bf16 [rows, k, V]: this slab's columns
+ *   w1                  device bf16 [vocab_total, R]: every row (any token feeds)
+ *   w2                  device bf16 [V, R]: this slab's rows
+ *   feed                device int64, row r's feeding token at feed[r *
+ *                       feed_stride] (global id; clamped as unsigned to
+ *                       vocab_total - 1), e.g. the picked tokens of step-1
+ *   seeds, positions, k, step, temperature  as markov_sample_sequential
+ *   packets             device uint64 [rows] (write): the slab's winner of
+ *                       each row, packed as markov_greedy_sequential's winners
+ *                       (an orderable key of the winning noised logit, then
+ *                       the complement of its global id)
+ *   workspace           as markov_sample_sequential, for this shape
+ * One kernel launch; the workgroup that finishes last writes the packets and
+ * re-zeroes the workspace's slots. Errors: as markov_sample_sequential, and
+ * MARKOV_ERR_SHAPE for step outside [0, k), feed_stride < 1, or a slab
+ * outside [0, vocab_total).
+ */
+int markov_shard_step(const void* base_logits, const void* w1, const void* w2, const int64_t* feed,
+                      int64_t feed_stride, const int64_t* seeds, const int64_t* positions,
+                      int32_t k, int32_t step, const float* temperature, void* cache,
+                      uint64_t* packets, int32_t vocab_offset, int32_t vocab_total,
+                      markov_stream_t stream, const markov_shape_t* shape, void* workspace,
+                      size_t workspace_bytes);
+
+/*
+ * The token of each row over `shards` slabs' packets (device uint64
+ * [shards, rows], e.g. gathered from every GPU): the largest packet, so the
+ * first NaN key, else the largest key, else the lowest global id.
+ * tokens[r * stride] gets the global id (device int64; stride >= 1, e.g. k to
+ * fill column s of a [rows, k] array), and winner[r] (device uint64, or
+ * NULL) the winning packet. One small kernel on `stream`.
+ */
+int markov_pick(const uint64_t* packets, int32_t shards, int32_t rows, int64_t* tokens,
+                int64_t stride, uint64_t* winner, markov_stream_t stream);
+
 /* A readable name of a status code (static string). */
 const char* markov_status_string(int status);
 

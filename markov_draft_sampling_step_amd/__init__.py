@@ -72,6 +72,11 @@ _SIGS = {
                                                     ctypes.c_size_t]),
     "markov_debug_e4m3_encode": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
     "markov_debug_e4m3_decode": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
+    "markov_shard_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, _P, ctypes.c_int32,
+                                         ctypes.c_int32, _P, _P, _P, ctypes.c_int32,
+                                         ctypes.c_int32, _P, ctypes.POINTER(Shape), _P,
+                                         ctypes.c_size_t]),
+    "markov_pick": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P, _P]),
     "markov_debug_bias_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(Shape), _P]),
     "markov_sample_step_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                               ctypes.c_int32, _P, _P, _P, _P,
@@ -369,6 +374,42 @@ def debug_bias_fp8(w1, w2q, w2_scales, tok, bias, stream=None):
                                        _dev(tok, torch.int64, "tok"),
                                        _dev(bias, torch.bfloat16, "bias", (rows, V)),
                                        ctypes.byref(sh), _stream_ptr(stream)), "markov_debug_bias_fp8")
+
+
+def shard_step(base_logits, w1, w2, feed, seeds, positions, temperature, cache, packets,
+               workspace, step: int, vocab_offset: int, feed_stride: int = 1, mult: float = 1.0,
+               softcap: float = 0.0, stream=None):
+    """markov_shard_step: base_logits / cache bf16 [rows, k, Vs] (this slab),
+    w1 bf16 [V_total, R], w2 bf16 [Vs, R] (this slab), feed int64 (row r at
+    feed[r * feed_stride]), packets int64 [rows] (u64 bits)."""
+    import torch
+
+    rows, k, Vs = base_logits.shape
+    Vt, R = w1.shape
+    sh = make_shape(rows, Vs, R, mult, softcap)
+    _check(lib().markov_shard_step(
+        _dev(base_logits, torch.bfloat16, "base_logits"), _dev(w1, torch.bfloat16, "w1"),
+        _dev(w2, torch.bfloat16, "w2", (Vs, R)), _dev(feed, torch.int64, "feed"),
+        int(feed_stride), _dev(seeds, torch.int64, "seeds", (rows,)),
+        _dev(positions, torch.int64, "positions", (rows, k)), ctypes.c_int32(k),
+        ctypes.c_int32(step), _dev(temperature, torch.float32, "temperature", (rows,)),
+        _dev(cache, torch.bfloat16, "cache", (rows, k, Vs)),
+        _dev(packets, torch.int64, "packets", (rows,)), ctypes.c_int32(vocab_offset),
+        ctypes.c_int32(Vt), _stream_ptr(stream), ctypes.byref(sh),
+        _dev(workspace, torch.uint8, "workspace"), ctypes.c_size_t(workspace.numel())),
+        "markov_shard_step")
+
+
+def pick(packets, tokens, stride: int = 1, winner=None, stream=None):
+    """markov_pick: packets int64 [G, rows] (u64 bits); tokens int64 (row r's
+    global token at tokens[r * stride])."""
+    import torch
+
+    G, rows = packets.shape
+    _check(lib().markov_pick(_dev(packets, torch.int64, "packets"), G, rows,
+                             _dev(tokens, torch.int64, "tokens"), int(stride),
+                             _opt(winner, torch.int64, "winner", (rows,)), _stream_ptr(stream)),
+           "markov_pick")
 
 
 def noalloc_max_rows() -> int:

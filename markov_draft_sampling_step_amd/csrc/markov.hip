@@ -227,40 +227,44 @@ int check_shape(const markov_shape_t* sh, int32_t k) {
   return MARKOV_OK;
 }
 
+// Per (kernel, device): its dynamic-LDS limit raised to the largest any plan
+// uses (the attribute holds one value per kernel, so it is set once, to the
+// maximum, rather than per launch size), and the device's CU count.
 struct LaunchCache {
   StepFn fn;
   int device;
-  size_t lds;
   int cus;
 };
-LaunchCache g_cache[64];
+constexpr int LAUNCH_CACHE = 512;
+LaunchCache g_cache[LAUNCH_CACHE];
 int g_cache_n = 0;
 std::mutex g_cache_mutex;   // host threads may launch concurrently
 
 // Workgroups to launch: one per CU (the kernel is sized for one resident
-// 8-wave workgroup), never more than there are slab pairs (one slab for each
-// of a SIMD's two waves).
-int launch_grid(StepFn fn, size_t lds, int nslabs, int S, int* grid) {
+// 8-wave workgroup), never more than there are slabs (a workgroup's second
+// waves take slab blockIdx + grid, if there is one).
+int launch_grid(StepFn fn, size_t lds, int nslabs, int* grid) {
+  if (lds > LDS_MAX) return MARKOV_ERR_ROWS;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MARKOV_ERR_HIP;
   int cus = 0;
   std::lock_guard<std::mutex> lock(g_cache_mutex);
   for (int i = 0; i < g_cache_n; ++i)
-    if (g_cache[i].fn == fn && g_cache[i].device == dev && g_cache[i].lds == lds) cus = g_cache[i].cus;
+    if (g_cache[i].fn == fn && g_cache[i].device == dev) cus = g_cache[i].cus;
   if (cus == 0) {
-    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-        hipSuccess)
+    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)LDS_MAX) != hipSuccess)
       return MARKOV_ERR_HIP;
     int occ = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return MARKOV_ERR_HIP;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)fn, NTH, lds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)fn, NTH, LDS_MAX) !=
+        hipSuccess)
       return MARKOV_ERR_HIP;
     if (occ < 1 || cus < 1) return MARKOV_ERR_ROWS;
-    if (g_cache_n < 64) g_cache[g_cache_n++] = LaunchCache{fn, dev, lds, cus};
+    if (g_cache_n < LAUNCH_CACHE) g_cache[g_cache_n++] = LaunchCache{fn, dev, cus};
   }
-  const int want = (nslabs + S - 1) / S;
-  *grid = want < cus ? want : cus;
+  *grid = nslabs < cus ? nslabs : cus;
   return MARKOV_OK;
 }
 
@@ -278,6 +282,9 @@ struct Call {
   unsigned long long* winners = nullptr;
   const uint8_t* w2q = nullptr;               // E4M3 w2 (with var & V_W8)
   const uint16_t* w2s = nullptr;
+  unsigned long long* packets = nullptr;      // a vocabulary shard's output
+  int64_t feed_stride = 1;
+  int32_t id_offset = 0, vocab_total = 0;     // 0: the shape's vocab
   void* bias_out = nullptr;
   int32_t k = 1, s_begin = 0, s_end = 1;
 };
@@ -293,7 +300,7 @@ int launch_steps(const Call& c, markov_stream_t stream, const markov_shape_t* sh
   const size_t lds = (tt_layout ? TT_BYTES : 0) + lds_total(rp, sh->rank, greedy);
   const int nslabs = (sh->vocab + SLAB - 1) / SLAB;
   int grid = 0;
-  int rc = launch_grid(fn, lds, nslabs, plan.rg == 1 ? 2 : 1, &grid);
+  int rc = launch_grid(fn, lds, nslabs, &grid);
   if (rc) return rc;
   StepArgs a;
   memset(&a, 0, sizeof(a));
@@ -309,6 +316,10 @@ int launch_steps(const Call& c, markov_stream_t stream, const markov_shape_t* sh
   a.winners = c.winners;
   a.w2q = c.w2q;
   a.w2s = c.w2s;
+  a.packets = c.packets;
+  a.feed_stride = c.feed_stride;
+  a.id_offset = c.id_offset;
+  a.V_total = c.vocab_total > 0 ? c.vocab_total : sh->vocab;
   a.bias_out = (uint16_t*)c.bias_out;
   if (workspace) {
     a.gtable = (const float*)workspace;
@@ -452,6 +463,22 @@ __global__ void debug_e4m3_encode_kernel(const float* x, uint8_t* out, int64_t n
 __global__ void debug_e4m3_decode_kernel(const uint2* codes, bf16x8_t* out, int64_t n8) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n8) out[i] = decode8(codes[i].x, codes[i].y);
+}
+
+// A row's token over G vocabulary shards: the largest packed winner (the
+// packing orders as the total order, global ids included) decoded.
+__global__ __launch_bounds__(256) void pick_kernel(const unsigned long long* packets, int G, int rows,
+                                                   int64_t* tokens, int64_t stride,
+                                                   unsigned long long* winner) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  unsigned long long w = 0ull;
+  for (int g = 0; g < G; ++g) {
+    const unsigned long long c = packets[(size_t)g * rows + r];
+    w = c > w ? c : w;
+  }
+  tokens[(int64_t)r * stride] = slot_token(w);
+  if (winner) winner[r] = w;
 }
 
 // The packed winners' token ids (the low word holds ~id).
@@ -679,6 +706,56 @@ int markov_greedy_step_fp8(const void* base_logits, const void* w1, const uint8_
   return greedy_common(base_logits, w1, nullptr, prev, k, step, step + 1, cache, tokens,
                        (unsigned long long*)winners, stream, shape, workspace, workspace_bytes,
                        w2q, w2_scales);
+}
+
+int markov_shard_step(const void* base_logits, const void* w1, const void* w2, const int64_t* feed,
+                      int64_t feed_stride, const int64_t* seeds, const int64_t* positions,
+                      int32_t k, int32_t step, const float* temperature, void* cache,
+                      uint64_t* packets, int32_t vocab_offset, int32_t vocab_total,
+                      markov_stream_t stream, const markov_shape_t* shape, void* workspace,
+                      size_t workspace_bytes) {
+  int rc = check_shape(shape, k);
+  if (rc) return rc;
+  if (step < 0 || step >= k || feed_stride < 1 || vocab_offset < 0 || vocab_total < 1 ||
+      (int64_t)vocab_offset + shape->vocab > (int64_t)vocab_total)
+    return MARKOV_ERR_SHAPE;
+  if (!base_logits || !w1 || !w2 || !feed || !seeds || !positions || !temperature || !cache ||
+      !packets || !workspace)
+    return MARKOV_ERR_NULL;
+  if (!aligned16(base_logits) || !aligned16(w1) || !aligned16(w2) || !aligned16(cache) ||
+      !aligned16(workspace))
+    return MARKOV_ERR_ALIGN;
+  if (workspace_bytes < ws_bytes(shape->rows)) return MARKOV_ERR_WORKSPACE;
+  Call c;
+  c.mode = MODE_SAMPLE;
+  c.var = V_SAMPLE;
+  c.base = base_logits;
+  c.w1 = w1;
+  c.w2 = w2;
+  c.prev = feed;
+  c.feed_stride = feed_stride;
+  c.seeds = seeds;
+  c.positions = positions;
+  c.temperature = temperature;
+  c.cache = cache;
+  c.packets = (unsigned long long*)packets;
+  c.id_offset = vocab_offset;
+  c.vocab_total = vocab_total;
+  c.k = k;
+  c.s_begin = step;
+  c.s_end = step + 1;
+  return launch_steps(c, stream, shape, workspace);
+}
+
+int markov_pick(const uint64_t* packets, int32_t shards, int32_t rows, int64_t* tokens,
+                int64_t stride, uint64_t* winner, markov_stream_t stream) {
+  if (shards < 1 || rows < 1 || stride < 1) return MARKOV_ERR_SHAPE;
+  if (!packets || !tokens) return MARKOV_ERR_NULL;
+  pick_kernel<<<dim3((unsigned)((rows + 255) / 256)), 256, 0, (hipStream_t)stream>>>(
+      (const unsigned long long*)packets, shards, rows, tokens, stride,
+      (unsigned long long*)winner);
+  if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
+  return MARKOV_OK;
 }
 
 int markov_debug_e4m3_encode(const float* x, uint8_t* out, int64_t n, markov_stream_t stream) {

@@ -68,6 +68,13 @@ struct StepArgs {
   unsigned long long* winners;  // greedy: [rows, k] packed winners (NULL: not written)
   const uint8_t* w2q;           // E4M3 w2 [V, R] codes (the V_W8 variant)
   const uint16_t* w2s;          // its FP16 row scales [V]
+  // vocabulary shard: the step on tokens [id_offset, id_offset + V) of a
+  // vocabulary of V_total (w1 has V_total rows), fed from prev[r *
+  // feed_stride] at every step; its per-row winner (global id) goes to
+  // packets[r] instead of a token (NULL: not a shard)
+  unsigned long long* packets;
+  int64_t feed_stride;
+  int id_offset, V_total;
   int rows, V, R, k, step, nslabs, mode;
   int tt_layout;              // LDS holds the transform table at address 0
   float mult, inv_cap, cap;
@@ -654,6 +661,10 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   const int R = KB >= 2 ? 32 * KB : a.R;
   const int rows = a.rows, rp = (rows + 15) & ~15, V = a.V, K = a.k;
   const int s = a.step;
+  const bool shard = a.packets != nullptr;             // uniform
+  const int sset = shard ? 0 : s % 3;                  // this launch's slot set
+  const bool feed_prev = bias_mode || shard || s == 0; // the feeding token comes from prev
+  const int gofs = a.id_offset;                        // global id of local token 0
   const int nslabs = a.nslabs, G = gridDim.x;
   const int cpr = R >> 3;
   const int swz = (cpr < 16 ? cpr : 16) - 1;
@@ -695,8 +706,8 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     }
     // the feeding token: prev at step 0, else the previous step's winner
     // slots (decoded after the wait below)
-    if (bias_mode || s == 0) {
-      tok = a.prev[r];
+    if (feed_prev) {
+      tok = a.prev[(int64_t)r * a.feed_stride];
     } else {
       const unsigned long long* sp0 = a.slots + (size_t)((s + 2) % 3) * SG * rows + r;
 #pragma unroll
@@ -731,7 +742,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   const float rcp_r = 1.0f / T;
   const uint32_t prefix_r = (valid && !bias_mode && !GREEDY) ? row_prefix_of(seed, s, pos) : 0u;
   unsigned long long win_in = 0ull;   // the previous step's packed winner of this row
-  if (!(bias_mode || s == 0)) {
+  if (!feed_prev) {
     win_in = slot_in[0];
 #pragma unroll
     for (int q = 1; q < SG; ++q) win_in = slot_in[q] > win_in ? slot_in[q] : win_in;
@@ -786,10 +797,10 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
                                 : tot_n + pre_z + (int)lanes_below(bz);
       n_row[pos_n] = r;
       // the feeding token (any int64 at step 0, clamped as unsigned)
-      const uint64_t ut = (uint64_t)tok, last = (uint64_t)(V - 1);
+      const uint64_t ut = (uint64_t)tok, last = (uint64_t)(a.V_total - 1);
       n_src[pos_n] = (int)(ut < last ? ut : last);
       n_info[pos_n] = RowInfo{r * K + s, rcp_r, prefix_r, T};
-      if (!bias_mode && blockIdx.x == 0) {
+      if (!bias_mode && !shard && blockIdx.x == 0) {
         if (s > 0) {                                                 // previous step's
           a.tokens[(int64_t)r * K + s - 1] = (int64_t)(uint32_t)tok32;
           if (a.winners) a.winners[(int64_t)r * K + s - 1] = win_in;
@@ -830,7 +841,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   bool sp[MRB];
   uint32_t lw[CARRY ? MRB : 1];   // noisy rows: the word of cached logits holding the top element's
 
-  unsigned long long* slots_step = bias_mode ? nullptr : a.slots + (size_t)(s % 3) * SG * rows;
+  unsigned long long* slots_step = bias_mode ? nullptr : a.slots + (size_t)sset * SG * rows;
   unsigned long long* slots_cur = bias_mode ? nullptr : slots_step + (size_t)(blockIdx.x % SG) * rows;
   lds_barrier();
   if (ROWREG) {
@@ -914,7 +925,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     const int psl = sl + slab_step;
     uint32_t kw[8];
     if (!bias_mode && !GREEDY) {
-      uint32_t kc = (uint32_t)tg * MM_C1;
+      uint32_t kc = (uint32_t)(tg + gofs) * MM_C1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         kw[e] = rotl32(rotl32(kc, 15) * MM_C2, 13);   // the token word, rotated for mm_finish_rot
@@ -1223,7 +1234,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         const uint32_t wd = load_cache_word(a.cache, e & ~(size_t)1);
         l1 = (e & 1) ? bf_hi(wd) : bf_lo(wd);
       }
-      key = key_exact(l1, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)st.id)));
+      key = key_exact(l1, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)(st.id + gofs))));
       const float v2u = slack_up(st.v2);
       if (!(key > v2u)) {
         // not certified: some other element's bound reaches the key. If a
@@ -1247,7 +1258,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       fb_row[i] = n;
       fb_thr[i] = thr;
     } else if (st.id != NONE) {
-      __hip_atomic_fetch_max(slots_cur + rr, pack_winner(key, st.id), __ATOMIC_RELAXED,
+      __hip_atomic_fetch_max(slots_cur + rr, pack_winner(key, st.id + gofs), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -1312,7 +1323,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
           const int t = t0[b] + e;
           const float l = e ? bf_hi(wd[b]) : bf_lo(wd[b]);
           if (screen) {
-            const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
+            const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)(t + gofs)));
             if (!(key_upper(l, info.rcp, noise_bound<LIN>(gtab, h)) < thr)) {
               if (nc == 0) {
                 ct0 = t;
@@ -1330,7 +1341,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
             if (noisy && nan_mode)
               key = key_is_nan(l, info.T) ? __builtin_nanf("") : -INFINITY;
             else if (noisy)
-              key = key_exact(l, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)t)));
+              key = key_exact(l, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)(t + gofs))));
             if (before(key, t, bv, bi)) {
               bv = key;
               bi = t;
@@ -1360,7 +1371,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
           for (int e = 0; e < 2; ++e) {
             const int t = t0[b] + e;
             const float l = e ? bf_hi(wd[b]) : bf_lo(wd[b]);
-            const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)t));
+            const uint32_t h = mm_finish(info.prefix, mm_token_word((uint32_t)(t + gofs)));
             if (key_upper(l, info.rcp, noise_bound<LIN>(gtab, h)) < thr) continue;
             const float key = key_exact(l, info.T, h);
             if (before(key, t, bv, bi)) {
@@ -1381,18 +1392,19 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       }
     }
     if (lane == 0 && bi != NONE)
-      __hip_atomic_fetch_max(slots_cur + rr, pack_winner(bv, bi), __ATOMIC_RELAXED,
+      __hip_atomic_fetch_max(slots_cur + rr, pack_winner(bv, bi + gofs), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // 7. the last step: the workgroup that finishes last turns the winners into
-  //    tokens[:, k-1] and leaves every slot and the ticket zeroed for the next
-  //    call. The slots and the ticket are only ever read or written by
+  // 7. the last step (and every step of a vocabulary shard): the workgroup
+  //    that finishes last turns the winners into tokens[:, k-1] (a shard's
+  //    into its packets, the packed winner with the global id) and leaves
+  //    every slot and the ticket zeroed for the next call. The slots and the ticket are only ever read or written by
   //    device-scope atomics, which are performed at one point for the whole
   //    device; each workgroup takes its ticket only after its own slot
   //    atomics have completed (vmcnt(0)), so the one that takes the last
   //    ticket reads final values. Nothing waits on another workgroup.
-  if (s == K - 1) {
+  if (shard || s == K - 1) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
@@ -1402,7 +1414,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
                      : 0;
     __syncthreads();
     if (misc[17]) {
-      unsigned long long* fin_slots = a.slots + (size_t)(s % 3) * SG * rows;
+      unsigned long long* fin_slots = a.slots + (size_t)sset * SG * rows;
       for (int r2 = tid; r2 < rows; r2 += NTH) {
         unsigned long long w = 0ull;
 #pragma unroll
@@ -1411,11 +1423,15 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           w = c > w ? c : w;
         }
-        a.tokens[(int64_t)r2 * K + K - 1] = slot_token(w);
-        if (a.winners) a.winners[(int64_t)r2 * K + K - 1] = w;
+        if (shard) {
+          a.packets[r2] = w;
+        } else {
+          a.tokens[(int64_t)r2 * K + K - 1] = slot_token(w);
+          if (a.winners) a.winners[(int64_t)r2 * K + K - 1] = w;
+        }
       }
       for (int i = tid; i < 3 * SG * rows; i += NTH)
-        if (i / (SG * rows) != s % 3) a.slots[i] = 0ull;
+        if (i / (SG * rows) != sset) a.slots[i] = 0ull;
       if (tid == 0) __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
