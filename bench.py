@@ -48,13 +48,16 @@ def parse():
     ap.add_argument("--config", default="large",
                     choices=["tiny", "single", "small", "large", "stress"])
     ap.add_argument("--path", default="sample",
-                    choices=["sample", "greedy", "greedy-chain", "fp8", "fp8-greedy", "shard"],
+                    choices=["sample", "greedy", "greedy-chain", "fp8", "fp8-greedy", "shard",
+                             "verify-greedy", "verify-prob"],
                     help="sample: markov_sample_sequential (the headline); greedy: "
                          "markov_greedy_sequential writing the cache; greedy-chain: the same "
                          "without the cache write; fp8 / fp8-greedy: the same two with the E4M3 "
                          "w2 (quantized once, untimed); shard: one GPU's share of a vocabulary-"
                          "parallel loop (markov_shard_step on slab 0 of --shards, then "
                          "markov_pick over the shards' packets, per step)")
+    ap.add_argument("--verify-rows", type=int, default=64,
+                    help="batch rows of --path verify-* (P = 5 proposals, V = 163840)")
     ap.add_argument("--shards", type=int, default=8,
                     help="vocabulary slabs of --path shard (one GPU's share is timed)")
     ap.add_argument("--graph", action="store_true",
@@ -167,6 +170,59 @@ def time_loops(torch, launch, stream, n):
     return wall, [a.elapsed_time(b) * 1e3 for a, b in evs]
 
 
+def bench_verify(args, torch, m, workloads, dev, stream):
+    """One verifier launch per bench step over the synthetic drafted block
+    (64 rows, 5 proposals, V = 163840); value = verified rows per second.
+    Algorithmic bytes: the greedy verifier reads target positions 0..L of
+    each row (bf16), the probabilistic one the p and q rows of the first
+    rejection (or p_L) once (fp32)."""
+    v = workloads.make_verify(B=args.verify_rows)
+    B, P, V = v.B, v.P, v.V
+    acc = torch.empty((B, P + 1), dtype=torch.int64, device=dev)
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = m.new_verify_workspace(B, P, device=dev)
+    L = torch.from_numpy(v.lengths).to(dev)
+    if args.path == "verify-greedy":
+        lg = torch.from_numpy(v.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+        dr = torch.from_numpy(v.draft_greedy).to(dev)
+        call = lambda: m.greedy_accept(lg, dr, L, acc, n, ws)   # noqa: E731
+    else:
+        t = torch.from_numpy(v.target).to(dev)
+        q = torch.from_numpy(v.draftp).to(dev)
+        dr = torch.from_numpy(v.draft_sampled).to(dev)
+        u = torch.from_numpy(v.uniforms).to(dev)
+        call = lambda: m.prob_accept(t, q, dr, L, u, acc, n, ws)   # noqa: E731
+    for _ in range(max(1, args.warmup)):
+        call()
+    torch.cuda.synchronize()
+    wall, ev = time_loops(torch, call, stream, args.steps)
+    kern_us = sum(ev) / len(ev)
+    nl = n.cpu().numpy()
+    Lc = np.clip(v.lengths, 0, P)
+    if args.path == "verify-greedy":
+        bytes_launch = int(((Lc + 1) * 2 * V).sum())
+    else:
+        rejected = nl <= Lc                      # the token after the accepted drafts was resampled
+        bytes_launch = int(np.where(rejected, 8 * V, 4 * V).sum())
+    achieved = bytes_launch / (kern_us * 1e-6) / 1e9
+    out = {
+        "metric": "verified rows/s (" + args.path + ")", "value": round(B / (wall * 1e-6), 1),
+        "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e-3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if args.path == "verify-greedy" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"verify: B={B} P={P} V={V}", "path": args.path, "mode": "eager"},
+        "us_per_launch_p10_p50_p90": [round(percentile(ev, q), 2) for q in (0.1, 0.5, 0.9)],
+        "accept_lengths": np.bincount(nl, minlength=P + 2).tolist(),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_us": round(kern_us, 3), "bytes_per_launch": bytes_launch,
+                     "kernel": "greedy_accept_kernel" if args.path == "verify-greedy"
+                     else "prob_accept_kernel"},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -192,6 +248,9 @@ def main():
             m.debug_copy(src, dst)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.path.startswith("verify"):
+        return bench_verify(args, torch, m, workloads, dev, stream)
 
     w = workloads.make(args.config)
     d = workloads.to_device(w, dev)

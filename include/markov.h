@@ -316,6 +316,54 @@ int markov_shard_step(const void* base_logits, const void* w1, const void* w2, c
 int markov_pick(const uint64_t* packets, int32_t shards, int32_t rows, int64_t* tokens,
                 int64_t stride, uint64_t* winner, markov_stream_t stream);
 
+/* ---- verification of a drafted block (TensorRT Edge-LLM "DSpark kernels"
+ * page: `dsparkGreedyAccept`, `dsparkProbabilisticAccept`) --------------------
+ *
+ * Shapes: B rows, P proposals per row, V tokens. Draft token j of row b
+ * (draft[b * draft_stride + j], j < P) sits at verify position j + 1 and is
+ * checked against the target at position j. proposal_lengths[b] = L_b (int32;
+ * above P counts as P, below 0 as 0). Outputs: accepted int64 [B, P + 1],
+ * the accepted drafts then one more token, -1 after; accept_len int32 [B],
+ * their count (accepted drafts + 1). workspace: device, at least
+ * markov_verify_workspace_bytes(B, P), 16-byte aligned, zeroed once by the
+ * caller (hipMemset) and left zeroed by every call; not shared by two calls
+ * in flight. One kernel launch each, no host synchronisation. Errors:
+ * MARKOV_ERR_SHAPE (B < 1, P < 0, draft_stride < P, V out of range),
+ * MARKOV_ERR_NULL, MARKOV_ERR_ALIGN, MARKOV_ERR_WORKSPACE, MARKOV_ERR_HIP.
+ */
+size_t markov_verify_workspace_bytes(int32_t batch, int32_t proposal_len);
+
+/*
+ * Greedy: a_j = the first NaN, else the lowest id of the largest value of
+ * target_logits[b][j][0..V) (device bf16 [B, P+1, V], 16-byte aligned, V a
+ * multiple of 8). Drafts j = 0, 1, ... are accepted while draft j == a_j and
+ * j < L_b; the token after them is a_n (n accepted), the base's bonus token.
+ */
+int markov_greedy_accept(const void* target_logits, const int64_t* draft, int32_t draft_stride,
+                         const int32_t* proposal_lengths, int64_t* accepted, int32_t* accept_len,
+                         int32_t batch, int32_t proposal_len, int32_t vocab, void* workspace,
+                         size_t workspace_bytes, markov_stream_t stream);
+
+/*
+ * Probabilistic (speculative sampling with a residual): target_probs p
+ * device fp32 [B, P+1, V], draft_probs q device fp32 [B, P, V], uniforms
+ * device fp32 [B, 2P+1]. Draft j (token d) is accepted iff u_j q_j(d) <
+ * p_j(d), both products exact in binary64 (an id outside [0, V) never is).
+ * At the first rejection j the token after the accepted drafts is sampled
+ * from r(x) = max(0, RN32(p_j(x) - q_j(x))) with u_{P+j}; if all L_b drafts
+ * pass, from p_{L_b} with u_{2P}. Sampling with u from weights w: the
+ * smallest x whose running sum of w exceeds u times the total, sums in
+ * binary64 (their order is the kernel's own, so the token may differ from
+ * an index-order sum only where u times the total lies within a few
+ * binary64 ulps of a running sum); with no residual mass p_j itself is
+ * sampled, and with none either token 0.
+ */
+int markov_prob_accept(const float* target_probs, const float* draft_probs, const int64_t* draft,
+                       int32_t draft_stride, const int32_t* proposal_lengths, const float* uniforms,
+                       int64_t* accepted, int32_t* accept_len, int32_t batch, int32_t proposal_len,
+                       int32_t vocab, void* workspace, size_t workspace_bytes,
+                       markov_stream_t stream);
+
 /* A readable name of a status code (static string). */
 const char* markov_status_string(int status);
 

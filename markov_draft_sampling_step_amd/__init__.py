@@ -77,6 +77,12 @@ _SIGS = {
                                          ctypes.c_int32, _P, ctypes.POINTER(Shape), _P,
                                          ctypes.c_size_t]),
     "markov_pick": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P, _P]),
+    "markov_verify_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
+    "markov_greedy_accept": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
+    "markov_prob_accept": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
+                                          ctypes.c_size_t, _P]),
     "markov_debug_bias_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(Shape), _P]),
     "markov_sample_step_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                               ctypes.c_int32, _P, _P, _P, _P,
@@ -410,6 +416,53 @@ def pick(packets, tokens, stride: int = 1, winner=None, stream=None):
                              _dev(tokens, torch.int64, "tokens"), int(stride),
                              _opt(winner, torch.int64, "winner", (rows,)), _stream_ptr(stream)),
            "markov_pick")
+
+
+def new_verify_workspace(batch: int, proposal_len: int, device="cuda"):
+    """A zeroed workspace for the verifiers (uint8 tensor)."""
+    import torch
+
+    n = int(lib().markov_verify_workspace_bytes(int(batch), int(proposal_len)))
+    if n == 0:
+        raise MarkovError(-2, "markov_verify_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def greedy_accept(target_logits, draft, proposal_lengths, accepted, accept_len, workspace,
+                  stream=None):
+    """markov_greedy_accept: target_logits bf16 [B, P+1, V]; draft int64 [B, S]
+    (S >= P); proposal_lengths int32 [B]; accepted int64 [B, P+1]; accept_len
+    int32 [B]."""
+    import torch
+
+    B, P1, V = target_logits.shape
+    _check(lib().markov_greedy_accept(
+        _dev(target_logits, torch.bfloat16, "target_logits"), _dev(draft, torch.int64, "draft"),
+        draft.shape[1], _dev(proposal_lengths, torch.int32, "proposal_lengths", (B,)),
+        _dev(accepted, torch.int64, "accepted", (B, P1)),
+        _dev(accept_len, torch.int32, "accept_len", (B,)), B, P1 - 1, V,
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream)),
+        "markov_greedy_accept")
+
+
+def prob_accept(target_probs, draft_probs, draft, proposal_lengths, uniforms, accepted,
+                accept_len, workspace, stream=None):
+    """markov_prob_accept: target_probs fp32 [B, P+1, V]; draft_probs fp32
+    [B, P, V]; draft int64 [B, S]; proposal_lengths int32 [B]; uniforms fp32
+    [B, 2P+1]; accepted int64 [B, P+1]; accept_len int32 [B]."""
+    import torch
+
+    B, P1, V = target_probs.shape
+    P = P1 - 1
+    _check(lib().markov_prob_accept(
+        _dev(target_probs, torch.float32, "target_probs"),
+        _dev(draft_probs, torch.float32, "draft_probs", (B, P, V)), _dev(draft, torch.int64, "draft"),
+        draft.shape[1], _dev(proposal_lengths, torch.int32, "proposal_lengths", (B,)),
+        _dev(uniforms, torch.float32, "uniforms", (B, 2 * P + 1)),
+        _dev(accepted, torch.int64, "accepted", (B, P1)),
+        _dev(accept_len, torch.int32, "accept_len", (B,)), B, P, V,
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream)),
+        "markov_prob_accept")
 
 
 def noalloc_max_rows() -> int:

@@ -43,7 +43,9 @@ def instances():
 
 def units():
     """(source, object, extra flags) of every translation unit."""
-    out = [(os.path.join(CSRC, "markov.hip"), os.path.join(OBJDIR, "markov.o"), [])]
+    out = [(src, os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o"), [])
+           for src in sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC))
+           if src.endswith(".hip") and not src.endswith("step_inst.hip")]
     for kb, var in instances():
         out.append((os.path.join(CSRC, "step_inst.hip"),
                     os.path.join(OBJDIR, f"step_kb{kb}_v{var}.o"),

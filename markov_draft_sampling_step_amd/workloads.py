@@ -199,3 +199,61 @@ def fetch(d: dict):
 
     cache = d["cache"].view(torch.int16).cpu().numpy().view(np.uint16)
     return cache, d["tokens"].cpu().numpy()
+
+
+# -- verification of a drafted block ---------------------------------------------
+# Synthetic target and draft distributions shaped like the large workload's
+# drafting (64 rows, k = 5 proposals, V = 163840): target logits N(0, 3)
+# per (row, position); draft logits the target's plus N(0, 1) noise, so the
+# draft is close to but not the target; probabilities are their softmax in
+# binary64 stored as binary32. Greedy drafts are the target's argmax with
+# probability 0.8 per position, else a uniform id; sampled drafts are drawn
+# from the draft distribution (Gumbel-max with numpy's generator). A quarter
+# of the rows propose fewer than P tokens. Uniforms are uniform in [0, 1).
+
+
+@dataclass
+class VerifyWorkload:
+    name: str
+    B: int
+    P: int
+    V: int
+    logits: np.ndarray        # uint16 bf16 [B, P+1, V]: the target's logits (greedy verifier)
+    target: np.ndarray        # float32 [B, P+1, V]
+    draftp: np.ndarray        # float32 [B, P, V]
+    draft_greedy: np.ndarray  # int64 [B, P]
+    draft_sampled: np.ndarray  # int64 [B, P]
+    lengths: np.ndarray       # int32 [B]
+    uniforms: np.ndarray      # float32 [B, 2P+1]
+
+
+def make_verify(B: int = 64, P: int = 5, V: int = 163840, data_seed: int = 5,
+                name: str = "verify") -> VerifyWorkload:
+    rng = np.random.default_rng(data_seed)
+    x = rng.standard_normal(size=(B, P + 1, V), dtype=np.float32) * np.float32(3.0)
+    logits = to_bf16_bits(x)
+    lf = bf16_bits_to_f32(logits).astype(np.float64)
+
+    def softmax(z):
+        z = z - z.max(axis=-1, keepdims=True)
+        e = np.exp(z)
+        return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+    target = np.empty((B, P + 1, V), dtype=np.float32)
+    draftp = np.empty((B, P, V), dtype=np.float32)
+    draft_sampled = np.empty((B, P), dtype=np.int64)
+    for b in range(B):
+        target[b] = softmax(lf[b])
+        dz = lf[b, :P] + rng.standard_normal(size=(P, V))
+        draftp[b] = softmax(dz)
+        g = -np.log(-np.log(rng.random(size=(P, V))))
+        draft_sampled[b] = np.argmax(np.log(np.maximum(draftp[b], 1e-45)) + g, axis=1)
+    am = np.argmax(bf16_bits_to_f32(logits[:, :P]), axis=2)
+    draft_greedy = np.where(rng.random((B, P)) < 0.8, am, rng.integers(0, V, size=(B, P))).astype(np.int64)
+    lengths = np.full(B, P, dtype=np.int32)
+    short = rng.random(B) < 0.25
+    lengths[short] = rng.integers(0, max(P, 1), size=int(short.sum()))
+    uniforms = rng.random((B, 2 * P + 1)).astype(np.float32)
+    return VerifyWorkload(name=name, B=B, P=P, V=V, logits=logits, target=target, draftp=draftp,
+                          draft_greedy=draft_greedy, draft_sampled=draft_sampled,
+                          lengths=lengths, uniforms=uniforms)

@@ -79,6 +79,8 @@ _SIGS = {
     "oracle_decided": (ctypes.c_int, [_I32, _P, _P, _F32, _I64, _I32, _I64, _I32, _P]),
     "oracle_cache_admissible": (ctypes.c_int, [ctypes.c_uint16, _P, _P, _I32, _F32, _F32,
                                                 ctypes.c_uint16]),
+    "oracle_greedy_accept_row": (_I32, [_P, _I64, _I32, _P, _I32, _P]),
+    "oracle_prob_accept_row": (_I32, [_P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _P]),
     "oracle_near_tie": (ctypes.c_int, [_I32, _P, _P, _F32, _I64, _I32, _I64, _I32, _I64]),
     "oracle_log_hard_cases": (_I64, [_F32, _F32, _F64, _P, _I64]),
     "oracle_noise_many": (None, [_U32, _I64, _P, _I32]),
@@ -328,6 +330,47 @@ def noise_many(h0: int, n: int, threads: int = 1) -> np.ndarray:
     out = np.empty(int(n), dtype=np.float32)
     lib().oracle_noise_many(int(h0) & 0xFFFFFFFF, int(n), _ptr(out), int(threads))
     return out
+
+
+def greedy_accept(logits: np.ndarray, draft: np.ndarray, lengths: np.ndarray):
+    """The greedy verifier for every row: logits bf16 bits [B, P+1, V], draft
+    int64 [B, >= P], lengths [B]. Returns (accepted int64 [B, P+1], count [B])."""
+    B, P1, V = logits.shape
+    P = P1 - 1
+    acc = np.empty((B, P1), dtype=np.int64)
+    cnt = np.empty(B, dtype=np.int32)
+    for b in range(B):
+        lg = np.ascontiguousarray(logits[b], dtype=np.uint16)
+        dr = np.ascontiguousarray(draft[b, :P], dtype=np.int64)
+        out = np.empty(P1, dtype=np.int64)
+        cnt[b] = lib().oracle_greedy_accept_row(_ptr(lg), V, P, _ptr(dr), int(lengths[b]), _ptr(out))
+        acc[b] = out
+    return acc, cnt
+
+
+def prob_accept(target: np.ndarray, draftp: np.ndarray, draft: np.ndarray, lengths: np.ndarray,
+                uniforms: np.ndarray):
+    """The probabilistic verifier for every row: target float32 [B, P+1, V],
+    draftp float32 [B, P, V], draft int64 [B, >= P], lengths [B], uniforms
+    float32 [B, 2P+1]. Returns (accepted [B, P+1], count [B], margin [B],
+    mass [B]): the sampled token's CDF margin and the sampled mass."""
+    B, P1, V = target.shape
+    P = P1 - 1
+    acc = np.empty((B, P1), dtype=np.int64)
+    cnt = np.empty(B, dtype=np.int32)
+    mar = np.empty(B, dtype=np.float64)
+    mas = np.empty(B, dtype=np.float64)
+    for b in range(B):
+        t = np.ascontiguousarray(target[b], dtype=np.float32)
+        q = np.ascontiguousarray(draftp[b], dtype=np.float32)
+        dr = np.ascontiguousarray(draft[b, :P], dtype=np.int64)
+        u = np.ascontiguousarray(uniforms[b], dtype=np.float32)
+        out = np.empty(P1, dtype=np.int64)
+        m, s = ctypes.c_double(), ctypes.c_double()
+        cnt[b] = lib().oracle_prob_accept_row(_ptr(t), _ptr(q), V, P, _ptr(dr), int(lengths[b]),
+                                              _ptr(u), _ptr(out), ctypes.byref(m), ctypes.byref(s))
+        acc[b], mar[b], mas[b] = out, m.value, s.value
+    return acc, cnt, mar, mas
 
 
 def log_hard_cases(lo: float, hi: float, ulps: float = 1.0, cap: int = 4096):

@@ -816,3 +816,136 @@ EXPORT void oracle_noise_many(uint32_t h0, int64_t n, float* out, int32_t thread
 #endif
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_gumbel_key(0.0f, 1.0f, (uint32_t)(h0 + (uint64_t)i), NULL, NULL);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Verification of a drafted block                                           */
+/* ------------------------------------------------------------------------ */
+/*
+ * [EDGE] TensorRT Edge-LLM "DSpark kernels" page: `dsparkGreedyAccept` (a
+ * draft token is accepted while it equals the base argmax at the previous
+ * verify position, then the base bonus token is appended) and
+ * `dsparkProbabilisticAccept` (the rejection-sampling verifier with a
+ * residual: acceptUniforms [B, 2P+1], the first P driving accept / reject,
+ * the next P the residual sample of a rejection at the matching step, the
+ * last the bonus sample when the whole proposal is accepted). The rule is
+ * the speculative-sampling rule: accept draft token d at step j with
+ * probability min(1, p_j(d) / q_j(d)); on the first rejection sample from
+ * max(0, p_j - q_j) normalised; if all L proposals pass, sample the bonus
+ * from p_L. Readings:
+ *   - draft token j sits at verify position j + 1, so it is checked against
+ *     the target at position j (the "previous verify position");
+ *   - accept iff u_j q_j(d) < p_j(d), both products exact in binary64;
+ *   - the residual is r(x) = max(0, RN32(p(x) - q(x))); a sample with
+ *     uniform u from weights w is the smallest x with C(x) > u S, C the
+ *     prefix sums of w in index order in binary64, S = C(V-1), u S one
+ *     binary64 product; with S = 0 the residual is replaced by p itself,
+ *     and with that 0 too the token is 0;
+ *   - a proposal length above P counts as P, below 0 as 0; accepted slots
+ *     after the emitted tokens are set to -1; a draft token outside [0, V)
+ *     is never accepted (its p and q are taken as 0).
+ */
+
+/* Sample from weights w[0..V) with uniform u (see above); *margin gets the
+ * distance of u S to the nearer of C(x-1) and C(x) (for the decided rule). */
+static int64_t cdf_sample(const double* w, int64_t V, double u, double* margin) {
+  double S = 0.0;
+  for (int64_t x = 0; x < V; ++x) S += w[x];
+  if (!(S > 0.0)) {
+    if (margin) *margin = INFINITY;
+    return -1;                              /* no mass */
+  }
+  const double t = u * S;
+  double C = 0.0;
+  for (int64_t x = 0; x < V; ++x) {
+    const double prev = C;
+    C += w[x];
+    if (C > t) {
+      if (margin) *margin = fmin(C - t, t - prev);
+      return x;
+    }
+  }
+  if (margin) *margin = 0.0;                /* rounding left u S at or above the total */
+  return V - 1;
+}
+
+/*
+ * The greedy verifier for one row b: argmax under the total order of each
+ * bf16 row logits[j][0..V) for j = 0..P, then acceptance. Returns the number
+ * of tokens written to accepted[0..P] (the accepted drafts and the bonus).
+ */
+EXPORT int32_t oracle_greedy_accept_row(const uint16_t* logits, int64_t V, int32_t P,
+                                        const int64_t* draft, int32_t L, int64_t* accepted) {
+  if (L > P) L = P;
+  if (L < 0) L = 0;
+  float* row = (float*)malloc(sizeof(float) * (size_t)V);
+  int32_t n = 0;
+  int64_t bonus = 0;
+  for (int32_t j = 0; j <= L; ++j) {
+    for (int64_t v = 0; v < V; ++v) row[v] = oracle_bf16_to_f32(logits[(size_t)j * V + v]);
+    const int64_t a = oracle_argmax(row, V);
+    if (j < L && draft[j] == a) {
+      accepted[n++] = draft[j];
+      continue;
+    }
+    bonus = a;
+    break;
+  }
+  accepted[n++] = bonus;
+  for (int32_t i = n; i <= P; ++i) accepted[i] = -1;
+  free(row);
+  return n;
+}
+
+/*
+ * The probabilistic verifier for one row b: target [P+1][V] and draft [P][V]
+ * binary32 probabilities, draft tokens [P], L, uniforms [2P+1]. Writes
+ * accepted[0..P], returns the count; *margin_out (optional) gets the
+ * sampled token's CDF margin relative to the mass S (the decided rule:
+ * any summation order keeps C within (V + 2) 2^-52 S of the index-order
+ * one, so a margin above that leaves the token unique).
+ */
+EXPORT int32_t oracle_prob_accept_row(const float* target, const float* draftp, int64_t V, int32_t P,
+                                      const int64_t* draft, int32_t L, const float* uniforms,
+                                      int64_t* accepted, double* margin_out, double* mass_out) {
+  if (L > P) L = P;
+  if (L < 0) L = 0;
+  int32_t n = 0;
+  int32_t j = 0;
+  for (; j < L; ++j) {
+    const int64_t d = draft[j];
+    const double p = (d >= 0 && d < V) ? (double)target[(size_t)j * V + d] : 0.0;
+    const double q = (d >= 0 && d < V) ? (double)draftp[(size_t)j * V + d] : 0.0;
+    if ((double)uniforms[j] * q < p) {
+      accepted[n++] = d;
+      continue;
+    }
+    break;
+  }
+  double* w = (double*)malloc(sizeof(double) * (size_t)V);
+  double u;
+  const float* prow = target + (size_t)j * V;
+  if (j < L) {                              /* rejected at j: the residual */
+    for (int64_t x = 0; x < V; ++x) {
+      const float r = prow[x] - draftp[(size_t)j * V + x];
+      w[x] = r > 0.0f ? (double)r : 0.0;
+    }
+    u = (double)uniforms[P + j];
+  } else {                                  /* all accepted: the bonus from p_L */
+    for (int64_t x = 0; x < V; ++x) w[x] = (double)prow[x];
+    u = (double)uniforms[2 * P];
+  }
+  double margin = 0.0, S = 0.0;
+  int64_t x = cdf_sample(w, V, u, &margin);
+  if (x < 0) {                              /* no residual mass: sample p itself */
+    for (int64_t y = 0; y < V; ++y) w[y] = (double)prow[y];
+    x = cdf_sample(w, V, u, &margin);
+    if (x < 0) { x = 0; margin = INFINITY; }
+  }
+  for (int64_t y = 0; y < V; ++y) S += w[y];
+  accepted[n++] = x;
+  for (int32_t i = n; i <= P; ++i) accepted[i] = -1;
+  if (margin_out) *margin_out = margin;
+  if (mass_out) *mass_out = S;
+  free(w);
+  return n;
+}
