@@ -1399,21 +1399,25 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   // 7. the last step (and every step of a vocabulary shard): the workgroup
   //    that finishes last turns the winners into tokens[:, k-1] (a shard's
   //    into its packets, the packed winner with the global id) and leaves
-  //    every slot and the ticket zeroed for the next call. The slots and the ticket are only ever read or written by
-  //    device-scope atomics, which are performed at one point for the whole
-  //    device; each workgroup takes its ticket only after its own slot
-  //    atomics have completed (vmcnt(0)), so the one that takes the last
-  //    ticket reads final values. Nothing waits on another workgroup.
+  //    every slot and the ticket zeroed for the next call. Every wave waits
+  //    for its own slot atomics (vmcnt(0)) before the workgroup barrier;
+  //    thread 0 then takes the ticket with an agent-scope release fetch-add,
+  //    so the workgroup's slot updates are visible at agent scope before its
+  //    ticket counts, and the workgroup that takes the last ticket executes
+  //    an agent-scope acquire fence before it reads the slots (the
+  //    acquire-release pairing of the HIP / AMDGPU memory model). Nothing
+  //    waits on another workgroup.
   if (shard || s == K - 1) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-      misc[17] = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      misc[17] = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) ==
                          (unsigned)G - 1u
                      ? 1
                      : 0;
     __syncthreads();
     if (misc[17]) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       unsigned long long* fin_slots = a.slots + (size_t)sset * SG * rows;
       for (int r2 = tid; r2 < rows; r2 += NTH) {
         unsigned long long w = 0ull;

@@ -1,22 +1,25 @@
 // MI355X (gfx950) verification of a drafted block (TensorRT Edge-LLM "DSpark
 // kernels" page: `dsparkGreedyAccept`, `dsparkProbabilisticAccept`).
 //
-// Both verifiers are one launch each, spread over workgroups that each read
-// one slice of a vocabulary row (the rows are large and few):
+// Each verifier is two launches: a wide pass over workgroups that each read
+// one slice of a vocabulary row (the rows are large and few), then one
+// workgroup per batch row that finishes it. The kernel boundary orders the
+// two, so no workgroup needs a device-scope fence (an agent-scope release in
+// every workgroup of the wide pass -- an L2 write-back each -- cost more than
+// the pass itself).
 //   * greedy: a workgroup per (batch row, verify position, vocabulary chunk)
 //     reduces its slice of the bf16 target logits to the first NaN, else the
 //     lowest id of the largest value, and publishes it as one packed 64-bit
-//     atomicMax (an order-preserving key, then the complement of the id);
-//     positions past the row's proposal length are skipped;
+//     atomicMax (an order-preserving key, then the complement of the id) into
+//     the position's slot; positions past the row's proposal length are
+//     skipped. The finisher scans the slots (the acceptance test) and zeroes
+//     them.
 //   * probabilistic: a workgroup per (batch row, vocabulary chunk) finds the
 //     first rejected proposal (the speculative-sampling test u q < p, exact
-//     in binary64), then the binary64 sum of its slice of the residual
-//     max(0, p - q) (or of p_L when every proposal passed);
-// and in both the workgroup that arrives last at its row's ticket (an
-// agent-scope acquire-release fetch-add: every other workgroup's results
-// are visible to it) finishes the row: the greedy acceptance scan, or the
-// inverse-CDF search over the chunk sums and then inside the chunk that holds
-// the threshold. It re-zeroes what it used, so the workspace stays zeroed.
+//     in binary64) and stores the binary64 sum of its slice of the residual
+//     max(0, p - q) (or of p_L when every proposal passed). The finisher adds
+//     the chunk sums in order, finds the chunk that holds the threshold u S,
+//     then the element, and zeroes the sums.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -27,7 +30,8 @@
 namespace {
 
 constexpr int VT = 256;             // threads per verifier workgroup
-constexpr int VCHUNKS = 8;          // vocabulary chunks per row
+constexpr int VCHUNKS = 8;          // vocabulary chunks per row (greedy)
+constexpr int PCHUNKS = 32;         // the most vocabulary chunks per row (probabilistic)
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -62,18 +66,17 @@ __device__ __forceinline__ int64_t unpack_id(unsigned long long w) {
 
 // ---------------------------------------------------------------- greedy
 
-// grid: (chunks, P + 1, B). Workspace: slots [B][P+1] u64, tickets [B] u32.
-__global__ __launch_bounds__(VT) void greedy_accept_kernel(
-    const uint16_t* logits, const int64_t* draft, const int32_t* lengths, int64_t* accepted,
-    int32_t* accept_len, unsigned long long* slots, unsigned int* tickets, int P, int V,
-    int draft_stride, int chunks) {
+// grid: (chunks, P + 1, B). Workspace: slots [B][P+1] u64 (zero between calls).
+__global__ __launch_bounds__(VT) void greedy_accept_kernel(const uint16_t* logits,
+                                                           const int32_t* lengths,
+                                                           unsigned long long* slots, int P, int V,
+                                                           int chunks) {
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int L = lengths[b];
   L = L < 0 ? 0 : L > P ? P : L;
   __shared__ float sv[VT / 64];
   __shared__ int si[VT / 64];
-  __shared__ int last;
   if (j <= L) {
     // this chunk of the row: 8 bf16 per 16-byte load, ids ascending per thread
     const int per = ((V / 8 + chunks - 1) / chunks);
@@ -81,15 +84,25 @@ __global__ __launch_bounds__(VT) void greedy_accept_kernel(
     const uint16_t* row = logits + ((size_t)b * (P + 1) + j) * V;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int q = q0 + tid; q < q1; q += VT) {
-      const u32x4_t w = *(const u32x4_t*)(row + (size_t)q * 8);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    // GU loads in flight per thread before any is used
+    constexpr int GU = 4;
+    for (int q = q0 + tid; q < q1; q += GU * VT) {
+      u32x4_t w[GU];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float l = (e & 1) ? bf_hi(ws[e >> 1]) : bf_lo(ws[e >> 1]);
-        if (before(l, q * 8 + e, bv, bi)) {
-          bv = l;
-          bi = q * 8 + e;
+      for (int u = 0; u < GU; ++u)
+        w[u] = q + u * VT < q1 ? *(const u32x4_t*)(row + (size_t)(q + u * VT) * 8) : (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        if (q + u * VT >= q1) break;
+        const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+        const int id0 = (q + u * VT) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float l = (e & 1) ? bf_hi(ws[e >> 1]) : bf_lo(ws[e >> 1]);
+          if (before(l, id0 + e, bv, bi)) {
+            bv = l;
+            bi = id0 + e;
+          }
         }
       }
     }
@@ -118,34 +131,34 @@ __global__ __launch_bounds__(VT) void greedy_accept_kernel(
                                __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  // the row's ticket: every workgroup of row b counts, skipped positions too
-  if (tid == 0) {
-    const unsigned n = (unsigned)((P + 1) * chunks);
-    last = __hip_atomic_fetch_add(tickets + b, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-           n - 1u;
-  }
-  __syncthreads();
-  if (!last || tid != 0) return;
+}
+
+// One thread per batch row: the acceptance scan over the row's slots.
+__global__ __launch_bounds__(64) void greedy_finish_kernel(const int64_t* draft, const int32_t* lengths,
+                                                           int64_t* accepted, int32_t* accept_len,
+                                                           unsigned long long* slots, int B, int P,
+                                                           int draft_stride) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  int L = lengths[b];
+  L = L < 0 ? 0 : L > P ? P : L;
+  unsigned long long* sl = slots + (size_t)b * (P + 1);
   int n = 0;
   int64_t bonus = 0;
-  for (int jj = 0; jj <= L; ++jj) {
-    const unsigned long long w = __hip_atomic_exchange(slots + (size_t)b * (P + 1) + jj, 0ull,
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int64_t a = unpack_id(w);
+  int jj = 0;
+  for (; jj <= L; ++jj) {
+    const int64_t a = unpack_id(sl[jj]);
     if (jj < L && draft[(size_t)b * draft_stride + jj] == a) {
       accepted[(size_t)b * (P + 1) + n++] = a;
       continue;
     }
     bonus = a;
-    for (int k2 = jj + 1; k2 <= L; ++k2)   // slots the scan did not reach
-      __hip_atomic_store(slots + (size_t)b * (P + 1) + k2, 0ull, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
     break;
   }
   accepted[(size_t)b * (P + 1) + n++] = bonus;
   for (int i = n; i <= P; ++i) accepted[(size_t)b * (P + 1) + i] = -1;
   accept_len[b] = n;
-  __hip_atomic_store(tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i <= L; ++i) sl[i] = 0ull;   // the slots this call filled
 }
 
 // ---------------------------------------------------------------- probabilistic
@@ -173,6 +186,41 @@ __device__ __forceinline__ double weight(const float* prow, const float* qrow, b
   if (!resid) return (double)prow[x];
   const float r = prow[x] - qrow[x];
   return r > 0.0f ? (double)r : 0.0;
+}
+
+// This thread's binary64 sum of the weights of x = x0 + tid, x0 + tid +
+// VT, ... < x1 in groups of four (16-byte loads, four groups in flight) when
+// the row is 16-byte aligned and x0 a multiple of 4, else one by one.
+__device__ double strided_sum(const float* prow, const float* qrow, bool resid, int x0, int x1) {
+  const int tid = threadIdx.x;
+  double s = 0.0;
+  const bool vec = ((((uintptr_t)prow) | (uintptr_t)(resid ? qrow : prow)) & 15u) == 0 && (x0 & 3) == 0;
+  if (vec) {
+    const int g0 = x0 / 4, g1 = x1 / 4;
+    for (int g = g0 + tid; g < g1; g += 4 * VT) {
+      float4 pv[4], qv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = g + u * VT < g1;
+        pv[u] = ok ? ((const float4*)prow)[g + u * VT] : make_float4(0.f, 0.f, 0.f, 0.f);
+        qv[u] = ok && resid ? ((const float4*)qrow)[g + u * VT] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float a[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+        const float b[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float r = resid ? a[e] - b[e] : a[e];
+          s += resid ? (r > 0.0f ? (double)r : 0.0) : (double)r;
+        }
+      }
+    }
+    for (int x = 4 * g1 + tid; x < x1; x += VT) s += weight(prow, qrow, resid, x);
+    return s;
+  }
+  for (int x = x0 + tid; x < x1; x += VT) s += weight(prow, qrow, resid, x);
+  return s;
 }
 
 // Block-wide binary64 sum (every thread gets it).
@@ -220,14 +268,13 @@ __device__ int find_in(const float* prow, const float* qrow, bool resid, int x0,
   return f == 0x7fffffff ? -1 : f;
 }
 
-// grid: (chunks, B). Workspace: partial sums [B][chunks] f64, tickets [B].
+// grid: (chunks, B). Workspace: partial sums [B][chunks] f64 (zero between calls).
 __global__ __launch_bounds__(VT) void prob_accept_kernel(
     const float* target, const float* draftp, const int64_t* draft, const int32_t* lengths,
-    const float* uniforms, int64_t* accepted, int32_t* accept_len, double* partial,
-    unsigned int* tickets, int P, int V, int draft_stride, int chunks) {
+    const float* uniforms, double* partial, int P, int V, int draft_stride, int chunks) {
   const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   __shared__ double red[VT];
-  __shared__ int sj, last, found;
+  __shared__ int sj;
   int L = lengths[b];
   L = L < 0 ? 0 : L > P ? P : L;
   if (tid == 0) sj = first_reject(target, draftp, draft, uniforms, b, L, P, V, draft_stride);
@@ -236,52 +283,57 @@ __global__ __launch_bounds__(VT) void prob_accept_kernel(
   const bool resid = j < L;
   const float* prow = target + ((size_t)b * (P + 1) + j) * V;
   const float* qrow = resid ? draftp + ((size_t)b * P + j) * V : nullptr;
-  const int per = (V + chunks - 1) / chunks;
-  const int x0 = c * per, x1 = min(V, x0 + per);
-  double s = 0.0;
-  for (int x = x0 + tid; x < x1; x += VT) s += weight(prow, qrow, resid, x);
-  s = block_sum(s, red);
-  if (tid == 0) {
-    __hip_atomic_store(partial + (size_t)b * chunks + c, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last = __hip_atomic_fetch_add(tickets + b, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-           (unsigned)chunks - 1u;
-  }
+  const int per = ((V + 4 * chunks - 1) / (4 * chunks)) * 4;   // a multiple of 4
+  const int x0 = min(V, c * per), x1 = min(V, x0 + per);
+  double s = block_sum(strided_sum(prow, qrow, resid, x0, x1), red);
+  if (tid == 0) partial[(size_t)b * chunks + c] = s;
+}
+
+// One workgroup per batch row: S over the chunks in order, the threshold u S,
+// the chunk that holds it, then the element; the chunk sums are re-zeroed.
+__global__ __launch_bounds__(VT) void prob_finish_kernel(
+    const float* target, const float* draftp, const int64_t* draft, const int32_t* lengths,
+    const float* uniforms, int64_t* accepted, int32_t* accept_len, double* partial, int P, int V,
+    int draft_stride, int chunks) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ double red[VT];
+  __shared__ int sj, found;
+  int L = lengths[b];
+  L = L < 0 ? 0 : L > P ? P : L;
+  if (tid == 0) sj = first_reject(target, draftp, draft, uniforms, b, L, P, V, draft_stride);
   __syncthreads();
-  if (!last) return;
-  // the row's finisher: S over the chunks in order, the threshold u S, the
-  // chunk that holds it, then the element
+  const int j = sj;
+  const bool resid = j < L;
+  const float* prow = target + ((size_t)b * (P + 1) + j) * V;
+  const float* qrow = resid ? draftp + ((size_t)b * P + j) * V : nullptr;
+  const int per = ((V + 4 * chunks - 1) / (4 * chunks)) * 4;
   double S = 0.0;
-  for (int i = 0; i < chunks; ++i)
-    S += __hip_atomic_load(partial + (size_t)b * chunks + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < chunks; ++i) S += partial[(size_t)b * chunks + i];
   bool rs = resid;
   const float u = uniforms[(size_t)b * (2 * P + 1) + (resid ? P + j : 2 * P)];
   int x = -1;
   if (!(S > 0.0) && rs) {       // no residual mass: sample p itself
     rs = false;
-    double s2 = 0.0;
-    for (int y = tid; y < V; y += VT) s2 += (double)prow[y];
-    S = block_sum(s2, red);
+    S = block_sum(strided_sum(prow, nullptr, false, 0, V), red);
   }
   if (S > 0.0) {
     const double t = (double)u * S;
     double base = 0.0;
     int cc = 0;
-    for (; cc < chunks; ++cc) {   // the chunk sums of the first pass, or p's
+    for (; cc < chunks; ++cc) {   // the chunk sums of the wide pass, or p's
       double cs;
       if (rs == resid) {
-        cs = __hip_atomic_load(partial + (size_t)b * chunks + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        cs = partial[(size_t)b * chunks + cc];
       } else {
-        const int a0 = cc * per, a1 = min(V, a0 + per);
-        double s3 = 0.0;
-        for (int y = a0 + tid; y < a1; y += VT) s3 += (double)prow[y];
-        cs = block_sum(s3, red);
+        const int a0 = min(V, cc * per), a1 = min(V, a0 + per);
+        cs = block_sum(strided_sum(prow, nullptr, false, a0, a1), red);
       }
       if (base + cs > t) break;
       base += cs;
     }
-    if (cc < chunks) x = find_in(prow, qrow, rs, cc * per, min(V, cc * per + per), base, t, red, &found);
+    if (cc < chunks) x = find_in(prow, qrow, rs, min(V, cc * per), min(V, cc * per + per), base, t, red, &found);
     if (x < 0) {                  // rounding left the threshold at the end: the last weighted id
-      const int a0 = cc < chunks ? cc * per : 0, a1 = cc < chunks ? min(V, a0 + per) : V;
+      const int a0 = cc < chunks ? min(V, cc * per) : 0, a1 = cc < chunks ? min(V, a0 + per) : V;
       if (tid == 0) {
         found = a0;
         for (int y = a1 - 1; y >= a0; --y)
@@ -296,22 +348,27 @@ __global__ __launch_bounds__(VT) void prob_accept_kernel(
   } else {
     x = 0;
   }
+  __syncthreads();
   if (tid == 0) {
     int n = 0;
     for (int i = 0; i < j; ++i) accepted[(size_t)b * (P + 1) + n++] = draft[(size_t)b * draft_stride + i];
     accepted[(size_t)b * (P + 1) + n++] = x;
     for (int i = n; i <= P; ++i) accepted[(size_t)b * (P + 1) + i] = -1;
     accept_len[b] = n;
-    for (int i = 0; i < chunks; ++i)
-      __hip_atomic_store(partial + (size_t)b * chunks + i, 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  for (int i = tid; i < chunks; i += VT) partial[(size_t)b * chunks + i] = 0.0;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-size_t greedy_ws(int32_t B, int32_t P) { return ((size_t)B * (P + 1) * 8 + (size_t)B * 4 + 255) & ~(size_t)255; }
-size_t prob_ws(int32_t B) { return ((size_t)B * VCHUNKS * 8 + (size_t)B * 4 + 255) & ~(size_t)255; }
+size_t greedy_ws(int32_t B, int32_t P) { return ((size_t)B * (P + 1) * 8 + 255) & ~(size_t)255; }
+size_t prob_ws(int32_t B) { return ((size_t)B * PCHUNKS * 8 + 255) & ~(size_t)255; }
+
+// chunks of a probabilistic row: about 4096 tokens each, 1 .. PCHUNKS
+int prob_chunks(int32_t V) {
+  const int c = V / 4096;
+  return c < 1 ? 1 : c > PCHUNKS ? PCHUNKS : c;
+}
 
 }  // namespace
 
@@ -335,12 +392,13 @@ int markov_greedy_accept(const void* target_logits, const int64_t* draft, int32_
   if (!aligned16(target_logits) || !aligned16(workspace)) return MARKOV_ERR_ALIGN;
   if (workspace_bytes < markov_verify_workspace_bytes(batch, proposal_len)) return MARKOV_ERR_WORKSPACE;
   unsigned long long* slots = (unsigned long long*)workspace;
-  unsigned int* tickets = (unsigned int*)(slots + (size_t)batch * (proposal_len + 1));
   const int chunks = vocab / 8 >= VCHUNKS * VT ? VCHUNKS : 1;
   dim3 grid((unsigned)chunks, (unsigned)(proposal_len + 1), (unsigned)batch);
   greedy_accept_kernel<<<grid, VT, 0, (hipStream_t)stream>>>(
-      (const uint16_t*)target_logits, draft, proposal_lengths, accepted, accept_len, slots, tickets,
-      proposal_len, vocab, draft_stride, chunks);
+      (const uint16_t*)target_logits, proposal_lengths, slots, proposal_len, vocab, chunks);
+  if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
+  greedy_finish_kernel<<<dim3((unsigned)((batch + 63) / 64)), 64, 0, (hipStream_t)stream>>>(
+      draft, proposal_lengths, accepted, accept_len, slots, batch, proposal_len, draft_stride);
   if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   return MARKOV_OK;
 }
@@ -358,12 +416,14 @@ int markov_prob_accept(const float* target_probs, const float* draft_probs, cons
   if (!aligned16(workspace)) return MARKOV_ERR_ALIGN;
   if (workspace_bytes < markov_verify_workspace_bytes(batch, proposal_len)) return MARKOV_ERR_WORKSPACE;
   double* partial = (double*)workspace;
-  unsigned int* tickets = (unsigned int*)(partial + (size_t)batch * VCHUNKS);
-  const int chunks = VCHUNKS;
-  dim3 grid((unsigned)chunks, (unsigned)batch);
-  prob_accept_kernel<<<grid, VT, 0, (hipStream_t)stream>>>(
+  const int chunks = prob_chunks(vocab);
+  prob_accept_kernel<<<dim3((unsigned)chunks, (unsigned)batch), VT, 0, (hipStream_t)stream>>>(
+      target_probs, draft_probs, draft, proposal_lengths, uniforms, partial, proposal_len, vocab,
+      draft_stride, chunks);
+  if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
+  prob_finish_kernel<<<dim3((unsigned)batch), VT, 0, (hipStream_t)stream>>>(
       target_probs, draft_probs, draft, proposal_lengths, uniforms, accepted, accept_len, partial,
-      tickets, proposal_len, vocab, draft_stride, chunks);
+      proposal_len, vocab, draft_stride, chunks);
   if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   return MARKOV_OK;
 }
