@@ -566,26 +566,46 @@ struct RowState {
   float l;
 };
 
-__device__ __forceinline__ void merge_order(RowState& a, const RowState& b) {
-  if (before(b.v1, b.id, a.v1, a.id)) {
-    a.v1 = b.v1;
-    a.id = b.id;
-    a.l = b.l;
-  }
+// One merge of b into a under the row's rule (TOP2 if top2, else ORDER), as
+// selects: a merge runs for every lane of a wave whatever its row's rule, and
+// a branch per field costs more than both rules' compares. Under TOP2 the
+// loser's v2 never exceeds its v1, so v2 becomes the largest bound but the
+// winner's. Both rules are associative and commutative (a strict total order
+// on (v1, id); a NaN bound marks the state sp and its row is re-scanned), so
+// states may be merged in any grouping.
+__device__ __forceinline__ void merge_state(RowState& a, const RowState& b, bool top2) {
+  // bitwise operators: no short-circuit branches. ORDER is before(b, a):
+  // TOP2's test, or b NaN and (a not NaN or b the lower id)
+  const bool lt_id = b.id < a.id;
+  const bool bw_top = (b.v1 > a.v1) | ((b.v1 == a.v1) & lt_id);
+  const bool bw_ord = bw_top | (__builtin_isnan(b.v1) & (!__builtin_isnan(a.v1) | lt_id));
+  const bool bw = top2 ? bw_top : bw_ord;
+  const float v2 = fmaxf(bw ? a.v1 : b.v1, bw ? b.v2 : a.v2);
+  a.v2 = top2 ? v2 : a.v2;
+  a.v1 = bw ? b.v1 : a.v1;
+  a.id = bw ? b.id : a.id;
+  a.l = bw ? b.l : a.l;
   a.sp |= b.sp;
 }
 
-__device__ __forceinline__ void merge_top2(RowState& a, const RowState& b) {
-  const bool bw = (b.v1 > a.v1) || (b.v1 == a.v1 && b.id < a.id);
-  const float lose = bw ? a.v1 : b.v1;
-  const float win2 = bw ? b.v2 : a.v2;
-  a.v2 = fmaxf(lose, win2);
-  if (bw) {
-    a.v1 = b.v1;
-    a.id = b.id;
-    a.l = b.l;
-  }
-  a.sp |= b.sp;
+// The value D (32 or 16) lanes up, for lanes 0..31 (D = 32) or 0..15 and
+// 32..47 (D = 16): v_permlane32_swap exchanges the upper half of its first
+// operand with the lower half of its second, v_permlane16_swap the odd rows
+// of 16 lanes of the first with the even rows of the second; with x as both
+// operands, the second result holds x from D lanes up in those lanes. VALU
+// only: no LDS round trip.
+template <int D>
+__device__ __forceinline__ uint32_t lanes_up(uint32_t x) {
+  static_assert(D == 16 || D == 32, "swap distance");
+  if constexpr (D == 32) return __builtin_amdgcn_permlane32_swap(x, x, false, false)[1];
+  else return __builtin_amdgcn_permlane16_swap(x, x, false, false)[1];
+}
+
+template <int D>
+__device__ __forceinline__ RowState state_up(const RowState& s) {
+  return RowState{__uint_as_float(lanes_up<D>(__float_as_uint(s.v1))), __uint_as_float(lanes_up<D>(__float_as_uint(s.v2))),
+                  (int)lanes_up<D>((uint32_t)s.id), (int)lanes_up<D>((uint32_t)s.sp),
+                  __uint_as_float(lanes_up<D>(__float_as_uint(s.l)))};
 }
 
 // LDS, all of it dynamic (the kernel declares no static LDS, so the dynamic
@@ -1162,17 +1182,11 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     st.l = 0.0f;
     if (CARRY) st.l = (__float_as_uint(v1[j]) & 1u) ? bf_hi(lw[CARRY ? j : 0]) : bf_lo(lw[CARRY ? j : 0]);
     const bool top2 = noisy && !EXACT;
-#pragma unroll
-    for (int sh = 16; sh <= 32; sh <<= 1) {
-      RowState o;
-      o.v1 = __shfl_xor(st.v1, sh);
-      o.v2 = __shfl_xor(st.v2, sh);
-      o.id = __shfl_xor(st.id, sh);
-      o.sp = __shfl_xor(st.sp, sh);
-      o.l = __shfl_xor(st.l, sh);
-      if (top2) merge_top2(st, o);
-      else merge_order(st, o);
-    }
+    // lanes m, m + 16, m + 32, m + 48 hold the row: lanes 0..31 merge the
+    // state 32 lanes up, then lanes 0..15 the state 16 lanes up (only they
+    // store the result)
+    merge_state(st, state_up<32>(st), top2);
+    merge_state(st, state_up<16>(st), top2);
     fin[j] = st;
   }
   // every wave past its last contraction (the states go over the
@@ -1204,7 +1218,9 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   }
   if (tid == 0) misc[16] = 0;
   lds_barrier();
-  for (int n = tid; n < rows; n += NTH) {
+  static_assert(ROWS_CAP <= NTH, "one thread per row");
+  if (tid < rows) {
+    const int n = tid;
     const RowInfo info = n_info[n];
     const bool noisy = !(info.T == 0.0f);
     const bool top2 = noisy && !EXACT;
@@ -1217,12 +1233,11 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       const int i = (w0 + q) * rp + n;
       o[q] = RowState{st_v1[i], st_v2[i], st_id[i], st_sp[i], st_l[i]};
     }
-    RowState st = o[0];
 #pragma unroll
-    for (int q = 1; q < NS; ++q) {
-      if (top2) merge_top2(st, o[q]);
-      else merge_order(st, o[q]);
-    }
+    for (int w = 1; w < NS; w <<= 1)   // a tree: independent merges side by side
+#pragma unroll
+      for (int q = 0; q + w < NS; q += 2 * w) merge_state(o[q], o[q + w], top2);
+    RowState st = o[0];
     const int rr = n_row[n];
     float key = st.v1;
     bool fb = !EXACT && (st.sp != 0 || (mode == MODE_SAMPLE_FALLBACK && noisy));
