@@ -77,6 +77,7 @@ struct StepArgs {
   int id_offset, V_total;
   int rows, V, R, k, step, nslabs, mode;
   int tt_layout;              // LDS holds the transform table at address 0
+  int sep_states;             // the waves' row states have LDS of their own (after misc)
   float mult, inv_cap, cap;
   int has_cap;
   float inf;                  // +infinity, opaque to the compiler (see the noise loop)
@@ -566,6 +567,13 @@ struct RowState {
   float l;
 };
 
+// v_pk_max_u16: the larger of each 16-bit half
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // One merge of b into a under the row's rule (TOP2 if top2, else ORDER), as
 // selects: a merge runs for every lane of a wave whatever its row's rule, and
 // a branch per field costs more than both rules' compares. Under TOP2 the
@@ -617,10 +625,15 @@ __device__ __forceinline__ RowState state_up(const RowState& s) {
 //                   row states [5][NWV][rp] (v1, v2, id, sp, l)
 //   info [rp] RowInfo, n_row [rp], n_src [rp], fb_row [rp], fb_thr [rp],
 //   misc [64] (per-wave row counts, fallback count, last-workgroup flag)
+//   [states]        when the launch has room: the waves' row states, so that
+//                   writing them need not wait for every wave's last read of
+//                   the embeddings
 __host__ __device__ __forceinline__ size_t region0_bytes(int rp, int R) {
   const size_t e = (size_t)rp * R * 2, st = (size_t)NWV * rp * 20;
   return e > st ? e : st;
 }
+
+__host__ __device__ __forceinline__ size_t states_bytes(int rp) { return (size_t)NWV * rp * 20; }
 
 __host__ __device__ __forceinline__ size_t lds_dynamic(int rp, int R) {
   return region0_bytes(rp, R) + (size_t)rp * 16 + (size_t)rp * 16 + 64 * 4;
@@ -755,6 +768,18 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
                                          16, 0, 0);
     }
   }
+  // the transform table likewise (the host asks for this layout only with a
+  // soft cap; whether the stamp matches is checked where it is used): its
+  // lines come from L2 once one workgroup of an XCD has read them, so it
+  // lands well before the first tiles it is waited for with (issued after
+  // the gather instead, the Large step took 0.4 us longer)
+  if (tt_lay) {
+    const unsigned char* src = (const unsigned char*)a.ttable + TT_HEAD;
+    for (int j = wave; j * 64 * 16 < (int)TT_BYTES; j += NWV)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)(j * 64 + lane) * 16),
+                                       (__attribute__((address_space(3))) void*)(lds + (size_t)j * 1024),
+                                       16, 0, 0);
+  }
   // everything the row set-up needs from the row data, before the tile loads
   // below
   const bool noisy_r = valid && !bias_mode && !(T == 0.0f);
@@ -859,6 +884,11 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   float v1[MRB], v2[MRB];
   int idt[MRB];
   bool sp[MRB];
+  // noisy rows of plans with registers to spare: the packed (high and low
+  // half) largest |cached logit| bits, checked once at the end; the others
+  // test every estimate
+  constexpr bool PKMAX = MRB <= 4;
+  uint32_t mxw[PKMAX ? MRB : 1];
   uint32_t lw[CARRY ? MRB : 1];   // noisy rows: the word of cached logits holding the top element's
 
   unsigned long long* slots_step = bias_mode ? nullptr : a.slots + (size_t)sset * SG * rows;
@@ -889,17 +919,6 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       }
     }
   }
-  // the transform table likewise (the host asks for this layout only with a
-  // soft cap; whether the stamp matches is checked where it is used): after
-  // the first tiles and the gather, so that it does not hold them up, and
-  // waited for with them (its lines come from L2)
-  if (tt_lay) {
-    const unsigned char* src = (const unsigned char*)a.ttable + TT_HEAD;
-    for (int j = wave; j * 64 * 16 < (int)TT_BYTES; j += NWV)
-      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)(j * 64 + lane) * 16),
-                                       (__attribute__((address_space(3))) void*)(lds + (size_t)j * 1024),
-                                       16, 0, 0);
-  }
   // the second tile in flight (two-tile waves), and the first of a wave that
   // did not request it above, issued after the gather so that waiting for
   // the gather does not wait for them (the compiler, which cannot tell that
@@ -920,6 +939,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     v2[j] = -INFINITY;
     idt[j] = NONE;
     sp[j] = false;
+    if (PKMAX) mxw[PKMAX ? j : 0] = 0u;
     if (CARRY) lw[CARRY ? j : 0] = 0u;
   }
   // everything but the tiles requested after the gather: the embeddings
@@ -1095,6 +1115,11 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
           float x1 = v1[j], x2 = v2[j];
           const float x1b = x1;
           bool spx = false;
+          // the largest magnitudes (bf16 bits, sign cleared), two per word
+          if (PKMAX)
+            mxw[PKMAX ? j : 0] = pk_max_u16(mxw[PKMAX ? j : 0],
+                                            pk_max_u16(pk_max_u16(cw[0] & 0x7fff7fffu, cw[1] & 0x7fff7fffu),
+                                                       pk_max_u16(cw[2] & 0x7fff7fffu, cw[3] & 0x7fff7fffu)));
           // all 8 table reads in flight before the first is used
           float fh[8];
           const uint32_t pr = rotl32(info.prefix, 13);
@@ -1113,7 +1138,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
             // roundings and the packed index is added once per row (see
             // slack_up), as it grows with the estimate
             const float hi = __builtin_fmaf(l[e], info.rcp, gh);
-            spx = spx || __builtin_amdgcn_class(hi, 0x207);       // NaN or infinite
+            if (!PKMAX) spx = spx || __builtin_amdgcn_class(hi, 0x207);   // NaN or infinite
             const float pk = __uint_as_float((__float_as_uint(hi) & ~7u) | (uint32_t)e);
             x2 = __builtin_amdgcn_fmed3f(x1, x2, pk);
             x1 = __builtin_amdgcn_fmed3f(x1, pk, pinf);   // max, no canonicalising
@@ -1127,7 +1152,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
           }
           v1[j] = x1;
           v2[j] = x2;
-          sp[j] = sp[j] || spx;
+          if (!PKMAX) sp[j] = sp[j] || spx;
         }
       }
       // temperature-0 rows: the exact largest logit, the earliest on ties
@@ -1171,11 +1196,22 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     fin[j] = RowState{-INFINITY, -INFINITY, NONE, 0, 0.0f};
     if (j >= my_nrb) continue;   // uniform: the shuffles below run for the whole wave
     const int n = 16 * (wr + RG * j) + m;
-    const bool noisy = !((ROWREG ? ri[ROWREG ? j : 0].T : n_info[n].T) == 0.0f);
+    const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[n];
+    const bool noisy = !(info.T == 0.0f);
     RowState st;
     st.v1 = v1[j];
     st.v2 = v2[j];
-    st.sp = sp[j] ? 1 : 0;
+    // a noisy row's estimates fma(l, RN(1/T), bound) are all finite when
+    // RN(|l| |RN(1/T)|) <= 2^127 for its largest |l| (the bound is finite
+    // and under 2^5); else (a NaN or infinite logit, a NaN or infinite
+    // 1/T, or a product past 2^127, where NaN compares false) re-scan it
+    bool spn = false;
+    if (PKMAX) {
+      const uint32_t mh = mxw[PKMAX ? j : 0] >> 16, ml = mxw[PKMAX ? j : 0] & 0xffffu;
+      const float lmax = __uint_as_float((mh > ml ? mh : ml) << 16);
+      spn = noisy && !EXACT && !(lmax * fabsf(info.rcp) <= 0x1p127f);
+    }
+    st.sp = (sp[j] || spn) ? 1 : 0;
     if (EXACT) st.id = idt[j];
     else if (idt[j] == NONE) st.id = NONE;
     else st.id = idt[j] + (int)((noisy ? __float_as_uint(v1[j]) : __float_as_uint(v2[j])) & 7u);
@@ -1189,17 +1225,24 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     merge_state(st, state_up<16>(st), top2);
     fin[j] = st;
   }
-  // every wave past its last contraction (the states go over the
-  // embeddings); with carried logits the cache stores drain meanwhile (the
-  // barrier before the fallback scans, which read them back, waits for
-  // them), else they are read back below and waited for here
-  if (CARRY || GREEDY) {
-    lds_barrier();
-  } else {
+  // the states go over the embeddings unless they have LDS of their own:
+  // then every wave must be past its last contraction first. With carried
+  // logits the cache stores drain meanwhile (the barrier before the
+  // fallback scans, which read them back, waits for them), else they are
+  // read back below and waited for here.
+  const bool sep = a.sep_states != 0;   // uniform
+  const bool reads_cache = !(CARRY || GREEDY);
+  if (!sep) {
+    if (reads_cache) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    } else {
+      lds_barrier();
+    }
+  } else if (reads_cache) {
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
-  float* st_v1 = (float*)emb;
+  float* st_v1 = sep ? (float*)(misc + 64) : (float*)emb;
   float* st_v2 = st_v1 + NWV * rp;
   int* st_id = (int*)(st_v2 + NWV * rp);
   int* st_sp = st_id + NWV * rp;
@@ -1217,7 +1260,8 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     }
   }
   if (tid == 0) misc[16] = 0;
-  lds_barrier();
+  if (sep && reads_cache) __syncthreads();
+  else lds_barrier();
   static_assert(ROWS_CAP <= NTH, "one thread per row");
   if (tid < rows) {
     const int n = tid;
