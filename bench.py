@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="large",
                     choices=["tiny", "single", "small", "large", "stress"])
+    ap.add_argument("--rows", type=int, default=0,
+                    help="override the config's row count (same distributions; for the small-row "
+                         "contraction sweep)")
     ap.add_argument("--path", default="sample",
                     choices=["sample", "greedy", "greedy-chain", "fp8", "fp8-greedy", "shard",
                              "verify-greedy", "verify-prob"],
@@ -252,7 +255,7 @@ def main():
     if args.path.startswith("verify"):
         return bench_verify(args, torch, m, workloads, dev, stream)
 
-    w = workloads.make(args.config)
+    w = workloads.make(args.config, rows=args.rows or None)
     d = workloads.to_device(w, dev)
     bytes_step = w.bytes_per_step()
     if args.path == "sample":

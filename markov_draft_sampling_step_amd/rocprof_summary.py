@@ -3,10 +3,12 @@
   python -m markov_draft_sampling_step_amd.rocprof_summary stats DIR
       per-kernel calls / average / min / max duration from *_kernel_stats.csv
 
-  python -m markov_draft_sampling_step_amd.rocprof_summary counters DIR --elements N
+  python -m markov_draft_sampling_step_amd.rocprof_summary counters DIR --elements N [--rank R]
       per-dispatch counter means of one --pmc run and clock-free ratios
       (VALU lane-instructions per element, VALU share of wave time, LDS
-      bank-conflict stalls per LDS quad-cycle)
+      bank-conflict stalls per LDS quad-cycle; with the MFMA counters, the
+      MFMA-busy share of SIMD time and the useful share of the bf16 MFMA
+      flops, 2 x elements x R)
 
   python -m markov_draft_sampling_step_amd.rocprof_summary traffic \\
       --fetch DIR --write DIR --copy-bytes N [--kernel markov_step_kernel]
@@ -86,7 +88,8 @@ def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, kernel: str) -> str
     ])
 
 
-def counters(d: str, kernel: str, elements: int) -> str:
+def counters(d: str, kernel: str, elements: int, useful_flops: float = 0.0, cus: int = 256,
+             xcds: int = 8) -> str:
     """Per-dispatch means of every counter of one --pmc run for the kernel,
     and three ratios that need no clock: VALU lane-instructions per (row,
     token) element (SQ_INSTS_VALU counts wave64 instructions), the share of
@@ -114,6 +117,15 @@ def counters(d: str, kernel: str, elements: int) -> str:
     if "SQ_ACTIVE_INST_VALU" in mean and "SQ_WAVE_CYCLES" in mean:
         out.append(f"VALU-issuing share of wave time = "
                    f"{mean['SQ_ACTIVE_INST_VALU'] / mean['SQ_WAVE_CYCLES']:.3f}")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean:
+        active = mean["GRBM_GUI_ACTIVE"] / xcds           # the counter sums the XCDs
+        out.append(f"MFMA-busy share of SIMD time = "
+                   f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (active * cus * 4):.4f} "
+                   f"(SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / {xcds} XCDs x {cus} CUs x 4 SIMDs)")
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean and useful_flops > 0:
+        done = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        out.append(f"bf16 MFMA flops per dispatch = {done:.4g} (MOPS x 512); the contraction needs "
+                   f"{useful_flops:.4g} (2 rows V R): {useful_flops / done:.4f} of them are useful")
     if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_ACTIVE_INST_LDS" in mean:
         out.append(f"LDS bank-conflict cycles per LDS-active quad-cycle = "
                    f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_ACTIVE_INST_LDS']:.3f}")
@@ -128,6 +140,9 @@ def main():
     c.add_argument("dir")
     c.add_argument("--kernel", default="markov_step_kernel")
     c.add_argument("--elements", type=int, default=0, help="(row, token) elements per dispatch")
+    c.add_argument("--rank", type=int, default=0, help="R, for the useful MFMA flops 2 x elements x R")
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--xcds", type=int, default=8)
     a = sub.add_parser("stats")
     a.add_argument("dir")
     b = sub.add_parser("traffic")
@@ -139,7 +154,8 @@ def main():
     if args.cmd == "stats":
         print(stats(args.dir))
     elif args.cmd == "counters":
-        print(counters(args.dir, args.kernel, args.elements))
+        print(counters(args.dir, args.kernel, args.elements, 2.0 * args.elements * args.rank, args.cus,
+                       args.xcds))
     else:
         print(traffic(args.fetch, args.write, args.copy_bytes, args.kernel))
 
