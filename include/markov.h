@@ -66,8 +66,12 @@ enum {
   MARKOV_ERR_ROWS = -5,        /* rows above what the rank's LDS budget holds */
   MARKOV_ERR_WORKSPACE = -6,   /* workspace smaller than markov_workspace_bytes */
   MARKOV_ERR_HIP = -7,         /* a HIP runtime call failed */
-  MARKOV_ERR_VOCAB = -8        /* vocab above 2^31 - 1 */
+  MARKOV_ERR_VOCAB = -8        /* vocab (or a shard's vocab_total) above MARKOV_MAX_VOCAB */
 };
+
+/* The largest vocabulary the library takes: token ids and in-slab offsets
+   are 32-bit integers, with room for one vocabulary slab past the end. */
+#define MARKOV_MAX_VOCAB 0x7fff0000
 
 /* The most rows one call takes at a given rank (at most 512; the embedding
  * rows are staged in LDS next to per-row data, within 160 KiB). */
@@ -229,7 +233,7 @@ int markov_greedy_finalize(const uint64_t* winners, int64_t n, int64_t* tokens,
  *   w2q        device uint8 [vocab, rank] (write), 16-byte aligned for the steps below
  *   w2_scales  device uint16 [vocab] FP16 bit patterns (write), 16-byte aligned likewise
  * One kernel on `stream` (a wave per row). Errors: NULL pointers, vocab < 1,
- * rank not a power of two in [16, 512].
+ * vocab above MARKOV_MAX_VOCAB, rank not a power of two in [16, 512].
  */
 int markov_quantize_w2_fp8(const void* w2, uint8_t* w2q, uint16_t* w2_scales, int32_t vocab,
                            int32_t rank, markov_stream_t stream);
@@ -296,7 +300,8 @@ int markov_greedy_step_fp8(const void* base_logits, const void* w1, const uint8_
  * One kernel launch; the workgroup that finishes last writes the packets and
  * re-zeroes the workspace's slots. Errors: as markov_sample_sequential, and
  * MARKOV_ERR_SHAPE for step outside [0, k), feed_stride < 1, or a slab
- * outside [0, vocab_total).
+ * outside [0, vocab_total), MARKOV_ERR_VOCAB for vocab_total above
+ * MARKOV_MAX_VOCAB.
  */
 int markov_shard_step(const void* base_logits, const void* w1, const void* w2, const int64_t* feed,
                       int64_t feed_stride, const int64_t* seeds, const int64_t* positions,
@@ -329,7 +334,8 @@ int markov_pick(const uint64_t* packets, int32_t shards, int32_t rows, int64_t* 
  * caller (hipMemset) and left zeroed by every call; not shared by two calls
  * in flight. One kernel launch each, no host synchronisation. Errors:
  * MARKOV_ERR_SHAPE (B < 1, P < 0, draft_stride < P, V out of range),
- * MARKOV_ERR_NULL, MARKOV_ERR_ALIGN, MARKOV_ERR_WORKSPACE, MARKOV_ERR_HIP.
+ * MARKOV_ERR_VOCAB (V above MARKOV_MAX_VOCAB), MARKOV_ERR_NULL,
+ * MARKOV_ERR_ALIGN, MARKOV_ERR_WORKSPACE, MARKOV_ERR_HIP.
  */
 size_t markov_verify_workspace_bytes(int32_t batch, int32_t proposal_len);
 

@@ -222,6 +222,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int check_shape(const markov_shape_t* sh, int32_t k) {
   if (!sh) return MARKOV_ERR_NULL;
   if (sh->rows < 1 || sh->vocab < 1 || (sh->vocab & 7) || k < 1) return MARKOV_ERR_SHAPE;
+  if (sh->vocab > MARKOV_MAX_VOCAB) return MARKOV_ERR_VOCAB;
   if (!pow2_rank(sh->rank)) return MARKOV_ERR_RANK;
   if (sh->rows > max_rows_of(sh->rank)) return MARKOV_ERR_ROWS;
   return MARKOV_OK;
@@ -600,6 +601,7 @@ const char* markov_why_not(const markov_shape_t* shape, int32_t k) {
   if (shape->rows < 1) return "no requests";
   if (k < 1) return "no draft steps";
   if (shape->vocab < 1 || (shape->vocab & 7)) return "vocabulary not a positive multiple of 8";
+  if (shape->vocab > MARKOV_MAX_VOCAB) return "vocabulary above MARKOV_MAX_VOCAB";
   if (!pow2_rank(shape->rank)) return "Markov rank not a power of two in [16, 512]";
   if (shape->rows > max_rows_of(shape->rank)) return "more requests than the rank's LDS budget holds";
   return nullptr;
@@ -658,6 +660,7 @@ int markov_greedy_step(const void* base_logits, const void* w1, const void* w2,
 int markov_quantize_w2_fp8(const void* w2, uint8_t* w2q, uint16_t* w2_scales, int32_t vocab,
                            int32_t rank, markov_stream_t stream) {
   if (vocab < 1 || !pow2_rank(rank)) return vocab < 1 ? MARKOV_ERR_SHAPE : MARKOV_ERR_RANK;
+  if (vocab > MARKOV_MAX_VOCAB) return MARKOV_ERR_VOCAB;
   if (!w2 || !w2q || !w2_scales) return MARKOV_ERR_NULL;
   const unsigned blocks = (unsigned)((vocab + 3) / 4);
   quantize_w2_fp8_kernel<<<dim3(blocks), 256, 0, (hipStream_t)stream>>>(
@@ -722,6 +725,7 @@ int markov_shard_step(const void* base_logits, const void* w1, const void* w2, c
   if (step < 0 || step >= k || feed_stride < 1 || vocab_offset < 0 || vocab_total < 1 ||
       (int64_t)vocab_offset + shape->vocab > (int64_t)vocab_total)
     return MARKOV_ERR_SHAPE;
+  if (vocab_total > MARKOV_MAX_VOCAB) return MARKOV_ERR_VOCAB;
   if (!base_logits || !w1 || !w2 || !feed || !seeds || !positions || !temperature || !cache ||
       !packets || !workspace)
     return MARKOV_ERR_NULL;

@@ -365,10 +365,13 @@ __device__ __forceinline__ uint32_t load_cache_word(const uint16_t* cache, size_
 }
 
 // ---------------------------------------------------------------- output transform
-// tanh for the soft cap: an odd minimax polynomial z + z^3 P(z^2) below
-// |z| = 0.625 (fitted here for binary32 Horner evaluation, within 0.7 ulp),
-// else 1 - 2 / (e^{2|z|} + 1) with the hardware exp2 and reciprocal (about
-// 2 ulp). The cache rounds the result to bf16.
+// tanh for the soft cap: below |z| = 0.625 an odd polynomial z + z^3 P(z^2),
+// P of degree 5 in z^2 (the Taylor series' odd terms through z^13, each
+// coefficient adjusted by a fit to tanh on that interval and rounded to
+// binary32); this binary32 Horner evaluation is within 0.73 ulp of tanh over
+// every binary32 z in [2^-8, 0.625] (a CPU sweep, its worst case confirmed in
+// 50-digit arithmetic). Above, 1 - 2 / (e^{2|z|} + 1) with the hardware exp2
+// and reciprocal (about 2 ulp). The cache rounds the result to bf16.
 __device__ __forceinline__ float tanh_poly(float z) {
   const float t = z * z;
   float p = 0x1.18dc88p-9f;

@@ -384,6 +384,7 @@ int markov_greedy_accept(const void* target_logits, const int64_t* draft, int32_
                          const int32_t* proposal_lengths, int64_t* accepted, int32_t* accept_len,
                          int32_t batch, int32_t proposal_len, int32_t vocab, void* workspace,
                          size_t workspace_bytes, markov_stream_t stream) {
+  if (vocab > MARKOV_MAX_VOCAB) return MARKOV_ERR_VOCAB;
   if (batch < 1 || proposal_len < 0 || vocab < 8 || (vocab & 7) || draft_stride < proposal_len)
     return MARKOV_ERR_SHAPE;
   if (!target_logits || (proposal_len > 0 && !draft) || !proposal_lengths || !accepted ||
@@ -408,6 +409,7 @@ int markov_prob_accept(const float* target_probs, const float* draft_probs, cons
                        int64_t* accepted, int32_t* accept_len, int32_t batch, int32_t proposal_len,
                        int32_t vocab, void* workspace, size_t workspace_bytes,
                        markov_stream_t stream) {
+  if (vocab > MARKOV_MAX_VOCAB) return MARKOV_ERR_VOCAB;
   if (batch < 1 || proposal_len < 0 || vocab < 1 || draft_stride < proposal_len)
     return MARKOV_ERR_SHAPE;
   if (!target_probs || !proposal_lengths || !uniforms || !accepted || !accept_len || !workspace ||

@@ -74,6 +74,8 @@ def test_max_rows_and_workspace(lib):
     (0, 4096, 32, 3, "no requests"),
     (2, 4096, 32, 0, "no draft steps"),
     (2, 4100, 32, 3, "vocabulary"),
+    (2, 0x7fff0008, 32, 3, "MARKOV_MAX_VOCAB"),
+    (2, 0x7fff0000, 32, 3, None),
     (2, 4096, 48, 3, "rank"),
     (2, 4096, 1024, 3, "rank"),
     (273, 4096, 256, 3, "LDS"),
@@ -102,6 +104,9 @@ def test_host_errors_before_any_device_work(lib):
     sh = m.make_shape(2, 4096, 32)
     assert _call(lib, m.make_shape(0, 4096, 32), good) == -2
     assert _call(lib, m.make_shape(2, 4100, 32), good) == -2
+    assert _call(lib, m.make_shape(2, 0x7fff0008, 32), good) == -8   # past MARKOV_MAX_VOCAB
+    assert lib.markov_quantize_w2_fp8(ctypes.c_void_p(good[0]), ctypes.c_void_p(good[1]),
+                                      ctypes.c_void_p(good[2]), 0x7fff0008, 256, None) == -8
     assert _call(lib, sh, good, k=0) == -2
     assert _call(lib, m.make_shape(2, 4096, 40), good) == -3
     assert _call(lib, m.make_shape(300, 4096, 256), good) == -5
