@@ -166,16 +166,25 @@ __global__ __launch_bounds__(64) void greedy_finish_kernel(const int64_t* draft,
 // The first rejected proposal of row b (L if none), as the oracle: accept
 // iff u_j q_j(d) < p_j(d) in binary64 (both products exact); an id outside
 // [0, V) has p = q = 0.
+// Called by a whole wave: lane j tests proposal j (64 at a time), so the
+// loads of every proposal are in flight together.
 __device__ int first_reject(const float* target, const float* draftp, const int64_t* draft,
                             const float* uniforms, int b, int L, int P, int V, int draft_stride) {
-  for (int j = 0; j < L; ++j) {
-    const int64_t d = draft[(size_t)b * draft_stride + j];
-    double p = 0.0, q = 0.0;
-    if (d >= 0 && d < V) {
-      p = (double)target[((size_t)b * (P + 1) + j) * V + d];
-      q = (double)draftp[((size_t)b * P + j) * V + d];
+  const int lane = threadIdx.x & 63;
+  for (int j0 = 0; j0 < L; j0 += 64) {
+    const int j = j0 + lane;
+    bool rej = false;
+    if (j < L) {
+      const int64_t d = draft[(size_t)b * draft_stride + j];
+      double p = 0.0, q = 0.0;
+      if (d >= 0 && d < V) {
+        p = (double)target[((size_t)b * (P + 1) + j) * V + d];
+        q = (double)draftp[((size_t)b * P + j) * V + d];
+      }
+      rej = !((double)uniforms[(size_t)b * (2 * P + 1) + j] * q < p);
     }
-    if (!((double)uniforms[(size_t)b * (2 * P + 1) + j] * q < p)) return j;
+    const unsigned long long m = __ballot(rej);
+    if (m) return j0 + __builtin_ctzll(m);
   }
   return L;
 }
@@ -236,36 +245,94 @@ __device__ double block_sum(double v, double* red) {
   return t;
 }
 
-// The smallest x in [x0, x1) whose running sum from `base` exceeds t: each
-// thread sums a contiguous run, an exclusive scan of the runs finds the
-// thread whose run holds the crossing, and it walks its run (the lowest
-// crossing any thread finds wins). -1 if none.
-__device__ int find_in(const float* prow, const float* qrow, bool resid, int x0, int x1, double base,
-                       double t, double* red, int* found) {
-  const int tid = threadIdx.x;
-  const int per = (x1 - x0 + VT - 1) / VT;
-  const int a = x0 + tid * per, e = min(x1, a + per);
+// The binary64 sum, in index order, of the weights of [a, e): 16-byte loads
+// four deep when the rows are 16-byte aligned and a is a multiple of 4.
+__device__ double run_sum(const float* prow, const float* qrow, bool resid, int a, int e) {
   double s = 0.0;
-  for (int x = a; x < e; ++x) s += weight(prow, qrow, resid, x);
-  __syncthreads();
-  red[tid] = s;
-  if (tid == 0) *found = 0x7fffffff;
-  __syncthreads();
-  double pre = base;
-  for (int i = 0; i < tid; ++i) pre += red[i];   // VT terms: small next to the row
-  if (pre + s > t && pre <= t) {
-    double cum = pre;
-    for (int x = a; x < e; ++x) {
-      cum += weight(prow, qrow, resid, x);
-      if (cum > t) {
-        atomicMin(found, x);
-        break;
+  const bool vec = ((((uintptr_t)prow) | (uintptr_t)(resid ? qrow : prow)) & 15u) == 0 && (a & 3) == 0;
+  int x = a;
+  if (vec) {
+    for (; x + 16 <= e; x += 16) {
+      float4 pv[4], qv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        pv[u] = ((const float4*)(prow + x))[u];
+        qv[u] = resid ? ((const float4*)(qrow + x))[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float pa[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+        const float qa[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float r = resid ? pa[k] - qa[k] : pa[k];
+          s += resid ? (r > 0.0f ? (double)r : 0.0) : (double)r;
+        }
       }
     }
   }
+  for (; x < e; ++x) s += weight(prow, qrow, resid, x);
+  return s;
+}
+
+// The smallest x in [x0, x1) whose running sum from `base` exceeds t. Each
+// thread sums a contiguous run (in index order); a block-wide exclusive scan
+// of the run sums gives every run's starting sum B_i, so that the runs
+// partition [base, B_VT) consistently (B is non-decreasing, the weights
+// being non-negative); the thread whose [B_i, B_i+1) holds t walks its run
+// from B_i, and where rounding leaves the walk short of t it takes the run's
+// last weighted id. -1 if no run holds t.
+__device__ int find_in(const float* prow, const float* qrow, bool resid, int x0, int x1, double base,
+                       double t, double* red, int* found) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ double bnd[VT + 1];
+  const int rp = (((x1 - x0 + VT - 1) / VT) + 3) & ~3;   // a multiple of 4
+  const int a = min(x1, x0 + tid * rp), e = min(x1, a + rp);
+  const double s = run_sum(prow, qrow, resid, a, e);
+  // exclusive scan: within the wave by shuffles, then the waves' totals
+  double v = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  double ex = __shfl_up(v, 1);
+  if (lane == 0) ex = 0.0;
+  __syncthreads();
+  if (lane == 63) red[wave] = v;
+  if (tid == 0) *found = 0x7fffffff;
+  __syncthreads();
+  double before = base;
+  for (int w = 0; w < wave; ++w) before += red[w];
+  bnd[tid] = before + ex;
+  if (tid == VT - 1) {
+    double tot = base;
+    for (int w = 0; w < VT / 64; ++w) tot += red[w];
+    bnd[VT] = tot;
+  }
+  __syncthreads();
+  const double b0 = bnd[tid], b1 = bnd[tid + 1];
+  if (b0 <= t && t < b1) {
+    // the walk loads 16 weights at a time, all in flight together
+    double cum = b0;
+    int hit = -1, last = -1;
+    for (int x = a; x < e && hit < 0; x += 16) {
+      double w[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) w[k] = x + k < e ? weight(prow, qrow, resid, x + k) : 0.0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (hit >= 0) break;
+        if (w[k] > 0.0) last = x + k;
+        cum += w[k];
+        if (cum > t) hit = x + k;
+      }
+    }
+    atomicMin(found, hit >= 0 ? hit : last);
+  }
   __syncthreads();
   const int f = *found;
-  return f == 0x7fffffff ? -1 : f;
+  return f == 0x7fffffff || f < 0 ? -1 : f;
 }
 
 // grid: (chunks, B). Workspace: partial sums [B][chunks] f64 (zero between calls).
@@ -277,7 +344,10 @@ __global__ __launch_bounds__(VT) void prob_accept_kernel(
   __shared__ int sj;
   int L = lengths[b];
   L = L < 0 ? 0 : L > P ? P : L;
-  if (tid == 0) sj = first_reject(target, draftp, draft, uniforms, b, L, P, V, draft_stride);
+  if (tid < 64) {
+    const int j0 = first_reject(target, draftp, draft, uniforms, b, L, P, V, draft_stride);
+    if (tid == 0) sj = j0;
+  }
   __syncthreads();
   const int j = sj;
   const bool resid = j < L;
@@ -297,10 +367,15 @@ __global__ __launch_bounds__(VT) void prob_finish_kernel(
     int draft_stride, int chunks) {
   const int b = blockIdx.x, tid = threadIdx.x;
   __shared__ double red[VT];
+  __shared__ double csum[PCHUNKS];
   __shared__ int sj, found;
   int L = lengths[b];
   L = L < 0 ? 0 : L > P ? P : L;
-  if (tid == 0) sj = first_reject(target, draftp, draft, uniforms, b, L, P, V, draft_stride);
+  if (tid < 64) {
+    const int j0 = first_reject(target, draftp, draft, uniforms, b, L, P, V, draft_stride);
+    if (tid == 0) sj = j0;
+  }
+  if (tid < chunks) csum[tid] = partial[(size_t)b * chunks + tid];   // the wide pass's chunk sums
   __syncthreads();
   const int j = sj;
   const bool resid = j < L;
@@ -308,7 +383,7 @@ __global__ __launch_bounds__(VT) void prob_finish_kernel(
   const float* qrow = resid ? draftp + ((size_t)b * P + j) * V : nullptr;
   const int per = ((V + 4 * chunks - 1) / (4 * chunks)) * 4;
   double S = 0.0;
-  for (int i = 0; i < chunks; ++i) S += partial[(size_t)b * chunks + i];
+  for (int i = 0; i < chunks; ++i) S += csum[i];
   bool rs = resid;
   const float u = uniforms[(size_t)b * (2 * P + 1) + (resid ? P + j : 2 * P)];
   int x = -1;
@@ -323,7 +398,7 @@ __global__ __launch_bounds__(VT) void prob_finish_kernel(
     for (; cc < chunks; ++cc) {   // the chunk sums of the wide pass, or p's
       double cs;
       if (rs == resid) {
-        cs = partial[(size_t)b * chunks + cc];
+        cs = csum[cc];
       } else {
         const int a0 = min(V, cc * per), a1 = min(V, a0 + per);
         cs = block_sum(strided_sum(prow, nullptr, false, a0, a1), red);
