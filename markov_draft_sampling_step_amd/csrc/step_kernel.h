@@ -599,24 +599,38 @@ __device__ __forceinline__ void merge_state(RowState& a, const RowState& b, bool
   a.sp |= b.sp;
 }
 
-// The value D (32 or 16) lanes up, for lanes 0..31 (D = 32) or 0..15 and
-// 32..47 (D = 16): v_permlane32_swap exchanges the upper half of its first
-// operand with the lower half of its second, v_permlane16_swap the odd rows
-// of 16 lanes of the first with the even rows of the second; with x as both
-// operands, the second result holds x from D lanes up in those lanes. VALU
-// only: no LDS round trip.
-template <int D>
-__device__ __forceinline__ uint32_t lanes_up(uint32_t x) {
-  static_assert(D == 16 || D == 32, "swap distance");
-  if constexpr (D == 32) return __builtin_amdgcn_permlane32_swap(x, x, false, false)[1];
-  else return __builtin_amdgcn_permlane16_swap(x, x, false, false)[1];
+// A lane's row state after the slab loop as one 16-byte LDS record: v1, v2,
+// id, and the carried logit's bf16 bits (high half) with the re-scan flag
+// (bit 0).
+struct __attribute__((aligned(16))) StateRec {
+  float v1, v2;
+  int id;
+  uint32_t lsp;
+};
+
+// The value at this lane's partner in step STEP of a merge over 2^L
+// consecutive lanes (L <= 4, steps 0 .. L-1): lane ^ 1, lane ^ 2 (quad
+// permutations), then the mirror image within 8 lanes and within 16 (the
+// row mirrors), one DPP move each. Each step pairs every lane with one of the
+// other half of its next larger group, so after L steps every lane of the
+// group holds the whole group's merge.
+template <int STEP>
+__device__ __forceinline__ uint32_t dpp_partner(uint32_t x) {
+  static_assert(STEP >= 0 && STEP < 4, "step");
+  constexpr int CTRL = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
 
-template <int D>
-__device__ __forceinline__ RowState state_up(const RowState& s) {
-  return RowState{__uint_as_float(lanes_up<D>(__float_as_uint(s.v1))), __uint_as_float(lanes_up<D>(__float_as_uint(s.v2))),
-                  (int)lanes_up<D>((uint32_t)s.id), (int)lanes_up<D>((uint32_t)s.sp),
-                  __uint_as_float(lanes_up<D>(__float_as_uint(s.l)))};
+template <int STEP>
+__device__ __forceinline__ RowState state_partner(const RowState& s) {
+  return RowState{__uint_as_float(dpp_partner<STEP>(__float_as_uint(s.v1))),
+                  __uint_as_float(dpp_partner<STEP>(__float_as_uint(s.v2))),
+                  (int)dpp_partner<STEP>((uint32_t)s.id), (int)dpp_partner<STEP>((uint32_t)s.sp),
+                  __uint_as_float(dpp_partner<STEP>(__float_as_uint(s.l)))};
+}
+
+__device__ __forceinline__ RowState state_of(const StateRec& r) {
+  return RowState{r.v1, r.v2, r.id, (int)(r.lsp & 1u), __uint_as_float(r.lsp & 0xffff0000u)};
 }
 
 // LDS, all of it dynamic (the kernel declares no static LDS, so the dynamic
@@ -624,19 +638,44 @@ __device__ __forceinline__ RowState state_up(const RowState& s) {
 //   [tt]            with the transform-table layout, its 32768 entries (64 KiB)
 //                   at address 0, else nothing
 //   table           the noise bound table (lines or constants)
-//   region0         embeddings [rp][R] bf16; after the slab loop the waves'
-//                   row states [5][NWV][rp] (v1, v2, id, sp, l)
+//   region0         embeddings [rp][R] bf16; after the slab loop the lanes'
+//                   row states, 16-byte records, slot-major (state_stride)
 //   info [rp] RowInfo, n_row [rp], n_src [rp], fb_row [rp], fb_thr [rp],
 //   misc [64] (per-wave row counts, fallback count, last-workgroup flag)
 //   [states]        when the launch has room: the waves' row states, so that
 //                   writing them need not wait for every wave's last read of
 //                   the embeddings
-__host__ __device__ __forceinline__ size_t region0_bytes(int rp, int R) {
-  const size_t e = (size_t)rp * R * 2, st = (size_t)NWV * rp * 20;
-  return e > st ? e : st;
+// records per row: one per (wave of the row's group, lane group g); the
+// plans with more than MRB_MAX row blocks split the waves into two groups
+__host__ __device__ __forceinline__ int state_slots(int rp) {
+  return ((rp >> 4) > MRB_MAX ? NWV / 2 : NWV) * 4;
 }
 
-__host__ __device__ __forceinline__ size_t states_bytes(int rp) { return (size_t)NWV * rp * 20; }
+// log2 of the threads per row that merge the records: as many as fit in
+// the workgroup, at most 16 (one DPP row) and at most the row's records
+__host__ __device__ __forceinline__ int state_lt(int rp) {
+  int lt = 0;
+  while (lt < 4 && (2 << lt) <= state_slots(rp) && (rp << (lt + 1)) <= NTH) ++lt;
+  return lt;
+}
+
+// Record q of row n sits at byte q * stride + 16 n. The stride, a multiple of
+// 256 bytes plus 256 / TPR, puts the 16 records that 16 consecutive lanes
+// read at once (TPR slots of 16 / TPR rows) on 16 different groups of four
+// banks; 16 consecutive writers write 16 consecutive rows of one slot.
+__host__ __device__ __forceinline__ size_t state_stride(int rp) {
+  const int lt = state_lt(rp);
+  return (((size_t)rp * 16 + 255) & ~(size_t)255) + (lt > 0 ? (size_t)(256 >> lt) : 0);
+}
+
+__host__ __device__ __forceinline__ size_t states_bytes(int rp) {
+  return (size_t)state_slots(rp) * state_stride(rp);
+}
+
+__host__ __device__ __forceinline__ size_t region0_bytes(int rp, int R) {
+  const size_t e = (size_t)rp * R * 2, st = states_bytes(rp);
+  return e > st ? e : st;
+}
 
 __host__ __device__ __forceinline__ size_t lds_dynamic(int rp, int R) {
   return region0_bytes(rp, R) + (size_t)rp * 16 + (size_t)rp * 16 + 64 * 4;
@@ -1189,21 +1228,26 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   }
   if (bias_mode) return;
 
-  // 5. each row's state: this lane's, merged over the row's 4 lanes, stored
-  //    per wave (over the embeddings, once every wave is past its last
-  //    contraction), merged over the waves; then per row either the packed
-  //    atomicMax of its certified winner or the fallback list.
-  RowState fin[MRB];
+  // 5. each row's state. Every lane keeps one state per row block (its share
+  //    of the row over the wave's units). They go to LDS as records, per row
+  //    one for each (wave of the row's group, lane group g), over the
+  //    embeddings once every wave is past its last contraction (or in LDS of
+  //    their own); after one barrier, TPR consecutive threads per row merge
+  //    its records (every TPR-th each, then across the TPR lanes with DPP
+  //    moves), and the first of them takes the exact key of the winner and
+  //    publishes it with the packed atomicMax, or lists the row for a re-scan.
+  //    No wave merges across its own lanes: the last wave to leave the slab
+  //    loop only writes its records before the barrier.
+  constexpr int SLOTS = (RG == 1 ? NWV : NWV / 2) * 4;
+  const int S16 = (int)(state_stride(rp) >> 4);        // records between slots
+  const int place = RG == 1 ? wave : (wave & 3);      // the wave's place in its row group
+  StateRec mine[MRB];
 #pragma unroll
   for (int j = 0; j < MRB; ++j) {
-    fin[j] = RowState{-INFINITY, -INFINITY, NONE, 0, 0.0f};
-    if (j >= my_nrb) continue;   // uniform: the shuffles below run for the whole wave
-    const int n = 16 * (wr + RG * j) + m;
-    const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[n];
+    mine[j] = StateRec{-INFINITY, -INFINITY, NONE, 0u};
+    if (j >= my_nrb) continue;
+    const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[16 * (wr + RG * j) + m];
     const bool noisy = !(info.T == 0.0f);
-    RowState st;
-    st.v1 = v1[j];
-    st.v2 = v2[j];
     // a noisy row's estimates fma(l, RN(1/T), bound) are all finite when
     // RN(|l| |RN(1/T)|) <= 2^127 for its largest |l| (the bound is finite
     // and under 2^5); else (a NaN or infinite logit, a NaN or infinite
@@ -1214,21 +1258,16 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       const float lmax = __uint_as_float((mh > ml ? mh : ml) << 16);
       spn = noisy && !EXACT && !(lmax * fabsf(info.rcp) <= 0x1p127f);
     }
-    st.sp = (sp[j] || spn) ? 1 : 0;
-    if (EXACT) st.id = idt[j];
-    else if (idt[j] == NONE) st.id = NONE;
-    else st.id = idt[j] + (int)((noisy ? __float_as_uint(v1[j]) : __float_as_uint(v2[j])) & 7u);
-    st.l = 0.0f;
-    if (CARRY) st.l = (__float_as_uint(v1[j]) & 1u) ? bf_hi(lw[CARRY ? j : 0]) : bf_lo(lw[CARRY ? j : 0]);
-    const bool top2 = noisy && !EXACT;
-    // lanes m, m + 16, m + 32, m + 48 hold the row: lanes 0..31 merge the
-    // state 32 lanes up, then lanes 0..15 the state 16 lanes up (only they
-    // store the result)
-    merge_state(st, state_up<32>(st), top2);
-    merge_state(st, state_up<16>(st), top2);
-    fin[j] = st;
+    int id;
+    if (EXACT) id = idt[j];
+    else if (idt[j] == NONE) id = NONE;
+    else id = idt[j] + (int)((noisy ? __float_as_uint(v1[j]) : __float_as_uint(v2[j])) & 7u);
+    uint32_t lbits = 0u;
+    if (CARRY)
+      lbits = (__float_as_uint(v1[j]) & 1u) ? (lw[CARRY ? j : 0] & 0xffff0000u) : (lw[CARRY ? j : 0] << 16);
+    mine[j] = StateRec{v1[j], v2[j], id, lbits | ((sp[j] || spn) ? 1u : 0u)};
   }
-  // the states go over the embeddings unless they have LDS of their own:
+  // the records go over the embeddings unless they have LDS of their own:
   // then every wave must be past its last contraction first. With carried
   // logits the cache stores drain meanwhile (the barrier before the
   // fallback scans, which read them back, waits for them), else they are
@@ -1245,46 +1284,49 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   } else if (reads_cache) {
     __builtin_amdgcn_s_waitcnt(0);
   }
-  float* st_v1 = sep ? (float*)(misc + 64) : (float*)emb;
-  float* st_v2 = st_v1 + NWV * rp;
-  int* st_id = (int*)(st_v2 + NWV * rp);
-  int* st_sp = st_id + NWV * rp;
-  float* st_l = (float*)(st_sp + NWV * rp);
+  StateRec* const rec = sep ? (StateRec*)(misc + 64) : (StateRec*)emb;
 #pragma unroll
   for (int j = 0; j < MRB; ++j) {
     if (j >= my_nrb) break;
-    const int n = 16 * (wr + RG * j) + m;
-    if (g == 0) {
-      st_v1[wave * rp + n] = fin[j].v1;
-      st_v2[wave * rp + n] = fin[j].v2;
-      st_id[wave * rp + n] = fin[j].id;
-      st_sp[wave * rp + n] = fin[j].sp;
-      st_l[wave * rp + n] = fin[j].l;
-    }
+    rec[(place * 4 + g) * S16 + 16 * (wr + RG * j) + m] = mine[j];
   }
   if (tid == 0) misc[16] = 0;
   if (sep && reads_cache) __syncthreads();
   else lds_barrier();
   static_assert(ROWS_CAP <= NTH, "one thread per row");
-  if (tid < rows) {
-    const int n = tid;
+  // TPR = 2^lt consecutive threads per row
+  const int lt = state_lt(rp);
+  const int n = tid >> lt, kq = tid & ((1 << lt) - 1);
+  RowState st{-INFINITY, -INFINITY, NONE, 0, 0.0f};
+  if (n < rows) {
     const RowInfo info = n_info[n];
     const bool noisy = !(info.T == 0.0f);
     const bool top2 = noisy && !EXACT;
-    // the row's wave states, all loads issued before the first merge
-    constexpr int NS = RG == 1 ? NWV : 4;
-    const int w0 = RG == 1 ? 0 : 4 * ((n >> 4) & 1);
-    RowState o[NS];
+    // the thread's records, four loads in flight before their merges
+    const StateRec* const rr0 = rec + kq * S16 + n;
+    const int step_q = S16 << lt, cnt = SLOTS >> lt;
+    if (cnt >= 4) {
+      for (int q = 0; q < cnt; q += 4) {
+        RowState o[4];
 #pragma unroll
-    for (int q = 0; q < NS; ++q) {
-      const int i = (w0 + q) * rp + n;
-      o[q] = RowState{st_v1[i], st_v2[i], st_id[i], st_sp[i], st_l[i]};
+        for (int i = 0; i < 4; ++i) o[i] = state_of(rr0[(q + i) * step_q]);
+        merge_state(o[0], o[1], top2);
+        merge_state(o[2], o[3], top2);
+        merge_state(o[0], o[2], top2);
+        merge_state(st, o[0], top2);
+      }
+    } else {
+      for (int q = 0; q < cnt; ++q) merge_state(st, state_of(rr0[q * step_q]), top2);
     }
-#pragma unroll
-    for (int w = 1; w < NS; w <<= 1)   // a tree: independent merges side by side
-#pragma unroll
-      for (int q = 0; q + w < NS; q += 2 * w) merge_state(o[q], o[q + w], top2);
-    RowState st = o[0];
+    if (lt > 0) merge_state(st, state_partner<0>(st), top2);
+    if (lt > 1) merge_state(st, state_partner<1>(st), top2);
+    if (lt > 2) merge_state(st, state_partner<2>(st), top2);
+    if (lt > 3) merge_state(st, state_partner<3>(st), top2);
+  }
+  if (n < rows && kq == 0) {
+    const RowInfo info = n_info[n];
+    const bool noisy = !(info.T == 0.0f);
+    const bool top2 = noisy && !EXACT;
     const int rr = n_row[n];
     float key = st.v1;
     bool fb = !EXACT && (st.sp != 0 || (mode == MODE_SAMPLE_FALLBACK && noisy));
