@@ -528,10 +528,12 @@ __device__ __forceinline__ void decode_w2q_tile(const u32x4_t* Qa, const u32x4_t
 }
 
 // The bias of one 16-row block for the wave's 32 tokens: lane (g, m) gets
-// row n = 16 rb + m, tokens tg .. tg+3 in c0 and tg+4 .. tg+7 in c1.
+// row n = n0 + m (n0 = 16 rb), tokens tg .. tg+3 in c0 and tg+4 .. tg+7 in
+// c1. The swizzle mask is below 16, so n & swz = m & swz: the lane's part of
+// the address is the same for every block.
 template <int KB, bool W8 = false>
 __device__ __forceinline__ void block_bias(const bf16x8_t* A0, const bf16x8_t* A1, const uint16_t* emb,
-                                           int n, int R, int g, int swz, bool kzero, f32x4_t& c0,
+                                           int n0, int m, int R, int g, int swz, bool kzero, f32x4_t& c0,
                                            f32x4_t& c1) {
   c0 = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   c1 = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -542,7 +544,7 @@ __device__ __forceinline__ void block_bias(const bf16x8_t* A0, const bf16x8_t* A
       B = (bf16x8_t){};
     } else {
       const int ch = chunk_of<KB, W8>(i, g);
-      B = *(const bf16x8_t*)(emb + (size_t)n * R + ((ch ^ (n & swz)) * 8));
+      B = *(const bf16x8_t*)(emb + (size_t)n0 * R + (m * R + ((ch ^ (m & swz)) * 8)));
     }
     c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[i], B, c0, 0, 0, 0);
     c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[i], B, c1, 0, 0, 0);
@@ -925,7 +927,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   const float pinf = a.inf;
   float v1[MRB], v2[MRB];
   int idt[MRB];
-  bool sp[MRB];
+  uint32_t spm = 0u;   // bit j: row block j has a non-finite estimate or logit
   // noisy rows of plans with registers to spare: the packed (high and low
   // half) largest |cached logit| bits, checked once at the end; the others
   // test every estimate
@@ -980,7 +982,6 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     v1[j] = -INFINITY;
     v2[j] = -INFINITY;
     idt[j] = NONE;
-    sp[j] = false;
     if (PKMAX) mxw[PKMAX ? j : 0] = 0u;
     if (CARRY) lw[CARRY ? j : 0] = 0u;
   }
@@ -998,6 +999,11 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   // one 32-token unit (the wave's unit i, slab `sl`) with w2 tile buffer BUF
   auto unit = [&](auto bufc, int i, int sl) {
     constexpr int BUF = decltype(bufc)::value;
+    // an opaque zero added to the row blocks' embedding offsets: with many
+    // row blocks the compiler would otherwise keep every block's operand
+    // addresses across the unit loop, more than the registers hold
+    int z0 = 0;
+    if (MRB > 4) asm volatile("" : "+s"(z0));
     const int tok0 = sl * SLAB + tw * TOK_PER_WAVE;
     const int tg = tok0 + 8 * g;               // this lane's 8 tokens: tg .. tg+7
     const bool tok_ok = tg < V;
@@ -1030,7 +1036,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
 #pragma unroll
     for (int j = 0; j < D; ++j)
       if (j < my_nrb)
-        block_bias<KB, W8>(A0[AB], A1[AB], emb, 16 * (wr + RG * j) + m, R, g, swz, kzero, cb0[j], cb1[j]);
+        block_bias<KB, W8>(A0[AB], A1[AB], emb, 16 * (wr + RG * j) + z0, m, R, g, swz, kzero, cb0[j], cb1[j]);
     if (LATE && D > 0 && my_nrb <= D && ntile) tile(BUF, nsl * SLAB + tw * TOK_PER_WAVE);
 #pragma unroll
     for (int j = 0; j < MRB; ++j) {
@@ -1039,11 +1045,11 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       // once the unit's last one has issued, this buffer's next tile
       if (D == 0) {
         if (j < my_nrb) {
-          block_bias<KB, W8>(A0[AB], A1[AB], emb, n, R, g, swz, kzero, cb0[j], cb1[j]);
+          block_bias<KB, W8>(A0[AB], A1[AB], emb, n - m + z0, m, R, g, swz, kzero, cb0[j], cb1[j]);
           if (LATE && j == my_nrb - 1 && ntile) tile(BUF, nsl * SLAB + tw * TOK_PER_WAVE);
         }
       } else if (j + D < MRB && j + D < my_nrb) {
-        block_bias<KB, W8>(A0[AB], A1[AB], emb, n + 16 * RG * D, R, g, swz, kzero, cb0[j + D], cb1[j + D]);
+        block_bias<KB, W8>(A0[AB], A1[AB], emb, n - m + 16 * RG * D + z0, m, R, g, swz, kzero, cb0[j + D], cb1[j + D]);
         if (LATE && j + D == my_nrb - 1 && ntile) tile(BUF, nsl * SLAB + tw * TOK_PER_WAVE);
       }
       const u32x4_t bv = bq[j];
@@ -1194,7 +1200,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
           }
           v1[j] = x1;
           v2[j] = x2;
-          if (!PKMAX) sp[j] = sp[j] || spx;
+          if (!PKMAX) spm |= (spx ? 1u : 0u) << j;
         }
       }
       // temperature-0 rows: the exact largest logit, the earliest on ties
@@ -1215,7 +1221,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
           if (x1 != x1b) idt[j] = tg;
           v1[j] = x1;
           v2[j] = __uint_as_float(e1);
-          sp[j] = sp[j] || spx;
+          spm |= (spx ? 1u : 0u) << j;
         }
       }
     }
@@ -1241,32 +1247,6 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   constexpr int SLOTS = (RG == 1 ? NWV : NWV / 2) * 4;
   const int S16 = (int)(state_stride(rp) >> 4);        // records between slots
   const int place = RG == 1 ? wave : (wave & 3);      // the wave's place in its row group
-  StateRec mine[MRB];
-#pragma unroll
-  for (int j = 0; j < MRB; ++j) {
-    mine[j] = StateRec{-INFINITY, -INFINITY, NONE, 0u};
-    if (j >= my_nrb) continue;
-    const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[16 * (wr + RG * j) + m];
-    const bool noisy = !(info.T == 0.0f);
-    // a noisy row's estimates fma(l, RN(1/T), bound) are all finite when
-    // RN(|l| |RN(1/T)|) <= 2^127 for its largest |l| (the bound is finite
-    // and under 2^5); else (a NaN or infinite logit, a NaN or infinite
-    // 1/T, or a product past 2^127, where NaN compares false) re-scan it
-    bool spn = false;
-    if (PKMAX) {
-      const uint32_t mh = mxw[PKMAX ? j : 0] >> 16, ml = mxw[PKMAX ? j : 0] & 0xffffu;
-      const float lmax = __uint_as_float((mh > ml ? mh : ml) << 16);
-      spn = noisy && !EXACT && !(lmax * fabsf(info.rcp) <= 0x1p127f);
-    }
-    int id;
-    if (EXACT) id = idt[j];
-    else if (idt[j] == NONE) id = NONE;
-    else id = idt[j] + (int)((noisy ? __float_as_uint(v1[j]) : __float_as_uint(v2[j])) & 7u);
-    uint32_t lbits = 0u;
-    if (CARRY)
-      lbits = (__float_as_uint(v1[j]) & 1u) ? (lw[CARRY ? j : 0] & 0xffff0000u) : (lw[CARRY ? j : 0] << 16);
-    mine[j] = StateRec{v1[j], v2[j], id, lbits | ((sp[j] || spn) ? 1u : 0u)};
-  }
   // the records go over the embeddings unless they have LDS of their own:
   // then every wave must be past its last contraction first. With carried
   // logits the cache stores drain meanwhile (the barrier before the
@@ -1287,8 +1267,28 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   StateRec* const rec = sep ? (StateRec*)(misc + 64) : (StateRec*)emb;
 #pragma unroll
   for (int j = 0; j < MRB; ++j) {
-    if (j >= my_nrb) break;
-    rec[(place * 4 + g) * S16 + 16 * (wr + RG * j) + m] = mine[j];
+    if (j >= my_nrb) continue;   // (not break: the loop stays a counted one, unrolled)
+    const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[16 * (wr + RG * j) + m];
+    const bool noisy = !(info.T == 0.0f);
+    // a noisy row's estimates fma(l, RN(1/T), bound) are all finite when
+    // RN(|l| |RN(1/T)|) <= 2^127 for its largest |l| (the bound is finite
+    // and under 2^5); else (a NaN or infinite logit, a NaN or infinite
+    // 1/T, or a product past 2^127, where NaN compares false) re-scan it
+    bool spn = false;
+    if (PKMAX) {
+      const uint32_t mh = mxw[PKMAX ? j : 0] >> 16, ml = mxw[PKMAX ? j : 0] & 0xffffu;
+      const float lmax = __uint_as_float((mh > ml ? mh : ml) << 16);
+      spn = noisy && !EXACT && !(lmax * fabsf(info.rcp) <= 0x1p127f);
+    }
+    int id;
+    if (EXACT) id = idt[j];
+    else if (idt[j] == NONE) id = NONE;
+    else id = idt[j] + (int)((noisy ? __float_as_uint(v1[j]) : __float_as_uint(v2[j])) & 7u);
+    uint32_t lbits = 0u;
+    if (CARRY)
+      lbits = (__float_as_uint(v1[j]) & 1u) ? (lw[CARRY ? j : 0] & 0xffff0000u) : (lw[CARRY ? j : 0] << 16);
+    rec[(place * 4 + g) * S16 + 16 * (wr + RG * j) + m] =
+        StateRec{v1[j], v2[j], id, lbits | (((spm >> j) & 1u) | (spn ? 1u : 0u))};
   }
   if (tid == 0) misc[16] = 0;
   if (sep && reads_cache) __syncthreads();
