@@ -84,7 +84,11 @@ __global__ __launch_bounds__(VT) void greedy_accept_kernel(const uint16_t* logit
     const uint16_t* row = logits + ((size_t)b * (P + 1) + j) * V;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    // GU loads in flight per thread before any is used
+    // GU loads in flight per thread before any is used. A thread meets its
+    // elements in rising id, so one is taken over the kept one iff the kept
+    // one is not NaN and it is NaN or larger (a tie keeps the earlier id);
+    // a thread whose elements are all -inf takes none, and then its first
+    // (the lowest id among equal values) below.
     constexpr int GU = 4;
     for (int q = q0 + tid; q < q1; q += GU * VT) {
       u32x4_t w[GU];
@@ -99,13 +103,13 @@ __global__ __launch_bounds__(VT) void greedy_accept_kernel(const uint16_t* logit
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float l = (e & 1) ? bf_hi(ws[e >> 1]) : bf_lo(ws[e >> 1]);
-          if (before(l, id0 + e, bv, bi)) {
-            bv = l;
-            bi = id0 + e;
-          }
+          const bool take = !__builtin_isnan(bv) & (__builtin_isnan(l) | (l > bv));
+          bv = take ? l : bv;
+          bi = take ? id0 + e : bi;
         }
       }
     }
+    if (bi == 0x7fffffff && q0 + tid < q1) bi = (q0 + tid) * 8;
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) {
       const float ov = __shfl_xor(bv, sh);
