@@ -299,8 +299,6 @@ int launch_steps(const Call& c, markov_stream_t stream, const markov_shape_t* sh
   const bool tt_layout = c.mode != MODE_BIAS && sh->softcap > 0.0f && plan.rg == 1 &&
                          tt_fits(rp, sh->rank, greedy);
   size_t lds = (tt_layout ? TT_BYTES : 0) + lds_total(rp, sh->rank, greedy);
-  const bool sep_states = lds + states_bytes(rp) <= LDS_MAX;
-  if (sep_states) lds += states_bytes(rp);
   const int nslabs = (sh->vocab + SLAB - 1) / SLAB;
   int grid = 0;
   int rc = launch_grid(fn, lds, nslabs, &grid);
@@ -331,7 +329,6 @@ int launch_steps(const Call& c, markov_stream_t stream, const markov_shape_t* sh
     a.ticket = (unsigned int*)((unsigned char*)workspace + WS_TICKET);
   }
   a.tt_layout = tt_layout ? 1 : 0;
-  a.sep_states = sep_states ? 1 : 0;
   a.rows = sh->rows;
   a.V = sh->vocab;
   a.R = sh->rank;

@@ -77,7 +77,6 @@ struct StepArgs {
   int id_offset, V_total;
   int rows, V, R, k, step, nslabs, mode;
   int tt_layout;              // LDS holds the transform table at address 0
-  int sep_states;             // the waves' row states have LDS of their own (after misc)
   float mult, inv_cap, cap;
   int has_cap;
   float inf;                  // +infinity, opaque to the compiler (see the noise loop)
@@ -332,6 +331,13 @@ __device__ __forceinline__ unsigned long long pack_winner(float v, int id) {
   return ((unsigned long long)o << 32) | (unsigned long long)(uint32_t)(~(uint32_t)id);
 }
 
+// The order key of a value (the high word of pack_winner), and back: every
+// NaN decodes to a NaN, -0 to +0.
+__device__ __forceinline__ uint32_t order_key(float v) { return (uint32_t)(pack_winner(v, 0) >> 32); }
+__device__ __forceinline__ float order_value(uint32_t o) {
+  return o == 0xffffffffu ? __builtin_nanf("") : __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
 // The winner slot of a row decodes to its token id.
 __device__ __forceinline__ int64_t slot_token(unsigned long long w) {
   return (int64_t)(uint32_t)(~(uint32_t)w);
@@ -560,18 +566,6 @@ struct RowInfo {
   float T;
 };
 
-// Merge rules of the per-row states. ORDER: the exact (key, id) under the
-// total order. TOP2: (v1, id) is the element with the largest upper bound
-// v1, v2 the largest upper bound among all other elements, l the logit of
-// element id (so its exact key needs no read of the cache). sp: some element
-// had a non-finite estimate (noisy rows) or a NaN / -inf logit (T = 0 rows).
-struct RowState {
-  float v1, v2;
-  int id;
-  int sp;
-  float l;
-};
-
 // v_pk_max_u16: the larger of each 16-bit half
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   uint32_t r;
@@ -579,108 +573,33 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return r;
 }
 
-// One merge of b into a under the row's rule (TOP2 if top2, else ORDER), as
-// selects: a merge runs for every lane of a wave whatever its row's rule, and
-// a branch per field costs more than both rules' compares. Under TOP2 the
-// loser's v2 never exceeds its v1, so v2 becomes the largest bound but the
-// winner's. Both rules are associative and commutative (a strict total order
-// on (v1, id); a NaN bound marks the state sp and its row is re-scanned), so
-// states may be merged in any grouping.
-__device__ __forceinline__ void merge_state(RowState& a, const RowState& b, bool top2) {
-  // bitwise operators: no short-circuit branches. ORDER is before(b, a):
-  // TOP2's test, or b NaN and (a not NaN or b the lower id)
-  const bool lt_id = b.id < a.id;
-  const bool bw_top = (b.v1 > a.v1) | ((b.v1 == a.v1) & lt_id);
-  const bool bw_ord = bw_top | (__builtin_isnan(b.v1) & (!__builtin_isnan(a.v1) | lt_id));
-  const bool bw = top2 ? bw_top : bw_ord;
-  const float v2 = fmaxf(bw ? a.v1 : b.v1, bw ? b.v2 : a.v2);
-  a.v2 = top2 ? v2 : a.v2;
-  a.v1 = bw ? b.v1 : a.v1;
-  a.id = bw ? b.id : a.id;
-  a.l = bw ? b.l : a.l;
-  a.sp |= b.sp;
-}
-
-// A lane's row state after the slab loop as one 16-byte LDS record: v1, v2,
-// id, and the carried logit's bf16 bits (high half) with the re-scan flag
-// (bit 0).
-struct __attribute__((aligned(16))) StateRec {
-  float v1, v2;
-  int id;
-  uint32_t lsp;
-};
-
-// The value at this lane's partner in step STEP of a merge over 2^L
-// consecutive lanes (L <= 4, steps 0 .. L-1): lane ^ 1, lane ^ 2 (quad
-// permutations), then the mirror image within 8 lanes and within 16 (the
-// row mirrors), one DPP move each. Each step pairs every lane with one of the
-// other half of its next larger group, so after L steps every lane of the
-// group holds the whole group's merge.
-template <int STEP>
-__device__ __forceinline__ uint32_t dpp_partner(uint32_t x) {
-  static_assert(STEP >= 0 && STEP < 4, "step");
-  constexpr int CTRL = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-}
-
-template <int STEP>
-__device__ __forceinline__ RowState state_partner(const RowState& s) {
-  return RowState{__uint_as_float(dpp_partner<STEP>(__float_as_uint(s.v1))),
-                  __uint_as_float(dpp_partner<STEP>(__float_as_uint(s.v2))),
-                  (int)dpp_partner<STEP>((uint32_t)s.id), (int)dpp_partner<STEP>((uint32_t)s.sp),
-                  __uint_as_float(dpp_partner<STEP>(__float_as_uint(s.l)))};
-}
-
-__device__ __forceinline__ RowState state_of(const StateRec& r) {
-  return RowState{r.v1, r.v2, r.id, (int)(r.lsp & 1u), __uint_as_float(r.lsp & 0xffff0000u)};
-}
-
+// The rows' states after the slab loop. ORDER rows (T = 0, and every row of
+// the exact variant): the (key, id) first under the total order. TOP2 rows:
+// (v1, id) is the element with the largest upper bound v1, v2 the largest
+// upper bound among all other elements, l the logit of element id (so its
+// exact key needs no read of the cache). sp: some element had a non-finite
+// estimate (noisy rows) or a NaN / -inf logit (T = 0 rows). A workgroup
+// accumulates them per row in LDS with atomics: the winner as the packed
+// order key of (v1, id) (ds_max_u64: a NaN first, then the larger value, the
+// lower id on equal values), then, once the winner is known, v2 as the
+// order key of every other state's v1 and every state's v2 (ds_max_u32), l
+// from the winning lane and sp as ors into one word (l's bf16 bits high, sp
+// bit 0).
+//
 // LDS, all of it dynamic (the kernel declares no static LDS, so the dynamic
 // array starts at address 0):
 //   [tt]            with the transform-table layout, its 32768 entries (64 KiB)
 //                   at address 0, else nothing
 //   table           the noise bound table (lines or constants)
-//   region0         embeddings [rp][R] bf16; after the slab loop the lanes'
-//                   row states, 16-byte records, slot-major (state_stride)
+//   region0         embeddings [rp][R] bf16
 //   info [rp] RowInfo, n_row [rp], n_src [rp], fb_row [rp], fb_thr [rp],
-//   misc [64] (per-wave row counts, fallback count, last-workgroup flag)
-//   [states]        when the launch has room: the waves' row states, so that
-//                   writing them need not wait for every wave's last read of
-//                   the embeddings
-// records per row: one per (wave of the row's group, lane group g); the
-// plans with more than MRB_MAX row blocks split the waves into two groups
-__host__ __device__ __forceinline__ int state_slots(int rp) {
-  return ((rp >> 4) > MRB_MAX ? NWV / 2 : NWV) * 4;
-}
-
-// log2 of the threads per row that merge the records: as many as fit in
-// the workgroup, at most 16 (one DPP row) and at most the row's records
-__host__ __device__ __forceinline__ int state_lt(int rp) {
-  int lt = 0;
-  while (lt < 4 && (2 << lt) <= state_slots(rp) && (rp << (lt + 1)) <= NTH) ++lt;
-  return lt;
-}
-
-// Record q of row n sits at byte q * stride + 16 n. The stride, a multiple of
-// 256 bytes plus 256 / TPR, puts the 16 records that 16 consecutive lanes
-// read at once (TPR slots of 16 / TPR rows) on 16 different groups of four
-// banks; 16 consecutive writers write 16 consecutive rows of one slot.
-__host__ __device__ __forceinline__ size_t state_stride(int rp) {
-  const int lt = state_lt(rp);
-  return (((size_t)rp * 16 + 255) & ~(size_t)255) + (lt > 0 ? (size_t)(256 >> lt) : 0);
-}
-
-__host__ __device__ __forceinline__ size_t states_bytes(int rp) {
-  return (size_t)state_slots(rp) * state_stride(rp);
-}
-
-__host__ __device__ __forceinline__ size_t region0_bytes(int rp, int R) {
-  const size_t e = (size_t)rp * R * 2, st = states_bytes(rp);
-  return e > st ? e : st;
-}
+//   misc [64] (per-wave row counts, fallback count, last-workgroup flag),
+//   the row accumulators win [rp] u64 and l|sp [rp] u32 (the accumulated v2
+//   reuses n_src, free once the embeddings are gathered)
+__host__ __device__ __forceinline__ size_t region0_bytes(int rp, int R) { return (size_t)rp * R * 2; }
 
 __host__ __device__ __forceinline__ size_t lds_dynamic(int rp, int R) {
-  return region0_bytes(rp, R) + (size_t)rp * 16 + (size_t)rp * 16 + 64 * 4;
+  return region0_bytes(rp, R) + (size_t)rp * 16 + (size_t)rp * 16 + 64 * 4 + (size_t)rp * 12;
 }
 
 // the noise table in LDS: the lines for one row group (up to MRB_MAX row
@@ -765,6 +684,9 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   int* fb_row = n_src + rp;
   float* fb_thr = (float*)(fb_row + rp);
   int* misc = (int*)(fb_thr + rp);
+  unsigned long long* acc_win = (unsigned long long*)(misc + 64);   // the row accumulators
+  uint32_t* acc_lsp = (uint32_t*)(acc_win + rp);
+  uint32_t* acc_v2 = (uint32_t*)n_src;                              // once the gather is done
 
   // 0. this thread's request row: everything the first step needs, in one
   //    round trip
@@ -903,6 +825,10 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       n_src[r] = 0;
       n_info[r] = RowInfo{0, 0.0f, 0u, 0.0f};
     }
+    if (r < rp) {   // the row accumulators start empty (v2 below, after the gather)
+      acc_win[r] = 0ull;
+      acc_lsp[r] = 0u;
+    }
   }
 
   u32x4_t bq[MRB];
@@ -995,6 +921,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   else wait_vm<VM_AFTER>();
   lds_barrier();
   if (!tile_first && NB == 1 && U > 0) tile(0, slab0 * SLAB + tw * TOK_PER_WAVE);
+  if (tid < rp) acc_v2[tid] = order_key(-INFINITY);   // n_src is read by the gather only
 
   // one 32-token unit (the wave's unit i, slab `sl`) with w2 tile buffer BUF
   auto unit = [&](auto bufc, int i, int sl) {
@@ -1235,40 +1162,24 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   if (bias_mode) return;
 
   // 5. each row's state. Every lane keeps one state per row block (its share
-  //    of the row over the wave's units). They go to LDS as records, per row
-  //    one for each (wave of the row's group, lane group g), over the
-  //    embeddings once every wave is past its last contraction (or in LDS of
-  //    their own); after one barrier, TPR consecutive threads per row merge
-  //    its records (every TPR-th each, then across the TPR lanes with DPP
-  //    moves), and the first of them takes the exact key of the winner and
-  //    publishes it with the packed atomicMax, or lists the row for a re-scan.
-  //    No wave merges across its own lanes: the last wave to leave the slab
-  //    loop only writes its records before the barrier.
-  constexpr int SLOTS = (RG == 1 ? NWV : NWV / 2) * 4;
-  const int S16 = (int)(state_stride(rp) >> 4);        // records between slots
-  const int place = RG == 1 ? wave : (wave & 3);      // the wave's place in its row group
-  // the records go over the embeddings unless they have LDS of their own:
-  // then every wave must be past its last contraction first. With carried
-  // logits the cache stores drain meanwhile (the barrier before the
-  // fallback scans, which read them back, waits for them), else they are
-  // read back below and waited for here.
-  const bool sep = a.sep_states != 0;   // uniform
-  const bool reads_cache = !(CARRY || GREEDY);
-  if (!sep) {
-    if (reads_cache) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    } else {
-      lds_barrier();
-    }
-  } else if (reads_cache) {
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-  StateRec* const rec = sep ? (StateRec*)(misc + 64) : (StateRec*)emb;
+  //    of the row over the wave's units). It goes into the row's LDS
+  //    accumulators: the winner's packed order key by a 64-bit atomic max
+  //    (a lane's own re-scan flag by an atomic or) as soon as the wave leaves
+  //    the slab loop; after one barrier, the second bound by a 32-bit atomic
+  //    max of every other state's v1 and the winner's v2, and the winner's
+  //    carried logit from its lane; after a second barrier, one thread per
+  //    row takes the exact key of the winner and publishes it with the packed
+  //    atomicMax, or lists the row for a re-scan.
+  auto state_id = [&](int j, bool noisy) -> int {
+    if (EXACT) return idt[j];
+    if (idt[j] == NONE) return NONE;
+    return idt[j] + (int)((noisy ? __float_as_uint(v1[j]) : __float_as_uint(v2[j])) & 7u);
+  };
 #pragma unroll
   for (int j = 0; j < MRB; ++j) {
     if (j >= my_nrb) continue;   // (not break: the loop stays a counted one, unrolled)
-    const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[16 * (wr + RG * j) + m];
+    const int n = 16 * (wr + RG * j) + m;
+    const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[n];
     const bool noisy = !(info.T == 0.0f);
     // a noisy row's estimates fma(l, RN(1/T), bound) are all finite when
     // RN(|l| |RN(1/T)|) <= 2^127 for its largest |l| (the bound is finite
@@ -1280,66 +1191,65 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       const float lmax = __uint_as_float((mh > ml ? mh : ml) << 16);
       spn = noisy && !EXACT && !(lmax * fabsf(info.rcp) <= 0x1p127f);
     }
-    int id;
-    if (EXACT) id = idt[j];
-    else if (idt[j] == NONE) id = NONE;
-    else id = idt[j] + (int)((noisy ? __float_as_uint(v1[j]) : __float_as_uint(v2[j])) & 7u);
-    uint32_t lbits = 0u;
-    if (CARRY)
-      lbits = (__float_as_uint(v1[j]) & 1u) ? (lw[CARRY ? j : 0] & 0xffff0000u) : (lw[CARRY ? j : 0] << 16);
-    rec[(place * 4 + g) * S16 + 16 * (wr + RG * j) + m] =
-        StateRec{v1[j], v2[j], id, lbits | (((spm >> j) & 1u) | (spn ? 1u : 0u))};
+    const int id = state_id(j, noisy);
+    if (id != NONE)
+      __hip_atomic_fetch_max(acc_win + n, pack_winner(v1[j], id), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (((spm >> j) & 1u) | (spn ? 1u : 0u))
+      __hip_atomic_fetch_or(acc_lsp + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  lds_barrier();
+  if (!EXACT && !GREEDY) {
+#pragma unroll
+    for (int j = 0; j < MRB; ++j) {
+      if (j >= my_nrb) continue;
+      const int n = 16 * (wr + RG * j) + m;
+      const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[n];
+      if (info.T == 0.0f) continue;   // an ORDER row keeps no second bound
+      const int id = state_id(j, true);
+      const bool is_w = id != NONE && (uint32_t)acc_win[n] == ~(uint32_t)id;
+      // a lane's v2 never exceeds its v1: the winner's lane gives its v2,
+      // every other lane its v1
+      const float c = is_w ? v2[j] : v1[j];
+      if (c > -INFINITY)
+        __hip_atomic_fetch_max(acc_v2 + n, order_key(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (CARRY && is_w)
+        __hip_atomic_fetch_or(acc_lsp + n,
+                              (__float_as_uint(v1[j]) & 1u) ? (lw[CARRY ? j : 0] & 0xffff0000u) : (lw[CARRY ? j : 0] << 16),
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
   }
   if (tid == 0) misc[16] = 0;
-  if (sep && reads_cache) __syncthreads();
-  else lds_barrier();
-  static_assert(ROWS_CAP <= NTH, "one thread per row");
-  // TPR = 2^lt consecutive threads per row
-  const int lt = state_lt(rp);
-  const int n = tid >> lt, kq = tid & ((1 << lt) - 1);
-  RowState st{-INFINITY, -INFINITY, NONE, 0, 0.0f};
-  if (n < rows) {
-    const RowInfo info = n_info[n];
-    const bool noisy = !(info.T == 0.0f);
-    const bool top2 = noisy && !EXACT;
-    // the thread's records, four loads in flight before their merges
-    const StateRec* const rr0 = rec + kq * S16 + n;
-    const int step_q = S16 << lt, cnt = SLOTS >> lt;
-    if (cnt >= 4) {
-      for (int q = 0; q < cnt; q += 4) {
-        RowState o[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = state_of(rr0[(q + i) * step_q]);
-        merge_state(o[0], o[1], top2);
-        merge_state(o[2], o[3], top2);
-        merge_state(o[0], o[2], top2);
-        merge_state(st, o[0], top2);
-      }
-    } else {
-      for (int q = 0; q < cnt; ++q) merge_state(st, state_of(rr0[q * step_q]), top2);
-    }
-    if (lt > 0) merge_state(st, state_partner<0>(st), top2);
-    if (lt > 1) merge_state(st, state_partner<1>(st), top2);
-    if (lt > 2) merge_state(st, state_partner<2>(st), top2);
-    if (lt > 3) merge_state(st, state_partner<3>(st), top2);
+  // without carried logits the winner's is read back from the cache below:
+  // every wave's cache stores first
+  const bool reads_cache = !(CARRY || GREEDY);
+  if (reads_cache) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  } else {
+    lds_barrier();
   }
-  if (n < rows && kq == 0) {
+  static_assert(ROWS_CAP <= NTH, "one thread per row");
+  if (tid < rows) {
+    const int n = tid;
     const RowInfo info = n_info[n];
     const bool noisy = !(info.T == 0.0f);
     const bool top2 = noisy && !EXACT;
+    const unsigned long long w = acc_win[n];
+    const int st_id = w == 0ull ? NONE : (int)~(uint32_t)w;
+    const float st_v1 = order_value((uint32_t)(w >> 32));
     const int rr = n_row[n];
-    float key = st.v1;
-    bool fb = !EXACT && (st.sp != 0 || (mode == MODE_SAMPLE_FALLBACK && noisy));
+    float key = st_v1;
+    bool fb = !EXACT && ((acc_lsp[n] & 1u) != 0u || (mode == MODE_SAMPLE_FALLBACK && noisy));
     float thr = -INFINITY;
-    if (!fb && top2 && st.id != NONE) {
-      float l1 = st.l;
+    if (!fb && top2 && st_id != NONE) {
+      float l1 = __uint_as_float(acc_lsp[n] & 0xffff0000u);
       if (!CARRY) {
-        const size_t e = (size_t)info.rk * V + st.id;
+        const size_t e = (size_t)info.rk * V + st_id;
         const uint32_t wd = load_cache_word(a.cache, e & ~(size_t)1);
         l1 = (e & 1) ? bf_hi(wd) : bf_lo(wd);
       }
-      key = key_exact(l1, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)(st.id + gofs))));
-      const float v2u = slack_up(st.v2);
+      key = key_exact(l1, info.T, mm_finish(info.prefix, mm_token_word((uint32_t)(st_id + gofs))));
+      const float v2u = slack_up(order_value(acc_v2[n]));
       if (!(key > v2u)) {
         // not certified: some other element's bound reaches the key. If a
         // key already published for this row (by another workgroup) lies
@@ -1361,8 +1271,8 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       const int i = atomicAdd(&misc[16], 1);
       fb_row[i] = n;
       fb_thr[i] = thr;
-    } else if (st.id != NONE) {
-      __hip_atomic_fetch_max(slots_cur + rr, pack_winner(key, st.id + gofs), __ATOMIC_RELAXED,
+    } else if (st_id != NONE) {
+      __hip_atomic_fetch_max(slots_cur + rr, pack_winner(key, st_id + gofs), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
     }
   }
