@@ -17,9 +17,10 @@
 //   * probabilistic: a workgroup per (batch row, vocabulary chunk) finds the
 //     first rejected proposal (the speculative-sampling test u q < p, exact
 //     in binary64) and stores the binary64 sum of its slice of the residual
-//     max(0, p - q) (or of p_L when every proposal passed). The finisher adds
+//     max(0, p - q) (or of p_L when every proposal passed); the row's first
+//     chunk also records that proposal and its uniform. The finisher adds
 //     the chunk sums in order, finds the chunk that holds the threshold u S,
-//     then the element, and zeroes the sums.
+//     then the element, and zeroes the sums and the record.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -32,6 +33,7 @@ namespace {
 constexpr int VT = 256;             // threads per verifier workgroup
 constexpr int VCHUNKS = 8;          // vocabulary chunks per row (greedy)
 constexpr int PCHUNKS = 32;         // the most vocabulary chunks per row (probabilistic)
+constexpr int RPMAX = 32;           // the longest per-thread run the finisher keeps in LDS
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -171,21 +173,28 @@ __global__ __launch_bounds__(64) void greedy_finish_kernel(const int64_t* draft,
 // iff u_j q_j(d) < p_j(d) in binary64 (both products exact); an id outside
 // [0, V) has p = q = 0.
 // Called by a whole wave: lane j tests proposal j (64 at a time), so the
-// loads of every proposal are in flight together.
+// loads of every proposal are in flight together; the proposals and their
+// uniforms do not wait for L (only their test does).
 __device__ int first_reject(const float* target, const float* draftp, const int64_t* draft,
                             const float* uniforms, int b, int L, int P, int V, int draft_stride) {
   const int lane = threadIdx.x & 63;
-  for (int j0 = 0; j0 < L; j0 += 64) {
+  for (int j0 = 0; j0 < P; j0 += 64) {
     const int j = j0 + lane;
+    int64_t d = -1;
+    float uj = 0.0f;
+    if (j < P) {
+      d = draft[(size_t)b * draft_stride + j];
+      uj = uniforms[(size_t)b * (2 * P + 1) + j];
+    }
+    if (j0 >= L) break;
     bool rej = false;
     if (j < L) {
-      const int64_t d = draft[(size_t)b * draft_stride + j];
       double p = 0.0, q = 0.0;
       if (d >= 0 && d < V) {
         p = (double)target[((size_t)b * (P + 1) + j) * V + d];
         q = (double)draftp[((size_t)b * P + j) * V + d];
       }
-      rej = !((double)uniforms[(size_t)b * (2 * P + 1) + j] * q < p);
+      rej = !((double)uj * q < p);
     }
     const unsigned long long m = __ballot(rej);
     if (m) return j0 + __builtin_ctzll(m);
@@ -250,8 +259,11 @@ __device__ double block_sum(double v, double* red) {
 }
 
 // The binary64 sum, in index order, of the weights of [a, e): 16-byte loads
-// four deep when the rows are 16-byte aligned and a is a multiple of 4.
-__device__ double run_sum(const float* prow, const float* qrow, bool resid, int a, int e) {
+// four deep when the rows are 16-byte aligned and a is a multiple of 4. With
+// STAGE, weight a + k also goes to st[k * VT] (as binary32: the weights are
+// binary32 values, so the conversion back is exact).
+template <bool STAGE>
+__device__ double run_sum(const float* prow, const float* qrow, bool resid, int a, int e, float* st) {
   double s = 0.0;
   const bool vec = ((((uintptr_t)prow) | (uintptr_t)(resid ? qrow : prow)) & 15u) == 0 && (a & 3) == 0;
   int x = a;
@@ -270,12 +282,18 @@ __device__ double run_sum(const float* prow, const float* qrow, bool resid, int 
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float r = resid ? pa[k] - qa[k] : pa[k];
-          s += resid ? (r > 0.0f ? (double)r : 0.0) : (double)r;
+          const float w = resid ? (r > 0.0f ? r : 0.0f) : r;
+          if (STAGE) st[(x - a + 4 * u + k) * VT] = w;
+          s += (double)w;
         }
       }
     }
   }
-  for (; x < e; ++x) s += weight(prow, qrow, resid, x);
+  for (; x < e; ++x) {
+    const double w = weight(prow, qrow, resid, x);
+    if (STAGE) st[(x - a) * VT] = (float)w;
+    s += w;
+  }
   return s;
 }
 
@@ -286,13 +304,17 @@ __device__ double run_sum(const float* prow, const float* qrow, bool resid, int 
 // being non-negative); the thread whose [B_i, B_i+1) holds t walks its run
 // from B_i, and where rounding leaves the walk short of t it takes the run's
 // last weighted id. -1 if no run holds t.
+// Runs of up to RPMAX weights stay in LDS between the sum and the walk.
 __device__ int find_in(const float* prow, const float* qrow, bool resid, int x0, int x1, double base,
                        double t, double* red, int* found) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ double bnd[VT + 1];
+  __shared__ float wst[RPMAX * VT];   // weight a + k of thread tid at [k * VT + tid]
   const int rp = (((x1 - x0 + VT - 1) / VT) + 3) & ~3;   // a multiple of 4
   const int a = min(x1, x0 + tid * rp), e = min(x1, a + rp);
-  const double s = run_sum(prow, qrow, resid, a, e);
+  const bool staged = rp <= RPMAX;   // uniform
+  const double s = staged ? run_sum<true>(prow, qrow, resid, a, e, wst + tid)
+                          : run_sum<false>(prow, qrow, resid, a, e, nullptr);
   // exclusive scan: within the wave by shuffles, then the waves' totals
   double v = s;
 #pragma unroll
@@ -317,19 +339,32 @@ __device__ int find_in(const float* prow, const float* qrow, bool resid, int x0,
   __syncthreads();
   const double b0 = bnd[tid], b1 = bnd[tid + 1];
   if (b0 <= t && t < b1) {
-    // the walk loads 16 weights at a time, all in flight together
+    // the walk over the run: its staged weights, else 16 loads at a time,
+    // all in flight together
     double cum = b0;
     int hit = -1, last = -1;
-    for (int x = a; x < e && hit < 0; x += 16) {
-      double w[16];
+    if (staged) {
+      for (int x = a; x < e; ++x) {
+        const double w = (double)wst[(x - a) * VT + tid];
+        if (w > 0.0) last = x;
+        cum += w;
+        if (cum > t) {
+          hit = x;
+          break;
+        }
+      }
+    } else {
+      for (int x = a; x < e && hit < 0; x += 16) {
+        double w[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) w[k] = x + k < e ? weight(prow, qrow, resid, x + k) : 0.0;
+        for (int k = 0; k < 16; ++k) w[k] = x + k < e ? weight(prow, qrow, resid, x + k) : 0.0;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        if (hit >= 0) break;
-        if (w[k] > 0.0) last = x + k;
-        cum += w[k];
-        if (cum > t) hit = x + k;
+        for (int k = 0; k < 16; ++k) {
+          if (hit >= 0) break;
+          if (w[k] > 0.0) last = x + k;
+          cum += w[k];
+          if (cum > t) hit = x + k;
+        }
       }
     }
     atomicMin(found, hit >= 0 ? hit : last);
@@ -339,10 +374,21 @@ __device__ int find_in(const float* prow, const float* qrow, bool resid, int x0,
   return f == 0x7fffffff || f < 0 ? -1 : f;
 }
 
-// grid: (chunks, B). Workspace: partial sums [B][chunks] f64 (zero between calls).
+// A row's pick, recorded by its first chunk's workgroup: the first rejected
+// proposal j (L if none), whether the row samples the residual (j < L), and
+// the uniform of that sample.
+struct RowPick {
+  int32_t j, resid;
+  float u;
+  int32_t pad;
+};
+
+// grid: (chunks, B). Workspace: partial sums [B][PCHUNKS] f64 (row b's at
+// b * chunks), then the picks [B] (all zero between calls).
 __global__ __launch_bounds__(VT) void prob_accept_kernel(
     const float* target, const float* draftp, const int64_t* draft, const int32_t* lengths,
-    const float* uniforms, double* partial, int P, int V, int draft_stride, int chunks) {
+    const float* uniforms, double* partial, RowPick* pick, int P, int V, int draft_stride,
+    int chunks) {
   const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   __shared__ double red[VT];
   __shared__ int sj;
@@ -355,6 +401,8 @@ __global__ __launch_bounds__(VT) void prob_accept_kernel(
   __syncthreads();
   const int j = sj;
   const bool resid = j < L;
+  if (c == 0 && tid == 0)
+    pick[b] = RowPick{j, resid ? 1 : 0, uniforms[(size_t)b * (2 * P + 1) + (resid ? P + j : 2 * P)], 0};
   const float* prow = target + ((size_t)b * (P + 1) + j) * V;
   const float* qrow = resid ? draftp + ((size_t)b * P + j) * V : nullptr;
   const int per = ((V + 4 * chunks - 1) / (4 * chunks)) * 4;   // a multiple of 4
@@ -364,32 +412,35 @@ __global__ __launch_bounds__(VT) void prob_accept_kernel(
 }
 
 // One workgroup per batch row: S over the chunks in order, the threshold u S,
-// the chunk that holds it, then the element; the chunk sums are re-zeroed.
+// the chunk that holds it, then the element; the chunk sums and the pick are
+// re-zeroed. Everything it needs first (the pick and the sums) comes in one
+// round trip.
 __global__ __launch_bounds__(VT) void prob_finish_kernel(
-    const float* target, const float* draftp, const int64_t* draft, const int32_t* lengths,
-    const float* uniforms, int64_t* accepted, int32_t* accept_len, double* partial, int P, int V,
-    int draft_stride, int chunks) {
+    const float* target, const float* draftp, const int64_t* draft, int64_t* accepted,
+    int32_t* accept_len, double* partial, RowPick* pick, int P, int V, int draft_stride, int chunks) {
   const int b = blockIdx.x, tid = threadIdx.x;
   __shared__ double red[VT];
   __shared__ double csum[PCHUNKS];
-  __shared__ int sj, found;
-  int L = lengths[b];
-  L = L < 0 ? 0 : L > P ? P : L;
-  if (tid < 64) {
-    const int j0 = first_reject(target, draftp, draft, uniforms, b, L, P, V, draft_stride);
-    if (tid == 0) sj = j0;
-  }
+  __shared__ RowPick sp;
+  __shared__ int found;
   if (tid < chunks) csum[tid] = partial[(size_t)b * chunks + tid];   // the wide pass's chunk sums
+  if (tid == 0) sp = pick[b];
   __syncthreads();
-  const int j = sj;
-  const bool resid = j < L;
+  const int j = sp.j;
+  const bool resid = sp.resid != 0;
+  const float u = sp.u;
+  // the accepted drafts, then -1 past the sampled token (in flight during
+  // the search)
+  for (int i = tid; i <= P; i += VT) {
+    if (i < j) accepted[(size_t)b * (P + 1) + i] = draft[(size_t)b * draft_stride + i];
+    else if (i > j) accepted[(size_t)b * (P + 1) + i] = -1;
+  }
   const float* prow = target + ((size_t)b * (P + 1) + j) * V;
   const float* qrow = resid ? draftp + ((size_t)b * P + j) * V : nullptr;
   const int per = ((V + 4 * chunks - 1) / (4 * chunks)) * 4;
   double S = 0.0;
   for (int i = 0; i < chunks; ++i) S += csum[i];
   bool rs = resid;
-  const float u = uniforms[(size_t)b * (2 * P + 1) + (resid ? P + j : 2 * P)];
   int x = -1;
   if (!(S > 0.0) && rs) {       // no residual mass: sample p itself
     rs = false;
@@ -427,13 +478,10 @@ __global__ __launch_bounds__(VT) void prob_finish_kernel(
   } else {
     x = 0;
   }
-  __syncthreads();
   if (tid == 0) {
-    int n = 0;
-    for (int i = 0; i < j; ++i) accepted[(size_t)b * (P + 1) + n++] = draft[(size_t)b * draft_stride + i];
-    accepted[(size_t)b * (P + 1) + n++] = x;
-    for (int i = n; i <= P; ++i) accepted[(size_t)b * (P + 1) + i] = -1;
-    accept_len[b] = n;
+    accepted[(size_t)b * (P + 1) + j] = x;
+    accept_len[b] = j + 1;
+    pick[b] = RowPick{0, 0, 0.0f, 0};
   }
   for (int i = tid; i < chunks; i += VT) partial[(size_t)b * chunks + i] = 0.0;
 }
@@ -441,7 +489,8 @@ __global__ __launch_bounds__(VT) void prob_finish_kernel(
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t greedy_ws(int32_t B, int32_t P) { return ((size_t)B * (P + 1) * 8 + 255) & ~(size_t)255; }
-size_t prob_ws(int32_t B) { return ((size_t)B * PCHUNKS * 8 + 255) & ~(size_t)255; }
+size_t prob_sums_bytes(int32_t B) { return ((size_t)B * PCHUNKS * 8 + 255) & ~(size_t)255; }
+size_t prob_ws(int32_t B) { return prob_sums_bytes(B) + (((size_t)B * sizeof(RowPick) + 255) & ~(size_t)255); }
 
 // chunks of a probabilistic row: about 4096 tokens each, 1 .. PCHUNKS
 int prob_chunks(int32_t V) {
@@ -497,14 +546,15 @@ int markov_prob_accept(const float* target_probs, const float* draft_probs, cons
   if (!aligned16(workspace)) return MARKOV_ERR_ALIGN;
   if (workspace_bytes < markov_verify_workspace_bytes(batch, proposal_len)) return MARKOV_ERR_WORKSPACE;
   double* partial = (double*)workspace;
+  RowPick* pick = (RowPick*)((unsigned char*)workspace + prob_sums_bytes(batch));
   const int chunks = prob_chunks(vocab);
   prob_accept_kernel<<<dim3((unsigned)chunks, (unsigned)batch), VT, 0, (hipStream_t)stream>>>(
-      target_probs, draft_probs, draft, proposal_lengths, uniforms, partial, proposal_len, vocab,
-      draft_stride, chunks);
+      target_probs, draft_probs, draft, proposal_lengths, uniforms, partial, pick, proposal_len,
+      vocab, draft_stride, chunks);
   if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   prob_finish_kernel<<<dim3((unsigned)batch), VT, 0, (hipStream_t)stream>>>(
-      target_probs, draft_probs, draft, proposal_lengths, uniforms, accepted, accept_len, partial,
-      proposal_len, vocab, draft_stride, chunks);
+      target_probs, draft_probs, draft, accepted, accept_len, partial, pick, proposal_len, vocab,
+      draft_stride, chunks);
   if (hipGetLastError() != hipSuccess) return MARKOV_ERR_HIP;
   return MARKOV_OK;
 }
