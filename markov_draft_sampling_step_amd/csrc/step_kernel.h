@@ -968,6 +968,21 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
 #pragma unroll
     for (int j = 0; j < MRB; ++j) {
       const int n = 16 * (wr + RG * j) + m;
+      // block j's base logits of the next unit (a whole unit ahead). With
+      // one row group of 2 or 4 blocks they are requested before the
+      // contraction below: after it, the copy that hands the loop-carried
+      // registers over waits for every load in flight, the next tile
+      // included, which the contraction of the unit's last block has just
+      // requested; before it, the tile streams through the unit's element
+      // work. (Measured: the other plans are as fast or faster with the
+      // request after the contraction, where the earlier requests do not
+      // queue ahead of the tile, vector memory completing in issue order.)
+      constexpr bool EARLY_BASE = RG == 1 && (MRB == 2 || MRB == 4);
+      u32x4_t bv;
+      if constexpr (EARLY_BASE) {
+        bv = bq[j];
+        if (!bias_mode && pnext) fetch_base(j, psl, bq[j]);
+      }
       // the contraction of block j + D (of block j itself when D == 0);
       // once the unit's last one has issued, this buffer's next tile
       if (D == 0) {
@@ -979,11 +994,10 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
         block_bias<KB, W8>(A0[AB], A1[AB], emb, n - m + 16 * RG * D + z0, m, R, g, swz, kzero, cb0[j + D], cb1[j + D]);
         if (LATE && j + D == my_nrb - 1 && ntile) tile(BUF, nsl * SLAB + tw * TOK_PER_WAVE);
       }
-      const u32x4_t bv = bq[j];
-      // block j of the next unit (a whole unit ahead: earlier requests
-      // would queue behind the next tile, vector memory completing in
-      // issue order)
-      if (!bias_mode && pnext) fetch_base(j, psl, bq[j]);
+      if constexpr (!EARLY_BASE) {
+        bv = bq[j];
+        if (!bias_mode && pnext) fetch_base(j, psl, bq[j]);
+      }
       if (j >= my_nrb) continue;
 
       const RowInfo info = ROWREG ? ri[ROWREG ? j : 0] : n_info[n];
