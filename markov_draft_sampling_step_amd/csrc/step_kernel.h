@@ -631,7 +631,8 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   constexpr bool GREEDY = (VAR & V_GREEDY) != 0;
   constexpr bool W8 = (VAR & V_W8) != 0;
   constexpr int NB = MRB == 1 ? 2 : 1;                   // w2 tiles in flight per wave
-  constexpr int D = MRB - 1 < 3 ? MRB - 1 : 3;           // row blocks contracted ahead
+  // row blocks contracted ahead (measured: with 4 blocks, 2 ahead beat 3 and 1)
+  constexpr int D = MRB == 4 ? 2 : MRB - 1 < 3 ? MRB - 1 : 3;
   constexpr int S = RG == 1 ? 2 : 1;                     // waves splitting one SIMD's slabs
   constexpr bool ROWREG = MRB <= 4;                      // row constants in registers
   constexpr bool LIN = RG == 1;                          // the line bound (else the constant)
