@@ -714,6 +714,16 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
       for (int q = 0; q < SG; ++q) slot_in[q] = sp0[(size_t)q * rows];
     }
   }
+  // the transform table's stamp (the three words that say whether the table
+  // serves this launch's (mult, cap)), with the row data: read later, its
+  // loads would wait behind the first tile and the table copies, and so
+  // would the base logits and the gather requested after them
+  uint32_t tts0 = 0u, tts1 = 0u, tts2 = 0u;
+  if (LIN && a.tt_layout != 0) {
+    tts0 = a.ttable[0];
+    tts1 = a.ttable[1];
+    tts2 = a.ttable[2];
+  }
   // the row data, waited for before the table copy is issued: a wait the
   // compiler sees, so that no later use of a row register waits for the copy;
   // the empty asm keeps every use of the four values (the row hash) below it,
@@ -722,6 +732,7 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   asm volatile("" : "+v"(T), "+v"(seed), "+v"(pos), "+v"(tok));
   asm volatile("" : "+v"(slot_in[0]), "+v"(slot_in[1]), "+v"(slot_in[2]), "+v"(slot_in[3]),
                "+v"(slot_in[4]), "+v"(slot_in[5]), "+v"(slot_in[6]), "+v"(slot_in[7]));
+  asm volatile("" : "+v"(tts0), "+v"(tts1), "+v"(tts2));
   static_assert(SG == 8, "the asm above pins SG slot values");
   // the noise bound table, straight into LDS: waited for with the first tile
   // (before the unit loop), in flight through the row set-up
@@ -849,8 +860,8 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   const float mult = a.mult, cap = a.cap, inv_cap = a.inv_cap;
   const bool has_cap = a.has_cap != 0;
   // the transform table in LDS holds this launch's (mult, cap)
-  const bool tt = tt_lay && a.ttable[0] == TT_MAGIC && a.ttable[1] == __float_as_uint(mult) &&
-                  a.ttable[2] == __float_as_uint(cap);
+  const bool tt = tt_lay && (tts0 == TT_MAGIC) & (tts1 == __float_as_uint(mult)) &
+                            (tts2 == __float_as_uint(cap));
   const float pinf = a.inf;
   float v1[MRB], v2[MRB];
   int idt[MRB];
