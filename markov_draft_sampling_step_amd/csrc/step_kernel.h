@@ -699,16 +699,18 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
 #pragma unroll
   for (int q = 0; q < SG; ++q) slot_in[q] = 0ull;
   if (valid) {
+    // the feeding token: prev at step 0, else the previous step's winner
+    // slots (decoded after the wait below). prev is read first and at every
+    // step (the caller's array is always there): requested under the step-0
+    // branch after the loads below, its 64-bit address arithmetic took a
+    // register of a load in flight and waited for it.
+    tok = a.prev[(int64_t)r * a.feed_stride];
     if (!bias_mode && !GREEDY) {
       T = a.temperature[r];
       seed = a.seeds[r];
       pos = a.positions[(int64_t)r * K + s];
     }
-    // the feeding token: prev at step 0, else the previous step's winner
-    // slots (decoded after the wait below)
-    if (feed_prev) {
-      tok = a.prev[(int64_t)r * a.feed_stride];
-    } else {
+    if (!feed_prev) {
       const unsigned long long* sp0 = a.slots + (size_t)((s + 2) % 3) * SG * rows + r;
 #pragma unroll
       for (int q = 0; q < SG; ++q) slot_in[q] = sp0[(size_t)q * rows];
