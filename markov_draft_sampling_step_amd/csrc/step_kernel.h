@@ -631,8 +631,9 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   constexpr bool GREEDY = (VAR & V_GREEDY) != 0;
   constexpr bool W8 = (VAR & V_W8) != 0;
   constexpr int NB = MRB == 1 ? 2 : 1;                   // w2 tiles in flight per wave
-  // row blocks contracted ahead (measured: with 4 blocks, 2 ahead beat 3 and 1)
-  constexpr int D = MRB == 4 ? 2 : MRB - 1 < 3 ? MRB - 1 : 3;
+  // row blocks contracted ahead (measured: with 4 bf16 blocks, 2 ahead beat 3
+  // and 1; the E4M3 plan keeps 3, as with 2 it needs more than 256 registers)
+  constexpr int D = (MRB == 4 && !W8) ? 2 : MRB - 1 < 3 ? MRB - 1 : 3;
   constexpr int S = RG == 1 ? 2 : 1;                     // waves splitting one SIMD's slabs
   constexpr bool ROWREG = MRB <= 4;                      // row constants in registers
   constexpr bool LIN = RG == 1;                          // the line bound (else the constant)
@@ -983,15 +984,16 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
     for (int j = 0; j < MRB; ++j) {
       const int n = 16 * (wr + RG * j) + m;
       // block j's base logits of the next unit (a whole unit ahead). With
-      // one row group of 2 or 4 blocks they are requested before the
+      // one row group of 2 or 4 bf16 blocks they are requested before the
       // contraction below: after it, the copy that hands the loop-carried
       // registers over waits for every load in flight, the next tile
       // included, which the contraction of the unit's last block has just
       // requested; before it, the tile streams through the unit's element
-      // work. (Measured: the other plans are as fast or faster with the
-      // request after the contraction, where the earlier requests do not
-      // queue ahead of the tile, vector memory completing in issue order.)
-      constexpr bool EARLY_BASE = RG == 1 && (MRB == 2 || MRB == 4);
+      // work. (Measured: the other plans, E4M3 ones included, are as fast
+      // or faster with the request after the contraction, where the earlier
+      // requests do not queue ahead of the tile, vector memory completing in
+      // issue order.)
+      constexpr bool EARLY_BASE = RG == 1 && (MRB == 2 || MRB == 4) && !W8;
       u32x4_t bv;
       if constexpr (EARLY_BASE) {
         bv = bq[j];
