@@ -782,7 +782,9 @@ __global__ __launch_bounds__(NTH) void markov_step_kernel(StepArgs a) {
   //    rows). With one row group, only the first wave of each SIMD (the one
   //    with more units) requests it here; the second requests its own after
   //    the embedding gather, so that the gather waits behind half the bytes.
-  const bool tile_first = RG == 2 || sub == 0;   // uniform per wave
+  // (E4M3 tiles are half the bytes: every wave requests its own early, which
+  // measured faster there)
+  const bool tile_first = RG == 2 || sub == 0 || W8;   // uniform per wave
   // bf16 w2: NB tiles of MFMA operands in flight. E4M3 w2: NB raw tiles in
   // flight (codes and scales) and one decoded tile of operands.
   constexpr int NA = W8 ? 1 : NB;
