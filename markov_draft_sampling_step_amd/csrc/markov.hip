@@ -296,8 +296,9 @@ int launch_steps(const Call& c, markov_stream_t stream, const markov_shape_t* sh
   if (!fn) return MARKOV_ERR_ROWS;
   const bool greedy = (c.var & V_GREEDY) != 0;
   const int rp = (sh->rows + 15) & ~15;
-  const bool tt_layout = c.mode != MODE_BIAS && sh->softcap > 0.0f && plan.rg == 1 &&
-                         tt_fits(rp, sh->rank, greedy);
+  // (the kernel reads the table's stamp from the workspace whenever this is set)
+  const bool tt_layout = c.mode != MODE_BIAS && workspace != nullptr && sh->softcap > 0.0f &&
+                         plan.rg == 1 && tt_fits(rp, sh->rank, greedy);
   size_t lds = (tt_layout ? TT_BYTES : 0) + lds_total(rp, sh->rank, greedy);
   const int nslabs = (sh->vocab + SLAB - 1) / SLAB;
   int grid = 0;
